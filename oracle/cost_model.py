@@ -1,0 +1,211 @@
+"""Oracle for the polymerization cost model and its exhaustive search.
+
+TEST INFRASTRUCTURE ONLY: imported by tests (and nothing on the product path).
+It shares no code with the C++ planner; the two only agree on the text format
+of the performance table, which both parse on their own.
+
+Source: MikPoly page, section 3 "polymerization cost model" equations:
+    Cost(S, H) = sum over regions (R_i, K_i) of f_wave * f_pipe
+    f_wave     = ceil(f_parallel(R_i, K_i) / |P_multi|)
+    f_pipe     = g_predict(f_num(R_i, K_i), K_i, H)
+with f_parallel the number of pipeline tasks (output tiles) in region R_i and
+f_num the micro-kernel instances (K steps) one task runs; g_predict is the
+per-micro-kernel table measured offline for t in [1, T]  (section 3
+"micro-kernel performance model", T = 5120 by experience).
+
+Readings where the page is silent (each is listed in the design doc):
+  * |P_multi| for kernel k is slots(k) = CUs x resident workgroups per CU,
+    i.e. the case study's resident-warp count (8 warps/SM on 108 SMs) divided
+    by the warps one workgroup uses.
+  * regions run one after another (additive cost), each as its own launch;
+    a per-launch overhead `launch_us` is added per region (0 reproduces the
+    page's formula exactly).
+  * split-K (not on the page): s splits multiply the tasks by s, divide the K
+    steps per task to ceil(t3/s), and add a reduction term
+    red_launch_us + (2s+1)*4*m*n*batch bytes / red_GBps.
+  * g between measured points is linear; beyond the last point it continues
+    the last segment's slope.
+  * Pattern I: one region = whole output, one kernel.  Pattern II-M (II-N):
+    a cut of the M (N) extent at a multiple of the first kernel's tile, the
+    two parts on two different kernels (the case study's 3072 | 1024 cut).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+
+@dataclasses.dataclass
+class Kernel:
+    name: str
+    uM: int
+    uN: int
+    uK: int
+    wg_per_cu: int
+    pts: List[Tuple[float, float]]  # (t, microseconds) sorted by t
+
+
+@dataclasses.dataclass
+class Table:
+    cus: int
+    launch_us: float
+    red_launch_us: float
+    red_gbps: float
+    splits: List[int]
+    patterns: List[str]
+    kernels: Dict[str, Kernel]
+
+    def slots(self, k: Kernel) -> int:
+        return self.cus * k.wg_per_cu
+
+
+def parse_table(text: str) -> Table:
+    """Parse the line-oriented performance-table text (own parser)."""
+    cus = 0
+    launch = 0.0
+    red_l, red_bw = 0.0, 1.0
+    splits = [1]
+    patterns = ["I", "II-M", "II-N"]
+    kernels: Dict[str, Kernel] = {}
+    gpts: Dict[str, List[Tuple[float, float]]] = {}
+    for raw in text.splitlines():
+        line = raw.split("#", 1)[0].strip()
+        if not line:
+            continue
+        tok = line.split()
+        key = tok[0]
+        if key == "device":
+            cus = int(tok[1])
+        elif key == "launch_us":
+            launch = float(tok[1])
+        elif key == "reduce":
+            red_l, red_bw = float(tok[1]), float(tok[2])
+        elif key == "splitk":
+            splits = [int(x) for x in tok[1:]]
+        elif key == "patterns":
+            patterns = tok[1:]
+        elif key == "kernel":
+            kernels[tok[1]] = Kernel(tok[1], int(tok[2]), int(tok[3]), int(tok[4]), int(tok[5]), [])
+        elif key == "g":
+            pts = []
+            for p in tok[2:]:
+                t, v = p.split(":")
+                pts.append((float(t), float(v)))
+            gpts.setdefault(tok[1], []).extend(pts)
+        else:
+            raise ValueError(f"unknown table line: {raw!r}")
+    for name, pts in gpts.items():
+        kernels[name].pts = sorted(pts)
+    for k in kernels.values():
+        if not k.pts:
+            raise ValueError(f"kernel {k.name} has no g points")
+    return Table(cus, launch, red_l, red_bw, splits, patterns, kernels)
+
+
+def g_predict(k: Kernel, t: float) -> float:
+    """Time of one wave of tasks that each run t micro-kernel instances."""
+    pts = k.pts
+    if len(pts) == 1 or t <= pts[0][0]:
+        if len(pts) == 1:
+            return pts[0][1] * t / pts[0][0]
+        return pts[0][1]
+    for (t0, v0), (t1, v1) in zip(pts, pts[1:]):
+        if t <= t1:
+            return v0 + (v1 - v0) * (t - t0) / (t1 - t0)
+    (t0, v0), (t1, v1) = pts[-2], pts[-1]
+    return v1 + (v1 - v0) * (t - t1) / (t1 - t0)
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def split_steps(t3: int, s: int) -> Tuple[int, int]:
+    """(K steps per split, splits actually used) for a requested factor s."""
+    per = ceil_div(t3, s)
+    return per, ceil_div(t3, per)
+
+
+@dataclasses.dataclass(frozen=True)
+class Region:
+    m0: int
+    n0: int
+    m: int
+    n: int
+    kernel: str
+    s: int
+
+
+def region_cost(tab: Table, r: Region, K: int, batch: int) -> float:
+    k = tab.kernels[r.kernel]
+    t3 = ceil_div(K, k.uK)
+    per, s_eff = split_steps(t3, r.s)
+    f_parallel = ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch
+    f_wave = ceil_div(f_parallel, tab.slots(k))
+    f_pipe = g_predict(k, per)
+    c = tab.launch_us + f_wave * f_pipe
+    if s_eff > 1:
+        c += tab.red_launch_us + (2 * s_eff + 1) * 4.0 * r.m * r.n * batch / (tab.red_gbps * 1e3)
+    return c
+
+
+def plan_cost(tab: Table, regions: Sequence[Region], K: int, batch: int) -> float:
+    return sum(region_cost(tab, r, K, batch) for r in regions)
+
+
+def _valid_splits(tab: Table, k: Kernel, K: int) -> List[int]:
+    t3 = ceil_div(K, k.uK)
+    return [s for s in tab.splits if 1 <= s <= max(t3, 1)]
+
+
+def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1):
+    """Every candidate strategy of the search space, no pruning."""
+    names = sorted(tab.kernels)
+    if "I" in tab.patterns:
+        for a in names:
+            for s in _valid_splits(tab, tab.kernels[a], K):
+                yield "I", (Region(0, 0, M, N, a, s),)
+    for pat, ext, tile_of in (("II-M", M, lambda k: k.uM), ("II-N", N, lambda k: k.uN)):
+        if pat not in tab.patterns:
+            continue
+        for a in names:
+            ka = tab.kernels[a]
+            step = tile_of(ka)
+            for cut in range(step, ext, step):
+                for b in names:
+                    if b == a:
+                        continue
+                    for s1 in _valid_splits(tab, ka, K):
+                        for s2 in _valid_splits(tab, tab.kernels[b], K):
+                            if pat == "II-M":
+                                r1 = Region(0, 0, cut, N, a, s1)
+                                r2 = Region(cut, 0, M - cut, N, b, s2)
+                            else:
+                                r1 = Region(0, 0, M, cut, a, s1)
+                                r2 = Region(0, cut, M, N - cut, b, s2)
+                            yield pat, (r1, r2)
+
+
+def exhaustive_best(tab: Table, M: int, N: int, K: int, batch: int = 1):
+    """Minimum modelled cost over the whole space (the page's ORACLE variant
+    searches exhaustively; here only the modelled cost is minimised)."""
+    best: Optional[Tuple[float, str, tuple]] = None
+    for pat, regs in enumerate_plans(tab, M, N, K, batch):
+        c = plan_cost(tab, regs, K, batch)
+        if best is None or c < best[0]:
+            best = (c, pat, regs)
+    return best
+
+
+def covers_exactly(M: int, N: int, regions: Sequence[Region], tiles: Dict[str, Tuple[int, int]]) -> bool:
+    """Count, per output element, how many tiles of the plan write it (brute force)."""
+    import numpy as np
+
+    cnt = np.zeros((M, N), dtype=np.int32)
+    for r in regions:
+        uM, uN = tiles[r.kernel]
+        for i0 in range(r.m0, r.m0 + r.m, uM):
+            for j0 in range(r.n0, r.n0 + r.n, uN):
+                cnt[i0:min(i0 + uM, r.m0 + r.m), j0:min(j0 + uN, r.n0 + r.n)] += 1
+    return bool((cnt == 1).all())

@@ -1,0 +1,113 @@
+"""Pins of the cost-model oracle against the MikPoly page's own arithmetic
+(section 6 case study, stored with its citation in
+tests/golden/mikpoly_case_study.json) and against brute-force invariants."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import cost_model as cm
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "mikpoly_case_study.json")
+
+
+def case_table(Ta, Tb, launch=0.0, patterns="I II-M II-N"):
+    gold = json.load(open(GOLD))
+    sms = gold["sms"]
+    per_sm = gold["resident_warps_per_sm"]
+    A, B = gold["kernel_A"], gold["kernel_B"]
+    # workgroups resident per SM = resident warps / warps per workgroup
+    wa = per_sm // A["warps"]
+    wb = per_sm // B["warps"]
+    fa = gold["shape"][2] // A["tile"][2]  # K steps of A = 128
+    fb = gold["shape"][2] // B["tile"][2]  # K steps of B = 64
+    text = f"""
+device {sms}
+launch_us {launch}
+splitk 1
+patterns {patterns}
+kernel A {A['tile'][0]} {A['tile'][1]} {A['tile'][2]} {wa}
+kernel B {B['tile'][0]} {B['tile'][1]} {B['tile'][2]} {wb}
+g A 1:{Ta / fa} {fa}:{Ta}
+g B 1:{Tb / fb} {fb}:{Tb}
+"""
+    return cm.parse_table(text), gold
+
+
+def test_case_study_wave_arithmetic():
+    tab, gold = case_table(10.0, 3.0)
+    M, N, K = gold["shape"]
+    kA, kB = tab.kernels["A"], tab.kernels["B"]
+    # slots per kernel reproduce the page's resident-warp counts
+    assert tab.slots(kA) * gold["kernel_A"]["warps"] == gold["warps_per_wave"]
+    assert tab.slots(kB) * gold["kernel_B"]["warps"] == gold["warps_per_wave"]
+    tasks_a = math.ceil(M / kA.uM) * math.ceil(N / kA.uN)
+    assert tasks_a == gold["single_A"]["tasks"]
+    assert tasks_a * gold["kernel_A"]["warps"] == gold["single_A"]["warps"]
+    assert math.ceil(tasks_a / tab.slots(kA)) == gold["single_A"]["waves"]
+    cut = gold["pattern_II"]["cut_m"]
+    t1 = math.ceil(cut / kA.uM) * math.ceil(N / kA.uN)
+    t2 = math.ceil((M - cut) / kB.uM) * math.ceil(N / kB.uN)
+    assert t1 == gold["pattern_II"]["region_1"]["tasks"]
+    assert t2 == gold["pattern_II"]["region_2"]["tasks"]
+    warps = t1 * gold["kernel_A"]["warps"] + t2 * gold["kernel_B"]["warps"]
+    assert warps == gold["pattern_II"]["total_warps"]
+    assert math.ceil(warps / gold["warps_per_wave"]) == gold["pattern_II"]["waves"]
+
+
+@pytest.mark.parametrize("Ta,Tb", [(10.0, 3.0), (10.0, 4.9), (10.0, 5.1), (10.0, 8.0)])
+def test_case_study_costs(Ta, Tb):
+    tab, gold = case_table(Ta, Tb)
+    M, N, K = gold["shape"]
+    cut = gold["pattern_II"]["cut_m"]
+    single = cm.plan_cost(tab, [cm.Region(0, 0, M, N, "A", 1)], K, 1)
+    poly = cm.plan_cost(tab, [cm.Region(0, 0, cut, N, "A", 1), cm.Region(cut, 0, M - cut, N, "B", 1)], K, 1)
+    assert single == pytest.approx(2 * Ta, rel=1e-12)
+    assert poly == pytest.approx(Ta + 2 * Tb, rel=1e-12)
+    assert single / poly == pytest.approx(2 * Ta / (Ta + 2 * Tb), rel=1e-12)
+    # the page's choice between the two: polymerize iff Ta > 2 Tb
+    assert (poly < single) == (Ta > 2 * Tb)
+    # the exhaustive search over the whole space is never worse than either
+    best = cm.exhaustive_best(tab, M, N, K)
+    assert best[0] <= min(single, poly) + 1e-9
+
+
+def test_g_interpolation():
+    tab = cm.parse_table("device 4\nkernel X 16 16 16 1\ng X 1:2 4:5 8:13\n")
+    k = tab.kernels["X"]
+    assert cm.g_predict(k, 1) == 2 and cm.g_predict(k, 4) == 5 and cm.g_predict(k, 8) == 13
+    assert cm.g_predict(k, 2) == pytest.approx(3.0)
+    assert cm.g_predict(k, 6) == pytest.approx(9.0)
+    assert cm.g_predict(k, 10) == pytest.approx(17.0)
+
+
+def test_split_accounting():
+    assert cm.split_steps(10, 4) == (3, 4)
+    assert cm.split_steps(10, 8) == (2, 5)
+    assert cm.split_steps(64, 16) == (4, 16)
+    tab = cm.parse_table("device 8\nsplitk 1 2 4\nreduce 1.0 1000\nkernel X 16 16 16 1\ng X 1:1 100:100\n")
+    c1 = cm.region_cost(tab, cm.Region(0, 0, 16, 16, "X", 1), 160, 1)
+    c2 = cm.region_cost(tab, cm.Region(0, 0, 16, 16, "X", 2), 160, 1)
+    assert c1 == pytest.approx(10.0)
+    assert c2 == pytest.approx(5.0 + 1.0 + 5 * 4 * 256 / 1e6)
+
+
+def test_plans_cover_output_exactly():
+    tab = cm.parse_table("""device 4
+splitk 1 2
+kernel P 32 16 16 1
+kernel Q 16 32 16 2
+g P 1:1 10:8
+g Q 1:0.7 10:5
+""")
+    tiles = {n: (k.uM, k.uN) for n, k in tab.kernels.items()}
+    rng = np.random.default_rng(3)
+    for _ in range(6):
+        M, N, K = (int(x) for x in rng.integers(1, 90, size=3))
+        count = 0
+        for pat, regs in cm.enumerate_plans(tab, M, N, K):
+            assert cm.covers_exactly(M, N, regs, tiles), (pat, regs)
+            count += 1
+        assert count > 0
