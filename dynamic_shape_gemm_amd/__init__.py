@@ -1,0 +1,192 @@
+"""Python binding of libmkp (run-time polymerized dense GEMM for MI355X).
+
+Argument marshalling only: every step of the GEMM (plan lookup, the
+polymerizer, every kernel) runs inside libmkp.so.  PyTorch is used only to
+hand over device pointers and the current HIP stream.  If the library has not
+been built this module raises on import: there is no fallback path.
+
+Names follow the C-ABI in include/mkp.h: mkp_gemm(M,N,K,A,lda,B,ldb,C,ldc,
+stream) and mkp_gemm_batched(...).
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmkp.so")
+
+MKP_OK = 0
+MKP_ERR_INVALID_ARG = -1
+MKP_ERR_UNSUPPORTED = -2
+MKP_ERR_OOM = -3
+MKP_ERR_HIP = -4
+MKP_ERR_BUFFER = -5
+
+
+class MkpError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mkp error {code}: {msg}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python dynamic_shape_gemm_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _p, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_lib.mkp_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.mkp_gemm.restype = _int
+_lib.mkp_gemm_batched.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
+_lib.mkp_gemm_batched.restype = _int
+_lib.mkp_plan_describe.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.c_char_p, ctypes.c_size_t]
+_lib.mkp_plan_describe.restype = _int
+_lib.mkp_plan_with_table.argtypes = [ctypes.c_char_p, _int, _i64, _i64, _i64, _i64, ctypes.c_char_p, ctypes.c_size_t]
+_lib.mkp_plan_with_table.restype = _int
+_lib.mkp_load_calibration.argtypes = [ctypes.c_char_p]
+_lib.mkp_load_calibration.restype = _int
+_lib.mkp_calibrate.argtypes = [ctypes.c_char_p, _int]
+_lib.mkp_calibrate.restype = _int
+_lib.mkp_set_option.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
+_lib.mkp_set_option.restype = _int
+_lib.mkp_kernel_count.argtypes = []
+_lib.mkp_kernel_count.restype = _int
+_lib.mkp_kernel_name.argtypes = [_int]
+_lib.mkp_kernel_name.restype = ctypes.c_char_p
+_lib.mkp_cache_clear.argtypes = []
+_lib.mkp_cache_clear.restype = None
+_lib.mkp_stats.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+_lib.mkp_stats.restype = _int
+_lib.mkp_trace_dump.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+_lib.mkp_trace_dump.restype = _int
+_lib.mkp_last_error.argtypes = []
+_lib.mkp_last_error.restype = ctypes.c_char_p
+
+EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_plan_describe", "mkp_plan_with_table", "mkp_load_calibration",
+            "mkp_calibrate", "mkp_set_option", "mkp_kernel_count", "mkp_kernel_name", "mkp_cache_clear",
+            "mkp_stats", "mkp_trace_dump", "mkp_last_error"]
+
+
+def last_error() -> str:
+    return (_lib.mkp_last_error() or b"").decode()
+
+
+def _check(rc: int) -> int:
+    if rc != MKP_OK:
+        raise MkpError(rc, last_error())
+    return rc
+
+
+def _addr(x) -> int:
+    """Device address of a torch tensor, or an int address as given."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def mkp_gemm(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    """C[MxN] := A[MxK] . B[KxN] (bf16 in, fp32 out), enqueued on `stream`
+    (default: torch's current stream).  Raises MkpError on a bad argument."""
+    return _check(_lib.mkp_gemm(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)))
+
+
+def mkp_gemm_batched(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream=None) -> int:
+    return _check(_lib.mkp_gemm_batched(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB, _addr(C),
+                                        ldc, strideC, _stream(stream)))
+
+
+def mkp_gemm_raw(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    """As mkp_gemm but returns the status code instead of raising."""
+    return _lib.mkp_gemm(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, stream or 0)
+
+
+def mkp_gemm_batched_raw(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream) -> int:
+    return _lib.mkp_gemm_batched(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC,
+                                 stream or 0)
+
+
+def _text_call(fn, *args, size=1 << 16):
+    buf = ctypes.create_string_buffer(size)
+    _check(fn(*args, buf, size))
+    return buf.value.decode()
+
+
+def mkp_plan_describe(batch, M, N, K, align_flags=7) -> dict:
+    return json.loads(_text_call(_lib.mkp_plan_describe, batch, M, N, K, align_flags))
+
+
+def mkp_plan_with_table(table_text: str, batch, M, N, K, exhaustive=False) -> dict:
+    return json.loads(_text_call(_lib.mkp_plan_with_table, table_text.encode(), 1 if exhaustive else 0,
+                                 batch, M, N, K))
+
+
+def mkp_load_calibration(path=None) -> int:
+    return _check(_lib.mkp_load_calibration(path.encode() if path else None))
+
+
+def mkp_calibrate(path: str, max_points: int = 0) -> int:
+    return _check(_lib.mkp_calibrate(path.encode(), max_points))
+
+
+def mkp_set_option(key: str, value) -> int:
+    return _check(_lib.mkp_set_option(key.encode(), str(value).encode()))
+
+
+def mkp_kernel_names() -> list:
+    return [_lib.mkp_kernel_name(i).decode() for i in range(_lib.mkp_kernel_count())]
+
+
+def mkp_cache_clear() -> None:
+    _lib.mkp_cache_clear()
+
+
+def mkp_stats() -> dict:
+    return json.loads(_text_call(_lib.mkp_stats))
+
+
+def mkp_trace_dump() -> list:
+    return json.loads(_text_call(_lib.mkp_trace_dump, size=1 << 24))
+
+
+def gemm(a, b, out=None, stream=None):
+    """torch convenience: a (M,K) bf16, b (K,N) bf16 on the GPU, any strides
+    with unit column stride; returns (or fills) out (M,N) fp32."""
+    import torch
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("a and b must be bfloat16")
+    if a.stride(1) != 1 or b.stride(1) != 1:
+        raise ValueError("rows must be contiguous (unit column stride)")
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    mkp_gemm(M, N, K, a, max(a.stride(0), 1), b, max(b.stride(0), 1), out, max(out.stride(0), 1), stream)
+    return out
+
+
+def gemm_batched(a, b, out=None, stream=None):
+    """torch convenience: a (batch,M,K), b (batch,K,N) bf16 -> out (batch,M,N) fp32."""
+    import torch
+    batch, M, K = a.shape
+    N = b.shape[2]
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=torch.float32, device=a.device)
+    mkp_gemm_batched(batch, M, N, K, a, max(a.stride(1), 1), a.stride(0), b, max(b.stride(1), 1), b.stride(0),
+                     out, max(out.stride(1), 1), out.stride(0), stream)
+    return out

@@ -1,0 +1,745 @@
+// C-ABI of the polymerized GEMM library: argument checks, plan cache,
+// split-K workspaces, region launches and the offline calibration.
+//
+// Flow per call (MikPoly page, section 3 "complete algorithm" and section 4
+// GPU platform): the shape becomes known -> the cached strategy for it is
+// looked up, or built by the cost-model search on a miss -> every region's
+// fixed-size micro-kernel is launched with the region's start addresses and
+// trip counts as scalars; the hardware scheduler deals workgroups to CUs.
+#include <dlfcn.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <functional>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <shared_mutex>
+#include <sstream>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/mkp.h"
+#include "kernels.h"
+#include "planner.h"
+
+namespace mkp {
+namespace {
+
+thread_local std::string t_last_error;
+
+int fail(int code, const std::string& msg) {
+    t_last_error = msg;
+    return code;
+}
+
+struct Key {
+    int64_t batch, M, N, K;
+    int align, device;
+    bool operator==(const Key& o) const {
+        return batch == o.batch && M == o.M && N == o.N && K == o.K && align == o.align && device == o.device;
+    }
+};
+struct KeyHash {
+    size_t operator()(const Key& k) const {
+        uint64_t h = 1469598103934665603ull;
+        auto mix = [&](uint64_t v) {
+            h ^= v;
+            h *= 1099511628211ull;
+        };
+        mix((uint64_t)k.batch);
+        mix((uint64_t)k.M);
+        mix((uint64_t)k.N);
+        mix((uint64_t)k.K);
+        mix((uint64_t)k.align);
+        mix((uint64_t)k.device);
+        return (size_t)h;
+    }
+};
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+struct TraceRec {
+    int kernel;            // library kernel index, -1 = split-K reduction, -2 = zero fill
+    double flops, bytes;   // algorithmic work of the launch
+    hipEvent_t e0, e1;
+};
+
+struct Library {
+    std::shared_mutex mu;                         // guards table, opts, cache
+    PerfTable table;
+    std::string table_origin = "analytic";
+    SearchOptions opts;
+    std::unordered_map<Key, std::shared_ptr<const Plan>, KeyHash> cache;
+    size_t cache_cap = 1 << 16;
+
+    std::mutex ws_mu;
+    std::map<std::pair<int, void*>, Workspace> workspaces;
+
+    std::atomic<int64_t> hits{0}, misses{0}, launches{0};
+    std::atomic<int64_t> plan_ns{0};
+
+    std::atomic<bool> trace{false};               // time every launch with events
+    std::mutex trace_mu;
+    std::vector<TraceRec> trace_recs;
+};
+
+Library& lib() {
+    static Library* L = new Library();  // never destroyed: safe at process exit
+    return *L;
+}
+
+// ---- tables -----------------------------------------------------------------
+
+// Analytic stand-in used until a measured table is loaded: MFMA time at a
+// tile-size dependent efficiency vs. operand traffic, per K step.
+PerfTable analytic_table() {
+    PerfTable t;
+    t.cus = 256;
+    t.launch_us = 2.0;
+    t.red_launch_us = 2.0;
+    t.red_gbps = 4000.0;
+    t.splits = {1, 2, 4, 8, 16, 32};
+    for (int i = 0; i < kernel_count(); ++i) {
+        const KernelInfo& ki = kernel_info(i);
+        TableKernel k;
+        k.name = ki.name;
+        k.uM = ki.uM;
+        k.uN = ki.uN;
+        k.uK = ki.uK;
+        k.lib_index = i;
+        int by_lds = std::max(1, (160 * 1024) / std::max(ki.lds_bytes, 1));
+        k.wg_per_cu = std::min(by_lds, 2);
+        const double slots = (double)t.cus * k.wg_per_cu;
+        const double area = (double)ki.uM * ki.uN;
+        const double eff = 0.7 * std::min(1.0, std::pow(area / (256.0 * 256.0), 0.25));
+        const double cu_rate = 4096.0 * 2400.0 * eff;                   // FLOP per us per CU
+        const double t_c = k.wg_per_cu * 2.0 * ki.uM * ki.uN * ki.uK / cu_rate;
+        const double t_m = slots * 2.0 * (ki.uM + ki.uN) * ki.uK / 12.0e6;  // ~12 TB/s via L2
+        const double step = std::max(t_c, t_m);
+        const double epi = slots * 4.0 * ki.uM * ki.uN / 6.0e6 + 0.5;
+        for (int tt : {1, 2, 4, 8, 16, 32, 64, 128, 256}) k.pts.emplace_back((double)tt, epi + tt * step);
+        t.kernels.push_back(k);
+    }
+    return t;
+}
+
+// Resolve table kernel names to library kernels.
+bool bind_table(PerfTable& t, std::string& err) {
+    for (auto& k : t.kernels) {
+        k.lib_index = kernel_find(k.name.c_str());
+        if (k.lib_index < 0) {
+            err = "table names kernel '" + k.name + "' that the library does not have";
+            return false;
+        }
+        const KernelInfo& ki = kernel_info(k.lib_index);
+        if (ki.uM != k.uM || ki.uN != k.uN || ki.uK != k.uK) {
+            err = "table tile of kernel '" + k.name + "' differs from the library's";
+            return false;
+        }
+    }
+    return true;
+}
+
+std::string default_table_path() {
+    if (const char* e = std::getenv("MKP_CALIB")) return e;
+    Dl_info info;
+    if (dladdr((void*)&default_table_path, &info) && info.dli_fname) {
+        std::string so = info.dli_fname;
+        auto slash = so.rfind('/');
+        std::string dir = slash == std::string::npos ? "." : so.substr(0, slash);
+        return dir + "/calib/gfx950.tbl";
+    }
+    return "calib/gfx950.tbl";
+}
+
+bool read_file(const std::string& path, std::string& out) {
+    std::ifstream f(path);
+    if (!f) return false;
+    std::stringstream ss;
+    ss << f.rdbuf();
+    out = ss.str();
+    return true;
+}
+
+// Load the table at `path` (or the shipped one) into the library; caller holds the lock.
+int load_table_locked(Library& L, const char* path, bool quiet_missing) {
+    std::string p = path ? std::string(path) : default_table_path();
+    std::string text, err;
+    if (!read_file(p, text)) {
+        if (quiet_missing) {
+            L.table = analytic_table();
+            L.table_origin = "analytic";
+            L.cache.clear();
+            return MKP_OK;
+        }
+        return fail(MKP_ERR_INVALID_ARG, "cannot read performance table " + p);
+    }
+    PerfTable t;
+    if (!parse_table(text, t, err) || !bind_table(t, err))
+        return fail(MKP_ERR_INVALID_ARG, "performance table " + p + ": " + err);
+    L.table = t;
+    L.table_origin = p;
+    L.cache.clear();
+    return MKP_OK;
+}
+
+void read_env_options(Library& L) {
+    if (const char* e = std::getenv("MKP_PATTERNS")) L.opts.allow_II = std::strstr(e, "II") != nullptr;
+    if (const char* e = std::getenv("MKP_SPLITK_MAX")) L.opts.splitk_max = std::max(1, std::atoi(e));
+    if (const char* e = std::getenv("MKP_FORCE_SPLITK")) L.opts.force_splitk = std::max(0, std::atoi(e));
+    if (const char* e = std::getenv("MKP_CACHE_CAP")) L.cache_cap = (size_t)std::max(1, std::atoi(e));
+    if (const char* e = std::getenv("MKP_FORCE_KERNEL")) {
+        for (size_t i = 0; i < L.table.kernels.size(); ++i)
+            if (L.table.kernels[i].name == e) L.opts.force_kernel = (int)i;
+    }
+}
+
+std::once_flag g_init;
+void ensure_init() {
+    std::call_once(g_init, [] {
+        Library& L = lib();
+        std::unique_lock<std::shared_mutex> lk(L.mu);
+        if (load_table_locked(L, nullptr, true) != MKP_OK) {
+            L.table = analytic_table();
+            L.table_origin = "analytic";
+        }
+        read_env_options(L);
+    });
+}
+
+// ---- plans ------------------------------------------------------------------
+
+std::shared_ptr<const Plan> get_plan(const Key& key) {
+    Library& L = lib();
+    {
+        std::shared_lock<std::shared_mutex> lk(L.mu);
+        auto it = L.cache.find(key);
+        if (it != L.cache.end()) {
+            L.hits.fetch_add(1, std::memory_order_relaxed);
+            return it->second;
+        }
+    }
+    std::unique_lock<std::shared_mutex> lk(L.mu);
+    auto it = L.cache.find(key);
+    if (it != L.cache.end()) {
+        L.hits.fetch_add(1, std::memory_order_relaxed);
+        return it->second;
+    }
+    auto plan = std::make_shared<Plan>(polymerize(L.table, key.batch, key.M, key.N, key.K, L.opts));
+    L.misses.fetch_add(1, std::memory_order_relaxed);
+    L.plan_ns.fetch_add((int64_t)(plan->plan_us * 1000.0), std::memory_order_relaxed);
+    if (L.cache.size() >= L.cache_cap) L.cache.clear();
+    L.cache.emplace(key, plan);
+    return plan;
+}
+
+// ---- workspaces -------------------------------------------------------------
+
+int get_workspace(int dev, hipStream_t st, size_t bytes, void** out) {
+    Library& L = lib();
+    std::lock_guard<std::mutex> lk(L.ws_mu);
+    Workspace& w = L.workspaces[{dev, (void*)st}];
+    if (w.bytes < bytes) {
+        size_t want = std::max(bytes, w.bytes * 2);
+        want = (want + 4095) & ~(size_t)4095;
+        if (w.ptr) {
+            hipError_t e = hipFreeAsync(w.ptr, st);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+        }
+        void* p = nullptr;
+        hipError_t e = hipMallocAsync(&p, want, st);
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(MKP_ERR_OOM, "split-K workspace of " + std::to_string(want) + " bytes: allocation failed");
+        }
+        w.ptr = p;
+        w.bytes = want;
+    }
+    *out = w.ptr;
+    return MKP_OK;
+}
+
+void free_workspaces() {
+    Library& L = lib();
+    std::lock_guard<std::mutex> lk(L.ws_mu);
+    if (L.workspaces.empty()) return;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (auto& kv : L.workspaces) {
+        if (!kv.second.ptr) continue;
+        (void)hipSetDevice(kv.first.first);
+        (void)hipDeviceSynchronize();
+        (void)hipFree(kv.second.ptr);
+    }
+    (void)hipSetDevice(cur);
+    L.workspaces.clear();
+}
+
+// ---- dispatch ---------------------------------------------------------------
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Run one launch; in trace mode bracket it with events on the same stream.
+template <class F>
+hipError_t traced(Library& L, hipStream_t st, int kernel, double flops, double bytes, F&& fn) {
+    if (!L.trace.load(std::memory_order_relaxed)) return fn();
+    TraceRec r{kernel, flops, bytes, nullptr, nullptr};
+    if (hipEventCreate(&r.e0) != hipSuccess || hipEventCreate(&r.e1) != hipSuccess) return fn();
+    (void)hipEventRecord(r.e0, st);
+    hipError_t e = fn();
+    (void)hipEventRecord(r.e1, st);
+    std::lock_guard<std::mutex> lk(L.trace_mu);
+    L.trace_recs.push_back(r);
+    return e;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int64_t lda, int64_t sA,
+             const void* Bv, int64_t ldb, int64_t sB, float* C, int64_t ldc, int64_t sC, void* stream_v) {
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "dimension exceeds 2^31-1");
+    if (batch == 0 || M == 0 || N == 0) return MKP_OK;
+    if (K > 0 && lda < K) return fail(MKP_ERR_INVALID_ARG, "lda < K");
+    if (K > 0 && ldb < N) return fail(MKP_ERR_INVALID_ARG, "ldb < N");
+    if (ldc < N) return fail(MKP_ERR_INVALID_ARG, "ldc < N");
+    if (!C) return fail(MKP_ERR_INVALID_ARG, "C is NULL");
+    if (K > 0 && (!Av || !Bv)) return fail(MKP_ERR_INVALID_ARG, "A or B is NULL");
+    if (batch > 1 && (sA < 0 || sB < 0 || sC < 0)) return fail(MKP_ERR_INVALID_ARG, "negative batch stride");
+    ensure_init();
+    hipStream_t st = (hipStream_t)stream_v;
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
+
+    Library& L = lib();
+    if (K == 0) {
+        he = traced(L, st, -2, 0.0, 4.0 * M * N * batch,
+                    [&] { return launch_zero_fill(C, ldc, sC, (int)M, (int)N, (int)batch, st); });
+        if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("zero fill launch: ") + hipGetErrorString(he));
+        L.launches.fetch_add(1, std::memory_order_relaxed);
+        return MKP_OK;
+    }
+    if (batch > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "batch exceeds 2^31-1");
+
+    const uint16_t* A = (const uint16_t*)Av;
+    const uint16_t* B = (const uint16_t*)Bv;
+    const bool vA = aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0);
+    const bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0);
+    const bool vC = aligned16(C) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
+    const int align = (vA ? 1 : 0) | (vB ? 2 : 0) | (vC ? 4 : 0);
+
+    Key key{batch, M, N, K, align, dev};
+    std::shared_ptr<const Plan> plan = get_plan(key);
+    if (plan->regions.empty()) return fail(MKP_ERR_UNSUPPORTED, "no plan for this shape");
+
+    // workspace for split regions (regions run in order on one stream and share it)
+    size_t ws_bytes = 0;
+    for (auto& r : plan->regions)
+        if (r.s > 1) {
+            const int64_t ldw = (r.n + 3) & ~int64_t(3);
+            ws_bytes = std::max(ws_bytes, (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float));
+        }
+    void* ws = nullptr;
+    if (ws_bytes) {
+        int rc = get_workspace(dev, st, ws_bytes, &ws);
+        if (rc != MKP_OK) return rc;
+    }
+
+    for (size_t i = 0; i < plan->regions.size(); ++i) {
+        const Region& r = plan->regions[i];
+        const int li = r.lib;
+        if (li < 0 || li >= kernel_count()) return fail(MKP_ERR_UNSUPPORTED, "plan kernel is not launchable");
+        const KernelInfo& ki = kernel_info(li);
+        KArgs a;
+        a.A = A + r.m0 * lda;
+        a.B = B + r.n0;
+        a.lda = lda;
+        a.ldb = ldb;
+        a.sA = sA;
+        a.sB = sB;
+        a.M = (int)r.m;
+        a.N = (int)r.n;
+        a.K = (int)K;
+        a.tiles_m = (int)ceil_div(r.m, ki.uM);
+        a.tiles_n = (int)ceil_div(r.n, ki.uN);
+        a.steps_per_split = r.steps;
+        a.splits = r.s;
+        a.batch = (int)batch;
+        a.flags = (vA ? KF_VEC_A : 0) | (vB ? KF_VEC_B : 0);
+        float* Creg = C + r.m0 * ldc + r.n0;
+        const int64_t ldw = (r.n + 3) & ~int64_t(3);
+        if (r.s == 1) {
+            a.C = Creg;
+            a.ldc = ldc;
+            a.sC = sC;
+            a.sCsplit = 0;
+            a.flags |= vC ? KF_VEC_C : 0;
+        } else {
+            a.C = (float*)ws;
+            a.ldc = ldw;
+            a.sC = r.m * ldw;
+            a.sCsplit = batch * r.m * ldw;
+            a.flags |= KF_VEC_C;
+        }
+        const int64_t G = (int64_t)a.tiles_m * a.tiles_n * a.splits * batch;
+        if (G > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
+        const double flops = 2.0 * r.m * r.n * K * batch;
+        const double bytes = (double)batch * (2.0 * r.m * K + 2.0 * K * r.n + 4.0 * r.m * r.n);
+        he = traced(L, st, li, flops, bytes, [&] { return ki.launch(a, dim3((unsigned)G), st); });
+        if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
+        L.launches.fetch_add(1, std::memory_order_relaxed);
+        if (r.s > 1) {
+            he = traced(L, st, -1, 0.0, (double)(r.s + 1) * 4.0 * r.m * r.n * batch, [&] {
+                return launch_splitk_reduce((const float*)ws, r.s, batch * r.m * ldw, r.m * ldw, ldw, Creg, ldc, sC,
+                                            (int)r.m, (int)r.n, (int)batch, vC ? 1 : 0, st);
+            });
+            if (he != hipSuccess)
+                return fail(MKP_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
+            L.launches.fetch_add(1, std::memory_order_relaxed);
+        }
+    }
+    return MKP_OK;
+}
+
+int write_out(const std::string& s, char* buf, size_t len) {
+    if (!buf || len == 0) return fail(MKP_ERR_BUFFER, "output buffer is empty");
+    if (s.size() + 1 > len) {
+        std::memcpy(buf, s.data(), len - 1);
+        buf[len - 1] = 0;
+        return fail(MKP_ERR_BUFFER, "output buffer too small: need " + std::to_string(s.size() + 1));
+    }
+    std::memcpy(buf, s.c_str(), s.size() + 1);
+    return MKP_OK;
+}
+
+// ---- calibration ------------------------------------------------------------
+
+double time_launches(const std::function<hipError_t()>& fn, int warm, int reps, hipError_t* err) {
+    *err = hipSuccess;
+    for (int i = 0; i < warm; ++i)
+        if ((*err = fn()) != hipSuccess) return 0;
+    hipEvent_t e0, e1;
+    (void)hipEventCreate(&e0);
+    (void)hipEventCreate(&e1);
+    (void)hipEventRecord(e0, nullptr);
+    for (int i = 0; i < reps; ++i)
+        if ((*err = fn()) != hipSuccess) break;
+    (void)hipEventRecord(e1, nullptr);
+    (void)hipEventSynchronize(e1);
+    float ms = 0;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return 1000.0 * ms / reps;
+}
+
+}  // namespace
+}  // namespace mkp
+
+using namespace mkp;
+
+extern "C" {
+
+int mkp_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+             int64_t ldc, void* stream) {
+    return run_gemm(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
+}
+
+int mkp_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t strideA,
+                     const void* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc, int64_t strideC,
+                     void* stream) {
+    return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream);
+}
+
+int mkp_plan_describe(int64_t batch, int64_t M, int64_t N, int64_t K, int align_flags, char* buf, size_t len) {
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
+    (void)align_flags;
+    ensure_init();
+    Library& L = lib();
+    std::shared_lock<std::shared_mutex> lk(L.mu);
+    Plan p = polymerize(L.table, batch, M, N, K, L.opts);
+    return write_out(plan_to_json(p, L.table), buf, len);
+}
+
+int mkp_plan_with_table(const char* table_text, int exhaustive, int64_t batch, int64_t M, int64_t N, int64_t K,
+                        char* buf, size_t len) {
+    if (!table_text) return fail(MKP_ERR_INVALID_ARG, "table text is NULL");
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
+    PerfTable t;
+    std::string err;
+    if (!parse_table(table_text, t, err)) return fail(MKP_ERR_INVALID_ARG, err);
+    SearchOptions o;
+    o.exhaustive = exhaustive != 0;
+    o.splitk_max = INT_MAX;
+    Plan p = polymerize(t, batch, M, N, K, o);
+    return write_out(plan_to_json(p, t), buf, len);
+}
+
+int mkp_load_calibration(const char* path) {
+    ensure_init();
+    Library& L = lib();
+    std::unique_lock<std::shared_mutex> lk(L.mu);
+    // NULL restores the shipped table (or the analytic stand-in without one)
+    int rc = load_table_locked(L, path, path == nullptr);
+    if (rc == MKP_OK) {
+        L.opts.force_kernel = -1;
+    }
+    return rc;
+}
+
+int mkp_set_option(const char* key, const char* value) {
+    if (!key || !value) return fail(MKP_ERR_INVALID_ARG, "NULL option");
+    ensure_init();
+    Library& L = lib();
+    std::unique_lock<std::shared_mutex> lk(L.mu);
+    std::string k = key, v = value;
+    if (k == "force_kernel") {
+        if (v.empty()) {
+            L.opts.force_kernel = -1;
+        } else {
+            int idx = -1;
+            for (size_t i = 0; i < L.table.kernels.size(); ++i)
+                if (L.table.kernels[i].name == v) idx = (int)i;
+            if (idx < 0) return fail(MKP_ERR_UNSUPPORTED, "no kernel named " + v + " in the active table");
+            L.opts.force_kernel = idx;
+        }
+    } else if (k == "force_splitk") {
+        int s = std::atoi(v.c_str());
+        if (s < 0) return fail(MKP_ERR_INVALID_ARG, "force_splitk < 0");
+        L.opts.force_splitk = s;
+    } else if (k == "patterns") {
+        if (v == "I") L.opts.allow_II = false;
+        else if (v == "I,II" || v == "II") L.opts.allow_II = true;
+        else return fail(MKP_ERR_INVALID_ARG, "patterns must be I or I,II");
+    } else if (k == "trace") {
+        L.trace.store(std::atoi(v.c_str()) != 0);
+        return MKP_OK;
+    } else if (k == "exhaustive") {
+        L.opts.exhaustive = std::atoi(v.c_str()) != 0;
+    } else if (k == "splitk_max") {
+        int s = std::atoi(v.c_str());
+        if (s < 1) return fail(MKP_ERR_INVALID_ARG, "splitk_max < 1");
+        L.opts.splitk_max = s;
+    } else {
+        return fail(MKP_ERR_INVALID_ARG, "unknown option " + k);
+    }
+    L.cache.clear();
+    return MKP_OK;
+}
+
+int mkp_kernel_count(void) { return kernel_count(); }
+
+const char* mkp_kernel_name(int i) {
+    if (i < 0 || i >= kernel_count()) return nullptr;
+    return kernel_info(i).name;
+}
+
+void mkp_cache_clear(void) {
+    ensure_init();
+    {
+        Library& L = lib();
+        std::unique_lock<std::shared_mutex> lk(L.mu);
+        L.cache.clear();
+    }
+    free_workspaces();
+}
+
+int mkp_stats(char* buf, size_t len) {
+    ensure_init();
+    Library& L = lib();
+    std::ostringstream o;
+    size_t entries;
+    std::string origin;
+    {
+        std::shared_lock<std::shared_mutex> lk(L.mu);
+        entries = L.cache.size();
+        origin = L.table_origin;
+    }
+    o << "{\"hits\":" << L.hits.load() << ",\"misses\":" << L.misses.load() << ",\"entries\":" << entries
+      << ",\"plan_us_total\":" << (double)L.plan_ns.load() / 1000.0 << ",\"launches\":" << L.launches.load()
+      << ",\"table\":\"" << origin << "\"}";
+    return write_out(o.str(), buf, len);
+}
+
+const char* mkp_last_error(void) { return t_last_error.c_str(); }
+
+int mkp_trace_dump(char* buf, size_t len) {
+    Library& L = lib();
+    std::vector<TraceRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(L.trace_mu);
+        recs.swap(L.trace_recs);
+    }
+    std::ostringstream o;
+    o.precision(9);
+    o << "[";
+    for (size_t i = 0; i < recs.size(); ++i) {
+        float ms = 0.f;
+        (void)hipEventSynchronize(recs[i].e1);
+        (void)hipEventElapsedTime(&ms, recs[i].e0, recs[i].e1);
+        (void)hipEventDestroy(recs[i].e0);
+        (void)hipEventDestroy(recs[i].e1);
+        const int k = recs[i].kernel;
+        const char* name = k >= 0 ? kernel_info(k).name : (k == -1 ? "splitk_reduce" : "zero_fill");
+        if (i) o << ",";
+        o << "{\"kernel\":\"" << name << "\",\"us\":" << 1000.0 * ms << ",\"flops\":" << recs[i].flops
+          << ",\"bytes\":" << recs[i].bytes << "}";
+    }
+    o << "]";
+    return write_out(o.str(), buf, len);
+}
+
+int mkp_calibrate(const char* path, int max_points) {
+    if (!path) return fail(MKP_ERR_INVALID_ARG, "path is NULL");
+    ensure_init();
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
+    hipDeviceProp_t prop;
+    he = hipGetDeviceProperties(&prop, dev);
+    if (he != hipSuccess) return fail(MKP_ERR_HIP, "hipGetDeviceProperties failed");
+    const int cus = prop.multiProcessorCount;
+    static const int grid_t[] = {1, 2, 4, 8, 16, 32, 64, 128, 256};
+    int npts = (int)(sizeof(grid_t) / sizeof(grid_t[0]));
+    if (max_points > 0) npts = std::min(npts, max_points);
+    const int64_t kmax_cap = 16384;
+
+    // buffers sized for the largest point of any kernel
+    size_t a_elems = 0, b_elems = 0, c_elems = 0;
+    struct Shape { int tm, tn; };
+    std::vector<Shape> shapes;
+    std::vector<int> occ;
+    for (int i = 0; i < kernel_count(); ++i) {
+        const KernelInfo& ki = kernel_info(i);
+        int n = 0;
+        he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ki.func, ki.threads, 0);
+        if (he != hipSuccess || n < 1) n = 1;
+        occ.push_back(n);
+        const int slots = cus * n;
+        Shape s;
+        if (ki.uM <= 32) {
+            s = {1, slots};
+        } else {
+            int tm = (int)std::floor(std::sqrt((double)slots));
+            while (slots % tm) --tm;
+            s = {tm, slots / tm};
+        }
+        shapes.push_back(s);
+        const int64_t M = (int64_t)s.tm * ki.uM, N = (int64_t)s.tn * ki.uN;
+        const int64_t K = std::min<int64_t>((int64_t)grid_t[npts - 1] * ki.uK, kmax_cap);
+        a_elems = std::max(a_elems, (size_t)(M * K));
+        b_elems = std::max(b_elems, (size_t)(K * N));
+        c_elems = std::max(c_elems, (size_t)(M * N));
+    }
+    uint16_t *dA = nullptr, *dB = nullptr;
+    float* dC = nullptr;
+    if (hipMalloc(&dA, a_elems * 2) != hipSuccess || hipMalloc(&dB, b_elems * 2) != hipSuccess ||
+        hipMalloc(&dC, c_elems * 4) != hipSuccess) {
+        (void)hipFree(dA);
+        (void)hipFree(dB);
+        return fail(MKP_ERR_OOM, "calibration buffers");
+    }
+    (void)launch_fill_random_bf16(dA, (int64_t)a_elems, 12345u, nullptr);
+    (void)launch_fill_random_bf16(dB, (int64_t)b_elems, 67890u, nullptr);
+    (void)hipDeviceSynchronize();
+
+    PerfTable t;
+    t.cus = cus;
+    t.splits = {1, 2, 4, 8, 16, 32};
+    hipError_t err = hipSuccess;
+    // launch overhead: a one-workgroup kernel back to back
+    t.launch_us = time_launches([&] { return launch_zero_fill(dC, 1, 0, 1, 1, 1, nullptr); }, 20, 200, &err);
+    // split-K reduction bandwidth on a typical partial volume (8 x 256 x 4096)
+    {
+        const int s = 8, m = 256, n = 4096;
+        float* W = nullptr;
+        if (hipMalloc(&W, (size_t)s * m * n * 4) == hipSuccess) {
+            (void)hipMemset(W, 0, (size_t)s * m * n * 4);
+            double us = time_launches(
+                [&] { return launch_splitk_reduce(W, s, (int64_t)m * n, 0, n, dC, n, 0, m, n, 1, 1, nullptr); }, 20,
+                50, &err);
+            t.red_launch_us = t.launch_us;
+            t.red_gbps = (double)(s + 1) * 4.0 * m * n / std::max(us - t.launch_us, 0.1) / 1e3;
+            (void)hipFree(W);
+        }
+    }
+    for (int i = 0; i < kernel_count() && err == hipSuccess; ++i) {
+        const KernelInfo& ki = kernel_info(i);
+        TableKernel k;
+        k.name = ki.name;
+        k.uM = ki.uM;
+        k.uN = ki.uN;
+        k.uK = ki.uK;
+        k.wg_per_cu = occ[i];
+        k.lib_index = i;
+        const Shape s = shapes[i];
+        for (int p = 0; p < npts; ++p) {
+            const int tt = grid_t[p];
+            const int64_t K = (int64_t)tt * ki.uK;
+            if (K > kmax_cap) break;
+            KArgs a{};
+            a.A = dA;
+            a.B = dB;
+            a.C = dC;
+            a.M = s.tm * ki.uM;
+            a.N = s.tn * ki.uN;
+            a.K = (int)K;
+            a.lda = K;
+            a.ldb = a.N;
+            a.ldc = a.N;
+            a.tiles_m = s.tm;
+            a.tiles_n = s.tn;
+            a.steps_per_split = tt;
+            a.splits = 1;
+            a.batch = 1;
+            a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+            const dim3 grid((unsigned)(s.tm * s.tn));
+            // single-launch time, then enough repetitions for ~2 ms
+            double us = time_launches([&] { return ki.launch(a, grid, nullptr); }, 3, 3, &err);
+            if (err != hipSuccess) break;
+            int reps = (int)std::min(200.0, std::max(5.0, 2000.0 / std::max(us, 1.0)));
+            us = time_launches([&] { return ki.launch(a, grid, nullptr); }, 20, reps, &err);
+            if (err != hipSuccess) break;
+            k.pts.emplace_back((double)tt, std::max(us - t.launch_us, 0.05));
+        }
+        t.kernels.push_back(k);
+    }
+    (void)hipDeviceSynchronize();
+    (void)hipFree(dA);
+    (void)hipFree(dB);
+    (void)hipFree(dC);
+    if (err != hipSuccess) return fail(MKP_ERR_HIP, std::string("calibration launch: ") + hipGetErrorString(err));
+
+    std::string text = "# measured by mkp_calibrate on " + std::string(prop.name) + " (" +
+                       std::string(prop.gcnArchName) + "), " + std::to_string(cus) + " CUs\n" + table_to_text(t);
+    {
+        std::ofstream f(path);
+        if (!f) return fail(MKP_ERR_INVALID_ARG, std::string("cannot write ") + path);
+        f << text;
+    }
+    Library& L = lib();
+    std::unique_lock<std::shared_mutex> lk(L.mu);
+    L.table = t;
+    L.table_origin = path;
+    L.opts.force_kernel = -1;
+    L.cache.clear();
+    return MKP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Host-side view of the micro-kernel library: the argument block every
+// micro-kernel takes and the registry of launchable instances.
+//
+// Each micro-kernel is a fixed uM x uN x uK tile (MikPoly page, section 3,
+// "micro-kernel generation"); the region's start addresses, extents and K
+// trip counts arrive as run-time scalars (section 4, GPU platform).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mkp {
+
+// flags bits
+enum : int {
+    KF_VEC_A = 1,   // A rows 16-byte aligned: 128-bit loads allowed
+    KF_VEC_B = 2,   // B rows 16-byte aligned
+    KF_VEC_C = 4,   // C rows 16-byte aligned: 128-bit stores allowed
+};
+
+struct KArgs {
+    const uint16_t* A;    // region origin in A (row m0, column 0)
+    const uint16_t* B;    // region origin in B (row 0, column n0)
+    float* C;             // region origin in C, or the split-K workspace
+    int64_t lda, ldb, ldc;
+    int64_t sA, sB, sC;   // batch strides (elements)
+    int64_t sCsplit;      // elements between split partials (0 when s == 1)
+    int M, N, K;          // region extents and full K
+    int tiles_m, tiles_n;
+    int steps_per_split;  // K steps of uK per split
+    int splits;           // K splits (grid covers tiles x splits x batch)
+    int batch;
+    int flags;
+};
+
+struct KernelInfo {
+    const char* name;
+    int uM, uN, uK;
+    int threads;
+    int lds_bytes;
+    const void* func;     // __global__ entry, for occupancy queries
+    hipError_t (*launch)(const KArgs&, dim3 grid, hipStream_t);
+};
+
+int kernel_count();
+const KernelInfo& kernel_info(int i);
+int kernel_find(const char* name);
+
+// Sum of `splits` partials W[z] (z ascending) into C; W is [splits][batch][M][ldw].
+hipError_t launch_splitk_reduce(const float* W, int splits, int64_t sWsplit, int64_t sWbatch, int64_t ldw,
+                                float* C, int64_t ldc, int64_t sC, int M, int N, int batch, int vec,
+                                hipStream_t st);
+// C := 0 for batch matrices of M x N (K == 0: empty sum).
+hipError_t launch_zero_fill(float* C, int64_t ldc, int64_t sC, int M, int N, int batch, hipStream_t st);
+
+// Calibration helpers: fill a buffer with pseudo-random bf16 in [-1, 1).
+hipError_t launch_fill_random_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t st);
+
+}  // namespace mkp

@@ -1,0 +1,308 @@
+// Run-time polymerizer (see planner.h for the model and its sources).
+#include "planner.h"
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <limits>
+#include <sstream>
+
+namespace mkp {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
+    PerfTable t;
+    t.kernels.clear();
+    std::istringstream in(text);
+    std::string raw;
+    int lineno = 0;
+    std::vector<std::pair<std::string, std::vector<std::pair<double, double>>>> gs;
+    while (std::getline(in, raw)) {
+        ++lineno;
+        auto hash = raw.find('#');
+        std::string line = hash == std::string::npos ? raw : raw.substr(0, hash);
+        std::istringstream ls(line);
+        std::string key;
+        if (!(ls >> key)) continue;
+        auto fail = [&](const char* what) {
+            err = "table line " + std::to_string(lineno) + ": " + what;
+            return false;
+        };
+        if (key == "device") {
+            if (!(ls >> t.cus) || t.cus <= 0) return fail("bad device line");
+        } else if (key == "launch_us") {
+            if (!(ls >> t.launch_us) || t.launch_us < 0) return fail("bad launch_us");
+        } else if (key == "reduce") {
+            if (!(ls >> t.red_launch_us >> t.red_gbps) || t.red_gbps <= 0) return fail("bad reduce line");
+        } else if (key == "splitk") {
+            t.splits.clear();
+            int s;
+            while (ls >> s) {
+                if (s < 1) return fail("split factor < 1");
+                t.splits.push_back(s);
+            }
+            if (t.splits.empty()) return fail("empty splitk");
+        } else if (key == "patterns") {
+            t.pat_I = t.pat_IIM = t.pat_IIN = false;
+            std::string p;
+            while (ls >> p) {
+                if (p == "I") t.pat_I = true;
+                else if (p == "II-M") t.pat_IIM = true;
+                else if (p == "II-N") t.pat_IIN = true;
+                else return fail("unknown pattern");
+            }
+        } else if (key == "kernel") {
+            TableKernel k;
+            if (!(ls >> k.name >> k.uM >> k.uN >> k.uK >> k.wg_per_cu)) return fail("bad kernel line");
+            if (k.uM <= 0 || k.uN <= 0 || k.uK <= 0 || k.wg_per_cu <= 0) return fail("bad kernel tile");
+            for (auto& e : t.kernels)
+                if (e.name == k.name) return fail("duplicate kernel");
+            t.kernels.push_back(k);
+        } else if (key == "g") {
+            std::string name, tok;
+            if (!(ls >> name)) return fail("bad g line");
+            std::vector<std::pair<double, double>> pts;
+            while (ls >> tok) {
+                auto c = tok.find(':');
+                if (c == std::string::npos) return fail("bad g point");
+                double tt = std::atof(tok.substr(0, c).c_str());
+                double v = std::atof(tok.substr(c + 1).c_str());
+                if (!(tt > 0) || !(v >= 0)) return fail("bad g value");
+                pts.emplace_back(tt, v);
+            }
+            gs.emplace_back(name, pts);
+        } else {
+            return fail("unknown key");
+        }
+    }
+    for (auto& g : gs) {
+        bool found = false;
+        for (auto& k : t.kernels)
+            if (k.name == g.first) {
+                k.pts.insert(k.pts.end(), g.second.begin(), g.second.end());
+                found = true;
+            }
+        if (!found) {
+            err = "g line for unknown kernel " + g.first;
+            return false;
+        }
+    }
+    for (auto& k : t.kernels) {
+        if (k.pts.empty()) {
+            err = "kernel " + k.name + " has no g points";
+            return false;
+        }
+        std::sort(k.pts.begin(), k.pts.end());
+    }
+    if (t.kernels.empty()) {
+        err = "table has no kernels";
+        return false;
+    }
+    out = t;
+    return true;
+}
+
+std::string table_to_text(const PerfTable& t) {
+    std::ostringstream o;
+    o.precision(9);
+    o << "device " << t.cus << "\n";
+    o << "launch_us " << t.launch_us << "\n";
+    o << "reduce " << t.red_launch_us << " " << t.red_gbps << "\n";
+    o << "splitk";
+    for (int s : t.splits) o << " " << s;
+    o << "\npatterns" << (t.pat_I ? " I" : "") << (t.pat_IIM ? " II-M" : "") << (t.pat_IIN ? " II-N" : "")
+      << "\n";
+    for (auto& k : t.kernels)
+        o << "kernel " << k.name << " " << k.uM << " " << k.uN << " " << k.uK << " " << k.wg_per_cu << "\n";
+    for (auto& k : t.kernels) {
+        o << "g " << k.name;
+        for (auto& p : k.pts) o << " " << p.first << ":" << p.second;
+        o << "\n";
+    }
+    return o.str();
+}
+
+// Piecewise-linear in t between measured points; the first point's value
+// below it; the last segment's slope beyond the last point.
+double g_predict(const TableKernel& k, double t) {
+    const auto& p = k.pts;
+    if (p.size() == 1) return p[0].second * t / p[0].first;
+    if (t <= p[0].first) return p[0].second;
+    for (size_t i = 1; i < p.size(); ++i) {
+        if (t <= p[i].first) {
+            const double t0 = p[i - 1].first, v0 = p[i - 1].second;
+            const double t1 = p[i].first, v1 = p[i].second;
+            return v0 + (v1 - v0) * (t - t0) / (t1 - t0);
+        }
+    }
+    const double t0 = p[p.size() - 2].first, v0 = p[p.size() - 2].second;
+    const double t1 = p.back().first, v1 = p.back().second;
+    return v1 + (v1 - v0) * (t - t1) / (t1 - t0);
+}
+
+// Cost of one region served by one kernel with a requested split factor:
+//   launch + ceil(tasks / slots) * g(steps) [+ split-K reduction]
+double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K, int64_t batch,
+                   int s_req, Region* out) {
+    const TableKernel& k = tab.kernels[kernel];
+    const int64_t t3 = ceil_div(K, k.uK);
+    const int64_t per = ceil_div(t3, s_req);
+    const int64_t s_eff = ceil_div(t3, per);
+    const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * s_eff * batch;
+    const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
+    const int64_t waves = ceil_div(tasks, slots);
+    double c = tab.launch_us + (double)waves * g_predict(k, (double)per);
+    if (s_eff > 1)
+        c += tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch /
+                                     (tab.red_gbps * 1e3);
+    if (out) {
+        out->kernel = kernel;
+        out->lib = k.lib_index;
+        out->m = m;
+        out->n = n;
+        out->s = (int)s_eff;
+        out->steps = (int)per;
+        out->tasks = tasks;
+        out->waves = waves;
+        out->cost = c;
+    }
+    return c;
+}
+
+namespace {
+
+struct Searcher {
+    const PerfTable& tab;
+    const SearchOptions& opt;
+    int64_t batch, M, N, K;
+    int64_t evaluated = 0;
+    std::vector<int> splits;   // allowed requested factors
+
+    Searcher(const PerfTable& t, const SearchOptions& o, int64_t b, int64_t m, int64_t n, int64_t k)
+        : tab(t), opt(o), batch(b), M(m), N(n), K(k) {
+        if (opt.force_splitk > 0) {
+            splits.push_back(opt.force_splitk);
+        } else {
+            for (int s : tab.splits)
+                if (s <= opt.splitk_max) splits.push_back(s);
+            if (splits.empty()) splits.push_back(1);
+        }
+    }
+
+    bool kernel_allowed(int k) const { return opt.force_kernel < 0 || opt.force_kernel == k; }
+
+    // best split for one region; returns cost and fills r
+    double best_region(int kernel, int64_t m, int64_t n, Region* r) {
+        const int64_t t3 = ceil_div(K, tab.kernels[kernel].uK);
+        double best = std::numeric_limits<double>::infinity();
+        for (int s : splits) {
+            if (s > 1 && s > t3) continue;
+            Region tmp;
+            ++evaluated;
+            double c = region_cost(tab, kernel, m, n, K, batch, s, &tmp);
+            if (c < best) {
+                best = c;
+                *r = tmp;
+            }
+        }
+        return best;
+    }
+
+    Plan run() {
+        Plan best;
+        best.cost_us = std::numeric_limits<double>::infinity();
+        const int nk = (int)tab.kernels.size();
+        if (tab.pat_I) {
+            for (int a = 0; a < nk; ++a) {
+                if (!kernel_allowed(a)) continue;
+                Region r;
+                double c = best_region(a, M, N, &r);
+                if (c < best.cost_us) {
+                    best.pattern = PAT_I;
+                    best.cost_us = c;
+                    r.m0 = 0;
+                    r.n0 = 0;
+                    best.regions.assign(1, r);
+                }
+            }
+        }
+        if (opt.force_kernel >= 0 || !opt.allow_II) return best;
+        for (int dir = 0; dir < 2; ++dir) {
+            if (dir == 0 && !tab.pat_IIM) continue;
+            if (dir == 1 && !tab.pat_IIN) continue;
+            const int64_t ext = dir == 0 ? M : N;
+            for (int a = 0; a < nk; ++a) {
+                const int64_t step = dir == 0 ? tab.kernels[a].uM : tab.kernels[a].uN;
+                for (int64_t cut = step; cut < ext; cut += step) {
+                    Region r1;
+                    const double c1 = dir == 0 ? best_region(a, cut, N, &r1) : best_region(a, M, cut, &r1);
+                    // region-1 cost never falls as the cut grows: prune the rest
+                    if (!opt.exhaustive && c1 >= best.cost_us) break;
+                    for (int b = 0; b < nk; ++b) {
+                        if (b == a) continue;
+                        Region r2;
+                        const double c2 = dir == 0 ? best_region(b, M - cut, N, &r2)
+                                                   : best_region(b, M, N - cut, &r2);
+                        const double c = c1 + c2;
+                        if (c < best.cost_us) {
+                            best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
+                            best.cost_us = c;
+                            if (dir == 0) {
+                                r1.m0 = 0; r1.n0 = 0;
+                                r2.m0 = cut; r2.n0 = 0;
+                            } else {
+                                r1.m0 = 0; r1.n0 = 0;
+                                r2.m0 = 0; r2.n0 = cut;
+                            }
+                            best.regions.assign({r1, r2});
+                        }
+                    }
+                }
+            }
+        }
+        return best;
+    }
+};
+
+}  // namespace
+
+Plan polymerize(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_t K,
+                const SearchOptions& opt) {
+    auto t0 = std::chrono::steady_clock::now();
+    Plan p;
+    if (batch == 0 || M == 0 || N == 0) {
+        p.pattern = PAT_EMPTY;
+    } else if (K == 0) {
+        p.pattern = PAT_ZERO;
+    } else {
+        Searcher s(tab, opt, batch, M, N, K);
+        p = s.run();
+        p.evaluated = s.evaluated;
+    }
+    auto t1 = std::chrono::steady_clock::now();
+    p.plan_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+    return p;
+}
+
+std::string plan_to_json(const Plan& p, const PerfTable& tab) {
+    static const char* names[] = {"empty", "zero", "I", "II-M", "II-N"};
+    std::ostringstream o;
+    o.precision(17);
+    o << "{\"pattern\":\"" << names[p.pattern] << "\",\"cost_us\":" << (p.regions.empty() ? 0.0 : p.cost_us)
+      << ",\"plan_us\":" << p.plan_us << ",\"evaluated\":" << p.evaluated << ",\"regions\":[";
+    for (size_t i = 0; i < p.regions.size(); ++i) {
+        const Region& r = p.regions[i];
+        const TableKernel& k = tab.kernels[r.kernel];
+        if (i) o << ",";
+        o << "{\"m0\":" << r.m0 << ",\"n0\":" << r.n0 << ",\"m\":" << r.m << ",\"n\":" << r.n
+          << ",\"kernel\":\"" << k.name << "\",\"uM\":" << k.uM << ",\"uN\":" << k.uN << ",\"uK\":" << k.uK
+          << ",\"s\":" << r.s << ",\"steps\":" << r.steps << ",\"tasks\":" << r.tasks
+          << ",\"waves\":" << r.waves << ",\"cost_us\":" << r.cost << "}";
+    }
+    o << "]}";
+    return o.str();
+}
+
+}  // namespace mkp

@@ -1,0 +1,84 @@
+// Run-time polymerizer: performance table, cost model and strategy search.
+//
+// Pure host C++ (no HIP): it decides, for a GEMM shape known only at run
+// time, how the output is cut into regions, which fixed-size micro-kernel
+// serves each region and how many K splits each region uses.
+//
+// MikPoly page, section 3:
+//  * "micro-kernel performance model": a task is one uM x uN output tile that
+//    runs t = ceil(K/uK) micro-kernel instances back to back on one PE;
+//    g_predict(t) is measured offline per micro-kernel.
+//  * "polymerization cost model": Cost(S,H) = sum_i f_wave * f_pipe with
+//    f_wave = ceil(f_parallel / |P_multi|), f_pipe = g_predict(f_num).
+//  * "complete algorithm": candidate strategies whose partial cost already
+//    reaches the best one found are skipped.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <utility>
+#include <vector>
+
+namespace mkp {
+
+struct TableKernel {
+    std::string name;
+    int uM = 0, uN = 0, uK = 0;
+    int wg_per_cu = 1;                               // resident workgroups per CU
+    std::vector<std::pair<double, double>> pts;      // (t, us), sorted by t
+    int lib_index = -1;                              // index in the kernel library, -1 if none
+};
+
+struct PerfTable {
+    int cus = 256;
+    double launch_us = 0.0;       // per launch (per region)
+    double red_launch_us = 0.0;   // split-K reduction: fixed part
+    double red_gbps = 1000.0;     // split-K reduction: bandwidth
+    std::vector<int> splits{1};
+    bool pat_I = true, pat_IIM = true, pat_IIN = true;
+    std::vector<TableKernel> kernels;
+};
+
+enum PatternKind { PAT_EMPTY = 0, PAT_ZERO = 1, PAT_I = 2, PAT_IIM = 3, PAT_IIN = 4 };
+
+struct Region {
+    int64_t m0 = 0, n0 = 0, m = 0, n = 0;
+    int kernel = -1;        // index into PerfTable::kernels
+    int lib = -1;           // library kernel that serves it (-1: not launchable)
+    int s = 1;              // K splits actually used
+    int steps = 0;          // K steps (of uK) per split = f_num
+    int64_t tasks = 0;      // f_parallel (includes splits and batch)
+    int64_t waves = 0;      // f_wave
+    double cost = 0.0;
+};
+
+struct Plan {
+    int pattern = PAT_EMPTY;
+    std::vector<Region> regions;
+    double cost_us = 0.0;
+    double plan_us = 0.0;
+    int64_t evaluated = 0;   // candidate regions scored
+};
+
+struct SearchOptions {
+    bool exhaustive = false;
+    int force_kernel = -1;   // table index; -1 = free choice
+    int force_splitk = 0;    // 0 = free choice
+    int splitk_max = 64;
+    bool allow_II = true;
+};
+
+// Parse the text form of a table.  Returns false and sets err on bad input.
+bool parse_table(const std::string& text, PerfTable& out, std::string& err);
+std::string table_to_text(const PerfTable& t);
+
+double g_predict(const TableKernel& k, double t);
+double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K,
+                   int64_t batch, int s_req, Region* out);
+
+Plan polymerize(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_t K,
+                const SearchOptions& opt);
+
+std::string plan_to_json(const Plan& p, const PerfTable& tab);
+
+}  // namespace mkp

@@ -1,0 +1,154 @@
+/*
+ * mkp.h - run-time polymerized dense GEMM for AMD MI355X (gfx950).
+ *
+ * C = A . B with (M, N, K) known only at run time.  A fixed library of
+ * hand-written CDNA4 micro-kernels (fixed uM x uN x uK tiles on bf16 MFMA with
+ * fp32 accumulation) is composed per shape by a cost-model polymerizer
+ * (MikPoly page, section 3: two-stage flow, micro-kernel performance model,
+ * polymerization patterns and cost model); plans are cached by shape.
+ *
+ * Data types: A and B hold bf16 values (the upper 16 bits of an IEEE binary32,
+ * passed as 16-bit words); C is IEEE binary32.  All matrices are row-major;
+ * leading dimensions and strides count elements, not bytes.  Products are
+ * accumulated in binary32.  C is overwritten (C := A.B, no alpha/beta): the
+ * page's loops zero C before accumulating.
+ *
+ * Pointers A, B, C are device pointers owned by the caller; `stream` is a
+ * hipStream_t passed as void* (NULL = the null stream).  Calls are
+ * asynchronous: they return once the work is enqueued.  Argument errors are
+ * reported synchronously, before anything is written to C.  Faults inside a
+ * kernel surface at the caller's next synchronisation of `stream`.
+ *
+ * Thread safety: every entry point may be called from several host threads;
+ * the plan cache is shared under a lock and split-K workspaces are kept per
+ * (device, stream).  Two calls that run concurrently on different streams
+ * must not write the same C.  C must not alias A or B.
+ *
+ * Status codes: MKP_OK (0) on success, negative on error; mkp_last_error()
+ * returns a thread-local message for the last error raised on this thread.
+ */
+#ifndef MKP_H
+#define MKP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MKP_OK = 0,
+    MKP_ERR_INVALID_ARG = -1, /* bad dimension, leading dimension, null pointer */
+    MKP_ERR_UNSUPPORTED = -2, /* forced kernel/option the library cannot serve */
+    MKP_ERR_OOM = -3,         /* split-K workspace could not be allocated */
+    MKP_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+    MKP_ERR_BUFFER = -5       /* output text buffer too small */
+};
+
+/*
+ * C[M x N] := A[M x K] . B[K x N].
+ *   lda >= K, ldb >= N, ldc >= N (elements).  A, B, C may be NULL only when
+ *   the matrix they name is empty.  M == 0 or N == 0: nothing is launched.
+ *   K == 0: C := 0 (empty sum).  Pointers and leading dimensions need no
+ *   particular alignment; unaligned ones are served by element-wise loads.
+ * Source of the operation: MikPoly page, part 1 item 2 (C[i][j] += A[i][k] *
+ * B[k][j] over zeroed C) and section 4 (tensor start addresses and loop trip
+ * counts passed at run time to fixed-size micro-kernels).
+ */
+int mkp_gemm(int64_t M, int64_t N, int64_t K,
+             const void *A, int64_t lda,
+             const void *B, int64_t ldb,
+             float *C, int64_t ldc,
+             void *stream);
+
+/*
+ * batch independent products C_b := A_b . B_b, entry b at A + b*strideA,
+ * B + b*strideB, C + b*strideC (elements).  One plan serves every entry:
+ * same-shape GEMMs merged into one batched GEMM (BladeDISC v0.2.0 release
+ * notes, "GEMM merge" optimisation, second kind).  batch == 0 is a no-op.
+ * The C_b must not overlap: |strideC| >= (M-1)*ldc + N unless batch == 1.
+ */
+int mkp_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, int64_t strideA,
+                     const void *B, int64_t ldb, int64_t strideB,
+                     float *C, int64_t ldc, int64_t strideC,
+                     void *stream);
+
+/*
+ * Describe the plan the polymerizer picks for a shape, without launching.
+ * align_flags: bit0 = A rows 16-byte aligned, bit1 = B rows, bit2 = C rows
+ * (pass 7 for aligned operands).  Writes NUL-terminated JSON into buf:
+ *   {"pattern":..., "cost_us":..., "plan_us":..., "regions":[{"m0","n0","m",
+ *    "n","kernel","uM","uN","uK","s","steps","tasks","waves"}...]}
+ * Uses the active performance table (calibrated, or the built-in analytic
+ * one).  Pure host code: needs no GPU.  Returns MKP_OK, MKP_ERR_INVALID_ARG
+ * or MKP_ERR_BUFFER.
+ */
+int mkp_plan_describe(int64_t batch, int64_t M, int64_t N, int64_t K, int align_flags,
+                      char *buf, size_t len);
+
+/*
+ * As mkp_plan_describe but with a caller-given performance table (text, the
+ * format read by mkp_load_calibration) and the pruned or the exhaustive
+ * search (exhaustive != 0: every candidate is scored, the page's ORACLE
+ * variant of section 5 "cost-model effectiveness").  Kernel names in the
+ * table need not exist in the library: nothing is launched.  Pure host code.
+ */
+int mkp_plan_with_table(const char *table_text, int exhaustive,
+                        int64_t batch, int64_t M, int64_t N, int64_t K,
+                        char *buf, size_t len);
+
+/*
+ * Load a performance table (MikPoly page, section 3 "micro-kernel
+ * performance model": g_predict per micro-kernel over t K-steps) from a text
+ * file; path NULL reloads the table that ships with the library.  Lines:
+ *   device <cus>                     launch_us <us>
+ *   reduce <launch_us> <GB/s>        splitk <s1> <s2> ...
+ *   patterns I II-M II-N             kernel <name> <uM> <uN> <uK> <wg_per_cu>
+ *   g <name> <t>:<us> <t>:<us> ...
+ * Kernels named here must exist in the library.  Clears the plan cache.
+ */
+int mkp_load_calibration(const char *path);
+
+/*
+ * Offline stage: measure g for every library kernel on the current device
+ * and write the table to `path` (20 warm-up launches per point, as the page's
+ * evaluation does).  Synchronous; uses the null stream.  Returns MKP_OK or an
+ * error; the new table becomes active.
+ */
+int mkp_calibrate(const char *path, int max_points);
+
+/* Set an option: "force_kernel" (kernel name or ""), "force_splitk" (integer,
+ * 0 = free), "patterns" ("I" or "I,II"), "exhaustive" (0/1),
+ * "splitk_max" (integer), "trace" (0/1, see mkp_trace_dump).  Every option
+ * but "trace" clears the plan cache.  Returns MKP_OK or
+ * MKP_ERR_INVALID_ARG / MKP_ERR_UNSUPPORTED. */
+int mkp_set_option(const char *key, const char *value);
+
+/* Number of micro-kernels in the library and the name of kernel i
+ * (NULL if out of range).  The string is static. */
+int mkp_kernel_count(void);
+const char *mkp_kernel_name(int i);
+
+/* Drop every cached plan and free split-K workspaces (synchronises the
+ * streams that own them). */
+void mkp_cache_clear(void);
+
+/* JSON counters: cache hits/misses, plans built, planning time, launches. */
+int mkp_stats(char *buf, size_t len);
+
+/* Launch trace (option "trace" = 1): every kernel launch is bracketed by
+ * HIP events on its stream.  Waits for the recorded launches, writes a JSON
+ * list [{"kernel","us","flops","bytes"}...] (algorithmic work per launch:
+ * 2*m*n*K flops; 2mK + 2Kn + 4mn bytes) and clears the record. */
+int mkp_trace_dump(char *buf, size_t len);
+
+/* Thread-local message of the last error on this thread ("" if none). */
+const char *mkp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MKP_H */

@@ -1,0 +1,254 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C-ABI.
+
+Every case prints its name before it touches the GPU.  Full-element checks
+at sizes the oracle finishes in seconds (several tiles plus ragged tails);
+sampled entries at the workloads' full sizes.  The gate is
+|dC| <= 1e-3*sqrt(K) per element, plus the binary32 summation bound.
+"""
+import json
+import math
+import os
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+from _gpu_util import GuardedC, assert_close, dev_bf16, padded  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def mkp(gpu):
+    import dynamic_shape_gemm_amd as m
+
+    m.mkp_load_calibration(None)
+    m.mkp_set_option("force_kernel", "")
+    m.mkp_set_option("force_splitk", 0)
+    m.mkp_set_option("patterns", "I,II")
+    yield m
+    m.mkp_set_option("force_kernel", "")
+    m.mkp_set_option("force_splitk", 0)
+
+
+def rand_bits(rng, shape, law="u"):
+    if law == "u":
+        v = rng.uniform(-1, 1, size=shape)
+    else:
+        v = rng.normal(0, 1, size=shape)
+    return f32_to_bf16_bits(v.astype(np.float32))
+
+
+def run_case(mkp, a, b, *, lda=None, ldb=None, ldc=None, offA=0, offB=0, offC=0, what=""):
+    """a (M,K), b (K,N) bf16 bits; full-element compare with guard bands."""
+    import torch
+
+    M, K = a.shape
+    N = b.shape[1]
+    lda = lda or max(K, 1)
+    ldb = ldb or max(N, 1)
+    print(f"[case] {what} M={M} N={N} K={K} lda={lda} ldb={ldb} ldc={ldc} off=({offA},{offB},{offC})", flush=True)
+    ta, pa = dev_bf16(padded(a, lda) if K else a, offA)
+    tb, pb = dev_bf16(padded(b, ldb) if N else b, offB)
+    gc = GuardedC(1, M, N, ld=ldc, offset=offC)
+    mkp.mkp_gemm(M, N, K, pa, lda, pb, ldb, gc.addr, gc.ld)
+    torch.cuda.synchronize()
+    got, untouched = gc.result()
+    ref, refabs = oracle.gemm(a, b, with_abs=True)
+    assert untouched, f"{what}: write outside C"
+    return assert_close(got[0], ref, refabs, K, what)
+
+
+def test_config1_full(mkp):
+    case = workloads.config_cases(1)[0]
+    a, b = workloads.make_operands(case)
+    run_case(mkp, a[0], b[0], what="config1")
+
+
+RAGGED = [(1, 1, 1), (1, 4096, 64), (17, 33, 65), (64, 64, 64), (65, 129, 257), (300, 257, 129),
+          (255, 511, 1023), (513, 1000, 777), (16, 5000, 300), (1000, 17, 2049), (7, 300, 12544)]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=[f"{m}x{n}x{k}" for m, n, k in RAGGED])
+def test_ragged_auto(mkp, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 1_000_003 + N * 1009 + K)
+    run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"auto {shape}")
+
+
+EDGE = [(1, 1, 1), (15, 17, 63), (129, 250, 200), (257, 385, 130)]
+
+
+@pytest.mark.parametrize("split", [1, 3])
+def test_each_kernel_forced(mkp, split):
+    rng = np.random.default_rng(split)
+    try:
+        mkp.mkp_set_option("force_splitk", split)
+        for name in mkp.mkp_kernel_names():
+            mkp.mkp_set_option("force_kernel", name)
+            for (M, N, K) in EDGE:
+                run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"{name} s={split}")
+    finally:
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("force_splitk", 0)
+
+
+@pytest.mark.parametrize("s", [2, 4, 8, 32])
+def test_splitk(mkp, s):
+    rng = np.random.default_rng(100 + s)
+    try:
+        mkp.mkp_set_option("force_splitk", s)
+        for (M, N, K) in [(33, 700, 4097), (200, 300, 2000)]:
+            run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"splitk {s}")
+    finally:
+        mkp.mkp_set_option("force_splitk", 0)
+
+
+def test_unaligned(mkp):
+    rng = np.random.default_rng(5)
+    M, N, K = 77, 131, 301
+    a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+    run_case(mkp, a, b, lda=K + 1, what="lda odd")
+    run_case(mkp, a, b, ldb=N + 3, what="ldb odd")
+    run_case(mkp, a, b, ldc=N + 1, what="ldc odd")
+    run_case(mkp, a, b, offA=1, offB=3, offC=1, what="misaligned pointers")
+    M, N, K = 256, 256, 256
+    a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+    run_case(mkp, a, b, offB=1, what="aligned shape, B pointer off by one")
+
+
+def test_k0_and_empty(mkp):
+    import torch
+
+    print("[case] K=0 / M=0 / N=0", flush=True)
+    gc = GuardedC(1, 37, 41)
+    mkp.mkp_gemm(37, 41, 0, 0, 1, 0, 41, gc.addr, gc.ld)
+    torch.cuda.synchronize()
+    got, untouched = gc.result()
+    assert untouched and np.all(got == 0.0)
+    gc = GuardedC(1, 5, 5)
+    mkp.mkp_gemm(0, 5, 7, 0, 7, 0, 5, gc.addr, gc.ld)
+    mkp.mkp_gemm(5, 0, 7, 0, 7, 0, 5, gc.addr, gc.ld)
+    mkp.mkp_gemm_batched(0, 5, 5, 7, 0, 7, 0, 0, 5, 0, gc.addr, gc.ld, 0)
+    torch.cuda.synchronize()
+    h = gc.t.cpu().numpy()
+    assert np.isnan(h).all()
+
+
+def test_batched_config5_members(mkp):
+    import torch
+
+    cases = workloads.config_cases(5)
+    for case in [cases[i] for i in (0, 1, 7, 31)] + [workloads.GemmCase(17, 17, 64, 48, ("normal", 0, 1),
+                                                                        ("normal", 0, 1), (1,), (2,))]:
+        a, b = workloads.make_operands(case)
+        S, B = case.M, case.batch
+        print(f"[case] batched {case.tag} S={S} batch={B}", flush=True)
+        ta, pa = dev_bf16(a)
+        tb, pb = dev_bf16(b)
+        gc = GuardedC(B, S, S, ld=S)
+        gc.stride = S * S  # packed like the workload
+        gc.t = torch.full((B * S * S + 64 * S,), float("nan"), dtype=torch.float32, device="cuda")
+        gc.addr = gc.t.data_ptr()
+        mkp.mkp_gemm_batched(B, S, S, 64, pa, 64, S * 64, pb, S, 64 * S, gc.addr, S, S * S)
+        torch.cuda.synchronize()
+        h = gc.t.cpu().numpy()
+        got = h[:B * S * S].reshape(B, S, S).astype(np.float64)
+        assert np.isnan(h[B * S * S:]).all()
+        ref, refabs = oracle.gemm(a, b, with_abs=True)
+        for z in range(B):
+            assert_close(got[z], ref[z], refabs[z], 64, f"{case.tag}[{z}]")
+
+
+def sampled_check(mkp, case, nsamp=2048, a=None, b=None):
+    import torch
+
+    if a is None:
+        a, b = workloads.make_operands(case)
+    M, N, K = case.M, case.N, case.K
+    print(f"[case] sampled {case.tag} M={M} N={N} K={K}", flush=True)
+    ta, pa = dev_bf16(a)
+    tb, pb = dev_bf16(b)
+    tc = torch.full((M * N + 256,), float("nan"), dtype=torch.float32, device="cuda")
+    mkp.mkp_gemm(M, N, K, pa, K, pb, N, tc.data_ptr(), N)
+    torch.cuda.synchronize()
+    h = tc.cpu().numpy()
+    assert np.isnan(h[M * N:]).all(), "write beyond C"
+    c = h[:M * N].reshape(M, N)
+    assert np.isfinite(c).all(), "hole in C"
+    rng = np.random.default_rng(M * 7 + N * 13 + K)
+    rows = np.concatenate([rng.integers(0, M, nsamp), [0, M - 1, M - 1, 0]])
+    cols = np.concatenate([rng.integers(0, N, nsamp), [0, N - 1, 0, N - 1]])
+    ref, refabs = oracle.gemm_entries(a[0], b[0], rows, cols)
+    assert_close(c[rows, cols].astype(np.float64), ref, refabs, K, case.tag)
+
+
+def test_config2_sampled(mkp):
+    for case in workloads.config_cases(2):
+        sampled_check(mkp, case, nsamp=1024)
+
+
+def test_config3_full_size_sampled(mkp):
+    for case in workloads.config_cases(3):
+        sampled_check(mkp, case, nsamp=4096)
+
+
+def test_config4_sampled(mkp):
+    weights = {}
+    for case in workloads.config_cases(4)[::5]:
+        if case.seed_b not in weights:
+            weights[case.seed_b] = workloads.make_b(case)
+        sampled_check(mkp, case, nsamp=1024, a=workloads.make_a(case), b=weights[case.seed_b])
+
+
+def test_determinism(mkp):
+    import torch
+
+    rng = np.random.default_rng(77)
+    M, N, K = 300, 1000, 5000
+    a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+    print("[case] determinism", flush=True)
+    ta, pa = dev_bf16(a)
+    tb, pb = dev_bf16(b)
+    outs = []
+    for s in (0, 0, 4, 4):
+        mkp.mkp_set_option("force_splitk", s)
+        tc = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        mkp.mkp_gemm(M, N, K, pa, K, pb, N, tc, N)
+        torch.cuda.synchronize()
+        outs.append(tc.cpu().numpy())
+    mkp.mkp_set_option("force_splitk", 0)
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[2], outs[3])
+
+
+def test_pattern_II_regions(mkp):
+    """A table whose costs make two-region plans win; the II plans must still
+    produce the exact product (regions partition C)."""
+    names = mkp.mkp_kernel_names()
+    big, small = "m128n128k64", "m64n64k64"
+    assert big in names and small in names
+    text = """device 256
+launch_us 0
+splitk 1
+patterns II-M II-N
+kernel m128n128k64 128 128 64 1
+kernel m64n64k64 64 64 64 1
+g m128n128k64 1:1 1000:1000
+g m64n64k64 1:0.3 1000:300
+"""
+    path = os.path.join(tempfile.mkdtemp(), "ii.tbl")
+    open(path, "w").write(text)
+    rng = np.random.default_rng(9)
+    try:
+        mkp.mkp_load_calibration(path)
+        for (M, N, K) in [(300, 200, 130), (129, 513, 64), (1000, 70, 99)]:
+            plan = mkp.mkp_plan_describe(1, M, N, K)
+            assert plan["pattern"] in ("II-M", "II-N"), plan
+            run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"II {plan['pattern']}")
+    finally:
+        mkp.mkp_load_calibration(None)

@@ -23,6 +23,8 @@ __all__ = [
     "GemmCase",
     "config_cases",
     "make_operands",
+    "make_a",
+    "make_b",
     "CONFIG_NAMES",
 ]
 
@@ -131,14 +133,22 @@ def _draw(law: tuple, seed: tuple, count: int) -> np.ndarray:
     return f32_to_bf16_bits(v)
 
 
+def make_a(case: GemmCase) -> np.ndarray:
+    """Packed bf16 bits of A, shape (batch, M, K), row-major."""
+    return _draw(case.law_a, case.seed_a, case.batch * case.M * case.K).reshape(case.batch, case.M, case.K)
+
+
+def make_b(case: GemmCase) -> np.ndarray:
+    """Packed bf16 bits of B, shape (batch, K, N), row-major."""
+    return _draw(case.law_b, case.seed_b, case.batch * case.K * case.N).reshape(case.batch, case.K, case.N)
+
+
 def make_operands(case: GemmCase) -> Tuple[np.ndarray, np.ndarray]:
-    """Packed bf16 bit arrays A (batch*M*K) and B (batch*K*N), row-major.
+    """Packed bf16 bit arrays A (batch, M, K) and B (batch, K, N), row-major.
 
     Batch entries are contiguous: strides M*K for A and K*N for B.
     """
-    a = _draw(case.law_a, case.seed_a, case.batch * case.M * case.K)
-    b = _draw(case.law_b, case.seed_b, case.batch * case.K * case.N)
-    return a.reshape(case.batch, case.M, case.K), b.reshape(case.batch, case.K, case.N)
+    return make_a(case), make_b(case)
 
 
 def digest(*arrays: np.ndarray) -> str:
