@@ -1,0 +1,272 @@
+"""Throughput of the polymerized dynamic-shape GEMM on one MI355X.
+
+One step = one pass over a workload's whole GEMM sweep through the C-ABI
+(plan-cache lookup, polymerization on a miss, every region's micro-kernel).
+Default workload: the dynamic-sequence-length encoder linears, 64 GEMMs with
+M = 16*L, L ~ U{1..512}, (N,K) cycling over (2304,768), (768,768),
+(3072,768), (768,3072), bf16 U[-1,1] inputs, fp32 output.
+
+Prints ONE JSON line (rank 0, N=1):
+  value = total algorithmic FLOPs of the step / step time, in TFLOP/s;
+  roofline = the dominant kernel's achieved rate over its launches (HIP
+    events on the launch stream, via the library's launch trace) against the
+    MI355X peak of its bound;
+  cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+Inputs are resident in HBM before timing; every GEMM of the sweep has its
+own buffers, so the working set (GBs) is far beyond the 256 MB MALL.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+METRIC = "TFLOP/s and % of bf16 MFMA / HBM roofline over dynamic-shape GEMM sweeps"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Device-resident operands for one sweep of a config."""
+
+    def __init__(self, cfg: int, copies: int = 1):
+        import torch
+        import workloads
+
+        self.cfg = cfg
+        self.cases = workloads.config_cases(cfg)
+        self.calls = []  # (case, A ptr, B ptr, C tensor)
+        self.host = []   # (a bits, b bits) kept for the CPU baseline
+        self.keep = []
+        weights = {}
+        for i, case in enumerate(self.cases):
+            a = workloads.make_a(case)
+            if cfg == 4:
+                # decoder weights are shared by every decode step; keep
+                # `copies` distinct device copies and rotate through them
+                if case.seed_b not in weights:
+                    b = workloads.make_b(case)
+                    tb = torch.from_numpy(b.view(np.int16)).cuda()
+                    weights[case.seed_b] = (b, [tb] + [tb.clone() for _ in range(copies - 1)])
+                b, tbs = weights[case.seed_b]
+                tb = tbs[i % len(tbs)]
+            else:
+                b = workloads.make_b(case)
+                tb = torch.from_numpy(b.view(np.int16)).cuda()
+            ta = torch.from_numpy(a.view(np.int16)).cuda()
+            tc = torch.empty((case.batch, case.M, case.N), dtype=torch.float32, device="cuda")
+            self.keep += [ta, tb]
+            self.calls.append((case, ta.data_ptr(), tb.data_ptr(), tc))
+            if i < 8:
+                self.host.append((case, a, b))
+        self.flops = sum(c.flops for c in self.cases)
+        self.bytes = sum(c.bytes for c in self.cases)
+
+    def step(self, mkp, stream):
+        for case, pa, pb, tc in self.calls:
+            if case.batch == 1:
+                mkp.mkp_gemm(case.M, case.N, case.K, pa, case.K, pb, case.N, tc, case.N, stream)
+            else:
+                mkp.mkp_gemm_batched(case.batch, case.M, case.N, case.K, pa, case.K, case.M * case.K, pb, case.N,
+                                     case.K * case.N, tc, case.N, case.M * case.N, stream)
+
+
+def timed_steps(wl, mkp, steps, stream):
+    import torch
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    s.record(cur)
+    for _ in range(steps):
+        wl.step(mkp, stream)
+    e.record(cur)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e)  # ms
+
+
+def roofline_from_trace(recs):
+    """Per-kernel aggregates of one traced step; the dominant kernel is the
+    one with the largest total time.  Its bound follows from the algorithmic
+    intensity of its launches (FLOPs / bytes against the MFMA/HBM ridge)."""
+    agg = {}
+    for r in recs:
+        a = agg.setdefault(r["kernel"], {"us": 0.0, "flops": 0.0, "bytes": 0.0, "n": 0})
+        a["us"] += r["us"]
+        a["flops"] += r["flops"]
+        a["bytes"] += r["bytes"]
+        a["n"] += 1
+    gemm = {k: v for k, v in agg.items() if v["flops"] > 0}
+    dom = max(gemm, key=lambda k: gemm[k]["us"])
+    d = gemm[dom]
+    intensity = d["flops"] / max(d["bytes"], 1.0)
+    if intensity >= RIDGE:
+        achieved = d["flops"] / (d["us"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        achieved = d["bytes"] / (d["us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(achieved / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["launches"] = d["n"]
+    roof["avg_launch_us"] = round(d["us"] / d["n"], 3)
+    roof["algorithmic_per_launch"] = {"flops": d["flops"] / d["n"], "bytes": d["bytes"] / d["n"]}
+    per_kernel = {k: {"launches": v["n"], "total_us": round(v["us"], 2)} for k, v in agg.items()}
+    return roof, per_kernel
+
+
+def sweep_fraction(recs_by_call, wl):
+    """Per-GEMM fraction of its own roofline R = min(P, I*BW)."""
+    fr = []
+    for case, us in zip(wl.cases, recs_by_call):
+        I = case.flops / case.bytes
+        R = min(PEAK_BF16_TFLOPS * 1e12, I * PEAK_HBM_GBS * 1e9)
+        fr.append(case.flops / (us * 1e-6) / R)
+    return fr
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle as it stands, on the first rows of the workload's GEMMs in
+    order, 64 rows at a time, until `budget_s` seconds have elapsed."""
+    import oracle
+    t0 = time.perf_counter()
+    flops = 0
+    rows_done = []
+    while time.perf_counter() - t0 < budget_s:
+        progressed = False
+        for idx, (case, a, b) in enumerate(wl.host):
+            if time.perf_counter() - t0 >= budget_s:
+                break
+            start = len([r for r in rows_done if r[0] == idx]) * 64
+            if start >= case.M:
+                continue
+            rows = min(64, case.M - start)
+            oracle.gemm(a[0, start:start + rows], b[0])
+            flops += 2 * rows * case.N * case.K
+            rows_done.append((idx, rows))
+            progressed = True
+        if not progressed:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle on the first rows of the sweep's first {len(wl.host)} GEMMs, 64-row blocks, "
+                      f"{sum(r for _, r in rows_done)} rows, {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--detail", action="store_true", help="per-GEMM timings to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dynamic_shape_gemm_amd as mkp
+    import workloads
+
+    torch.cuda.set_device(0)
+    log(f"[bench] generating config {args.config} inputs")
+    wl = Workload(args.config, copies=4)
+    stream = torch.cuda.current_stream().cuda_stream
+    mkp.mkp_cache_clear()
+
+    # first step: plan misses (polymerization) + launches, timed on its own
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    wl.step(mkp, stream)
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    stats0 = mkp.mkp_stats()
+    log(f"[bench] first step {first_ms:.2f} ms, {stats0['misses']} plans in {stats0['plan_us_total']:.1f} us")
+    for _ in range(max(args.warmup - 1, 0)):
+        wl.step(mkp, stream)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done, timing {args.steps} steps")
+    ms = timed_steps(wl, mkp, args.steps, stream)
+    ms_per_step = ms / args.steps
+    value = wl.flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # one traced step: per-launch HIP events on the launch stream
+    mkp.mkp_set_option("trace", 1)
+    wl.step(mkp, stream)
+    torch.cuda.synchronize()
+    recs = mkp.mkp_trace_dump()
+    mkp.mkp_set_option("trace", 0)
+    roof, per_kernel = roofline_from_trace(recs)
+    # per-call durations (a call may hold several launches)
+    per_call, i = [], 0
+    for case in wl.cases:
+        plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K)
+        n = sum(2 if r["s"] > 1 else 1 for r in plan["regions"])
+        per_call.append(sum(r["us"] for r in recs[i:i + n]))
+        i += n
+    fr = sweep_fraction(per_call, wl)
+    if args.detail:
+        for case, us, f in zip(wl.cases, per_call, fr):
+            plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K)
+            ks = "+".join(f"{r['kernel']}/s{r['s']}" for r in plan["regions"])
+            log(f"  {case.tag:>14} {case.M:5d}x{case.N:5d}x{case.K:5d} b{case.batch:<3d} {us:9.2f} us "
+                f"{case.flops / us / 1e6:8.1f} TF/s  {100 * f:5.1f}% of R  {plan['pattern']:4s} {ks}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": workloads.CONFIG_NAMES[args.config],
+            "config_index": args.config,
+            "gemms_per_step": len(wl.cases),
+            "flops_per_step": wl.flops,
+            "bytes_per_step": wl.bytes,
+            "first_step_ms": round(first_ms, 3),
+            "plans_built": stats0["misses"],
+            "plan_us_total": round(stats0["plan_us_total"], 1),
+            "roofline_frac_median": round(float(np.median(fr)), 4),
+            "roofline_frac_min": round(float(np.min(fr)), 4),
+            "kernels": per_kernel,
+            "table": mkp.mkp_stats()["table"],
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        log(f"[bench] CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -197,8 +197,10 @@ struct Searcher {
     double best_region(int kernel, int64_t m, int64_t n, Region* r) {
         const int64_t t3 = ceil_div(K, tab.kernels[kernel].uK);
         double best = std::numeric_limits<double>::infinity();
-        for (int s : splits) {
-            if (s > 1 && s > t3) continue;
+        for (int s_req : splits) {
+            // a factor above the K-step count degenerates to one step per split
+            const int s = (int)std::min<int64_t>(s_req, std::max<int64_t>(t3, 1));
+            if (s != s_req && opt.force_splitk <= 0) continue;
             Region tmp;
             ++evaluated;
             double c = region_cost(tab, kernel, m, n, K, batch, s, &tmp);
