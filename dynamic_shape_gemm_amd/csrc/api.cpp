@@ -339,8 +339,10 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
 
     const uint16_t* A = (const uint16_t*)Av;
     const uint16_t* B = (const uint16_t*)Bv;
-    const bool vA = aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0);
-    const bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0);
+    // 128-bit loads need 16-byte aligned rows; the direct-load path also
+    // keeps per-tile offsets (<= 256 rows of A, <= 64 rows of B) in 32 bits
+    const bool vA = aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0) && lda < (int64_t(1) << 23);
+    const bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0) && ldb < (int64_t(1) << 25);
     const bool vC = aligned16(C) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
     const int align = (vA ? 1 : 0) | (vB ? 2 : 0) | (vC ? 4 : 0);
 

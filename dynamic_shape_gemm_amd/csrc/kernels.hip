@@ -1,75 +1,114 @@
 // CDNA4 (gfx950) micro-kernel library.
 //
 // Every micro-kernel is one fixed uM x uN x uK tile; a workgroup runs one
-// pipeline task: it walks its K range in uK steps, each step loading the A
-// (uM x uK) and B (uK x uN) tiles from HBM into LDS, then running bf16 MFMAs
-// on them with fp32 accumulation, and finally writes the fp32 tile back
-// (MikPoly page, section 3 "micro-kernel performance model": load to local
-// memory, compute with intermediates kept local, write back).  Start
-// addresses, extents and K trip counts are run-time arguments (section 4).
-// Edge tiles are predicated element by element, so any shape is covered
-// without padding the operands ("partial padding", section 3, polymerization
+// pipeline task: it walks its K range in uK steps, each step bringing the A
+// (uM x uK) and B (uK x uN) tiles from HBM into LDS and running bf16 MFMAs on
+// them with fp32 accumulation, then writes the fp32 tile back (MikPoly page,
+// section 3 "micro-kernel performance model": load to local memory, compute
+// with intermediates kept local, write back).  Start addresses, extents and
+// K trip counts are run-time arguments (section 4, GPU platform).  Edge
+// tiles never read or write outside the operands, so any shape is covered
+// without padding them ("partial padding", section 3, polymerization
 // strategy).
 //
-// Data path per K step (register-staged double buffering, one barrier):
-//   * A rows are K-contiguous, which is what the MFMA operand wants: 128-bit
-//     global loads go straight into a K-major LDS tile.
-//   * B rows are N-contiguous; each thread loads a 4(k) x 8(n) block with
-//     four 128-bit loads, transposes it in registers and stores it into an
-//     N-major (K-contiguous) LDS tile, so both MFMA operands are read with
-//     one 128-bit LDS read per lane.
-//   * LDS rows are 16-byte-chunk XOR swizzled so the 16 lanes that read one
-//     MFMA fragment hit distinct banks.
-//   * v_mfma_f32_16x16x32_bf16 is issued with the B^T fragment as the first
-//     operand and the A^T fragment as the second, so each lane's four
-//     results are four consecutive columns of one C row: one 128-bit store.
+// Data path of one K step:
+//   * Direct global->LDS loads (global_load_lds_dwordx4): each wave
+//     instruction moves 64 x 16 bytes into 1 KB of LDS in lane order, with no
+//     register staging.  S LDS stages keep S-1 steps in flight; a bare
+//     barrier preceded by an explicit vmcnt wait releases exactly the step
+//     about to be used (a full workgroup fence would drain every load).
+//   * A is stored K-contiguous (as in HBM), rows 16-byte-chunk XOR swizzled.
+//   * B is stored N-contiguous (as in HBM), rows 32-byte-segment XOR
+//     swizzled, and read with the LDS transpose read (ds_read_b64_tr_b16),
+//     which hands each lane four K-consecutive values of one B column.
+//   * The MFMA (32x32x16 bf16, or 16x16x32 for 16-row wave tiles) takes the
+//     B^T fragment first and the A^T fragment second, so each lane's results
+//     come in runs of four consecutive columns of one C row (128-bit stores).
+//   * A fallback path (register loads with zero fill) serves the last K step
+//     when K is not a multiple of uK, operands whose rows are not 16-byte
+//     aligned, and the last tile column when N is not a multiple of 8.
 #include "kernels.h"
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 namespace mkp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_t;
 
+// A rows (uK*2 bytes) are XOR swizzled in 16-byte chunks: the 16 rows one
+// fragment read touches land in 16 distinct 16-byte bank windows.
 template <int BK>
-__device__ __forceinline__ int swz(int row);
-// 128-byte rows (8 chunks): rows r and r+8 differ in chunk parity, rows r
-// and r+1 fall in different halves of a 256-byte bank window.
+__device__ __forceinline__ int swzA(int row);
 template <>
-__device__ __forceinline__ int swz<64>(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-// 256-byte rows (16 chunks)
+__device__ __forceinline__ int swzA<64>(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 template <>
-__device__ __forceinline__ int swz<128>(int row) { return row & 15; }
+__device__ __forceinline__ int swzA<128>(int row) { return row & 15; }
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
+// B rows (uN*2 bytes) are XOR swizzled in 32-byte segments so that one
+// transposed read never hits a 32-byte bank window twice in a 32-lane pass.
+// 16x16x32 fragments read 8 consecutive K rows of one segment; 32x32x16
+// fragments read 4 consecutive K rows of two adjacent segments.
+template <int BN, int MF>
+__device__ __forceinline__ int swzB(int k) {
+    if constexpr (MF == 16) return BN >= 128 ? (k & 7) : ((k >> 1) & 3);
+    else return BN >= 128 ? ((k & 3) << 1) : (((k >> 1) & 1) << 1);
+}
+
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
-    static constexpr int NT = 64 * WGM * WGN;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
+    static constexpr int NW = WGM * WGN;
+    static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
-    static constexpr int FM = WTM / 16, FN = WTN / 16;
-    static constexpr int ROWB = BK * 2;             // bytes per LDS row
-    static constexpr int CPR = BK / 8;              // 16-byte chunks per row
-    static constexpr int A_CH = BM * CPR;           // A chunks per tile
-    static constexpr int B_Q = (BK / 4) * (BN / 8); // B 4x8 blocks per tile
-    static constexpr int NA = (A_CH + NT - 1) / NT;
-    static constexpr int NB = (B_Q + NT - 1) / NT;
-    static constexpr int A_BYTES = BM * ROWB;
-    static constexpr int B_BYTES = BN * ROWB;
+    // MFMA shape: 32x32x16 wherever the wave tile allows it (it reaches the
+    // bf16 peak from one wave per SIMD), 16x16x32 for 16-row wave tiles
+    static constexpr int MF = (WTM % 32 == 0 && WTN % 32 == 0) ? 32 : 16;
+    static constexpr int FM = WTM / MF, FN = WTN / MF;
+    static constexpr int A_ROWB = BK * 2, B_ROWB = BN * 2;
+    static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BK * B_ROWB;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int A_SLOTS = A_BYTES / 16, B_SLOTS = B_BYTES / 16;
+    static constexpr int A_GROUPS = A_SLOTS / 64, B_GROUPS = B_SLOTS / 64;   // 1 KB each
+    static constexpr int A_IPW = (A_GROUPS + NW - 1) / NW, B_IPW = (B_GROUPS + NW - 1) / NW;
+    static constexpr int IPS = A_IPW + B_IPW;        // LDS-DMA instructions per wave per step
+    static constexpr bool JUNK = (A_GROUPS % NW) != 0 || (B_GROUPS % NW) != 0;
+    static constexpr int LDS = S * STAGE + (JUNK ? 1024 : 0);
+    static constexpr int A_RPT = (A_SLOTS + NT - 1) / NT, B_RPT = (B_SLOTS + NT - 1) / NT;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(BK == 64 || BK == 128, "uK must be 64 or 128");
+    static_assert(BN >= 64 && BN % 64 == 0, "uN must be a multiple of 64");
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles must fill whole 1 KB groups");
+    static_assert(S >= 2 && IPS * (S - 2) <= 63, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
+// LDS slot (16 bytes) -> (row, first element) of the A tile.
+template <class T>
+__device__ __forceinline__ void slotA(int p, int& row, int& col) {
+    row = p / (T::BK / 8);
+    col = ((p % (T::BK / 8)) ^ swzA<T::BK>(row)) * 8;
+}
+// LDS slot -> (k row, first column) of the B tile.
+template <class T>
+__device__ __forceinline__ void slotB(int p, int& k, int& col) {
+    k = p / (T::BN / 8);
+    const int pq = p % (T::BN / 8);
+    col = ((((pq >> 1) ^ swzB<T::BN, T::MF>(k)) << 1) | (pq & 1)) * 8;
+}
+
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// Up to 8 consecutive bf16 values, element-wise (any alignment); missing
-// elements read as zero.  Nothing is read when nvalid <= 0.
+// Up to 8 consecutive bf16 values element by element (any alignment);
+// missing elements read as zero; nothing is read when nvalid <= 0.
 __device__ __forceinline__ u32x4 load8_elems(const uint16_t* p, int nvalid) {
     uint32_t w[4];
 #pragma unroll
@@ -81,85 +120,188 @@ __device__ __forceinline__ u32x4 load8_elems(const uint16_t* p, int nvalid) {
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-__device__ __forceinline__ uint32_t half16(uint32_t x, int hi) { return hi ? (x >> 16) : (x & 0xffffu); }
+// Wait until at most N vector-memory operations of this wave are in flight
+// and its LDS operations are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 template <class T>
-struct Pipe {
-    u32x4 ra[T::NA];
-    u32x4 rb[T::NB][4];
+__device__ __forceinline__ void wait_step(int ahead) {
+    // `ahead` later steps may stay in flight (each IPS instructions per wave)
+    if constexpr (T::S >= 4) {
+        if (ahead >= 2) { wait_and_barrier<2 * T::IPS>(); return; }
+    }
+    if constexpr (T::S >= 3) {
+        if (ahead >= 1) { wait_and_barrier<T::IPS>(); return; }
+    }
+    wait_and_barrier<0>();
+}
 
-    // Global -> registers for the K step starting at k0.
-    // fast: the whole tile and step are in range and rows are 16-byte aligned.
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ A, int64_t lda,
-                                         const uint16_t* __restrict__ B, int64_t ldb, int k0, int kend,
-                                         int Mr, int Nr, bool fast, bool vecA, bool vecB, int tid) {
+struct TileCtx {
+    const uint16_t* A;   // tile origin row m0 (row 0 of the tile), column 0
+    const uint16_t* B;   // tile origin column n0, row 0
+    int64_t lda, ldb;
+    int Mr, Nr;          // rows/columns of the tile inside the region
+    int kend;            // end of this split's K range
+    bool vecA, vecB;
+};
+
+// Per-lane element offsets of the direct loads, fixed for a tile: rows and
+// columns past the tile's valid extent are clamped to valid ones (they only
+// feed C rows/columns that are never stored).  A step then adds a uniform
+// base (A + k0, B + k0*ldb), so each load is a scalar base plus one 32-bit
+// offset.
+template <class T>
+struct DmaOffsets {
+    uint32_t a[T::A_IPW], b[T::B_IPW];
+
+    __device__ __forceinline__ void init(const TileCtx& c, int wave, int lane) {
 #pragma unroll
-        for (int i = 0; i < T::NA; ++i) {
-            const int q = tid + i * T::NT;
-            if (T::A_CH % T::NT == 0 || q < T::A_CH) {
-                const int row = q / T::CPR, kc = q % T::CPR;
-                const int k = k0 + kc * 8;
-                const uint16_t* p = A + (int64_t)row * lda + k;
-                if (fast) {
-                    ra[i] = *(const u32x4*)p;
-                } else if (row < Mr && k < kend) {
-                    ra[i] = (vecA && k + 8 <= kend) ? *(const u32x4*)p : load8_elems(p, kend - k);
-                } else {
-                    ra[i] = zero4();
-                }
-            }
+        for (int i = 0; i < T::A_IPW; ++i) {
+            const int g = i * T::NW + wave;
+            int row, col;
+            slotA<T>(g * 64 + lane, row, col);
+            row = min(row, c.Mr - 1);
+            const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
+            a[i] = real ? (uint32_t)(row * c.lda + col) : 0u;
         }
 #pragma unroll
-        for (int i = 0; i < T::NB; ++i) {
-            const int q = tid + i * T::NT;
-            if (T::B_Q % T::NT == 0 || q < T::B_Q) {
-                const int kq = q % (T::BK / 4), nq = q / (T::BK / 4);
-                const int n = nq * 8;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int k = k0 + kq * 4 + j;
-                    const uint16_t* p = B + (int64_t)k * ldb + n;
-                    if (fast) {
-                        rb[i][j] = *(const u32x4*)p;
-                    } else if (k < kend && n < Nr) {
-                        rb[i][j] = (vecB && n + 8 <= Nr) ? *(const u32x4*)p : load8_elems(p, Nr - n);
-                    } else {
-                        rb[i][j] = zero4();
-                    }
-                }
-            }
+        for (int i = 0; i < T::B_IPW; ++i) {
+            const int g = i * T::NW + wave;
+            int k, col;
+            slotB<T>(g * 64 + lane, k, col);
+            col = min(col, c.Nr - 8);
+            const bool real = (T::B_GROUPS % T::NW == 0) || g < T::B_GROUPS;
+            b[i] = real ? (uint32_t)(k * c.ldb + col) : 0u;
         }
     }
 
-    // Registers -> LDS stage (A K-major as loaded, B transposed to N-major).
-    __device__ __forceinline__ void store(unsigned char* st, int tid) {
+    // Direct global->LDS loads of one full K step.
+    __device__ __forceinline__ void issue(const TileCtx& c, int k0, lds_t* stage, lds_t* junk, int wave) const {
+        const uint16_t* ab = c.A + k0;
+        const uint16_t* bb = c.B + (int64_t)k0 * c.ldb;
 #pragma unroll
-        for (int i = 0; i < T::NA; ++i) {
-            const int q = tid + i * T::NT;
-            if (T::A_CH % T::NT == 0 || q < T::A_CH) {
-                const int row = q / T::CPR, kc = q % T::CPR;
-                *(u32x4*)(st + row * T::ROWB + ((kc ^ swz<T::BK>(row)) << 4)) = ra[i];
-            }
+        for (int i = 0; i < T::A_IPW; ++i) {
+            const int g = i * T::NW + wave;
+            const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
+            __builtin_amdgcn_global_load_lds((const void*)(ab + a[i]), (void*)(real ? stage + g * 1024 : junk), 16,
+                                             0, 0);
         }
-        unsigned char* sb = st + T::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < T::NB; ++i) {
-            const int q = tid + i * T::NT;
-            if (T::B_Q % T::NT == 0 || q < T::B_Q) {
-                const int kq = q % (T::BK / 4), nq = q / (T::BK / 4);
-                const int c = kq >> 1, h = kq & 1;
-#pragma unroll
-                for (int nn = 0; nn < 8; ++nn) {
-                    const int n = nq * 8 + nn;
-                    const int w = nn >> 1, hi = nn & 1;
-                    const uint32_t d0 = half16(rb[i][0][w], hi) | (half16(rb[i][1][w], hi) << 16);
-                    const uint32_t d1 = half16(rb[i][2][w], hi) | (half16(rb[i][3][w], hi) << 16);
-                    *(u32x2*)(sb + n * T::ROWB + ((c ^ swz<T::BK>(n)) << 4) + h * 8) = u32x2{d0, d1};
-                }
-            }
+        for (int i = 0; i < T::B_IPW; ++i) {
+            const int g = i * T::NW + wave;
+            const bool real = (T::B_GROUPS % T::NW == 0) || g < T::B_GROUPS;
+            __builtin_amdgcn_global_load_lds((const void*)(bb + b[i]),
+                                             (void*)(real ? stage + T::A_BYTES + g * 1024 : junk), 16, 0, 0);
         }
     }
 };
+
+// Register path of one K step: bounded, zero-filled loads, then LDS writes
+// into the same swizzled layout the direct loads produce.  Slots move in
+// batches of four per thread to bound register use.
+template <class T>
+__device__ __forceinline__ u32x4 reg_load_a(const TileCtx& c, int k0, int p) {
+    int row, col;
+    slotA<T>(p, row, col);
+    const int k = k0 + col;
+    if (row < c.Mr && k < c.kend) {
+        const uint16_t* src = c.A + (int64_t)row * c.lda + k;
+        return (c.vecA && k + 8 <= c.kend) ? *(const u32x4*)src : load8_elems(src, c.kend - k);
+    }
+    return zero4();
+}
+
+template <class T>
+__device__ __forceinline__ u32x4 reg_load_b(const TileCtx& c, int k0, int p) {
+    int k, col;
+    slotB<T>(p, k, col);
+    const int kk = k0 + k;
+    if (kk < c.kend && col < c.Nr) {
+        const uint16_t* src = c.B + (int64_t)kk * c.ldb + col;
+        return (c.vecB && col + 8 <= c.Nr) ? *(const u32x4*)src : load8_elems(src, c.Nr - col);
+    }
+    return zero4();
+}
+
+template <class T>
+__device__ __noinline__ void reg_step(const TileCtx& c, int k0, lds_t* stage, int tid) {
+    constexpr int TOT = T::A_SLOTS + T::B_SLOTS;
+    for (int base = 0; base < TOT; base += 4 * T::NT) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = base + u * T::NT + tid;
+            v[u] = p < T::A_SLOTS ? reg_load_a<T>(c, k0, p) : (p < TOT ? reg_load_b<T>(c, k0, p - T::A_SLOTS) : zero4());
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = base + u * T::NT + tid;
+            if (p < TOT) *(u32x4 __attribute__((address_space(3)))*)(stage + p * 16) = v[u];
+        }
+    }
+}
+
+// One LDS stage through 32x32x16 MFMAs.  Fragments are double-buffered in
+// registers: the reads of K sub-step ks+1 are issued before the MFMAs of
+// sub-step ks and interleaved with them, so LDS latency hides behind MFMA
+// issue instead of stalling it.
+template <class T>
+__device__ __forceinline__ void read_frags32(const lds_t* sa, const lds_t* sb, int ks, int lane, int wm, int wn,
+                                             bf16x8 (&xb)[T::FN], bf16x8 (&ya)[T::FM]) {
+    // lane = 32h + 16cs + s16: K half h, column half cs
+    const int h = lane >> 5, cs = (lane >> 4) & 1, s16 = lane & 15;
+    const int kk = ks * 16;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+        const int seg = ((wn * T::WTN + j * 32) >> 4) + cs;
+        const int k1 = kk + 8 * h + (s16 >> 2), k2 = k1 + 4;
+        const int o = (s16 & 3) * 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(sb + k1 * T::B_ROWB + ((seg ^ swzB<T::BN, 32>(k1)) << 5) + o));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(sb + k2 * T::B_ROWB + ((seg ^ swzB<T::BN, 32>(k2)) << 5) + o));
+        xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+        const int row = wm * T::WTM + i * 32 + (lane & 31);
+        const int c1 = (kk >> 3) + h;
+        ya[i] = __builtin_bit_cast(bf16x8, *(const u32x4 __attribute__((address_space(3)))*)(
+                                                sa + row * T::A_ROWB + ((c1 ^ swzA<T::BK>(row)) << 4)));
+    }
+}
+
+template <class T, class Acc>
+__device__ __forceinline__ void compute_stage32(const lds_t* sa, const lds_t* sb, Acc (&acc)[T::FM][T::FN], int lane,
+                                                int wm, int wn) {
+    constexpr int NKS = T::BK / 16;
+    constexpr int READS = 2 * T::FN + T::FM;   // LDS reads per sub-step
+    constexpr int MFMAS = T::FM * T::FN;
+    constexpr int PER = (READS + MFMAS - 1) / MFMAS;
+    bf16x8 xb[2][T::FN], ya[2][T::FM];
+    read_frags32<T>(sa, sb, 0, lane, wm, wn, xb[0], ya[0]);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < NKS) read_frags32<T>(sa, sb, ks + 1, lane, wm, wn, xb[cur ^ 1], ya[cur ^ 1]);
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[cur][j], ya[cur][i], acc[i][j], 0, 0, 0);
+        if (ks + 1 < NKS) {
+            // one MFMA, then up to PER reads of the next sub-step, repeated
+#pragma unroll
+            for (int t = 0; t < MFMAS; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (t * PER < READS) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+            }
+        }
+    }
+}
 
 // Map the flat workgroup id to (tile_m, tile_n, split, batch).  Workgroups
 // are dealt round-robin to the 8 XCDs; ids are first regrouped so that each
@@ -188,7 +330,9 @@ __device__ __forceinline__ void map_tile(int bid, int G, int tiles_m, int tiles_
 
 template <class T>
 __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[T::LDS];
+    lds_t* smem = (lds_t*)smem_raw;
+    lds_t* junk = smem + T::S * T::STAGE;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % T::WGM, wn = wave / T::WGM;
@@ -196,82 +340,118 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
     int tm, tn, split, b;
     map_tile<8>(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, args.splits, tm, tn, split, b);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
-    const uint16_t* __restrict__ A = args.A + (int64_t)b * args.sA + (int64_t)m0 * args.lda;
-    const uint16_t* __restrict__ B = args.B + (int64_t)b * args.sB + n0;
-    const int Mr = args.M - m0, Nr = args.N - n0;
+    TileCtx c;
+    c.A = args.A + (int64_t)b * args.sA + (int64_t)m0 * args.lda;
+    c.B = args.B + (int64_t)b * args.sB + n0;
+    c.lda = args.lda;
+    c.ldb = args.ldb;
+    c.Mr = args.M - m0;
+    c.Nr = args.N - n0;
     const int kbeg = split * args.steps_per_split * T::BK;
-    const int kend = min(args.K, kbeg + args.steps_per_split * T::BK);
-    const int nsteps = (kend - kbeg + T::BK - 1) / T::BK;
+    c.kend = min(args.K, kbeg + args.steps_per_split * T::BK);
+    c.vecA = args.flags & KF_VEC_A;
+    c.vecB = args.flags & KF_VEC_B;
+    const int nsteps = (c.kend - kbeg + T::BK - 1) / T::BK;
+    // direct loads need 16-byte aligned rows, 32-bit tile offsets (host
+    // clears the vector flags for leading dimensions too large for them)
+    // and, on the last tile column, N a multiple of 8
+    const bool dma_tile = c.vecA && c.vecB && (c.Nr >= T::BN || (args.N & 7) == 0);
+    const int dma_steps = dma_tile ? (c.kend - kbeg) / T::BK : 0;   // full steps
 
-    const bool vecA = args.flags & KF_VEC_A, vecB = args.flags & KF_VEC_B;
-    const bool tile_fast = vecA && vecB && Mr >= T::BM && Nr >= T::BN;
+    DmaOffsets<T> dma;
+    if (dma_tile) dma.init(c, wave, lane);
+    auto load_step = [&](int s) {
+        lds_t* st = smem + (s % T::S) * T::STAGE;
+        const int k0 = kbeg + s * T::BK;
+        if (s < dma_steps) dma.issue(c, k0, st, junk, wave);
+        else reg_step<T>(c, k0, st, tid);
+    };
 
-    f32x4 acc[T::FM][T::FN];
+    using acc_t = typename std::conditional<T::MF == 32, f32x16, f32x4>::type;
+    acc_t acc[T::FM][T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < T::FN; ++j) acc[i][j] = acc_t{};
 
-    Pipe<T> pipe;
-    {
-        const bool fast = tile_fast && kbeg + T::BK <= kend;
-        pipe.load(A, args.lda, B, args.ldb, kbeg, kend, Mr, Nr, fast, vecA, vecB, tid);
-        pipe.store(smem, tid);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < T::S - 1; ++s)
+        if (s < nsteps) load_step(s);
 
-    const int frow = lane & 15, fchunk = lane >> 4;
+    const int g4 = lane >> 4, s16 = lane & 15;
     for (int s = 0; s < nsteps; ++s) {
-        unsigned char* cur = smem + (s & 1) * T::STAGE;
-        const bool more = s + 1 < nsteps;
-        if (more) {
-            const int k0 = kbeg + (s + 1) * T::BK;
-            const bool fast = tile_fast && k0 + T::BK <= kend;
-            pipe.load(A, args.lda, B, args.ldb, k0, kend, Mr, Nr, fast, vecA, vecB, tid);
-        }
+        wait_step<T>(min(T::S - 2, nsteps - 1 - s));
+        if (s + T::S - 1 < nsteps) load_step(s + T::S - 1);
+        const lds_t* sa = smem + (s % T::S) * T::STAGE;
+        const lds_t* sb = sa + T::A_BYTES;
+        if constexpr (T::MF == 32) {
+            compute_stage32<T>(sa, sb, acc, lane, wm, wn);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < T::BK / 32; ++ks) {
-            const int c = ks * 4 + fchunk;
-            u32x4 xb[T::FN], ya[T::FM];
+            for (int ks = 0; ks < T::BK / 32; ++ks) {
+                const int kk = ks * 32;
+                bf16x8 xb[T::FN], ya[T::FM];
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
-                const int row = wn * T::WTN + j * 16 + frow;
-                xb[j] = *(const u32x4*)(cur + T::A_BYTES + row * T::ROWB + ((c ^ swz<T::BK>(row)) << 4));
+                for (int j = 0; j < T::FN; ++j) {
+                    const int seg = (wn * T::WTN + j * 16) >> 4;
+                    const int k1 = kk + 4 * g4 + (s16 >> 2), k2 = k1 + 16;
+                    const int o = (s16 & 3) * 8;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
+                        sb + k1 * T::B_ROWB + ((seg ^ swzB<T::BN, 16>(k1)) << 5) + o));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
+                        sb + k2 * T::B_ROWB + ((seg ^ swzB<T::BN, 16>(k2)) << 5) + o));
+                    xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+#pragma unroll
+                for (int i = 0; i < T::FM; ++i) {
+                    const int row = wm * T::WTM + i * 16 + s16;
+                    const int c1 = (kk >> 3) + (g4 >> 1), hb = (g4 & 1) * 8;
+                    const u32x2 lo = *(const u32x2 __attribute__((address_space(3)))*)(
+                        sa + row * T::A_ROWB + ((c1 ^ swzA<T::BK>(row)) << 4) + hb);
+                    const u32x2 hi = *(const u32x2 __attribute__((address_space(3)))*)(
+                        sa + row * T::A_ROWB + (((c1 + 2) ^ swzA<T::BK>(row)) << 4) + hb);
+                    ya[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+                }
+#pragma unroll
+                for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < T::FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], ya[i], acc[i][j], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < T::FM; ++i) {
-                const int row = wm * T::WTM + i * 16 + frow;
-                ya[i] = *(const u32x4*)(cur + row * T::ROWB + ((c ^ swz<T::BK>(row)) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, xb[j]), __builtin_bit_cast(bf16x8, ya[i]), acc[i][j], 0, 0, 0);
         }
-        if (more) pipe.store(smem + ((s + 1) & 1) * T::STAGE, tid);
-        __syncthreads();
     }
 
-    // Epilogue: lane holds C[m][n..n+3] of each fragment.
+    // Epilogue: every lane holds runs of four consecutive columns of one C row.
     float* __restrict__ C = args.C + (int64_t)b * args.sC + (int64_t)split * args.sCsplit +
                             (int64_t)m0 * args.ldc + n0;
     const bool vecC = args.flags & KF_VEC_C;
+    auto store4 = [&](int m, int n, f32x4 v) {
+        if (m >= c.Mr) return;
+        float* p = C + (int64_t)m * args.ldc + n;
+        if (vecC && n + 4 <= c.Nr) {
+            *(f32x4*)p = v;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < c.Nr) p[r] = v[r];
+        }
+    };
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-        const int m = wm * T::WTM + i * 16 + frow;
-        if (m >= Mr) continue;
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) {
-            const int n = wn * T::WTN + j * 16 + fchunk * 4;
-            float* p = C + (int64_t)m * args.ldc + n;
-            if (vecC && n + 4 <= Nr) {
-                *(f32x4*)p = acc[i][j];
-            } else {
+            if constexpr (T::MF == 32) {
+                // 32x32 block: lane holds rows (lane&31), columns 8q + 4h + (0..3)
+                const int m = wm * T::WTM + i * 32 + (lane & 31);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < Nr) p[r] = acc[i][j][r];
+                for (int q = 0; q < 4; ++q) {
+                    const int n = wn * T::WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+                    store4(m, n, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+                }
+            } else {
+                const int m = wm * T::WTM + i * 16 + s16;
+                const int n = wn * T::WTN + j * 16 + g4 * 4;
+                store4(m, n, acc[i][j]);
             }
         }
     }
@@ -333,18 +513,20 @@ __global__ __launch_bounds__(256) void fill_random_bf16_kernel(uint16_t* p, int6
     }
 }
 
-// The library: tile shapes and their wave layouts.
-using T_256x256 = Tile<256, 256, 64, 2, 2>;
-using T_256x128 = Tile<256, 128, 64, 2, 2>;
-using T_128x256 = Tile<128, 256, 64, 2, 2>;
-using T_128x128 = Tile<128, 128, 64, 2, 2>;
-using T_128x64 = Tile<128, 64, 64, 2, 2>;
-using T_64x128 = Tile<64, 128, 64, 2, 2>;
-using T_64x64 = Tile<64, 64, 64, 2, 2>;
-using T_32x128 = Tile<32, 128, 128, 1, 4>;
-using T_16x128 = Tile<16, 128, 128, 1, 4>;
-using T_16x256 = Tile<16, 256, 128, 1, 4>;
-using T_32x64 = Tile<32, 64, 128, 2, 2>;
+// The library: tile shapes, wave layouts and LDS stage counts.  The large
+// tiles run 8 waves (two per SIMD) so one wave's LDS waits overlap the
+// other's MFMAs; 128x128 runs two 4-wave workgroups per CU.
+using T_256x256 = Tile<256, 256, 64, 4, 2, 2>;
+using T_256x128 = Tile<256, 128, 64, 4, 2, 3>;
+using T_128x256 = Tile<128, 256, 64, 2, 4, 3>;
+using T_128x128 = Tile<128, 128, 64, 2, 2, 2>;
+using T_128x64 = Tile<128, 64, 64, 2, 2, 3>;
+using T_64x128 = Tile<64, 128, 64, 2, 2, 3>;
+using T_64x64 = Tile<64, 64, 64, 2, 2, 4>;
+using T_32x128 = Tile<32, 128, 64, 1, 4, 4>;
+using T_16x128 = Tile<16, 128, 64, 1, 4, 4>;
+using T_16x256 = Tile<16, 256, 64, 1, 4, 4>;
+using T_32x64 = Tile<32, 64, 64, 2, 2, 4>;
 
 #define MKP_KERNEL(NAME, T) \
     { NAME, T::BM, T::BN, T::BK, T::NT, T::LDS, (const void*)&gemm_tile_kernel<T>, &launch_tile<T> }
@@ -357,10 +539,10 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m128n64k64", T_128x64),
     MKP_KERNEL("m64n128k64", T_64x128),
     MKP_KERNEL("m64n64k64", T_64x64),
-    MKP_KERNEL("m32n128k128", T_32x128),
-    MKP_KERNEL("m16n128k128", T_16x128),
-    MKP_KERNEL("m16n256k128", T_16x256),
-    MKP_KERNEL("m32n64k128", T_32x64),
+    MKP_KERNEL("m32n128k64", T_32x128),
+    MKP_KERNEL("m16n128k64", T_16x128),
+    MKP_KERNEL("m16n256k64", T_16x256),
+    MKP_KERNEL("m32n64k64", T_32x64),
 };
 
 }  // namespace
