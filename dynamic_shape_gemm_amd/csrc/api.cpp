@@ -71,6 +71,11 @@ struct Workspace {
     size_t bytes = 0;
 };
 
+// Split-K workspace layout: kCounterCap arrival counters (int32), then the
+// partial tiles [splits][batch][m][ldw] (fp32, ldw = n rounded up to 4).
+constexpr int kCounterCap = 1 << 16;
+constexpr size_t kCounterBytes = (size_t)kCounterCap * 4;
+
 struct TraceRec {
     int kernel;            // library kernel index, -1 = split-K reduction, -2 = zero fill
     double flops, bytes;   // algorithmic work of the launch
@@ -91,6 +96,7 @@ struct Library {
     std::atomic<int64_t> hits{0}, misses{0}, launches{0};
     std::atomic<int64_t> plan_ns{0};
 
+    std::atomic<bool> fused_reduce{false};        // split-K: fused last-arrival sum (else 2 passes)
     std::atomic<bool> trace{false};               // time every launch with events
     std::mutex trace_mu;
     std::vector<TraceRec> trace_recs;
@@ -267,6 +273,13 @@ int get_workspace(int dev, hipStream_t st, size_t bytes, void** out) {
             (void)hipGetLastError();
             return fail(MKP_ERR_OOM, "split-K workspace of " + std::to_string(want) + " bytes: allocation failed");
         }
+        // the fused reduction's arrival counters start at zero (and every
+        // launch leaves them at zero)
+        e = launch_zero_fill((float*)p, kCounterCap, 0, 1, kCounterCap, 1, st);
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(p, st);
+            return fail(MKP_ERR_HIP, std::string("workspace clear: ") + hipGetErrorString(e));
+        }
         w.ptr = p;
         w.bytes = want;
     }
@@ -355,7 +368,8 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     for (auto& r : plan->regions)
         if (r.s > 1) {
             const int64_t ldw = (r.n + 3) & ~int64_t(3);
-            ws_bytes = std::max(ws_bytes, (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float));
+            ws_bytes = std::max(ws_bytes, kCounterBytes + (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw *
+                                                              sizeof(float));
         }
     void* ws = nullptr;
     if (ws_bytes) {
@@ -368,7 +382,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         const int li = r.lib;
         if (li < 0 || li >= kernel_count()) return fail(MKP_ERR_UNSUPPORTED, "plan kernel is not launchable");
         const KernelInfo& ki = kernel_info(li);
-        KArgs a;
+        KArgs a{};
         a.A = A + r.m0 * lda;
         a.B = B + r.n0;
         a.lda = lda;
@@ -393,12 +407,20 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
             a.sCsplit = 0;
             a.flags |= vC ? KF_VEC_C : 0;
         } else {
-            a.C = (float*)ws;
+            a.C = (float*)((char*)ws + kCounterBytes);
             a.ldc = ldw;
             a.sC = r.m * ldw;
             a.sCsplit = batch * r.m * ldw;
             a.flags |= KF_VEC_C;
         }
+        // fused reduction when the per-tile counters fit, else a second pass
+        const bool fused = r.s > 1 && L.fused_reduce.load(std::memory_order_relaxed) &&
+                           (int64_t)a.tiles_m * a.tiles_n * batch <= kCounterCap;
+        a.counters = fused ? (int*)ws : nullptr;
+        a.Cout = Creg;
+        a.ldcout = ldc;
+        a.sCout = sC;
+        if (vC) a.flags |= KF_VEC_COUT;
         const int64_t G = (int64_t)a.tiles_m * a.tiles_n * a.splits * batch;
         if (G > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
         const double flops = 2.0 * r.m * r.n * K * batch;
@@ -406,9 +428,9 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         he = traced(L, st, li, flops, bytes, [&] { return ki.launch(a, dim3((unsigned)G), st); });
         if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
         L.launches.fetch_add(1, std::memory_order_relaxed);
-        if (r.s > 1) {
+        if (r.s > 1 && !fused) {
             he = traced(L, st, -1, 0.0, (double)(r.s + 1) * 4.0 * r.m * r.n * batch, [&] {
-                return launch_splitk_reduce((const float*)ws, r.s, batch * r.m * ldw, r.m * ldw, ldw, Creg, ldc, sC,
+                return launch_splitk_reduce(a.C, r.s, batch * r.m * ldw, r.m * ldw, ldw, Creg, ldc, sC,
                                             (int)r.m, (int)r.n, (int)batch, vC ? 1 : 0, st);
             });
             if (he != hipSuccess)
@@ -529,6 +551,9 @@ int mkp_set_option(const char* key, const char* value) {
         if (v == "I") L.opts.allow_II = false;
         else if (v == "I,II" || v == "II") L.opts.allow_II = true;
         else return fail(MKP_ERR_INVALID_ARG, "patterns must be I or I,II");
+    } else if (k == "fused_reduce") {
+        L.fused_reduce.store(std::atoi(v.c_str()) != 0);
+        return MKP_OK;
     } else if (k == "trace") {
         L.trace.store(std::atoi(v.c_str()) != 0);
         return MKP_OK;

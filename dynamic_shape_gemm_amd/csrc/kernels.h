@@ -16,6 +16,7 @@ enum : int {
     KF_VEC_A = 1,   // A rows 16-byte aligned: 128-bit loads allowed
     KF_VEC_B = 2,   // B rows 16-byte aligned
     KF_VEC_C = 4,   // C rows 16-byte aligned: 128-bit stores allowed
+    KF_VEC_COUT = 8,  // final C rows (fused split-K) 16-byte aligned
 };
 
 struct KArgs {
@@ -31,6 +32,13 @@ struct KArgs {
     int splits;           // K splits (grid covers tiles x splits x batch)
     int batch;
     int flags;
+    // Fused split-K reduction (splits > 1 and counters != nullptr): C above is
+    // the partial workspace; the last split of a tile to finish sums the
+    // partials in split order into Cout.  counters: one int per tile and batch
+    // entry, zero before the launch and left zero after it.
+    int* counters;
+    float* Cout;
+    int64_t ldcout, sCout;
 };
 
 struct KernelInfo {

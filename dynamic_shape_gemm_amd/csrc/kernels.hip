@@ -227,7 +227,7 @@ __device__ __forceinline__ u32x4 reg_load_b(const TileCtx& c, int k0, int p) {
 }
 
 template <class T>
-__device__ __noinline__ void reg_step(const TileCtx& c, int k0, lds_t* stage, int tid) {
+__device__ __forceinline__ void reg_step(const TileCtx& c, int k0, lds_t* stage, int tid) {
     constexpr int TOT = T::A_SLOTS + T::B_SLOTS;
     for (int base = 0; base < TOT; base += 4 * T::NT) {
         u32x4 v[4];
@@ -425,10 +425,10 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
     float* __restrict__ C = args.C + (int64_t)b * args.sC + (int64_t)split * args.sCsplit +
                             (int64_t)m0 * args.ldc + n0;
     const bool vecC = args.flags & KF_VEC_C;
-    auto store4 = [&](int m, int n, f32x4 v) {
+    auto store4 = [&](float* base, int64_t ld, bool vec, int m, int n, f32x4 v) {
         if (m >= c.Mr) return;
-        float* p = C + (int64_t)m * args.ldc + n;
-        if (vecC && n + 4 <= c.Nr) {
+        float* p = base + (int64_t)m * ld + n;
+        if (vec && n + 4 <= c.Nr) {
             *(f32x4*)p = v;
         } else {
 #pragma unroll
@@ -436,25 +436,65 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
                 if (n + r < c.Nr) p[r] = v[r];
         }
     };
+    // visit every (row, first column, 4 values) the lane holds
+    auto for_each4 = [&](auto&& fn) {
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
+        for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-            if constexpr (T::MF == 32) {
-                // 32x32 block: lane holds rows (lane&31), columns 8q + 4h + (0..3)
-                const int m = wm * T::WTM + i * 32 + (lane & 31);
+            for (int j = 0; j < T::FN; ++j) {
+                if constexpr (T::MF == 32) {
+                    // 32x32 block: lane holds row (lane&31), columns 8q + 4h + (0..3)
+                    const int m = wm * T::WTM + i * 32 + (lane & 31);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = wn * T::WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-                    store4(m, n, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = wn * T::WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+                        fn(m, n, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                       acc[i][j][4 * q + 3]});
+                    }
+                } else {
+                    fn(wm * T::WTM + i * 16 + s16, wn * T::WTN + j * 16 + g4 * 4, acc[i][j]);
                 }
-            } else {
-                const int m = wm * T::WTM + i * 16 + s16;
-                const int n = wn * T::WTN + j * 16 + g4 * 4;
-                store4(m, n, acc[i][j]);
             }
         }
+    };
+    if (args.splits > 1 && args.counters != nullptr) {
+        // Fused split-K reduction.  Every split stores its partial tile; once
+        // all waves' stores have completed, wave 0 alone publishes them at
+        // agent scope (one L2 write-back per workgroup) and counts the
+        // arrival.  The last split to arrive makes the other splits' partials
+        // visible (one L2/L1 invalidate) and sums them in split order -- the
+        // same order whichever split arrives last.
+        __shared__ int s_last;
+        float* Wt = args.C + (int64_t)b * args.sC + (int64_t)m0 * args.ldc + n0;   // split 0's tile
+        for_each4([&](int m, int n, f32x4 v) { store4(C, args.ldc, vecC, m, n, v); });
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
+        __syncthreads();
+        int* cnt = args.counters + (int64_t)b * args.tiles_m * args.tiles_n + tm * args.tiles_n + tn;
+        if (wave == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            int last = 0;
+            if (lane == 0)
+                last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.splits - 1;
+            last = __builtin_amdgcn_readfirstlane(last);
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (lane == 0) s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        float* Co = args.Cout + (int64_t)b * args.sCout + (int64_t)m0 * args.ldcout + n0;
+        const bool vecCo = args.flags & KF_VEC_COUT;
+        for_each4([&](int m, int n, f32x4 own) {
+            if (m >= c.Mr || n >= c.Nr) return;
+            const float* w = Wt + (int64_t)m * args.ldc + n;   // workspace rows: 16-byte aligned
+            f32x4 sum = split == 0 ? own : *(const f32x4*)w;
+            for (int z = 1; z < args.splits; ++z)
+                sum += z == split ? own : *(const f32x4*)(w + (int64_t)z * args.sCsplit);
+            store4(Co, args.ldcout, vecCo, m, n, sum);
+        });
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
+    for_each4([&](int m, int n, f32x4 v) { store4(C, args.ldc, vecC, m, n, v); });
 }
 
 template <class T>

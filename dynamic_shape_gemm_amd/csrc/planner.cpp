@@ -173,39 +173,111 @@ double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64
 
 namespace {
 
+// Candidate strategies (MikPoly page, section 3 polymerization patterns;
+// GPU uses patterns I and II):
+//   I    : one region, one kernel, the whole M x N.
+//   II-M : rows [0, cut) on kernel a, rows [cut, M) on kernel b != a, where
+//          the cut is a wave boundary of region 1: the largest multiple of
+//          uM(a) whose tasks fill exactly w waves of kernel a (w = 1, 2, ...),
+//          as in the case study where region 1 is one full wave of kernel A.
+//   II-N : the same along N.
+// Every region takes its own split factor.  The search visits Pattern I
+// first (a tight bound), then the II cuts in increasing w, and stops as soon
+// as a partial cost plus a lower bound for the rest reaches the best found.
 struct Searcher {
     const PerfTable& tab;
     const SearchOptions& opt;
     int64_t batch, M, N, K;
     int64_t evaluated = 0;
-    std::vector<int> splits;   // allowed requested factors
+
+    struct SplitChoice {
+        int s_eff;
+        int per;
+        double g;
+    };
+    std::vector<std::vector<SplitChoice>> sc;   // per kernel: distinct usable splits
+    std::vector<double> min_g;                   // per kernel: cheapest single wave
+    std::vector<double> rate;                    // per kernel: lowest cost per output element
+    double lb_region = 0.0;                      // lower bound of any region's cost
+    double min_rate = 0.0;                       // lowest rate over allowed kernels
+
+    // Lower bound of a region of m x n on kernel b: its tasks fill at least
+    // m*n*s/(uM*uN*slots) (fractional) waves of g each; launch cost on top.
+    double lb(int b, int64_t m, int64_t n) const {
+        return tab.launch_us + std::max(min_g[b], (double)m * (double)n * (double)batch * rate[b]);
+    }
 
     Searcher(const PerfTable& t, const SearchOptions& o, int64_t b, int64_t m, int64_t n, int64_t k)
         : tab(t), opt(o), batch(b), M(m), N(n), K(k) {
+        std::vector<int> req;
         if (opt.force_splitk > 0) {
-            splits.push_back(opt.force_splitk);
+            req.push_back(opt.force_splitk);
         } else {
             for (int s : tab.splits)
-                if (s <= opt.splitk_max) splits.push_back(s);
-            if (splits.empty()) splits.push_back(1);
+                if (s <= opt.splitk_max) req.push_back(s);
+            if (req.empty()) req.push_back(1);
+        }
+        sc.resize(tab.kernels.size());
+        min_g.assign(tab.kernels.size(), std::numeric_limits<double>::infinity());
+        rate.assign(tab.kernels.size(), std::numeric_limits<double>::infinity());
+        lb_region = std::numeric_limits<double>::infinity();
+        min_rate = std::numeric_limits<double>::infinity();
+        for (size_t ki = 0; ki < tab.kernels.size(); ++ki) {
+            const TableKernel& kk = tab.kernels[ki];
+            const int64_t t3 = ceil_div(K, kk.uK);
+            for (int s_req : req) {
+                // a factor above the K-step count is only kept when forced
+                if (s_req > 1 && s_req > t3 && opt.force_splitk <= 0) continue;
+                const int64_t sr = std::min<int64_t>(s_req, std::max<int64_t>(t3, 1));
+                const int64_t per = ceil_div(t3, sr);
+                const int s_eff = (int)ceil_div(t3, per);
+                bool dup = false;
+                for (auto& c : sc[ki]) dup |= c.s_eff == s_eff;
+                if (dup) continue;
+                sc[ki].push_back({s_eff, (int)per, g_predict(kk, (double)per)});
+                min_g[ki] = std::min(min_g[ki], sc[ki].back().g);
+                const double slots = (double)tab.cus * kk.wg_per_cu;
+                rate[ki] = std::min(rate[ki], (double)s_eff * sc[ki].back().g / (slots * kk.uM * kk.uN));
+            }
+            if (kernel_allowed((int)ki)) {
+                lb_region = std::min(lb_region, tab.launch_us + min_g[ki]);
+                min_rate = std::min(min_rate, rate[ki]);
+            }
         }
     }
 
     bool kernel_allowed(int k) const { return opt.force_kernel < 0 || opt.force_kernel == k; }
 
-    // best split for one region; returns cost and fills r
-    double best_region(int kernel, int64_t m, int64_t n, Region* r) {
-        const int64_t t3 = ceil_div(K, tab.kernels[kernel].uK);
+    double cost(int ki, const SplitChoice& c, int64_t m, int64_t n, Region* r) {
+        ++evaluated;
+        const TableKernel& k = tab.kernels[ki];
+        const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * c.s_eff * batch;
+        const int64_t waves = ceil_div(tasks, (int64_t)tab.cus * k.wg_per_cu);
+        double v = tab.launch_us + (double)waves * c.g;
+        if (c.s_eff > 1)
+            v += tab.red_launch_us +
+                 (double)(2 * c.s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch / (tab.red_gbps * 1e3);
+        if (r) {
+            r->kernel = ki;
+            r->lib = k.lib_index;
+            r->m = m;
+            r->n = n;
+            r->s = c.s_eff;
+            r->steps = c.per;
+            r->tasks = tasks;
+            r->waves = waves;
+            r->cost = v;
+        }
+        return v;
+    }
+
+    double best_region(int ki, int64_t m, int64_t n, Region* r) {
         double best = std::numeric_limits<double>::infinity();
-        for (int s_req : splits) {
-            // a factor above the K-step count degenerates to one step per split
-            const int s = (int)std::min<int64_t>(s_req, std::max<int64_t>(t3, 1));
-            if (s != s_req && opt.force_splitk <= 0) continue;
+        for (auto& c : sc[ki]) {
             Region tmp;
-            ++evaluated;
-            double c = region_cost(tab, kernel, m, n, K, batch, s, &tmp);
-            if (c < best) {
-                best = c;
+            const double v = cost(ki, c, m, n, &tmp);
+            if (v < best) {
+                best = v;
                 *r = tmp;
             }
         }
@@ -220,12 +292,11 @@ struct Searcher {
             for (int a = 0; a < nk; ++a) {
                 if (!kernel_allowed(a)) continue;
                 Region r;
-                double c = best_region(a, M, N, &r);
+                const double c = best_region(a, M, N, &r);
                 if (c < best.cost_us) {
                     best.pattern = PAT_I;
                     best.cost_us = c;
-                    r.m0 = 0;
-                    r.n0 = 0;
+                    r.m0 = r.n0 = 0;
                     best.regions.assign(1, r);
                 }
             }
@@ -236,29 +307,43 @@ struct Searcher {
             if (dir == 1 && !tab.pat_IIN) continue;
             const int64_t ext = dir == 0 ? M : N;
             for (int a = 0; a < nk; ++a) {
-                const int64_t step = dir == 0 ? tab.kernels[a].uM : tab.kernels[a].uN;
-                for (int64_t cut = step; cut < ext; cut += step) {
-                    Region r1;
-                    const double c1 = dir == 0 ? best_region(a, cut, N, &r1) : best_region(a, M, cut, &r1);
-                    // region-1 cost never falls as the cut grows: prune the rest
-                    if (!opt.exhaustive && c1 >= best.cost_us) break;
-                    for (int b = 0; b < nk; ++b) {
-                        if (b == a) continue;
-                        Region r2;
-                        const double c2 = dir == 0 ? best_region(b, M - cut, N, &r2)
-                                                   : best_region(b, M, N - cut, &r2);
-                        const double c = c1 + c2;
-                        if (c < best.cost_us) {
-                            best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
-                            best.cost_us = c;
-                            if (dir == 0) {
-                                r1.m0 = 0; r1.n0 = 0;
-                                r2.m0 = cut; r2.n0 = 0;
-                            } else {
-                                r1.m0 = 0; r1.n0 = 0;
-                                r2.m0 = 0; r2.n0 = cut;
+                const TableKernel& ka = tab.kernels[a];
+                const int64_t step = dir == 0 ? ka.uM : ka.uN;
+                // tiles across the uncut dimension
+                const int64_t across = dir == 0 ? ceil_div(N, ka.uN) : ceil_div(M, ka.uM);
+                const int64_t slots = (int64_t)tab.cus * ka.wg_per_cu;
+                for (auto& c1s : sc[a]) {
+                    const int64_t per_line = across * c1s.s_eff * batch;   // tasks per tile row (column)
+                    int64_t prev_cut = 0;
+                    for (int64_t w = 1;; ++w) {
+                        const int64_t lines = w * slots / per_line;
+                        const int64_t cut = lines * step;
+                        if (cut >= ext) break;
+                        if (cut == 0 || cut == prev_cut) continue;
+                        prev_cut = cut;
+                        Region r1;
+                        const double c1 = dir == 0 ? cost(a, c1s, cut, N, &r1) : cost(a, c1s, M, cut, &r1);
+                        // c1 grows with w: once it cannot lead to a better plan, stop
+                        if (!opt.exhaustive && c1 + lb_region >= best.cost_us) break;
+                        const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
+                        if (!opt.exhaustive &&
+                            c1 + tab.launch_us + std::max((double)m2 * n2 * batch * min_rate, lb_region - tab.launch_us) >=
+                                best.cost_us)
+                            continue;
+                        for (int b = 0; b < nk; ++b) {
+                            if (b == a) continue;
+                            if (!opt.exhaustive && c1 + lb(b, m2, n2) >= best.cost_us) continue;
+                            Region r2;
+                            const double c2 = dir == 0 ? best_region(b, M - cut, N, &r2) : best_region(b, M, N - cut, &r2);
+                            const double c = c1 + c2;
+                            if (c < best.cost_us) {
+                                best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
+                                best.cost_us = c;
+                                r1.m0 = r1.n0 = 0;
+                                r2.m0 = dir == 0 ? cut : 0;
+                                r2.n0 = dir == 0 ? 0 : cut;
+                                best.regions.assign({r1, r2});
                             }
-                            best.regions.assign({r1, r2});
                         }
                     }
                 }

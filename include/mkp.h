@@ -121,8 +121,11 @@ int mkp_calibrate(const char *path, int max_points);
 
 /* Set an option: "force_kernel" (kernel name or ""), "force_splitk" (integer,
  * 0 = free), "patterns" ("I" or "I,II"), "exhaustive" (0/1),
- * "splitk_max" (integer), "trace" (0/1, see mkp_trace_dump).  Every option
- * but "trace" clears the plan cache.  Returns MKP_OK or
+ * "splitk_max" (integer), "trace" (0/1, see mkp_trace_dump), "fused_reduce"
+ * (0 = split-K partials summed by a second launch, the default; 1 = summed
+ * by the last-arriving workgroup of each tile, which on MI355X costs more in
+ * L2 write-back than the second launch).  "exhaustive", "force_*", "patterns" and
+ * "splitk_max" clear the plan cache.  Returns MKP_OK or
  * MKP_ERR_INVALID_ARG / MKP_ERR_UNSUPPORTED. */
 int mkp_set_option(const char *key, const char *value);
 

@@ -26,8 +26,11 @@ Readings where the page is silent (each is listed in the design doc):
   * g between measured points is linear; beyond the last point it continues
     the last segment's slope.
   * Pattern I: one region = whole output, one kernel.  Pattern II-M (II-N):
-    a cut of the M (N) extent at a multiple of the first kernel's tile, the
-    two parts on two different kernels (the case study's 3072 | 1024 cut).
+    a cut of the M (N) extent, the two parts on two different kernels (the
+    case study's 3072 | 1024 split).  The cut is a wave boundary of the
+    first region: the largest multiple of kernel a's tile whose tasks fill
+    exactly w whole waves of a (w = 1, 2, ...), the case study's first region
+    being one full wave of kernel A.  Each region has its own split factor.
 """
 from __future__ import annotations
 
@@ -166,17 +169,30 @@ def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1):
         for a in names:
             for s in _valid_splits(tab, tab.kernels[a], K):
                 yield "I", (Region(0, 0, M, N, a, s),)
-    for pat, ext, tile_of in (("II-M", M, lambda k: k.uM), ("II-N", N, lambda k: k.uN)):
+    for pat in ("II-M", "II-N"):
         if pat not in tab.patterns:
             continue
+        ext = M if pat == "II-M" else N
         for a in names:
             ka = tab.kernels[a]
-            step = tile_of(ka)
-            for cut in range(step, ext, step):
-                for b in names:
-                    if b == a:
+            step = ka.uM if pat == "II-M" else ka.uN
+            across = ceil_div(N, ka.uN) if pat == "II-M" else ceil_div(M, ka.uM)
+            t3 = ceil_div(K, ka.uK)
+            for s1 in _valid_splits(tab, ka, K):
+                s1_eff = split_steps(t3, s1)[1]
+                per_line = across * s1_eff * batch
+                prev, w = 0, 0
+                while True:
+                    w += 1
+                    cut = (w * tab.slots(ka) // per_line) * step
+                    if cut >= ext:
+                        break
+                    if cut == 0 or cut == prev:
                         continue
-                    for s1 in _valid_splits(tab, ka, K):
+                    prev = cut
+                    for b in names:
+                        if b == a:
+                            continue
                         for s2 in _valid_splits(tab, tab.kernels[b], K):
                             if pat == "II-M":
                                 r1 = Region(0, 0, cut, N, a, s1)

@@ -97,15 +97,49 @@ def test_each_kernel_forced(mkp, split):
         mkp.mkp_set_option("force_splitk", 0)
 
 
+@pytest.mark.parametrize("fused", [1, 0])
 @pytest.mark.parametrize("s", [2, 4, 8, 32])
-def test_splitk(mkp, s):
+def test_splitk(mkp, s, fused):
     rng = np.random.default_rng(100 + s)
     try:
         mkp.mkp_set_option("force_splitk", s)
-        for (M, N, K) in [(33, 700, 4097), (200, 300, 2000)]:
-            run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"splitk {s}")
+        mkp.mkp_set_option("fused_reduce", fused)
+        for (M, N, K) in [(33, 700, 4097), (200, 300, 2000), (1, 4096, 4096)]:
+            run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"splitk {s} fused={fused}")
     finally:
         mkp.mkp_set_option("force_splitk", 0)
+        mkp.mkp_set_option("fused_reduce", 0)
+
+
+def test_splitk_repeated_calls_reuse_counters(mkp):
+    """Back-to-back fused split-K calls on one stream (counters must return
+    to zero after every launch) and batched split-K."""
+    import torch
+    rng = np.random.default_rng(321)
+    try:
+        mkp.mkp_set_option("force_splitk", 8)
+        mkp.mkp_set_option("fused_reduce", 1)
+        for it in range(3):
+            run_case(mkp, rand_bits(rng, (70, 3000)), rand_bits(rng, (3000, 500)),
+                     what=f"repeat {it}")
+        batch, M, N, K = 5, 40, 300, 2048
+        a = rand_bits(rng, (batch, M, K))
+        b = rand_bits(rng, (batch, K, N))
+        print("[case] batched split-K", flush=True)
+        ta, pa = dev_bf16(a)
+        tb, pb = dev_bf16(b)
+        tc = torch.full((batch * M * N + 64,), float("nan"), dtype=torch.float32, device="cuda")
+        mkp.mkp_gemm_batched(batch, M, N, K, pa, K, M * K, pb, N, K * N, tc.data_ptr(), N, M * N)
+        torch.cuda.synchronize()
+        h = tc.cpu().numpy()
+        assert np.isnan(h[batch * M * N:]).all()
+        got = h[:batch * M * N].reshape(batch, M, N).astype(np.float64)
+        ref, refabs = oracle.gemm(a, b, with_abs=True)
+        for z in range(batch):
+            assert_close(got[z], ref[z], refabs[z], K, f"batched split-K [{z}]")
+    finally:
+        mkp.mkp_set_option("force_splitk", 0)
+        mkp.mkp_set_option("fused_reduce", 0)
 
 
 def test_unaligned(mkp):

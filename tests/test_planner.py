@@ -1,0 +1,133 @@
+"""The library's polymerizer (through the C-ABI, no GPU) against the
+cost-model oracle: the MikPoly page's case study, exact search (the pruned
+search reaches the exhaustive minimum over the same space), recomputed plan
+costs, and coverage of the output by the chosen regions."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import cost_model as cm
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "mikpoly_case_study.json")
+
+
+@pytest.fixture(scope="module")
+def mkp():
+    import dynamic_shape_gemm_amd as m
+    return m
+
+
+def to_regions(plan):
+    return [cm.Region(r["m0"], r["n0"], r["m"], r["n"], r["kernel"], r["s"]) for r in plan["regions"]]
+
+
+def case_table_text(Ta, Tb):
+    g = json.load(open(GOLD))
+    A, B = g["kernel_A"], g["kernel_B"]
+    fa = g["shape"][2] // A["tile"][2]
+    fb = g["shape"][2] // B["tile"][2]
+    wa = g["resident_warps_per_sm"] // A["warps"]
+    wb = g["resident_warps_per_sm"] // B["warps"]
+    return g, f"""device {g['sms']}
+launch_us 0
+splitk 1
+kernel A {A['tile'][0]} {A['tile'][1]} {A['tile'][2]} {wa}
+kernel B {B['tile'][0]} {B['tile'][1]} {B['tile'][2]} {wb}
+g A 1:{Ta / fa} {fa}:{Ta}
+g B 1:{Tb / fb} {fb}:{Tb}
+"""
+
+
+@pytest.mark.parametrize("Ta,Tb", [(10.0, 3.0), (10.0, 4.9), (10.0, 6.0), (10.0, 12.0)])
+def test_case_study_through_library(mkp, Ta, Tb):
+    g, text = case_table_text(Ta, Tb)
+    M, N, K = g["shape"]
+    tab = cm.parse_table(text)
+    plan = mkp.mkp_plan_with_table(text, 1, M, N, K)
+    ex = mkp.mkp_plan_with_table(text, 1, M, N, K, exhaustive=True)
+    best = cm.exhaustive_best(tab, M, N, K)
+    assert plan["cost_us"] == pytest.approx(best[0], rel=1e-12)
+    assert ex["cost_us"] == pytest.approx(best[0], rel=1e-12)
+    assert cm.plan_cost(tab, to_regions(plan), K, 1) == pytest.approx(plan["cost_us"], rel=1e-12)
+    # never worse than the page's two strategies (2 Ta and Ta + 2 Tb)
+    assert plan["cost_us"] <= min(2 * Ta, Ta + 2 * Tb) + 1e-9
+    if Ta > 2 * Tb:
+        assert plan["pattern"] in ("II-M", "II-N")
+    if Tb >= Ta:  # B is never cheaper per task: one wave of A per region pair cannot win
+        assert plan["cost_us"] == pytest.approx(2 * Ta)
+
+
+def random_table(rng, nk):
+    cus = int(rng.integers(2, 12))
+    lines = [f"device {cus}", f"launch_us {rng.uniform(0, 3):.3f}", "splitk 1 2 3 4 8",
+             f"reduce {rng.uniform(0, 2):.3f} {rng.uniform(100, 2000):.1f}"]
+    names = []
+    for i in range(nk):
+        uM = int(rng.choice([16, 32, 48, 64]))
+        uN = int(rng.choice([16, 32, 64]))
+        uK = int(rng.choice([16, 32]))
+        lines.append(f"kernel k{i} {uM} {uN} {uK} {int(rng.integers(1, 4))}")
+        names.append(f"k{i}")
+    for n in names:
+        base = rng.uniform(0.2, 2.0)
+        slope = rng.uniform(0.05, 1.0)
+        pts = " ".join(f"{t}:{base + slope * t * rng.uniform(0.9, 1.1):.4f}" for t in (1, 3, 8, 20))
+        lines.append(f"g {n} {pts}")
+    return "\n".join(lines) + "\n"
+
+
+def test_pruned_search_is_exact(mkp):
+    rng = np.random.default_rng(2024)
+    checked = 0
+    for trial in range(40):
+        text = random_table(rng, int(rng.integers(2, 4)))
+        tab = cm.parse_table(text)
+        M, N, K = (int(x) for x in rng.integers(1, 200, size=3))
+        batch = int(rng.choice([1, 1, 3]))
+        plan = mkp.mkp_plan_with_table(text, batch, M, N, K)
+        ex = mkp.mkp_plan_with_table(text, batch, M, N, K, exhaustive=True)
+        best = cm.exhaustive_best(tab, M, N, K, batch)
+        assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (trial, text, M, N, K)
+        assert ex["cost_us"] == pytest.approx(best[0], rel=1e-9)
+        regs = to_regions(plan)
+        assert cm.plan_cost(tab, regs, K, batch) == pytest.approx(plan["cost_us"], rel=1e-9)
+        tiles = {n: (k.uM, k.uN) for n, k in tab.kernels.items()}
+        assert cm.covers_exactly(M, N, regs, tiles)
+        assert plan["evaluated"] <= ex["evaluated"]
+        checked += 1
+    assert checked == 40
+
+
+def test_library_table_plans_cover_output(mkp):
+    """Plans from the active (shipped or analytic) table partition C."""
+    names = mkp.mkp_kernel_names()
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        M, N, K = int(rng.integers(1, 3000)), int(rng.integers(1, 3000)), int(rng.integers(1, 5000))
+        p = mkp.mkp_plan_describe(1, M, N, K)
+        regs = to_regions(p)
+        tiles = {r["kernel"]: (r["uM"], r["uN"]) for r in p["regions"]}
+        assert all(r.kernel in names for r in regs)
+        # tiles cover the output exactly once (cheap check on a coarse grid)
+        cnt = np.zeros((M, N), np.int8)
+        for r in regs:
+            cnt[r.m0:r.m0 + r.m, r.n0:r.n0 + r.n] += 1
+        assert (cnt == 1).all()
+        for r in p["regions"]:
+            assert 1 <= r["s"] and r["steps"] * r["s"] * r["uK"] >= K
+            assert (r["s"] - 1) * r["steps"] * r["uK"] < K   # no empty split
+
+
+def test_plan_time_is_microseconds(mkp):
+    import statistics
+    ts = []
+    rng = np.random.default_rng(6)
+    for _ in range(50):
+        p = mkp.mkp_plan_describe(1, int(rng.integers(1, 8192)), int(rng.integers(1, 8192)),
+                                  int(rng.integers(1, 8192)))
+        ts.append(p["plan_us"])
+    # the page reports 2 us per shape; this host is slower and unpinned: report, bound loosely
+    print(f"median plan time {statistics.median(ts):.1f} us")
+    assert statistics.median(ts) < 1000
