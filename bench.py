@@ -126,7 +126,7 @@ def roofline_from_trace(recs):
     roof["launches"] = d["n"]
     roof["avg_launch_us"] = round(d["us"] / d["n"], 3)
     roof["algorithmic_per_launch"] = {"flops": d["flops"] / d["n"], "bytes": d["bytes"] / d["n"]}
-    per_kernel = {k: {"launches": v["n"], "total_us": round(v["us"], 2)} for k, v in agg.items()}
+    per_kernel = {k: {"launches": v["n"], "avg_us": round(v["us"] / v["n"], 3)} for k, v in agg.items()}
     return roof, per_kernel
 
 
@@ -169,6 +169,51 @@ def cpu_baseline(wl, budget_s: float):
                       f"{sum(r for _, r in rows_done)} rows, {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    src = os.path.join(ROOT, "dynamic_shape_gemm_amd", "csrc", "kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def measured_ceilings(table_path: str):
+    """Sustained MFMA rate and copy bandwidth the offline stage measured."""
+    try:
+        for line in open(table_path):
+            tok = line.split("#", 1)[0].split()
+            if tok and tok[0] == "measured":
+                return {"mfma_tflops": round(float(tok[1]), 1), "hbm_gbps": round(float(tok[2]), 1)}
+    except OSError:
+        pass
+    return None
+
+
+def recorded_traffic(kernel: str, config: int):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record (profiles/traffic.json), valid only for the kernel source it was
+    taken from; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("config") != config:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def copy_reference(mib: int, reps: int):
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes_read": 4 * n, "copy_reference_bytes_written": 4 * n, "reps": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +223,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail", action="store_true", help="per-GEMM timings to stderr")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
+                    help="only run a plain copy of MiB (to scale rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -185,6 +232,10 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_reference:
+        torch.cuda.set_device(0)
+        copy_reference(args.copy_reference, 5)
+        return
     import dynamic_shape_gemm_amd as mkp
     import workloads
 
@@ -211,20 +262,27 @@ def main():
     value = wl.flops / (ms_per_step * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
-    # one traced step: per-launch HIP events on the launch stream
+    # traced steps: per-launch HIP events on the launch stream
+    ntr = 3
     mkp.mkp_set_option("trace", 1)
-    wl.step(mkp, stream)
-    torch.cuda.synchronize()
-    recs = mkp.mkp_trace_dump()
+    recs_all = []
+    for _ in range(ntr):
+        wl.step(mkp, stream)
+        torch.cuda.synchronize()
+        recs_all.append(mkp.mkp_trace_dump())
     mkp.mkp_set_option("trace", 0)
-    roof, per_kernel = roofline_from_trace(recs)
-    # per-call durations (a call may hold several launches)
-    per_call, i = [], 0
-    for case in wl.cases:
-        plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K)
-        n = sum(2 if r["s"] > 1 else 1 for r in plan["regions"])
-        per_call.append(sum(r["us"] for r in recs[i:i + n]))
-        i += n
+    roof, per_kernel = roofline_from_trace([r for recs in recs_all for r in recs])
+    roof["traffic"] = recorded_traffic(roof["kernel"], args.config)
+    # per-call durations (a call may hold several launches), median of the traced steps
+    per_step = []
+    for recs in recs_all:
+        by_call = {}
+        for r in recs:
+            by_call[r["call"]] = by_call.get(r["call"], 0.0) + r["us"]
+        calls = [by_call[k] for k in sorted(by_call)]
+        assert len(calls) == len(wl.cases), (len(calls), len(wl.cases))
+        per_step.append(calls)
+    per_call = [float(np.median(v)) for v in zip(*per_step)]
     fr = sweep_fraction(per_call, wl)
     if args.detail:
         for case, us, f in zip(wl.cases, per_call, fr):
@@ -258,7 +316,10 @@ def main():
             "roofline_frac_median": round(float(np.median(fr)), 4),
             "roofline_frac_min": round(float(np.min(fr)), 4),
             "kernels": per_kernel,
-            "table": mkp.mkp_stats()["table"],
+            "table": os.path.relpath(mkp.mkp_stats()["table"], ROOT) if os.path.isabs(mkp.mkp_stats()["table"])
+            else mkp.mkp_stats()["table"],
+            "measured_ceiling": measured_ceilings(mkp.mkp_stats()["table"]),
+            "kernel_source_sha256_16": kernel_source_hash(),
         },
         "roofline": roof,
     }

@@ -36,6 +36,7 @@ namespace mkp {
 namespace {
 
 thread_local std::string t_last_error;
+thread_local int64_t t_call = 0;   // sequence number of this thread's current GEMM call
 
 int fail(int code, const std::string& msg) {
     t_last_error = msg;
@@ -77,7 +78,8 @@ constexpr int kCounterCap = 1 << 16;
 constexpr size_t kCounterBytes = (size_t)kCounterCap * 4;
 
 struct TraceRec {
-    int kernel;            // library kernel index, -1 = split-K reduction, -2 = zero fill
+    int kernel;            // library kernel index, -1 = split-K reduction, -2 = zero fill, -3 = row pack
+    int64_t call;          // sequence number of the C-ABI call that made the launch
     double flops, bytes;   // algorithmic work of the launch
     hipEvent_t e0, e1;
 };
@@ -97,7 +99,9 @@ struct Library {
     std::atomic<int64_t> plan_ns{0};
 
     std::atomic<bool> fused_reduce{false};        // split-K: fused last-arrival sum (else 2 passes)
+    std::atomic<bool> pack_unaligned{true};       // stage unaligned re-read operands aligned
     std::atomic<bool> trace{false};               // time every launch with events
+    std::atomic<int64_t> calls{0};                // C-ABI GEMM calls so far
     std::mutex trace_mu;
     std::vector<TraceRec> trace_recs;
 };
@@ -311,7 +315,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 template <class F>
 hipError_t traced(Library& L, hipStream_t st, int kernel, double flops, double bytes, F&& fn) {
     if (!L.trace.load(std::memory_order_relaxed)) return fn();
-    TraceRec r{kernel, flops, bytes, nullptr, nullptr};
+    TraceRec r{kernel, t_call, flops, bytes, nullptr, nullptr};
     if (hipEventCreate(&r.e0) != hipSuccess || hipEventCreate(&r.e1) != hipSuccess) return fn();
     (void)hipEventRecord(r.e0, st);
     hipError_t e = fn();
@@ -335,6 +339,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     if (K > 0 && (!Av || !Bv)) return fail(MKP_ERR_INVALID_ARG, "A or B is NULL");
     if (batch > 1 && (sA < 0 || sB < 0 || sC < 0)) return fail(MKP_ERR_INVALID_ARG, "negative batch stride");
     ensure_init();
+    t_call = lib().calls.fetch_add(1, std::memory_order_relaxed);
     hipStream_t st = (hipStream_t)stream_v;
     int dev = 0;
     hipError_t he = hipGetDevice(&dev);
@@ -354,8 +359,8 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     const uint16_t* B = (const uint16_t*)Bv;
     // 128-bit loads need 16-byte aligned rows; the direct-load path also
     // keeps per-tile offsets (<= 256 rows of A, <= 64 rows of B) in 32 bits
-    const bool vA = aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0) && lda < (int64_t(1) << 23);
-    const bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0) && ldb < (int64_t(1) << 25);
+    bool vA = aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0) && lda < (int64_t(1) << 23);
+    bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0) && ldb < (int64_t(1) << 25);
     const bool vC = aligned16(C) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
     const int align = (vA ? 1 : 0) | (vB ? 2 : 0) | (vC ? 4 : 0);
 
@@ -363,18 +368,52 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     std::shared_ptr<const Plan> plan = get_plan(key);
     if (plan->regions.empty()) return fail(MKP_ERR_UNSUPPORTED, "no plan for this shape");
 
-    // workspace for split regions (regions run in order on one stream and share it)
-    size_t ws_bytes = 0;
+    // An operand with unaligned rows that several tile rows (columns) re-read
+    // is first copied into a staging buffer with rows padded to 8 elements
+    // (as the Bolt page pads kernels to alignment 8), so the micro-kernels
+    // take the direct-load path.  Workspace layout, regions in order on one
+    // stream sharing it: [split-K counters][split-K partials][A copy][B copy].
+    size_t part_bytes = 0;
     for (auto& r : plan->regions)
         if (r.s > 1) {
             const int64_t ldw = (r.n + 3) & ~int64_t(3);
-            ws_bytes = std::max(ws_bytes, kCounterBytes + (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw *
-                                                              sizeof(float));
+            part_bytes = std::max(part_bytes, (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float));
         }
+    const bool pack_on = L.pack_unaligned.load(std::memory_order_relaxed);
+    const int64_t ldap = (K + 7) & ~int64_t(7), ldbp = (N + 7) & ~int64_t(7);
+    // (a copy pays off once several tile rows/columns re-read the operand)
+    const bool packA = pack_on && !vA && N > 192 && ldap < (int64_t(1) << 23);
+    const bool packB = pack_on && !vB && M > 192 && ldbp < (int64_t(1) << 25);
+    auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t offA = kCounterBytes + round256(part_bytes);
+    const size_t bytesA = packA ? (size_t)batch * M * ldap * 2 : 0;
+    const size_t offB = offA + round256(bytesA);
+    const size_t bytesB = packB ? (size_t)batch * K * ldbp * 2 : 0;
+    const size_t ws_bytes = (part_bytes || packA || packB) ? offB + bytesB : 0;
     void* ws = nullptr;
     if (ws_bytes) {
         int rc = get_workspace(dev, st, ws_bytes, &ws);
         if (rc != MKP_OK) return rc;
+    }
+    if (packA) {
+        uint16_t* dst = (uint16_t*)((char*)ws + offA);
+        he = traced(L, st, -3, 0.0, (double)batch * M * (2.0 * K + 2.0 * ldap),
+                    [&] { return launch_pack_rows(A, lda, sA, dst, ldap, (int)M, (int)K, (int)batch, st); });
+        if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("pack launch: ") + hipGetErrorString(he));
+        A = dst;
+        lda = ldap;
+        sA = M * ldap;
+        vA = true;
+    }
+    if (packB) {
+        uint16_t* dst = (uint16_t*)((char*)ws + offB);
+        he = traced(L, st, -3, 0.0, (double)batch * K * (2.0 * N + 2.0 * ldbp),
+                    [&] { return launch_pack_rows(B, ldb, sB, dst, ldbp, (int)K, (int)N, (int)batch, st); });
+        if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("pack launch: ") + hipGetErrorString(he));
+        B = dst;
+        ldb = ldbp;
+        sB = K * ldbp;
+        vB = true;
     }
 
     for (size_t i = 0; i < plan->regions.size(); ++i) {
@@ -414,7 +453,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
             a.flags |= KF_VEC_C;
         }
         // fused reduction when the per-tile counters fit, else a second pass
-        const bool fused = r.s > 1 && L.fused_reduce.load(std::memory_order_relaxed) &&
+        const bool fused = r.s > 1 && ki.fused_ok && L.fused_reduce.load(std::memory_order_relaxed) &&
                            (int64_t)a.tiles_m * a.tiles_n * batch <= kCounterCap;
         a.counters = fused ? (int*)ws : nullptr;
         a.Cout = Creg;
@@ -551,6 +590,9 @@ int mkp_set_option(const char* key, const char* value) {
         if (v == "I") L.opts.allow_II = false;
         else if (v == "I,II" || v == "II") L.opts.allow_II = true;
         else return fail(MKP_ERR_INVALID_ARG, "patterns must be I or I,II");
+    } else if (k == "pack_unaligned") {
+        L.pack_unaligned.store(std::atoi(v.c_str()) != 0);
+        return MKP_OK;
     } else if (k == "fused_reduce") {
         L.fused_reduce.store(std::atoi(v.c_str()) != 0);
         return MKP_OK;
@@ -623,9 +665,10 @@ int mkp_trace_dump(char* buf, size_t len) {
         (void)hipEventDestroy(recs[i].e0);
         (void)hipEventDestroy(recs[i].e1);
         const int k = recs[i].kernel;
-        const char* name = k >= 0 ? kernel_info(k).name : (k == -1 ? "splitk_reduce" : "zero_fill");
+        const char* name = k >= 0 ? kernel_info(k).name : k == -1 ? "splitk_reduce" : k == -2 ? "zero_fill" : "pack_rows";
         if (i) o << ",";
-        o << "{\"kernel\":\"" << name << "\",\"us\":" << 1000.0 * ms << ",\"flops\":" << recs[i].flops
+        o << "{\"kernel\":\"" << name << "\",\"call\":" << recs[i].call << ",\"us\":" << 1000.0 * ms
+          << ",\"flops\":" << recs[i].flops
           << ",\"bytes\":" << recs[i].bytes << "}";
     }
     o << "]";
@@ -692,17 +735,29 @@ int mkp_calibrate(const char* path, int max_points) {
     hipError_t err = hipSuccess;
     // launch overhead: a one-workgroup kernel back to back
     t.launch_us = time_launches([&] { return launch_zero_fill(dC, 1, 0, 1, 1, 1, nullptr); }, 20, 200, &err);
-    // split-K reduction bandwidth on a typical partial volume (8 x 256 x 4096)
+    // split-K reduction: fixed cost and bandwidth fitted to two partial
+    // volumes, in the cost model's byte count (2s+1)*4*m*n
     {
-        const int s = 8, m = 256, n = 4096;
+        struct P { int s, m, n; };
+        const P pa{2, 16, 4096}, pb{8, 256, 8192};
         float* W = nullptr;
-        if (hipMalloc(&W, (size_t)s * m * n * 4) == hipSuccess) {
-            (void)hipMemset(W, 0, (size_t)s * m * n * 4);
-            double us = time_launches(
-                [&] { return launch_splitk_reduce(W, s, (int64_t)m * n, 0, n, dC, n, 0, m, n, 1, 1, nullptr); }, 20,
-                50, &err);
-            t.red_launch_us = t.launch_us;
-            t.red_gbps = (double)(s + 1) * 4.0 * m * n / std::max(us - t.launch_us, 0.1) / 1e3;
+        if (hipMalloc(&W, (size_t)pb.s * pb.m * pb.n * 4) == hipSuccess) {
+            (void)hipMemset(W, 0, (size_t)pb.s * pb.m * pb.n * 4);
+            float* Cr = nullptr;
+            if (hipMalloc(&Cr, (size_t)pb.m * pb.n * 4) == hipSuccess) {
+                auto run = [&](const P& q) {
+                    return time_launches([&] {
+                        return launch_splitk_reduce(W, q.s, (int64_t)q.m * q.n, 0, q.n, Cr, q.n, 0, q.m, q.n, 1, 1,
+                                                    nullptr);
+                    }, 20, 50, &err);
+                };
+                const double ta = run(pa), tb = run(pb);
+                const double ba = (2.0 * pa.s + 1) * 4.0 * pa.m * pa.n, bb = (2.0 * pb.s + 1) * 4.0 * pb.m * pb.n;
+                const double bw = (bb - ba) / std::max(tb - ta, 0.1);   // bytes per us
+                t.red_gbps = bw / 1e3;
+                t.red_launch_us = std::max(ta - ba / bw, 0.0);
+                (void)hipFree(Cr);
+            }
             (void)hipFree(W);
         }
     }
@@ -746,6 +801,22 @@ int mkp_calibrate(const char* path, int max_points) {
             k.pts.emplace_back((double)tt, std::max(us - t.launch_us, 0.05));
         }
         t.kernels.push_back(k);
+    }
+    // sustained ceilings: MFMA on random operands, streaming copy
+    if (err == hipSuccess) {
+        const int blocks = cus, iters = 256;
+        const double us = time_launches([&] { return launch_mfma_probe(dC, blocks, iters, nullptr); }, 5, 10, &err);
+        t.mfma_tflops = (double)blocks * 4 * 64.0 * iters * 32768.0 / us / 1e6;
+    }
+    if (err == hipSuccess) {
+        // copy between the two halves of the B buffer, up to 1 GB each way
+        // (well beyond the 256 MB MALL)
+        const int64_t half = (int64_t)b_elems * 2 / 2;
+        const int64_t bytes = std::min<int64_t>(half, int64_t(1) << 30) & ~int64_t(15);
+        char* base = (char*)dB;
+        const double us = time_launches(
+            [&] { return launch_copy_probe(base, base + (half & ~int64_t(255)), bytes, cus * 8, nullptr); }, 3, 10, &err);
+        t.hbm_gbps = 2.0 * (double)bytes / us / 1e3;
     }
     (void)hipDeviceSynchronize();
     (void)hipFree(dA);

@@ -46,6 +46,7 @@ struct KernelInfo {
     int uM, uN, uK;
     int threads;
     int lds_bytes;
+    bool fused_ok;        // compiled with the fused split-K reduction
     const void* func;     // __global__ entry, for occupancy queries
     hipError_t (*launch)(const KArgs&, dim3 grid, hipStream_t);
 };
@@ -60,6 +61,17 @@ hipError_t launch_splitk_reduce(const float* W, int splits, int64_t sWsplit, int
                                 hipStream_t st);
 // C := 0 for batch matrices of M x N (K == 0: empty sum).
 hipError_t launch_zero_fill(float* C, int64_t ldc, int64_t sC, int M, int N, int batch, hipStream_t st);
+
+// Copy batch x rows x cols bf16 (leading dimension ld_src, any alignment)
+// into dst with leading dimension ld_dst (a multiple of 8, >= cols; rows
+// zero-padded), batch entries rows*ld_dst apart.
+hipError_t launch_pack_rows(const uint16_t* src, int64_t ld_src, int64_t stride_src, uint16_t* dst, int64_t ld_dst,
+                            int rows, int cols, int batch, hipStream_t st);
+
+// Calibration probes: MFMA rate on random operands (blocks x 4 waves, each
+// 64*iters 32x32x16 MFMAs) and a streaming copy of `bytes` (multiple of 16).
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t st);
 
 // Calibration helpers: fill a buffer with pseudo-random bf16 in [-1, 1).
 hipError_t launch_fill_random_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t st);

@@ -83,12 +83,20 @@ struct Tile {
     static constexpr bool JUNK = (A_GROUPS % NW) != 0 || (B_GROUPS % NW) != 0;
     static constexpr int LDS = S * STAGE + (JUNK ? 1024 : 0);
     static constexpr int A_RPT = (A_SLOTS + NT - 1) / NT, B_RPT = (B_SLOTS + NT - 1) / NT;
+    // epilogue staging: one fragment row (MF rows x WTN columns) per wave,
+    // rows padded by 4 floats to spread LDS banks where the stages leave room
+    static constexpr int EPI_LD = (NW * MF * (WTN + 4) * 4 <= S * STAGE) ? WTN + 4 : WTN;
+    static constexpr int EPI_WAVE_BYTES = MF * EPI_LD * 4;
+    // the fused split-K reduction is compiled into all but the largest tile,
+    // whose accumulators leave no registers for it
+    static constexpr bool FUSED = BM * BN < 256 * 256;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(BK == 64 || BK == 128, "uK must be 64 or 128");
     static_assert(BN >= 64 && BN % 64 == 0, "uN must be a multiple of 64");
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "tiles must fill whole 1 KB groups");
     static_assert(S >= 2 && IPS * (S - 2) <= 63, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(NW * EPI_WAVE_BYTES <= S * STAGE, "epilogue staging fits in the stage buffers");
 };
 
 // LDS slot (16 bytes) -> (row, first element) of the A tile.
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
             }
         }
     };
-    if (args.splits > 1 && args.counters != nullptr) {
+    if (T::FUSED && args.splits > 1 && args.counters != nullptr) {
         // Fused split-K reduction.  Every split stores its partial tile; once
         // all waves' stores have completed, wave 0 alone publishes them at
         // agent scope (one L2 write-back per workgroup) and counts the
@@ -494,7 +502,57 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
         if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    for_each4([&](int m, int n, f32x4 v) { store4(C, args.ldc, vecC, m, n, v); });
+    // Plain epilogue: the tile goes through LDS one fragment row at a time
+    // so that every store instruction writes contiguous row segments.
+    __syncthreads();   // every wave is done with the K-loop stages
+    float __attribute__((address_space(3)))* stg =
+        (float __attribute__((address_space(3)))*)(smem + wave * T::EPI_WAVE_BYTES);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+        // fragment row i of this wave: MF rows x WTN columns, rows padded by 4 floats
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            if constexpr (T::MF == 32) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = lane & 31, col = j * 32 + 8 * q + 4 * (lane >> 5);
+                    *(f32x4 __attribute__((address_space(3)))*)(stg + r * T::EPI_LD + col) =
+                        f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                }
+            } else {
+                *(f32x4 __attribute__((address_space(3)))*)(stg + s16 * T::EPI_LD + j * 16 + g4 * 4) = acc[i][j];
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes land before its reads
+        const int row0 = wm * T::WTM + i * T::MF;             // tile row of staged row 0
+        const int col0 = wn * T::WTN;
+        if (vecC) {
+            constexpr int C4 = T::WTN / 4;                    // 16-byte chunks per staged row
+#pragma unroll 1
+            for (int it = 0; it < (T::MF * C4 + 63) / 64; ++it) {
+                const int id = it * 64 + lane;
+                if ((T::MF * C4) % 64 == 0 || id < T::MF * C4) {
+                    const int r = id / C4, c4 = (id % C4) * 4;
+                    const f32x4 v = *(const f32x4 __attribute__((address_space(3)))*)(stg + r * T::EPI_LD + c4);
+                    store4(C, args.ldc, true, row0 + r, col0 + c4, v);
+                }
+            }
+        } else {
+            // unaligned rows: lanes walk one row's columns, one float each
+#pragma unroll 1
+            for (int r = 0; r < T::MF; ++r) {
+                const int m = row0 + r;
+                if (m >= c.Mr) break;
+                float* dst = C + (int64_t)m * args.ldc + col0;
+#pragma unroll
+                for (int c0 = 0; c0 < T::WTN; c0 += 64) {
+                    const int col = c0 + lane;
+                    if ((T::WTN % 64 == 0 || col < T::WTN) && col0 + col < c.Nr) dst[col] = stg[r * T::EPI_LD + col];
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next row overwrites
+    }
 }
 
 template <class T>
@@ -527,6 +585,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+// Copy rows of bf16 into a staging buffer whose rows start 16-byte aligned
+// (leading dimension a multiple of 8 elements), zero-padding each row up to
+// it: operands with unaligned rows then take the direct-load path.  Each
+// thread writes one 16-byte chunk; reads are element-wise (any alignment).
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                                        int64_t stride_src, uint16_t* __restrict__ dst,
+                                                        int64_t ld_dst, int rows, int cols, int batch) {
+    const int64_t chunks_per_row = ld_dst >> 3;
+    const int64_t per = (int64_t)rows * chunks_per_row;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= per * batch) return;
+    const int b = (int)(idx / per);
+    const int64_t e = idx % per;
+    const int r = (int)(e / chunks_per_row);
+    const int c = (int)(e % chunks_per_row) * 8;
+    const uint16_t* s = src + (int64_t)b * stride_src + (int64_t)r * ld_src + c;
+    *(u32x4*)(dst + (int64_t)b * rows * ld_dst + (int64_t)r * ld_dst + c) = load8_elems(s, cols - c);
+}
+
 __global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ C, int64_t ldc, int64_t sC, int M,
                                                         int N, int batch) {
     const int64_t per = (int64_t)M * N;
@@ -536,6 +613,60 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ C, i
     const int64_t e = idx % per;
     const int m = (int)(e / N), n = (int)(e % N);
     C[(int64_t)b * sC + (int64_t)m * ldc + n] = 0.0f;
+}
+
+// Sustained-rate probes for the offline stage.  mfma_probe: every wave keeps
+// 16 independent 32x32x16 bf16 accumulations busy on random operands (MFMA
+// power, hence clock, depends on operand bits).  copy_probe: a streaming
+// 16-byte-per-lane copy.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x85EBCA6Bu;
+    x ^= x >> 13;
+    x *= 0xC2B2AE35u;
+    x ^= x >> 16;
+    return x;
+}
+
+__device__ __forceinline__ uint32_t rand_bf16_pair(uint32_t x) {
+    auto one = [](uint32_t h) { return ((h >> 31) << 15) | ((0x70u + (h >> 24) % 15u) << 7) | (h & 0x7fu); };
+    return one(mix32(x)) | (one(mix32(x * 2654435761u + 1u)) << 16);
+}
+
+__global__ __launch_bounds__(256) void mfma_probe_kernel(float* out, int iters, uint32_t seed) {
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        u32x4 ua, ub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t base = seed ^ (blockIdx.x * 4096u + threadIdx.x * 16u + s * 4u + e);
+            ua[e] = rand_bf16_pair(base);
+            ub[e] = rand_bf16_pair(base ^ 0x5bd1e995u);
+        }
+        a[s] = __builtin_bit_cast(bf16x8, ua);
+        b[s] = __builtin_bit_cast(bf16x8, ub);
+    }
+    f32x16 acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = f32x16{};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[(ks + j) & 3], acc[j], 0, 0, 0);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[j][r];
+    out[blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
+__global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = src[i];
 }
 
 __global__ __launch_bounds__(256) void fill_random_bf16_kernel(uint16_t* p, int64_t n, uint32_t seed) {
@@ -569,7 +700,7 @@ using T_16x256 = Tile<16, 256, 64, 1, 4, 4>;
 using T_32x64 = Tile<32, 64, 64, 2, 2, 4>;
 
 #define MKP_KERNEL(NAME, T) \
-    { NAME, T::BM, T::BN, T::BK, T::NT, T::LDS, (const void*)&gemm_tile_kernel<T>, &launch_tile<T> }
+    { NAME, T::BM, T::BN, T::BK, T::NT, T::LDS, T::FUSED, (const void*)&gemm_tile_kernel<T>, &launch_tile<T> }
 
 const KernelInfo g_kernels[] = {
     MKP_KERNEL("m256n256k64", T_256x256),
@@ -608,6 +739,24 @@ hipError_t launch_zero_fill(float* C, int64_t ldc, int64_t sC, int M, int N, int
     const int64_t items = (int64_t)M * N * batch;
     dim3 grid((unsigned)((items + 255) / 256));
     hipLaunchKernelGGL(zero_fill_kernel, grid, dim3(256), 0, st, C, ldc, sC, M, N, batch);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const uint16_t* src, int64_t ld_src, int64_t stride_src, uint16_t* dst, int64_t ld_dst,
+                            int rows, int cols, int batch, hipStream_t st) {
+    const int64_t items = (int64_t)rows * (ld_dst >> 3) * batch;
+    hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, src, ld_src,
+                       stride_src, dst, ld_dst, rows, cols, batch);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, st, out, iters, 0x9e3779b9u);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t st) {
+    hipLaunchKernelGGL(copy_probe_kernel, dim3(blocks), dim3(256), 0, st, (const u32x4*)src, (u32x4*)dst, bytes / 16);
     return hipGetLastError();
 }
 

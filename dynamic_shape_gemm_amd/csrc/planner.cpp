@@ -44,6 +44,9 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
                 t.splits.push_back(s);
             }
             if (t.splits.empty()) return fail("empty splitk");
+        } else if (key == "measured") {
+            // measured <mfma_tflops> <hbm_gbps>: sustained ceilings, reported only
+            if (!(ls >> t.mfma_tflops >> t.hbm_gbps)) return fail("bad measured line");
         } else if (key == "patterns") {
             t.pat_I = t.pat_IIM = t.pat_IIN = false;
             std::string p;
@@ -114,6 +117,7 @@ std::string table_to_text(const PerfTable& t) {
     for (int s : t.splits) o << " " << s;
     o << "\npatterns" << (t.pat_I ? " I" : "") << (t.pat_IIM ? " II-M" : "") << (t.pat_IIN ? " II-N" : "")
       << "\n";
+    if (t.mfma_tflops > 0 || t.hbm_gbps > 0) o << "measured " << t.mfma_tflops << " " << t.hbm_gbps << "\n";
     for (auto& k : t.kernels)
         o << "kernel " << k.name << " " << k.uM << " " << k.uN << " " << k.uK << " " << k.wg_per_cu << "\n";
     for (auto& k : t.kernels) {

@@ -36,6 +36,8 @@ struct PerfTable {
     double red_gbps = 1000.0;     // split-K reduction: bandwidth
     std::vector<int> splits{1};
     bool pat_I = true, pat_IIM = true, pat_IIN = true;
+    double mfma_tflops = 0.0;     // measured sustained bf16 MFMA rate (0: unknown)
+    double hbm_gbps = 0.0;        // measured streaming-copy bandwidth (0: unknown)
     std::vector<TableKernel> kernels;
 };
 

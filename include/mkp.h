@@ -124,7 +124,10 @@ int mkp_calibrate(const char *path, int max_points);
  * "splitk_max" (integer), "trace" (0/1, see mkp_trace_dump), "fused_reduce"
  * (0 = split-K partials summed by a second launch, the default; 1 = summed
  * by the last-arriving workgroup of each tile, which on MI355X costs more in
- * L2 write-back than the second launch).  "exhaustive", "force_*", "patterns" and
+ * L2 write-back than the second launch), "pack_unaligned" (1 = an operand
+ * whose rows are not 16-byte aligned and that several tiles re-read is
+ * first copied into aligned workspace rows, the default; 0 = such operands
+ * are read element by element).  "exhaustive", "force_*", "patterns" and
  * "splitk_max" clear the plan cache.  Returns MKP_OK or
  * MKP_ERR_INVALID_ARG / MKP_ERR_UNSUPPORTED. */
 int mkp_set_option(const char *key, const char *value);
@@ -141,9 +144,11 @@ void mkp_cache_clear(void);
 /* JSON counters: cache hits/misses, plans built, planning time, launches. */
 int mkp_stats(char *buf, size_t len);
 
-/* Launch trace (option "trace" = 1): every kernel launch is bracketed by
+/* Launch trace (option "trace" = 1): every kernel launch (micro-kernels,
+ * "splitk_reduce", "zero_fill", "pack_rows") is bracketed by
  * HIP events on its stream.  Waits for the recorded launches, writes a JSON
- * list [{"kernel","us","flops","bytes"}...] (algorithmic work per launch:
+ * list [{"kernel","call","us","flops","bytes"}...] ("call": sequence number
+ * of the GEMM call that made the launch; algorithmic work per launch:
  * 2*m*n*K flops; 2mK + 2Kn + 4mn bytes) and clears the record. */
 int mkp_trace_dump(char *buf, size_t len);
 

@@ -88,6 +88,8 @@ def parse_table(text: str) -> Table:
             splits = [int(x) for x in tok[1:]]
         elif key == "patterns":
             patterns = tok[1:]
+        elif key == "measured":
+            pass  # sustained-rate figures: reported, not part of the cost model
         elif key == "kernel":
             kernels[tok[1]] = Kernel(tok[1], int(tok[2]), int(tok[3]), int(tok[4]), int(tok[5]), [])
         elif key == "g":

@@ -142,17 +142,25 @@ def test_splitk_repeated_calls_reuse_counters(mkp):
         mkp.mkp_set_option("fused_reduce", 0)
 
 
-def test_unaligned(mkp):
+@pytest.mark.parametrize("pack", [1, 0])
+def test_unaligned(mkp, pack):
     rng = np.random.default_rng(5)
-    M, N, K = 77, 131, 301
-    a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
-    run_case(mkp, a, b, lda=K + 1, what="lda odd")
-    run_case(mkp, a, b, ldb=N + 3, what="ldb odd")
-    run_case(mkp, a, b, ldc=N + 1, what="ldc odd")
-    run_case(mkp, a, b, offA=1, offB=3, offC=1, what="misaligned pointers")
-    M, N, K = 256, 256, 256
-    a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
-    run_case(mkp, a, b, offB=1, what="aligned shape, B pointer off by one")
+    try:
+        mkp.mkp_set_option("pack_unaligned", pack)
+        M, N, K = 77, 131, 301
+        a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+        run_case(mkp, a, b, lda=K + 1, what=f"lda odd pack={pack}")
+        run_case(mkp, a, b, ldb=N + 3, what=f"ldb odd pack={pack}")
+        run_case(mkp, a, b, ldc=N + 1, what=f"ldc odd pack={pack}")
+        run_case(mkp, a, b, offA=1, offB=3, offC=1, what=f"misaligned pointers pack={pack}")
+        M, N, K = 256, 256, 256
+        a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+        run_case(mkp, a, b, offB=1, what=f"aligned shape, B pointer off by one pack={pack}")
+        M, N, K = 300, 509, 64
+        a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+        run_case(mkp, a, b, lda=K + 3, ldb=N, ldc=N, what=f"odd N, ldb=N pack={pack}")
+    finally:
+        mkp.mkp_set_option("pack_unaligned", 1)
 
 
 def test_k0_and_empty(mkp):
@@ -266,7 +274,7 @@ def test_pattern_II_regions(mkp):
     names = mkp.mkp_kernel_names()
     big, small = "m128n128k64", "m64n64k64"
     assert big in names and small in names
-    text = """device 256
+    text = """device 2
 launch_us 0
 splitk 1
 patterns II-M II-N
