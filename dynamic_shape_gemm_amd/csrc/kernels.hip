@@ -63,9 +63,10 @@ __device__ __forceinline__ int swzB(int k) {
     else return BN >= 128 ? ((k & 3) << 1) : (((k >> 1) & 1) << 1);
 }
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_, bool PREREAD_ = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
+    static constexpr bool PREREAD = PREREAD_;   // read a whole stage's fragments before its MFMAs
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -286,26 +287,45 @@ template <class T, class Acc>
 __device__ __forceinline__ void compute_stage32(const lds_t* sa, const lds_t* sb, Acc (&acc)[T::FM][T::FN], int lane,
                                                 int wm, int wn) {
     constexpr int NKS = T::BK / 16;
-    constexpr int READS = 2 * T::FN + T::FM;   // LDS reads per sub-step
-    constexpr int MFMAS = T::FM * T::FN;
-    constexpr int PER = (READS + MFMAS - 1) / MFMAS;
-    bf16x8 xb[2][T::FN], ya[2][T::FM];
-    read_frags32<T>(sa, sb, 0, lane, wm, wn, xb[0], ya[0]);
+    if constexpr (T::PREREAD) {
+        // Every fragment of the stage is read up front into its own
+        // registers; the scheduling fence keeps the compiler from sinking the
+        // reads next to their MFMAs (which would expose LDS latency once per
+        // sub-step), and the MFMAs then wait progressively.
+        bf16x8 xb[NKS][T::FN], ya[NKS][T::FM];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        const int cur = ks & 1;
-        if (ks + 1 < NKS) read_frags32<T>(sa, sb, ks + 1, lane, wm, wn, xb[cur ^ 1], ya[cur ^ 1]);
+        for (int ks = 0; ks < NKS; ++ks) read_frags32<T>(sa, sb, ks, lane, wm, wn, xb[ks], ya[ks]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[cur][j], ya[cur][i], acc[i][j], 0, 0, 0);
-        if (ks + 1 < NKS) {
-            // one MFMA, then up to PER reads of the next sub-step, repeated
+            for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-            for (int t = 0; t < MFMAS; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (t * PER < READS) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+                for (int j = 0; j < T::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[ks][j], ya[ks][i], acc[i][j], 0, 0, 0);
+    } else {
+        // Fragments double-buffered across sub-steps: the reads of ks+1 are
+        // interleaved with the MFMAs of ks.
+        constexpr int READS = 2 * T::FN + T::FM;
+        constexpr int MFMAS = T::FM * T::FN;
+        constexpr int PER = (READS + MFMAS - 1) / MFMAS;
+        bf16x8 xb[2][T::FN], ya[2][T::FM];
+        read_frags32<T>(sa, sb, 0, lane, wm, wn, xb[0], ya[0]);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < NKS) read_frags32<T>(sa, sb, ks + 1, lane, wm, wn, xb[cur ^ 1], ya[cur ^ 1]);
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[cur][j], ya[cur][i], acc[i][j], 0, 0, 0);
+            if (ks + 1 < NKS) {
+#pragma unroll
+                for (int t = 0; t < MFMAS; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (t * PER < READS) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+                }
             }
         }
     }
@@ -688,8 +708,8 @@ __global__ __launch_bounds__(256) void fill_random_bf16_kernel(uint16_t* p, int6
 // tiles run 8 waves (two per SIMD) so one wave's LDS waits overlap the
 // other's MFMAs; 128x128 runs two 4-wave workgroups per CU.
 using T_256x256 = Tile<256, 256, 64, 4, 2, 2>;
-using T_256x128 = Tile<256, 128, 64, 4, 2, 3>;
-using T_128x256 = Tile<128, 256, 64, 2, 4, 3>;
+using T_256x128 = Tile<256, 128, 64, 4, 2, 2, true>;
+using T_128x256 = Tile<128, 256, 64, 2, 4, 2>;
 using T_128x128 = Tile<128, 128, 64, 2, 2, 2>;
 using T_128x64 = Tile<128, 64, 64, 2, 2, 3>;
 using T_64x128 = Tile<64, 128, 64, 2, 2, 3>;
