@@ -34,6 +34,16 @@ class MkpError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python dynamic_shape_gemm_amd/build.py`")
 
+# One HIP runtime per process.  The PyTorch wheel carries its own copy of the
+# HIP and HSA runtimes under the same soname as the system's; whichever is
+# loaded first is the one libmkp binds to.  If libmkp came first, torch would
+# load a second runtime beside it and libmkp's would find no device.  So
+# torch, when installed, is loaded before the library.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _p, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 _lib.mkp_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]

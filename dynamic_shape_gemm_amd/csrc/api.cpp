@@ -366,7 +366,12 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
 
     Key key{batch, M, N, K, align, dev};
     std::shared_ptr<const Plan> plan = get_plan(key);
-    if (plan->regions.empty()) return fail(MKP_ERR_UNSUPPORTED, "no plan for this shape");
+    if (plan->regions.empty()) {
+        if (plan->rank > 0)
+            return fail(MKP_ERR_UNSUPPORTED, "plan_rank " + std::to_string(plan->rank) + " beyond the " +
+                                                 std::to_string(plan->candidates) + " candidates of this shape");
+        return fail(MKP_ERR_UNSUPPORTED, "no plan for this shape");
+    }
 
     // An operand with unaligned rows that several tile rows (columns) re-read
     // is first copied into a staging buffer with rows padded to 8 elements
@@ -550,6 +555,14 @@ int mkp_plan_with_table(const char* table_text, int exhaustive, int64_t batch, i
     SearchOptions o;
     o.exhaustive = exhaustive != 0;
     o.splitk_max = INT_MAX;
+    {
+        // the cost-model variant and the ranked-candidate option carry over
+        ensure_init();
+        Library& L = lib();
+        std::shared_lock<std::shared_mutex> lk(L.mu);
+        o.cost_mode = L.opts.cost_mode;
+        o.plan_rank = L.opts.plan_rank;
+    }
     Plan p = polymerize(t, batch, M, N, K, o);
     return write_out(plan_to_json(p, t), buf, len);
 }
@@ -601,6 +614,15 @@ int mkp_set_option(const char* key, const char* value) {
         return MKP_OK;
     } else if (k == "exhaustive") {
         L.opts.exhaustive = std::atoi(v.c_str()) != 0;
+    } else if (k == "cost_model") {
+        if (v == "full") L.opts.cost_mode = COST_FULL;
+        else if (v == "wave") L.opts.cost_mode = COST_WAVE;
+        else if (v == "pipe") L.opts.cost_mode = COST_PIPE;
+        else return fail(MKP_ERR_INVALID_ARG, "cost_model must be full, wave or pipe");
+    } else if (k == "plan_rank") {
+        int r = std::atoi(v.c_str());
+        if (r < 0) return fail(MKP_ERR_INVALID_ARG, "plan_rank < 0");
+        L.opts.plan_rank = r;
     } else if (k == "splitk_max") {
         int s = std::atoi(v.c_str());
         if (s < 1) return fail(MKP_ERR_INVALID_ARG, "splitk_max < 1");

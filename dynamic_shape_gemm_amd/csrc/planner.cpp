@@ -257,7 +257,10 @@ struct Searcher {
         const TableKernel& k = tab.kernels[ki];
         const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * c.s_eff * batch;
         const int64_t waves = ceil_div(tasks, (int64_t)tab.cus * k.wg_per_cu);
-        double v = tab.launch_us + (double)waves * c.g;
+        double v = tab.launch_us;
+        if (opt.cost_mode == COST_WAVE) v += (double)waves;
+        else if (opt.cost_mode == COST_PIPE) v += c.g;
+        else v += (double)waves * c.g;
         if (c.s_eff > 1)
             v += tab.red_launch_us +
                  (double)(2 * c.s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch / (tab.red_gbps * 1e3);
@@ -288,7 +291,84 @@ struct Searcher {
         return best;
     }
 
+    // The bounds below hold for the full model only; the ablations and the
+    // ranked list score every candidate.
+    bool prune() const { return !opt.exhaustive && opt.cost_mode == COST_FULL; }
+
+    // Every candidate of the space (each region with each of its splits),
+    // ordered by modelled cost (ties keep enumeration order); returns the
+    // rank-th (1-based) and the list size.
+    Plan ranked(int rank) {
+        struct Cand {
+            double cost;
+            int pattern;
+            Region r1, r2;
+        };
+        std::vector<Cand> all;
+        const int nk = (int)tab.kernels.size();
+        if (tab.pat_I)
+            for (int a = 0; a < nk; ++a) {
+                if (!kernel_allowed(a)) continue;
+                for (auto& c : sc[a]) {
+                    Cand x{0.0, PAT_I, {}, {}};
+                    x.cost = cost(a, c, M, N, &x.r1);
+                    all.push_back(x);
+                }
+            }
+        if (opt.force_kernel < 0 && opt.allow_II)
+            for (int dir = 0; dir < 2; ++dir) {
+                if (dir == 0 && !tab.pat_IIM) continue;
+                if (dir == 1 && !tab.pat_IIN) continue;
+                const int64_t ext = dir == 0 ? M : N;
+                for (int a = 0; a < nk; ++a) {
+                    const TableKernel& ka = tab.kernels[a];
+                    const int64_t step = dir == 0 ? ka.uM : ka.uN;
+                    const int64_t across = dir == 0 ? ceil_div(N, ka.uN) : ceil_div(M, ka.uM);
+                    const int64_t slots = (int64_t)tab.cus * ka.wg_per_cu;
+                    for (auto& c1s : sc[a]) {
+                        const int64_t per_line = across * c1s.s_eff * batch;
+                        int64_t prev_cut = 0;
+                        for (int64_t w = 1;; ++w) {
+                            const int64_t cut = (w * slots / per_line) * step;
+                            if (cut >= ext) break;
+                            if (cut == 0 || cut == prev_cut) continue;
+                            prev_cut = cut;
+                            const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
+                            const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
+                            for (int b = 0; b < nk; ++b) {
+                                if (b == a) continue;
+                                for (auto& c2s : sc[b]) {
+                                    Cand x{0.0, dir == 0 ? PAT_IIM : PAT_IIN, {}, {}};
+                                    x.cost = cost(a, c1s, m1, n1, &x.r1) + cost(b, c2s, m2, n2, &x.r2);
+                                    x.r2.m0 = dir == 0 ? cut : 0;
+                                    x.r2.n0 = dir == 0 ? 0 : cut;
+                                    all.push_back(x);
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+        std::stable_sort(all.begin(), all.end(), [](const Cand& x, const Cand& y) { return x.cost < y.cost; });
+        Plan p;
+        p.rank = rank;
+        p.candidates = (int64_t)all.size();
+        if (rank < 1 || rank > (int)all.size()) {
+            p.pattern = PAT_I;
+            p.cost_us = std::numeric_limits<double>::infinity();
+            return p;   // no regions: the caller reports "no plan"
+        }
+        const Cand& c = all[rank - 1];
+        p.pattern = c.pattern;
+        p.cost_us = c.cost;
+        p.regions.push_back(c.r1);
+        if (c.pattern != PAT_I) p.regions.push_back(c.r2);
+        p.regions[0].m0 = p.regions[0].n0 = 0;
+        return p;
+    }
+
     Plan run() {
+        if (opt.plan_rank > 0) return ranked(opt.plan_rank);
         Plan best;
         best.cost_us = std::numeric_limits<double>::infinity();
         const int nk = (int)tab.kernels.size();
@@ -328,15 +408,15 @@ struct Searcher {
                         Region r1;
                         const double c1 = dir == 0 ? cost(a, c1s, cut, N, &r1) : cost(a, c1s, M, cut, &r1);
                         // c1 grows with w: once it cannot lead to a better plan, stop
-                        if (!opt.exhaustive && c1 + lb_region >= best.cost_us) break;
+                        if (prune() && c1 + lb_region >= best.cost_us) break;
                         const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
-                        if (!opt.exhaustive &&
+                        if (prune() &&
                             c1 + tab.launch_us + std::max((double)m2 * n2 * batch * min_rate, lb_region - tab.launch_us) >=
                                 best.cost_us)
                             continue;
                         for (int b = 0; b < nk; ++b) {
                             if (b == a) continue;
-                            if (!opt.exhaustive && c1 + lb(b, m2, n2) >= best.cost_us) continue;
+                            if (prune() && c1 + lb(b, m2, n2) >= best.cost_us) continue;
                             Region r2;
                             const double c2 = dir == 0 ? best_region(b, M - cut, N, &r2) : best_region(b, M, N - cut, &r2);
                             const double c = c1 + c2;
@@ -382,7 +462,9 @@ std::string plan_to_json(const Plan& p, const PerfTable& tab) {
     std::ostringstream o;
     o.precision(17);
     o << "{\"pattern\":\"" << names[p.pattern] << "\",\"cost_us\":" << (p.regions.empty() ? 0.0 : p.cost_us)
-      << ",\"plan_us\":" << p.plan_us << ",\"evaluated\":" << p.evaluated << ",\"regions\":[";
+      << ",\"plan_us\":" << p.plan_us << ",\"evaluated\":" << p.evaluated;
+    if (p.rank > 0) o << ",\"rank\":" << p.rank << ",\"candidates\":" << p.candidates;
+    o << ",\"regions\":[";
     for (size_t i = 0; i < p.regions.size(); ++i) {
         const Region& r = p.regions[i];
         const TableKernel& k = tab.kernels[r.kernel];

@@ -60,7 +60,15 @@ struct Plan {
     double cost_us = 0.0;
     double plan_us = 0.0;
     int64_t evaluated = 0;   // candidate regions scored
+    int rank = 0;            // >0: this is the rank-th cheapest candidate
+    int64_t candidates = 0;  // size of the ranked candidate list (rank > 0 only)
 };
+
+// Which factors of the cost model the search scores (MikPoly page, section 4
+// ablation): the full product f_wave * f_pipe, f_wave alone (f_pipe taken as
+// 1 us), or f_pipe alone (f_wave taken as 1).  The launch and split-K
+// reduction terms stay in all three.
+enum CostMode { COST_FULL = 0, COST_WAVE = 1, COST_PIPE = 2 };
 
 struct SearchOptions {
     bool exhaustive = false;
@@ -68,6 +76,8 @@ struct SearchOptions {
     int force_splitk = 0;    // 0 = free choice
     int splitk_max = 64;
     bool allow_II = true;
+    int cost_mode = COST_FULL;
+    int plan_rank = 0;       // >0: return the rank-th cheapest candidate of the whole space
 };
 
 // Parse the text form of a table.  Returns false and sets err on bad input.

@@ -127,8 +127,20 @@ int mkp_calibrate(const char *path, int max_points);
  * L2 write-back than the second launch), "pack_unaligned" (1 = an operand
  * whose rows are not 16-byte aligned and that several tiles re-read is
  * first copied into aligned workspace rows, the default; 0 = such operands
- * are read element by element).  "exhaustive", "force_*", "patterns" and
- * "splitk_max" clear the plan cache.  Returns MKP_OK or
+ * are read element by element).
+ * Cost-model evaluation (MikPoly page, section 5 "cost-model effectiveness":
+ * the WAVE and PIPE ablations and the ORACLE that measures candidates):
+ * "cost_model" ("full" = f_wave * f_pipe, the default; "wave" = f_wave with
+ * f_pipe taken as 1 us; "pipe" = f_pipe with f_wave taken as 1; the launch
+ * and split-K reduction terms stay in all three; the ablations search the
+ * space without pruning), "plan_rank" (0 = the cheapest plan, the default;
+ * r > 0 = the r-th cheapest of every candidate of the space, each region
+ * with each of its split factors, ties in enumeration order, so that a
+ * caller can launch and time candidates one by one; a rank beyond the
+ * candidate count makes the GEMM fail with MKP_ERR_UNSUPPORTED).  Both also
+ * apply to mkp_plan_with_table, whose JSON then carries "rank" and
+ * "candidates".  Every option except "trace", "fused_reduce" and
+ * "pack_unaligned" clears the plan cache.  Returns MKP_OK or
  * MKP_ERR_INVALID_ARG / MKP_ERR_UNSUPPORTED. */
 int mkp_set_option(const char *key, const char *value);
 

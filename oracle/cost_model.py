@@ -25,6 +25,9 @@ Readings where the page is silent (each is listed in the design doc):
     red_launch_us + (2s+1)*4*m*n*batch bytes / red_GBps.
   * g between measured points is linear; beyond the last point it continues
     the last segment's slope.
+  * the ablations of section 5 "cost-model effectiveness" (MikPoly-WAVE,
+    MikPoly-PIPE) keep one factor of the product and take the other as 1
+    (f_pipe = 1 us, resp. f_wave = 1); the launch and reduction terms stay.
   * Pattern I: one region = whole output, one kernel.  Pattern II-M (II-N):
     a cut of the M (N) extent, the two parts on two different kernels (the
     case study's 3072 | 1024 split).  The cut is a wave boundary of the
@@ -142,21 +145,28 @@ class Region:
     s: int
 
 
-def region_cost(tab: Table, r: Region, K: int, batch: int) -> float:
+MODES = ("full", "wave", "pipe")
+
+
+def region_cost(tab: Table, r: Region, K: int, batch: int, mode: str = "full") -> float:
     k = tab.kernels[r.kernel]
     t3 = ceil_div(K, k.uK)
     per, s_eff = split_steps(t3, r.s)
     f_parallel = ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch
     f_wave = ceil_div(f_parallel, tab.slots(k))
     f_pipe = g_predict(k, per)
+    if mode == "wave":
+        f_pipe = 1.0
+    elif mode == "pipe":
+        f_wave = 1
     c = tab.launch_us + f_wave * f_pipe
     if s_eff > 1:
         c += tab.red_launch_us + (2 * s_eff + 1) * 4.0 * r.m * r.n * batch / (tab.red_gbps * 1e3)
     return c
 
 
-def plan_cost(tab: Table, regions: Sequence[Region], K: int, batch: int) -> float:
-    return sum(region_cost(tab, r, K, batch) for r in regions)
+def plan_cost(tab: Table, regions: Sequence[Region], K: int, batch: int, mode: str = "full") -> float:
+    return sum(region_cost(tab, r, K, batch, mode) for r in regions)
 
 
 def _valid_splits(tab: Table, k: Kernel, K: int) -> List[int]:
@@ -205,15 +215,31 @@ def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1):
                             yield pat, (r1, r2)
 
 
-def exhaustive_best(tab: Table, M: int, N: int, K: int, batch: int = 1):
+def exhaustive_best(tab: Table, M: int, N: int, K: int, batch: int = 1, mode: str = "full"):
     """Minimum modelled cost over the whole space (the page's ORACLE variant
     searches exhaustively; here only the modelled cost is minimised)."""
     best: Optional[Tuple[float, str, tuple]] = None
     for pat, regs in enumerate_plans(tab, M, N, K, batch):
-        c = plan_cost(tab, regs, K, batch)
+        c = plan_cost(tab, regs, K, batch, mode)
         if best is None or c < best[0]:
             best = (c, pat, regs)
     return best
+
+
+def distinct_candidates(tab: Table, M: int, N: int, K: int, batch: int = 1, mode: str = "full"):
+    """Every distinct candidate (two requested split factors that give the
+    same number of splits are one candidate) with its modelled cost, sorted
+    by cost."""
+    seen = {}
+    for pat, regs in enumerate_plans(tab, M, N, K, batch):
+        key = [pat]
+        for r in regs:
+            t3 = ceil_div(K, tab.kernels[r.kernel].uK)
+            key.append((r.m0, r.n0, r.m, r.n, r.kernel, split_steps(t3, r.s)[1]))
+        key = tuple(key)
+        if key not in seen:
+            seen[key] = (plan_cost(tab, regs, K, batch, mode), pat, regs)
+    return sorted(seen.values(), key=lambda x: x[0])
 
 
 def covers_exactly(M: int, N: int, regions: Sequence[Region], tiles: Dict[str, Tuple[int, int]]) -> bool:

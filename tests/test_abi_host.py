@@ -65,6 +65,10 @@ def test_options_and_errors(mkp):
     assert e.value.code == mkp.MKP_ERR_UNSUPPORTED
     with pytest.raises(mkp.MkpError):
         mkp.mkp_set_option("patterns", "III")
+    for key, bad in (("cost_model", "flops"), ("plan_rank", "-1")):
+        with pytest.raises(mkp.MkpError) as e:
+            mkp.mkp_set_option(key, bad)
+        assert e.value.code == mkp.MKP_ERR_INVALID_ARG
     with pytest.raises(mkp.MkpError):
         mkp.mkp_load_calibration("/nonexistent/table.tbl")
     mkp.mkp_load_calibration(None)

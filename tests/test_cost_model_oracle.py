@@ -111,3 +111,38 @@ g Q 1:0.7 10:5
             assert cm.covers_exactly(M, N, regs, tiles), (pat, regs)
             count += 1
         assert count > 0
+
+
+def test_ablation_costs_of_case_study():
+    """The section 5 ablations on the section 6 case study: with only f_wave
+    the single-kernel plan scores its 2 waves and the split plan 1 + 2
+    waves; with only f_pipe they score Ta and Ta + Tb (one g per region)."""
+    Ta, Tb = 10.0, 3.0
+    tab, gold = case_table(Ta, Tb)
+    M, N, K = gold["shape"]
+    cut = gold["pattern_II"]["cut_m"]
+    single = [cm.Region(0, 0, M, N, "A", 1)]
+    split = [cm.Region(0, 0, cut, N, "A", 1), cm.Region(cut, 0, M - cut, N, "B", 1)]
+    assert cm.plan_cost(tab, single, K, 1, "wave") == pytest.approx(gold["single_A"]["waves"])
+    # the page's timeline Ta + 2 Tb: one wave of A then two of B = its 3 waves
+    assert cm.plan_cost(tab, split, K, 1, "wave") == pytest.approx(gold["pattern_II"]["waves"])
+    assert cm.plan_cost(tab, single, K, 1, "pipe") == pytest.approx(Ta)
+    assert cm.plan_cost(tab, split, K, 1, "pipe") == pytest.approx(Ta + Tb)
+    # the full model is the product per region (the page's 2 Ta and Ta + 2 Tb)
+    assert cm.plan_cost(tab, single, K, 1) == pytest.approx(2 * Ta)
+    assert cm.plan_cost(tab, split, K, 1) == pytest.approx(Ta + 2 * Tb)
+
+
+def test_distinct_candidates_brute_force():
+    """The ranked list holds each distinct plan once, sorted, and its head is
+    the exhaustive minimum; on the case study it holds exactly the plans a
+    hand count gives (2 Pattern I plans; Pattern II cuts at wave boundaries)."""
+    tab, gold = case_table(10.0, 3.0)
+    M, N, K = gold["shape"]
+    c = cm.distinct_candidates(tab, M, N, K)
+    costs = [x[0] for x in c]
+    assert costs == sorted(costs)
+    assert costs[0] == pytest.approx(cm.exhaustive_best(tab, M, N, K)[0])
+    assert sum(1 for x in c if x[1] == "I") == 2
+    # with one split factor every enumerated plan is already distinct
+    assert len(c) == sum(1 for _ in cm.enumerate_plans(tab, M, N, K))

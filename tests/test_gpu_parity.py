@@ -294,3 +294,66 @@ g m64n64k64 1:0.3 1000:300
             run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"II {plan['pattern']}")
     finally:
         mkp.mkp_load_calibration(None)
+
+
+def test_ranked_and_ablated_plans(mkp):
+    """Every plan the measured search launches (the ranked candidates of the
+    shipped table, the WAVE and PIPE ablations, each kernel at 16 splits)
+    computes the product."""
+    rng = np.random.default_rng(12)
+    try:
+        for (M, N, K) in [(300, 257, 129), (1000, 700, 300)]:
+            a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+            for r in range(1, 17):
+                mkp.mkp_set_option("plan_rank", r)
+                plan = mkp.mkp_plan_describe(1, M, N, K)
+                if not plan["regions"]:
+                    break
+                run_case(mkp, a, b, what=f"rank {r} {plan['pattern']}")
+            mkp.mkp_set_option("plan_rank", 0)
+            for mode in ("wave", "pipe"):
+                mkp.mkp_set_option("cost_model", mode)
+                run_case(mkp, a, b, what=f"cost_model {mode}")
+            mkp.mkp_set_option("cost_model", "full")
+        a, b = rand_bits(rng, (300, 1100)), rand_bits(rng, (1100, 257))
+        mkp.mkp_set_option("force_splitk", 16)
+        for name in mkp.mkp_kernel_names():
+            mkp.mkp_set_option("force_kernel", name)
+            run_case(mkp, a, b, what=f"{name} s=16")
+    finally:
+        mkp.mkp_set_option("plan_rank", 0)
+        mkp.mkp_set_option("cost_model", "full")
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("force_splitk", 0)
+
+
+def test_package_imported_before_torch(tmp_path):
+    """A process that imports the package before torch still runs the GEMM
+    (one HIP runtime per process); checked in a child process."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = tmp_path / "c.npy"
+    code = f"""
+import sys
+sys.path.insert(0, {root!r})
+import dynamic_shape_gemm_amd as m
+import numpy as np
+import torch
+import workloads
+case = workloads.config_cases(1)[0]
+a, b = workloads.make_operands(case)
+ta = torch.from_numpy(a[0].view(np.int16)).cuda().view(torch.bfloat16)
+tb = torch.from_numpy(b[0].view(np.int16)).cuda().view(torch.bfloat16)
+c = m.gemm(ta, tb)
+torch.cuda.synchronize()
+np.save({str(out)!r}, c.cpu().numpy())
+"""
+    print("[case] child process: package imported before torch, config1", flush=True)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0, r.stderr[-2000:]
+    case = workloads.config_cases(1)[0]
+    a, b = workloads.make_operands(case)
+    ref, refabs = oracle.gemm(a[0], b[0], with_abs=True)
+    assert_close(np.load(out), ref, refabs, case.K, "package-first child")

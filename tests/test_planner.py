@@ -131,3 +131,51 @@ def test_plan_time_is_microseconds(mkp):
     # the page reports 2 us per shape; this host is slower and unpinned: report, bound loosely
     print(f"median plan time {statistics.median(ts):.1f} us")
     assert statistics.median(ts) < 1000
+
+
+@pytest.mark.parametrize("mode", ["wave", "pipe"])
+def test_ablation_search_matches_oracle(mkp, mode):
+    """MikPoly-WAVE / MikPoly-PIPE (one factor of the cost dropped): the
+    library's search returns the oracle's exhaustive minimum of that cost."""
+    rng = np.random.default_rng(31 if mode == "wave" else 32)
+    try:
+        mkp.mkp_set_option("cost_model", mode)
+        for trial in range(25):
+            text = random_table(rng, int(rng.integers(2, 4)))
+            tab = cm.parse_table(text)
+            M, N, K = (int(x) for x in rng.integers(1, 200, size=3))
+            batch = int(rng.choice([1, 2]))
+            plan = mkp.mkp_plan_with_table(text, batch, M, N, K)
+            best = cm.exhaustive_best(tab, M, N, K, batch, mode)
+            assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (mode, trial, M, N, K)
+            regs = to_regions(plan)
+            assert cm.plan_cost(tab, regs, K, batch, mode) == pytest.approx(plan["cost_us"], rel=1e-9)
+            assert cm.covers_exactly(M, N, regs, {n: (k.uM, k.uN) for n, k in tab.kernels.items()})
+    finally:
+        mkp.mkp_set_option("cost_model", "full")
+
+
+def test_ranked_candidates_match_oracle(mkp):
+    """plan_rank r returns the r-th cheapest distinct candidate of the space,
+    the list having as many entries as the oracle enumerates."""
+    rng = np.random.default_rng(33)
+    try:
+        for trial in range(15):
+            text = random_table(rng, int(rng.integers(2, 4)))
+            tab = cm.parse_table(text)
+            M, N, K = (int(x) for x in rng.integers(1, 160, size=3))
+            cands = cm.distinct_candidates(tab, M, N, K, 1)
+            n = len(cands)
+            for r in sorted({1, 2, max(1, n // 2), n}):
+                mkp.mkp_set_option("plan_rank", str(r))
+                p = mkp.mkp_plan_with_table(text, 1, M, N, K)
+                assert p["rank"] == r and p["candidates"] == n, (trial, r, n, p)
+                assert p["cost_us"] == pytest.approx(cands[r - 1][0], rel=1e-9), (trial, r)
+                regs = to_regions(p)
+                assert cm.plan_cost(tab, regs, K, 1) == pytest.approx(p["cost_us"], rel=1e-9)
+                assert cm.covers_exactly(M, N, regs, {k: (v.uM, v.uN) for k, v in tab.kernels.items()})
+            mkp.mkp_set_option("plan_rank", str(n + 1))
+            p = mkp.mkp_plan_with_table(text, 1, M, N, K)
+            assert p["regions"] == [] and p["candidates"] == n
+    finally:
+        mkp.mkp_set_option("plan_rank", "0")
