@@ -739,17 +739,36 @@ int mkp_calibrate(const char* path, int max_points) {
         b_elems = std::max(b_elems, (size_t)(K * N));
         c_elems = std::max(c_elems, (size_t)(M * N));
     }
-    uint16_t *dA = nullptr, *dB = nullptr;
-    float* dC = nullptr;
-    if (hipMalloc(&dA, a_elems * 2) != hipSuccess || hipMalloc(&dB, b_elems * 2) != hipSuccess ||
-        hipMalloc(&dC, c_elems * 4) != hipSuccess) {
-        (void)hipFree(dA);
-        (void)hipFree(dB);
+    // Operands come from a pool of at least 2 GiB (C from one of 1 GiB) whose
+    // slices rotate from launch to launch, so every timed launch streams its
+    // operands from HBM, as the sweeps' GEMMs do, instead of re-reading them
+    // from the 256 MB last-level cache.
+    auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t pool_ab = std::max<size_t>(size_t(2) << 30, 2 * (round256(a_elems * 2) + round256(b_elems * 2)));
+    const size_t pool_c = std::max<size_t>(size_t(1) << 30, 2 * round256(c_elems * 4));
+    char* pAB = nullptr;
+    char* pC = nullptr;
+    if (hipMalloc(&pAB, pool_ab) != hipSuccess || hipMalloc(&pC, pool_c) != hipSuccess) {
+        (void)hipFree(pAB);
         return fail(MKP_ERR_OOM, "calibration buffers");
     }
-    (void)launch_fill_random_bf16(dA, (int64_t)a_elems, 12345u, nullptr);
-    (void)launch_fill_random_bf16(dB, (int64_t)b_elems, 67890u, nullptr);
+    (void)launch_fill_random_bf16((uint16_t*)pAB, (int64_t)(pool_ab / 2), 12345u, nullptr);
+    (void)hipMemset(pC, 0, pool_c);
     (void)hipDeviceSynchronize();
+    uint16_t* dB = (uint16_t*)pAB;   // probes below use the pool directly
+    float* dC = (float*)pC;
+    int64_t rotation = 0;
+    // point a, for an M x K by K x N product, at the next slices of the pools
+    auto next_operands = [&](KArgs& a) {
+        const size_t fa = round256((size_t)a.M * a.K * 2), fb = round256((size_t)a.K * a.N * 2);
+        const size_t fc = round256((size_t)a.M * a.N * 4);
+        const size_t nab = std::max<size_t>(1, pool_ab / (fa + fb)), nc = std::max<size_t>(1, pool_c / fc);
+        const size_t i = (size_t)rotation++;
+        char* base = pAB + (i % nab) * (fa + fb);
+        a.A = (const uint16_t*)base;
+        a.B = (const uint16_t*)(base + fa);
+        a.C = (float*)(pC + (i % nc) * fc);
+    };
 
     PerfTable t;
     t.cus = cus;
@@ -798,9 +817,6 @@ int mkp_calibrate(const char* path, int max_points) {
             const int64_t K = (int64_t)tt * ki.uK;
             if (K > kmax_cap) break;
             KArgs a{};
-            a.A = dA;
-            a.B = dB;
-            a.C = dC;
             a.M = s.tm * ki.uM;
             a.N = s.tn * ki.uN;
             a.K = (int)K;
@@ -815,12 +831,62 @@ int mkp_calibrate(const char* path, int max_points) {
             a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
             const dim3 grid((unsigned)(s.tm * s.tn));
             // single-launch time, then enough repetitions for ~2 ms
-            double us = time_launches([&] { return ki.launch(a, grid, nullptr); }, 3, 3, &err);
+            auto launch = [&] {
+                next_operands(a);
+                return ki.launch(a, grid, nullptr);
+            };
+            double us = time_launches(launch, 3, 3, &err);
             if (err != hipSuccess) break;
             int reps = (int)std::min(200.0, std::max(5.0, 2000.0 / std::max(us, 1.0)));
-            us = time_launches([&] { return ki.launch(a, grid, nullptr); }, 20, reps, &err);
+            us = time_launches(launch, 20, reps, &err);
             if (err != hipSuccess) break;
             k.pts.emplace_back((double)tt, std::max(us - t.launch_us, 0.05));
+        }
+        // partial last wave, at 16 K steps, relative to a full wave of the
+        // same depth: a wave filling a fraction f of the slots on its own
+        // (tail), and the time f adds after one full wave (tailx)
+        const int t_ref = 16;
+        double g_ref = 0;
+        for (auto& pt : k.pts)
+            if (pt.first == t_ref) g_ref = pt.second;
+        if (err == hipSuccess && g_ref > 0) {
+            static const double fills[] = {1.0 / 16, 1.0 / 8, 1.0 / 4, 1.0 / 2, 3.0 / 4};
+            const int slots = s.tm * s.tn;
+            int prev_tn = 0;
+            for (double f : fills) {
+                const int tn = std::max(1, (int)std::lround(f * s.tn));
+                if (tn == prev_tn || tn >= s.tn) continue;
+                prev_tn = tn;
+                double us[2];
+                for (int after = 0; after < 2 && err == hipSuccess; ++after) {
+                    const int cols = tn + (after ? s.tn : 0);
+                    KArgs a{};
+                    a.M = s.tm * ki.uM;
+                    a.N = cols * ki.uN;
+                    a.K = t_ref * ki.uK;
+                    a.lda = a.K;
+                    a.ldb = a.N;
+                    a.ldc = a.N;
+                    a.tiles_m = s.tm;
+                    a.tiles_n = cols;
+                    a.steps_per_split = t_ref;
+                    a.splits = 1;
+                    a.batch = 1;
+                    a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+                    const dim3 grid((unsigned)(s.tm * cols));
+                    us[after] = time_launches(
+                        [&] {
+                            next_operands(a);
+                            return ki.launch(a, grid, nullptr);
+                        },
+                        20, 50, &err);
+                }
+                if (err != hipSuccess) break;
+                const double fill = (double)(s.tm * tn) / slots;
+                auto clamp = [](double r) { return std::min(1.0, std::max(0.02, r)); };
+                k.tail.emplace_back(fill, clamp(std::max(us[0] - t.launch_us, 0.05) / g_ref));
+                k.tailx.emplace_back(fill, clamp((us[1] - t.launch_us - g_ref) / g_ref));
+            }
         }
         t.kernels.push_back(k);
     }
@@ -831,9 +897,9 @@ int mkp_calibrate(const char* path, int max_points) {
         t.mfma_tflops = (double)blocks * 4 * 64.0 * iters * 32768.0 / us / 1e6;
     }
     if (err == hipSuccess) {
-        // copy between the two halves of the B buffer, up to 1 GB each way
-        // (well beyond the 256 MB MALL)
-        const int64_t half = (int64_t)b_elems * 2 / 2;
+        // copy between the two halves of the operand pool, up to 1 GB each
+        // way (well beyond the 256 MB MALL)
+        const int64_t half = (int64_t)(pool_ab / 2);
         const int64_t bytes = std::min<int64_t>(half, int64_t(1) << 30) & ~int64_t(15);
         char* base = (char*)dB;
         const double us = time_launches(
@@ -841,9 +907,8 @@ int mkp_calibrate(const char* path, int max_points) {
         t.hbm_gbps = 2.0 * (double)bytes / us / 1e3;
     }
     (void)hipDeviceSynchronize();
-    (void)hipFree(dA);
-    (void)hipFree(dB);
-    (void)hipFree(dC);
+    (void)hipFree(pAB);
+    (void)hipFree(pC);
     if (err != hipSuccess) return fail(MKP_ERR_HIP, std::string("calibration launch: ") + hipGetErrorString(err));
 
     std::string text = "# measured by mkp_calibrate on " + std::string(prop.name) + " (" +

@@ -18,7 +18,7 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
     std::istringstream in(text);
     std::string raw;
     int lineno = 0;
-    std::vector<std::pair<std::string, std::vector<std::pair<double, double>>>> gs;
+    std::vector<std::pair<std::string, std::vector<std::pair<double, double>>>> gs, tails, tailxs;
     while (std::getline(in, raw)) {
         ++lineno;
         auto hash = raw.find('#');
@@ -63,6 +63,20 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
             for (auto& e : t.kernels)
                 if (e.name == k.name) return fail("duplicate kernel");
             t.kernels.push_back(k);
+        } else if (key == "tail" || key == "tailx") {
+            // tail[x] <kernel> <f>:<ratio> ...  (partial-wave time relative to a full wave)
+            std::string name, tok;
+            if (!(ls >> name)) return fail("bad tail line");
+            std::vector<std::pair<double, double>> pts;
+            while (ls >> tok) {
+                auto c = tok.find(':');
+                if (c == std::string::npos) return fail("bad tail point");
+                double f = std::atof(tok.substr(0, c).c_str());
+                double r = std::atof(tok.substr(c + 1).c_str());
+                if (!(f > 0 && f < 1) || !(r > 0 && r <= 1)) return fail("bad tail value");
+                pts.emplace_back(f, r);
+            }
+            (key == "tail" ? tails : tailxs).emplace_back(name, pts);
         } else if (key == "g") {
             std::string name, tok;
             if (!(ls >> name)) return fail("bad g line");
@@ -92,7 +106,23 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
             return false;
         }
     }
+    for (int which = 0; which < 2; ++which)
+        for (auto& tl : which ? tailxs : tails) {
+            bool found = false;
+            for (auto& k : t.kernels)
+                if (k.name == tl.first) {
+                    auto& dst = which ? k.tailx : k.tail;
+                    dst.insert(dst.end(), tl.second.begin(), tl.second.end());
+                    found = true;
+                }
+            if (!found) {
+                err = "tail line for unknown kernel " + tl.first;
+                return false;
+            }
+        }
     for (auto& k : t.kernels) {
+        std::sort(k.tail.begin(), k.tail.end());
+        std::sort(k.tailx.begin(), k.tailx.end());
         if (k.pts.empty()) {
             err = "kernel " + k.name + " has no g points";
             return false;
@@ -125,6 +155,14 @@ std::string table_to_text(const PerfTable& t) {
         for (auto& p : k.pts) o << " " << p.first << ":" << p.second;
         o << "\n";
     }
+    for (int which = 0; which < 2; ++which)
+        for (auto& k : t.kernels) {
+            const auto& pts = which ? k.tailx : k.tail;
+            if (pts.empty()) continue;
+            o << (which ? "tailx " : "tail ") << k.name;
+            for (auto& p : pts) o << " " << p.first << ":" << p.second;
+            o << "\n";
+        }
     return o.str();
 }
 
@@ -146,8 +184,29 @@ double g_predict(const TableKernel& k, double t) {
     return v1 + (v1 - v0) * (t - t1) / (t1 - t0);
 }
 
+double tail_ratio(const std::vector<std::pair<double, double>>& p, double f) {
+    if (p.empty() || f >= 1.0) return 1.0;
+    if (f <= p[0].first) return p[0].second;
+    for (size_t i = 1; i <= p.size(); ++i) {
+        const double f1 = i < p.size() ? p[i].first : 1.0, r1 = i < p.size() ? p[i].second : 1.0;
+        if (f <= f1) {
+            const double f0 = p[i - 1].first, r0 = p[i - 1].second;
+            return r0 + (r1 - r0) * (f - f0) / (f1 - f0);
+        }
+    }
+    return 1.0;
+}
+
+double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots) {
+    const int64_t full = tasks / slots, rem = tasks % slots;
+    if (!rem) return (double)full;
+    return (double)full + tail_ratio(full ? k.tailx : k.tail, (double)rem / (double)slots);
+}
+
 // Cost of one region served by one kernel with a requested split factor:
-//   launch + ceil(tasks / slots) * g(steps) [+ split-K reduction]
+//   launch + (full waves + partial last wave) * g(steps) [+ split-K reduction]
+// (with a kernel that has no tail points the wave term is ceil(tasks/slots),
+// the page's f_wave).
 double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K, int64_t batch,
                    int s_req, Region* out) {
     const TableKernel& k = tab.kernels[kernel];
@@ -157,7 +216,8 @@ double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64
     const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * s_eff * batch;
     const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
     const int64_t waves = ceil_div(tasks, slots);
-    double c = tab.launch_us + (double)waves * g_predict(k, (double)per);
+    const double wf = wave_factor(k, tasks, slots);
+    double c = tab.launch_us + wf * g_predict(k, (double)per);
     if (s_eff > 1)
         c += tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch /
                                      (tab.red_gbps * 1e3);
@@ -170,6 +230,7 @@ double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64
         out->steps = (int)per;
         out->tasks = tasks;
         out->waves = waves;
+        out->wave_factor = wf;
         out->cost = c;
     }
     return c;
@@ -200,7 +261,7 @@ struct Searcher {
         double g;
     };
     std::vector<std::vector<SplitChoice>> sc;   // per kernel: distinct usable splits
-    std::vector<double> min_g;                   // per kernel: cheapest single wave
+    std::vector<double> min_g;                   // per kernel: cheapest single (possibly partial) wave
     std::vector<double> rate;                    // per kernel: lowest cost per output element
     double lb_region = 0.0;                      // lower bound of any region's cost
     double min_rate = 0.0;                       // lowest rate over allowed kernels
@@ -229,6 +290,15 @@ struct Searcher {
         for (size_t ki = 0; ki < tab.kernels.size(); ++ki) {
             const TableKernel& kk = tab.kernels[ki];
             const int64_t t3 = ceil_div(K, kk.uK);
+            // a region's wave factor is at least tmin (one possibly partial
+            // wave) and at least rho * tasks/slots (piecewise-linear ratios:
+            // r(f)/f is smallest at a point or at f = 1)
+            double tmin = 1.0, rho = 1.0;
+            for (auto& p : kk.tail) {
+                tmin = std::min(tmin, p.second);
+                rho = std::min(rho, p.second / p.first);
+            }
+            for (auto& p : kk.tailx) rho = std::min(rho, p.second / p.first);
             for (int s_req : req) {
                 // a factor above the K-step count is only kept when forced
                 if (s_req > 1 && s_req > t3 && opt.force_splitk <= 0) continue;
@@ -239,9 +309,9 @@ struct Searcher {
                 for (auto& c : sc[ki]) dup |= c.s_eff == s_eff;
                 if (dup) continue;
                 sc[ki].push_back({s_eff, (int)per, g_predict(kk, (double)per)});
-                min_g[ki] = std::min(min_g[ki], sc[ki].back().g);
+                min_g[ki] = std::min(min_g[ki], tmin * sc[ki].back().g);
                 const double slots = (double)tab.cus * kk.wg_per_cu;
-                rate[ki] = std::min(rate[ki], (double)s_eff * sc[ki].back().g / (slots * kk.uM * kk.uN));
+                rate[ki] = std::min(rate[ki], rho * (double)s_eff * sc[ki].back().g / (slots * kk.uM * kk.uN));
             }
             if (kernel_allowed((int)ki)) {
                 lb_region = std::min(lb_region, tab.launch_us + min_g[ki]);
@@ -256,11 +326,13 @@ struct Searcher {
         ++evaluated;
         const TableKernel& k = tab.kernels[ki];
         const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * c.s_eff * batch;
-        const int64_t waves = ceil_div(tasks, (int64_t)tab.cus * k.wg_per_cu);
+        const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
+        const int64_t waves = ceil_div(tasks, slots);
+        const double wf = wave_factor(k, tasks, slots);
         double v = tab.launch_us;
-        if (opt.cost_mode == COST_WAVE) v += (double)waves;
+        if (opt.cost_mode == COST_WAVE) v += (double)waves;   // the page's f_wave alone
         else if (opt.cost_mode == COST_PIPE) v += c.g;
-        else v += (double)waves * c.g;
+        else v += wf * c.g;
         if (c.s_eff > 1)
             v += tab.red_launch_us +
                  (double)(2 * c.s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch / (tab.red_gbps * 1e3);
@@ -273,6 +345,7 @@ struct Searcher {
             r->steps = c.per;
             r->tasks = tasks;
             r->waves = waves;
+            r->wave_factor = wf;
             r->cost = v;
         }
         return v;
@@ -472,7 +545,7 @@ std::string plan_to_json(const Plan& p, const PerfTable& tab) {
         o << "{\"m0\":" << r.m0 << ",\"n0\":" << r.n0 << ",\"m\":" << r.m << ",\"n\":" << r.n
           << ",\"kernel\":\"" << k.name << "\",\"uM\":" << k.uM << ",\"uN\":" << k.uN << ",\"uK\":" << k.uK
           << ",\"s\":" << r.s << ",\"steps\":" << r.steps << ",\"tasks\":" << r.tasks
-          << ",\"waves\":" << r.waves << ",\"cost_us\":" << r.cost << "}";
+          << ",\"waves\":" << r.waves << ",\"wave_factor\":" << r.wave_factor << ",\"cost_us\":" << r.cost << "}";
     }
     o << "]}";
     return o.str();

@@ -26,6 +26,12 @@ struct TableKernel {
     int uM = 0, uN = 0, uK = 0;
     int wg_per_cu = 1;                               // resident workgroups per CU
     std::vector<std::pair<double, double>> pts;      // (t, us), sorted by t
+    // Partial last wave: (fraction f of the slots filled, time of that wave
+    // relative to a full one), sorted by f; empty = every wave costs a full g.
+    // `tail` holds a wave that runs alone (fewer tasks than slots); `tailx`
+    // the extra time a partial wave adds after full waves, whose stragglers
+    // it overlaps.
+    std::vector<std::pair<double, double>> tail, tailx;
     int lib_index = -1;                              // index in the kernel library, -1 if none
 };
 
@@ -50,7 +56,8 @@ struct Region {
     int s = 1;              // K splits actually used
     int steps = 0;          // K steps (of uK) per split = f_num
     int64_t tasks = 0;      // f_parallel (includes splits and batch)
-    int64_t waves = 0;      // f_wave
+    int64_t waves = 0;      // f_wave = ceil(tasks / slots)
+    double wave_factor = 0; // full waves + relative time of the partial last one
     double cost = 0.0;
 };
 
@@ -85,6 +92,12 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err);
 std::string table_to_text(const PerfTable& t);
 
 double g_predict(const TableKernel& k, double t);
+// Time of a wave whose tasks fill a fraction f (0 < f <= 1) of the slots,
+// relative to a full wave: 1 without tail points; linear between points and
+// up to (1, 1); the first point's value below it.
+double tail_ratio(const std::vector<std::pair<double, double>>& pts, double f);
+// Waves a region of `tasks` tasks costs: full waves plus the partial last one.
+double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots);
 double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K,
                    int64_t batch, int s_req, Region* out);
 

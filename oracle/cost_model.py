@@ -25,6 +25,14 @@ Readings where the page is silent (each is listed in the design doc):
     red_launch_us + (2s+1)*4*m*n*batch bytes / red_GBps.
   * g between measured points is linear; beyond the last point it continues
     the last segment's slope.
+  * a partial last wave (not on the page): with tasks = w*slots + r, r > 0,
+    the wave term is w + tail(r/slots), where tail(f) is the measured time
+    of a wave filling a fraction f of the slots relative to a full wave
+    (linear between measured points and up to tail(1) = 1, the first
+    point's value below it) -- the `tail` points when w = 0 (the wave runs
+    alone), the `tailx` points when w > 0 (it follows full waves).  Without
+    points it is ceil(tasks/slots), the page's f_wave.  The WAVE ablation
+    keeps the page's ceil.
   * the ablations of section 5 "cost-model effectiveness" (MikPoly-WAVE,
     MikPoly-PIPE) keep one factor of the product and take the other as 1
     (f_pipe = 1 us, resp. f_wave = 1); the launch and reduction terms stay.
@@ -50,6 +58,8 @@ class Kernel:
     uK: int
     wg_per_cu: int
     pts: List[Tuple[float, float]]  # (t, microseconds) sorted by t
+    tail: List[Tuple[float, float]] = dataclasses.field(default_factory=list)   # (fill, ratio), alone
+    tailx: List[Tuple[float, float]] = dataclasses.field(default_factory=list)  # after full waves
 
 
 @dataclasses.dataclass
@@ -75,6 +85,8 @@ def parse_table(text: str) -> Table:
     patterns = ["I", "II-M", "II-N"]
     kernels: Dict[str, Kernel] = {}
     gpts: Dict[str, List[Tuple[float, float]]] = {}
+    tails: Dict[str, List[Tuple[float, float]]] = {}
+    tailxs: Dict[str, List[Tuple[float, float]]] = {}
     for raw in text.splitlines():
         line = raw.split("#", 1)[0].strip()
         if not line:
@@ -101,10 +113,18 @@ def parse_table(text: str) -> Table:
                 t, v = p.split(":")
                 pts.append((float(t), float(v)))
             gpts.setdefault(tok[1], []).extend(pts)
+        elif key in ("tail", "tailx"):
+            for p in tok[2:]:
+                f, r = p.split(":")
+                (tails if key == "tail" else tailxs).setdefault(tok[1], []).append((float(f), float(r)))
         else:
             raise ValueError(f"unknown table line: {raw!r}")
     for name, pts in gpts.items():
         kernels[name].pts = sorted(pts)
+    for name, pts in tails.items():
+        kernels[name].tail = sorted(pts)
+    for name, pts in tailxs.items():
+        kernels[name].tailx = sorted(pts)
     for k in kernels.values():
         if not k.pts:
             raise ValueError(f"kernel {k.name} has no g points")
@@ -127,6 +147,26 @@ def g_predict(k: Kernel, t: float) -> float:
 
 def ceil_div(a: int, b: int) -> int:
     return -(-a // b)
+
+
+def tail_ratio(points: List[Tuple[float, float]], f: float) -> float:
+    """Relative time of a wave filling a fraction f of the slots."""
+    if not points or f >= 1.0:
+        return 1.0
+    pts = list(points) + [(1.0, 1.0)]
+    if f <= pts[0][0]:
+        return pts[0][1]
+    for (f0, r0), (f1, r1) in zip(pts, pts[1:]):
+        if f <= f1:
+            return r0 + (r1 - r0) * (f - f0) / (f1 - f0)
+    return 1.0
+
+
+def wave_term(k: Kernel, tasks: int, slots: int) -> float:
+    full, rem = divmod(tasks, slots)
+    if not rem:
+        return full
+    return full + tail_ratio(k.tailx if full else k.tail, rem / slots)
 
 
 def split_steps(t3: int, s: int) -> Tuple[int, int]:
@@ -153,9 +193,10 @@ def region_cost(tab: Table, r: Region, K: int, batch: int, mode: str = "full") -
     t3 = ceil_div(K, k.uK)
     per, s_eff = split_steps(t3, r.s)
     f_parallel = ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch
-    f_wave = ceil_div(f_parallel, tab.slots(k))
+    f_wave = wave_term(k, f_parallel, tab.slots(k))
     f_pipe = g_predict(k, per)
     if mode == "wave":
+        f_wave = ceil_div(f_parallel, tab.slots(k))
         f_pipe = 1.0
     elif mode == "pipe":
         f_wave = 1

@@ -76,7 +76,9 @@ def test_options_and_errors(mkp):
 
 def test_bad_tables_rejected(mkp, tmp_path):
     for text in ["device 0\n", "kernel X 16 16 16 1\n", "device 4\nkernel X 16 16 16 1\ng Y 1:1\n",
-                 "frobnicate 3\n"]:
+                 "frobnicate 3\n", "device 4\nkernel X 16 16 16 1\ng X 1:1\ntail X 1.0:0.5\n",
+                 "device 4\nkernel X 16 16 16 1\ng X 1:1\ntail X 0.5:1.5\n",
+                 "device 4\nkernel X 16 16 16 1\ng X 1:1\ntail Y 0.5:0.5\n"]:
         with pytest.raises(mkp.MkpError):
             mkp.mkp_plan_with_table(text, 1, 64, 64, 64)
     p = tmp_path / "t.tbl"

@@ -146,3 +146,41 @@ def test_distinct_candidates_brute_force():
     assert sum(1 for x in c if x[1] == "I") == 2
     # with one split factor every enumerated plan is already distinct
     assert len(c) == sum(1 for _ in cm.enumerate_plans(tab, M, N, K))
+
+
+def test_partial_wave_term_closed_form():
+    """The partial-last-wave refinement: tail points interpolate linearly up
+    to (1, 1), hold their first value below the first point, and a region of
+    w*slots + r tasks costs (w + tail(r/slots)) * g, with the `tail` points
+    when w = 0 and the `tailx` points when w > 0; with no points the term is
+    the page's ceil(tasks/slots)."""
+    text = """device 4
+launch_us 0.5
+splitk 1
+kernel k 16 16 16 2
+g k 1:2 10:11
+tail k 0.25:0.4 0.5:0.7
+tailx k 0.5:0.2
+"""
+    tab = cm.parse_table(text)
+    k = tab.kernels["k"]
+    assert tab.slots(k) == 8
+    assert cm.tail_ratio(k.tail, 0.1) == pytest.approx(0.4)          # below the first point
+    assert cm.tail_ratio(k.tail, 0.25) == pytest.approx(0.4)
+    assert cm.tail_ratio(k.tail, 0.375) == pytest.approx(0.55)       # halfway 0.4 -> 0.7
+    assert cm.tail_ratio(k.tail, 0.75) == pytest.approx(0.85)        # halfway 0.7 -> 1
+    assert cm.tail_ratio(k.tail, 1.0) == 1.0
+    assert cm.tail_ratio(k.tailx, 0.3) == pytest.approx(0.2)         # the tailx points
+    assert cm.tail_ratio(k.tailx, 0.75) == pytest.approx(0.6)        # halfway 0.2 -> 1
+    # 16 x 16 output, K = 16: 1 task of g(1) = 2 us; 1 of 8 slots filled, alone
+    assert cm.region_cost(tab, cm.Region(0, 0, 16, 16, "k", 1), 16, 1) == pytest.approx(0.5 + 0.4 * 2)
+    # 11 tasks of t = 10 steps: one full wave (8) + 3/8 filled after it -> (1 + 0.2) * 11
+    r = cm.Region(0, 0, 16, 176, "k", 1)
+    assert cm.region_cost(tab, r, 160, 1) == pytest.approx(0.5 + 1.2 * 11)
+    # exactly two full waves: no partial term
+    assert cm.region_cost(tab, cm.Region(0, 0, 16, 256, "k", 1), 160, 1) == pytest.approx(0.5 + 2 * 11)
+    # the WAVE ablation keeps ceil(tasks / slots)
+    assert cm.region_cost(tab, r, 160, 1, "wave") == pytest.approx(0.5 + 2)
+    # without tail lines the full model is the page's ceil
+    tab0 = cm.parse_table(text.replace("tail k 0.25:0.4 0.5:0.7\n", "").replace("tailx k 0.5:0.2\n", ""))
+    assert cm.region_cost(tab0, r, 160, 1) == pytest.approx(0.5 + 2 * 11)

@@ -59,7 +59,7 @@ def test_case_study_through_library(mkp, Ta, Tb):
         assert plan["cost_us"] == pytest.approx(2 * Ta)
 
 
-def random_table(rng, nk):
+def random_table(rng, nk, tails=False):
     cus = int(rng.integers(2, 12))
     lines = [f"device {cus}", f"launch_us {rng.uniform(0, 3):.3f}", "splitk 1 2 3 4 8",
              f"reduce {rng.uniform(0, 2):.3f} {rng.uniform(100, 2000):.1f}"]
@@ -75,6 +75,10 @@ def random_table(rng, nk):
         slope = rng.uniform(0.05, 1.0)
         pts = " ".join(f"{t}:{base + slope * t * rng.uniform(0.9, 1.1):.4f}" for t in (1, 3, 8, 20))
         lines.append(f"g {n} {pts}")
+        if tails:
+            for key in ("tail", "tailx"):
+                fs = sorted(rng.uniform(0.05, 0.95, size=int(rng.integers(1, 4))))
+                lines.append(f"{key} {n} " + " ".join(f"{f:.3f}:{rng.uniform(0.05, 1.0):.3f}" for f in fs))
     return "\n".join(lines) + "\n"
 
 
@@ -179,3 +183,21 @@ def test_ranked_candidates_match_oracle(mkp):
             assert p["regions"] == [] and p["candidates"] == n
     finally:
         mkp.mkp_set_option("plan_rank", "0")
+
+
+def test_partial_wave_search_is_exact(mkp):
+    """With partial-wave (tail) points in the table, the pruned search still
+    reaches the oracle's exhaustive minimum, and every chosen plan's cost
+    recomputes to the oracle's."""
+    rng = np.random.default_rng(77)
+    for trial in range(40):
+        text = random_table(rng, int(rng.integers(2, 4)), tails=True)
+        tab = cm.parse_table(text)
+        M, N, K = (int(x) for x in rng.integers(1, 220, size=3))
+        batch = int(rng.choice([1, 1, 2]))
+        plan = mkp.mkp_plan_with_table(text, batch, M, N, K)
+        best = cm.exhaustive_best(tab, M, N, K, batch)
+        assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (trial, text, M, N, K, batch)
+        regs = to_regions(plan)
+        assert cm.plan_cost(tab, regs, K, batch) == pytest.approx(plan["cost_us"], rel=1e-9)
+        assert cm.covers_exactly(M, N, regs, {n: (k.uM, k.uN) for n, k in tab.kernels.items()})
