@@ -43,11 +43,14 @@ def log(msg):
 class Workload:
     """Device-resident operands for one sweep of a config."""
 
-    def __init__(self, cfg: int, copies: int = 1):
+    def __init__(self, cfg: int, copies: int = 1, b_layout: str = "kn"):
         import torch
         import workloads
 
         self.cfg = cfg
+        # kn: B is K x N (mkp_gemm); nk: B is kept as N x K, a linear layer's
+        # weight layout (mkp_gemm_bt) -- the same products either way
+        self.bt = b_layout == "nk"
         self.cases = workloads.config_cases(cfg)
         self.calls = []  # (case, A ptr, B ptr, C tensor)
         self.host = []   # (a bits, b bits) kept for the CPU baseline
@@ -60,13 +63,13 @@ class Workload:
                 # `copies` distinct device copies and rotate through them
                 if case.seed_b not in weights:
                     b = workloads.make_b(case)
-                    tb = torch.from_numpy(b.view(np.int16)).cuda()
+                    tb = self._dev_b(torch, b)
                     weights[case.seed_b] = (b, [tb] + [tb.clone() for _ in range(copies - 1)])
                 b, tbs = weights[case.seed_b]
                 tb = tbs[i % len(tbs)]
             else:
                 b = workloads.make_b(case)
-                tb = torch.from_numpy(b.view(np.int16)).cuda()
+                tb = self._dev_b(torch, b)
             ta = torch.from_numpy(a.view(np.int16)).cuda()
             tc = torch.empty((case.batch, case.M, case.N), dtype=torch.float32, device="cuda")
             self.keep += [ta, tb]
@@ -75,9 +78,16 @@ class Workload:
         self.flops = sum(c.flops for c in self.cases)
         self.bytes = sum(c.bytes for c in self.cases)
 
+    def _dev_b(self, torch, b):
+        t = torch.from_numpy(b.view(np.int16)).cuda()
+        return t.transpose(-1, -2).contiguous() if self.bt else t
+
     def step(self, mkp, stream):
         for case, pa, pb, tc in self.calls:
-            if case.batch == 1:
+            if self.bt:
+                mkp.mkp_gemm_batched_bt(case.batch, case.M, case.N, case.K, pa, case.K, case.M * case.K, pb, case.K,
+                                        case.N * case.K, tc, case.N, case.M * case.N, stream)
+            elif case.batch == 1:
                 mkp.mkp_gemm(case.M, case.N, case.K, pa, case.K, pb, case.N, tc, case.N, stream)
             else:
                 mkp.mkp_gemm_batched(case.batch, case.M, case.N, case.K, pa, case.K, case.M * case.K, pb, case.N,
@@ -222,6 +232,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail", action="store_true", help="per-GEMM timings to stderr")
+    ap.add_argument("--b-layout", choices=["kn", "nk"], default="kn",
+                    help="B as K x N (default) or kept N x K, a linear layer's weight layout")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of MiB (to scale rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -240,7 +252,7 @@ def main():
 
     torch.cuda.set_device(0)
     log(f"[bench] generating config {args.config} inputs")
-    wl = Workload(args.config, copies=4)
+    wl = Workload(args.config, copies=4, b_layout=args.b_layout)
     stream = torch.cuda.current_stream().cuda_stream
     mkp.mkp_cache_clear()
 
@@ -285,7 +297,7 @@ def main():
     fr = sweep_fraction(per_call, wl)
     if args.detail:
         for case, us, f in zip(wl.cases, per_call, fr):
-            plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K)
+            plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K, bt=wl.bt)
             ks = "+".join(f"{r['kernel']}/s{r['s']}" for r in plan["regions"])
             log(f"  {case.tag:>14} {case.M:5d}x{case.N:5d}x{case.K:5d} b{case.batch:<3d} {us:9.2f} us "
                 f"{case.flops / us / 1e6:8.1f} TF/s  {100 * f:5.1f}% of R  {plan['pattern']:4s} {ks}")
@@ -306,6 +318,7 @@ def main():
         "config": {
             "workload": workloads.CONFIG_NAMES[args.config],
             "config_index": args.config,
+            "b_layout": args.b_layout,
             "gemms_per_step": len(wl.cases),
             "flops_per_step": wl.flops,
             "bytes_per_step": wl.bytes,

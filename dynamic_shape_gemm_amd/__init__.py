@@ -23,6 +23,8 @@ MKP_ERR_UNSUPPORTED = -2
 MKP_ERR_OOM = -3
 MKP_ERR_HIP = -4
 MKP_ERR_BUFFER = -5
+MKP_PLAN_EXHAUSTIVE = 1
+MKP_PLAN_B_NK = 8
 
 
 class MkpError(RuntimeError):
@@ -50,6 +52,10 @@ _lib.mkp_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.mkp_gemm.restype = _int
 _lib.mkp_gemm_batched.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
 _lib.mkp_gemm_batched.restype = _int
+_lib.mkp_gemm_bt.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.mkp_gemm_bt.restype = _int
+_lib.mkp_gemm_batched_bt.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
+_lib.mkp_gemm_batched_bt.restype = _int
 _lib.mkp_plan_describe.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.c_char_p, ctypes.c_size_t]
 _lib.mkp_plan_describe.restype = _int
 _lib.mkp_plan_with_table.argtypes = [ctypes.c_char_p, _int, _i64, _i64, _i64, _i64, ctypes.c_char_p, ctypes.c_size_t]
@@ -73,7 +79,7 @@ _lib.mkp_trace_dump.restype = _int
 _lib.mkp_last_error.argtypes = []
 _lib.mkp_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_plan_describe", "mkp_plan_with_table", "mkp_load_calibration",
+EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_plan_describe", "mkp_plan_with_table", "mkp_load_calibration",
             "mkp_calibrate", "mkp_set_option", "mkp_kernel_count", "mkp_kernel_name", "mkp_cache_clear",
             "mkp_stats", "mkp_trace_dump", "mkp_last_error"]
 
@@ -127,19 +133,39 @@ def mkp_gemm_batched_raw(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, str
                                  stream or 0)
 
 
+def mkp_gemm_bt(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    """C[MxN] := A[MxK] . B^T with B given as N x K (ldb >= K)."""
+    return _check(_lib.mkp_gemm_bt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)))
+
+
+def mkp_gemm_batched_bt(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream=None) -> int:
+    return _check(_lib.mkp_gemm_batched_bt(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB,
+                                           _addr(C), ldc, strideC, _stream(stream)))
+
+
+def mkp_gemm_bt_raw(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return _lib.mkp_gemm_bt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, stream or 0)
+
+
+def mkp_gemm_batched_bt_raw(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream) -> int:
+    return _lib.mkp_gemm_batched_bt(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC,
+                                    stream or 0)
+
+
 def _text_call(fn, *args, size=1 << 16):
     buf = ctypes.create_string_buffer(size)
     _check(fn(*args, buf, size))
     return buf.value.decode()
 
 
-def mkp_plan_describe(batch, M, N, K, align_flags=7) -> dict:
-    return json.loads(_text_call(_lib.mkp_plan_describe, batch, M, N, K, align_flags))
+def mkp_plan_describe(batch, M, N, K, align_flags=7, bt=False) -> dict:
+    return json.loads(_text_call(_lib.mkp_plan_describe, batch, M, N, K,
+                                 align_flags | (MKP_PLAN_B_NK if bt else 0)))
 
 
-def mkp_plan_with_table(table_text: str, batch, M, N, K, exhaustive=False) -> dict:
-    return json.loads(_text_call(_lib.mkp_plan_with_table, table_text.encode(), 1 if exhaustive else 0,
-                                 batch, M, N, K))
+def mkp_plan_with_table(table_text: str, batch, M, N, K, exhaustive=False, bt=False) -> dict:
+    flags = (MKP_PLAN_EXHAUSTIVE if exhaustive else 0) | (MKP_PLAN_B_NK if bt else 0)
+    return json.loads(_text_call(_lib.mkp_plan_with_table, table_text.encode(), flags, batch, M, N, K))
 
 
 def mkp_load_calibration(path=None) -> int:
@@ -199,4 +225,25 @@ def gemm_batched(a, b, out=None, stream=None):
         out = torch.empty((batch, M, N), dtype=torch.float32, device=a.device)
     mkp_gemm_batched(batch, M, N, K, a, max(a.stride(1), 1), a.stride(0), b, max(b.stride(1), 1), b.stride(0),
                      out, max(out.stride(1), 1), out.stride(0), stream)
+    return out
+
+
+def gemm_bt(a, w, out=None, stream=None):
+    """torch convenience: a (M,K) bf16 and w (N,K) bf16 (a linear layer's
+    weight) on the GPU, unit column strides; returns (or fills) out = a . w^T
+    (M,N) fp32."""
+    import torch
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("a and w must be bfloat16")
+    if a.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("rows must be contiguous (unit column stride)")
+    M, K = a.shape
+    N, K2 = w.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    mkp_gemm_bt(M, N, K, a, max(a.stride(0), 1), w, max(w.stride(0), 1), out, max(out.stride(0), 1), stream)
     return out

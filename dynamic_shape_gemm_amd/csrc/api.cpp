@@ -46,8 +46,10 @@ int fail(int code, const std::string& msg) {
 struct Key {
     int64_t batch, M, N, K;
     int align, device;
+    bool bt;   // B given as N x K
     bool operator==(const Key& o) const {
-        return batch == o.batch && M == o.M && N == o.N && K == o.K && align == o.align && device == o.device;
+        return batch == o.batch && M == o.M && N == o.N && K == o.K && align == o.align && device == o.device &&
+               bt == o.bt;
     }
 };
 struct KeyHash {
@@ -63,6 +65,7 @@ struct KeyHash {
         mix((uint64_t)k.K);
         mix((uint64_t)k.align);
         mix((uint64_t)k.device);
+        mix((uint64_t)k.bt);
         return (size_t)h;
     }
 };
@@ -130,6 +133,7 @@ PerfTable analytic_table() {
         k.uN = ki.uN;
         k.uK = ki.uK;
         k.lib_index = i;
+        k.bt = ki.bt;
         int by_lds = std::max(1, (160 * 1024) / std::max(ki.lds_bytes, 1));
         k.wg_per_cu = std::min(by_lds, 2);
         const double slots = (double)t.cus * k.wg_per_cu;
@@ -155,10 +159,19 @@ bool bind_table(PerfTable& t, std::string& err) {
             return false;
         }
         const KernelInfo& ki = kernel_info(k.lib_index);
-        if (ki.uM != k.uM || ki.uN != k.uN || ki.uK != k.uK) {
-            err = "table tile of kernel '" + k.name + "' differs from the library's";
+        if (ki.uM != k.uM || ki.uN != k.uN || ki.uK != k.uK || ki.bt != k.bt) {
+            err = "table tile or layout of kernel '" + k.name + "' differs from the library's";
             return false;
         }
+    }
+    // a table without any kernel for one B layout (written before the
+    // library had them) gets the analytic estimates of that layout's kernels
+    for (int layout = 0; layout < 2; ++layout) {
+        bool any = false;
+        for (auto& k : t.kernels) any |= k.bt == (layout == 1);
+        if (any) continue;
+        for (auto& k : analytic_table().kernels)
+            if (k.bt == (layout == 1)) t.kernels.push_back(k);
     }
     return true;
 }
@@ -223,6 +236,9 @@ void ensure_init() {
         Library& L = lib();
         std::unique_lock<std::shared_mutex> lk(L.mu);
         if (load_table_locked(L, nullptr, true) != MKP_OK) {
+            // a shipped table that does not fit the library is a build error:
+            // say so once, and plan with the analytic estimates
+            std::fprintf(stderr, "libmkp: %s; planning with analytic estimates\n", t_last_error.c_str());
             L.table = analytic_table();
             L.table_origin = "analytic";
         }
@@ -248,7 +264,9 @@ std::shared_ptr<const Plan> get_plan(const Key& key) {
         L.hits.fetch_add(1, std::memory_order_relaxed);
         return it->second;
     }
-    auto plan = std::make_shared<Plan>(polymerize(L.table, key.batch, key.M, key.N, key.K, L.opts));
+    SearchOptions o = L.opts;
+    o.bt = key.bt;
+    auto plan = std::make_shared<Plan>(polymerize(L.table, key.batch, key.M, key.N, key.K, o));
     L.misses.fetch_add(1, std::memory_order_relaxed);
     L.plan_ns.fetch_add((int64_t)(plan->plan_us * 1000.0), std::memory_order_relaxed);
     if (L.cache.size() >= L.cache_cap) L.cache.clear();
@@ -327,13 +345,17 @@ hipError_t traced(Library& L, hipStream_t st, int kernel, double flops, double b
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// C = A . B with B given as K x N (bt false) or as N x K (bt true, C = A . B^T
+// of the stored matrix).
 int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int64_t lda, int64_t sA,
-             const void* Bv, int64_t ldb, int64_t sB, float* C, int64_t ldc, int64_t sC, void* stream_v) {
+             const void* Bv, int64_t ldb, int64_t sB, float* C, int64_t ldc, int64_t sC, void* stream_v,
+             bool bt = false) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "dimension exceeds 2^31-1");
     if (batch == 0 || M == 0 || N == 0) return MKP_OK;
     if (K > 0 && lda < K) return fail(MKP_ERR_INVALID_ARG, "lda < K");
-    if (K > 0 && ldb < N) return fail(MKP_ERR_INVALID_ARG, "ldb < N");
+    if (K > 0 && !bt && ldb < N) return fail(MKP_ERR_INVALID_ARG, "ldb < N");
+    if (K > 0 && bt && ldb < K) return fail(MKP_ERR_INVALID_ARG, "ldb < K");
     if (ldc < N) return fail(MKP_ERR_INVALID_ARG, "ldc < N");
     if (!C) return fail(MKP_ERR_INVALID_ARG, "C is NULL");
     if (K > 0 && (!Av || !Bv)) return fail(MKP_ERR_INVALID_ARG, "A or B is NULL");
@@ -358,13 +380,15 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     const uint16_t* A = (const uint16_t*)Av;
     const uint16_t* B = (const uint16_t*)Bv;
     // 128-bit loads need 16-byte aligned rows; the direct-load path also
-    // keeps per-tile offsets (<= 256 rows of A, <= 64 rows of B) in 32 bits
+    // keeps per-tile offsets (<= 256 rows of A, <= 64 rows of a K x N B,
+    // <= 256 rows of an N x K B) in 32 bits
     bool vA = aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0) && lda < (int64_t(1) << 23);
-    bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0) && ldb < (int64_t(1) << 25);
+    bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0) &&
+              ldb < (int64_t(1) << (bt ? 23 : 25));
     const bool vC = aligned16(C) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
     const int align = (vA ? 1 : 0) | (vB ? 2 : 0) | (vC ? 4 : 0);
 
-    Key key{batch, M, N, K, align, dev};
+    Key key{batch, M, N, K, align, dev, bt};
     std::shared_ptr<const Plan> plan = get_plan(key);
     if (plan->regions.empty()) {
         if (plan->rank > 0)
@@ -385,15 +409,17 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
             part_bytes = std::max(part_bytes, (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float));
         }
     const bool pack_on = L.pack_unaligned.load(std::memory_order_relaxed);
-    const int64_t ldap = (K + 7) & ~int64_t(7), ldbp = (N + 7) & ~int64_t(7);
+    // B rows: N long for a K x N B, K long for an N x K one
+    const int64_t b_rows = bt ? N : K, b_cols = bt ? K : N;
+    const int64_t ldap = (K + 7) & ~int64_t(7), ldbp = (b_cols + 7) & ~int64_t(7);
     // (a copy pays off once several tile rows/columns re-read the operand)
     const bool packA = pack_on && !vA && N > 192 && ldap < (int64_t(1) << 23);
-    const bool packB = pack_on && !vB && M > 192 && ldbp < (int64_t(1) << 25);
+    const bool packB = pack_on && !vB && M > 192 && ldbp < (int64_t(1) << (bt ? 23 : 25));
     auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t offA = kCounterBytes + round256(part_bytes);
     const size_t bytesA = packA ? (size_t)batch * M * ldap * 2 : 0;
     const size_t offB = offA + round256(bytesA);
-    const size_t bytesB = packB ? (size_t)batch * K * ldbp * 2 : 0;
+    const size_t bytesB = packB ? (size_t)batch * b_rows * ldbp * 2 : 0;
     const size_t ws_bytes = (part_bytes || packA || packB) ? offB + bytesB : 0;
     void* ws = nullptr;
     if (ws_bytes) {
@@ -412,12 +438,13 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     }
     if (packB) {
         uint16_t* dst = (uint16_t*)((char*)ws + offB);
-        he = traced(L, st, -3, 0.0, (double)batch * K * (2.0 * N + 2.0 * ldbp),
-                    [&] { return launch_pack_rows(B, ldb, sB, dst, ldbp, (int)K, (int)N, (int)batch, st); });
+        he = traced(L, st, -3, 0.0, (double)batch * b_rows * (2.0 * b_cols + 2.0 * ldbp), [&] {
+            return launch_pack_rows(B, ldb, sB, dst, ldbp, (int)b_rows, (int)b_cols, (int)batch, st);
+        });
         if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("pack launch: ") + hipGetErrorString(he));
         B = dst;
         ldb = ldbp;
-        sB = K * ldbp;
+        sB = b_rows * ldbp;
         vB = true;
     }
 
@@ -426,9 +453,10 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         const int li = r.lib;
         if (li < 0 || li >= kernel_count()) return fail(MKP_ERR_UNSUPPORTED, "plan kernel is not launchable");
         const KernelInfo& ki = kernel_info(li);
+        if (ki.bt != bt) return fail(MKP_ERR_UNSUPPORTED, "plan kernel has the other B layout");
         KArgs a{};
         a.A = A + r.m0 * lda;
-        a.B = B + r.n0;
+        a.B = bt ? B + r.n0 * ldb : B + r.n0;
         a.lda = lda;
         a.ldb = ldb;
         a.sA = sA;
@@ -535,17 +563,29 @@ int mkp_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const void*
     return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream);
 }
 
+int mkp_gemm_bt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                int64_t ldc, void* stream) {
+    return run_gemm(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream, true);
+}
+
+int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        int64_t strideA, const void* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc,
+                        int64_t strideC, void* stream) {
+    return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream, true);
+}
+
 int mkp_plan_describe(int64_t batch, int64_t M, int64_t N, int64_t K, int align_flags, char* buf, size_t len) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
-    (void)align_flags;
     ensure_init();
     Library& L = lib();
     std::shared_lock<std::shared_mutex> lk(L.mu);
-    Plan p = polymerize(L.table, batch, M, N, K, L.opts);
+    SearchOptions o = L.opts;
+    o.bt = (align_flags & MKP_PLAN_B_NK) != 0;
+    Plan p = polymerize(L.table, batch, M, N, K, o);
     return write_out(plan_to_json(p, L.table), buf, len);
 }
 
-int mkp_plan_with_table(const char* table_text, int exhaustive, int64_t batch, int64_t M, int64_t N, int64_t K,
+int mkp_plan_with_table(const char* table_text, int flags, int64_t batch, int64_t M, int64_t N, int64_t K,
                         char* buf, size_t len) {
     if (!table_text) return fail(MKP_ERR_INVALID_ARG, "table text is NULL");
     if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
@@ -553,7 +593,8 @@ int mkp_plan_with_table(const char* table_text, int exhaustive, int64_t batch, i
     std::string err;
     if (!parse_table(table_text, t, err)) return fail(MKP_ERR_INVALID_ARG, err);
     SearchOptions o;
-    o.exhaustive = exhaustive != 0;
+    o.exhaustive = (flags & MKP_PLAN_EXHAUSTIVE) != 0;
+    o.bt = (flags & MKP_PLAN_B_NK) != 0;
     o.splitk_max = INT_MAX;
     {
         // the cost-model variant and the ranked-candidate option carry over
@@ -811,6 +852,7 @@ int mkp_calibrate(const char* path, int max_points) {
         k.uK = ki.uK;
         k.wg_per_cu = occ[i];
         k.lib_index = i;
+        k.bt = ki.bt;
         const Shape s = shapes[i];
         for (int p = 0; p < npts; ++p) {
             const int tt = grid_t[p];
@@ -821,7 +863,7 @@ int mkp_calibrate(const char* path, int max_points) {
             a.N = s.tn * ki.uN;
             a.K = (int)K;
             a.lda = K;
-            a.ldb = a.N;
+            a.ldb = ki.bt ? a.K : a.N;
             a.ldc = a.N;
             a.tiles_m = s.tm;
             a.tiles_n = s.tn;
@@ -865,7 +907,7 @@ int mkp_calibrate(const char* path, int max_points) {
                     a.N = cols * ki.uN;
                     a.K = t_ref * ki.uK;
                     a.lda = a.K;
-                    a.ldb = a.N;
+                    a.ldb = ki.bt ? a.K : a.N;
                     a.ldc = a.N;
                     a.tiles_m = s.tm;
                     a.tiles_n = cols;

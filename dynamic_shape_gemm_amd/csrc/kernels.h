@@ -21,7 +21,7 @@ enum : int {
 
 struct KArgs {
     const uint16_t* A;    // region origin in A (row m0, column 0)
-    const uint16_t* B;    // region origin in B (row 0, column n0)
+    const uint16_t* B;    // B (row 0, column 0 of a K x N matrix, or of an N x K one); the kernel adds n0
     float* C;             // region origin in C, or the split-K workspace
     int64_t lda, ldb, ldc;
     int64_t sA, sB, sC;   // batch strides (elements)
@@ -47,6 +47,7 @@ struct KernelInfo {
     int threads;
     int lds_bytes;
     bool fused_ok;        // compiled with the fused split-K reduction
+    bool bt;              // B given as N x K (K-contiguous rows) instead of K x N
     const void* func;     // __global__ entry, for occupancy queries
     hipError_t (*launch)(const KArgs&, dim3 grid, hipStream_t);
 };

@@ -63,10 +63,14 @@ __device__ __forceinline__ int swzB(int k) {
     else return BN >= 128 ? ((k & 3) << 1) : (((k >> 1) & 1) << 1);
 }
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_, bool PREREAD_ = false>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_, bool PREREAD_ = false, bool BT_ = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
     static constexpr bool PREREAD = PREREAD_;   // read a whole stage's fragments before its MFMAs
+    // B given as N x K (K-contiguous rows, the layout of a linear layer's
+    // weights): its tile is stored like A's and read with the same 128-bit
+    // fragment reads instead of the transposed ones
+    static constexpr bool BT = BT_;
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -74,8 +78,8 @@ struct Tile {
     // bf16 peak from one wave per SIMD), 16x16x32 for 16-row wave tiles
     static constexpr int MF = (WTM % 32 == 0 && WTN % 32 == 0) ? 32 : 16;
     static constexpr int FM = WTM / MF, FN = WTN / MF;
-    static constexpr int A_ROWB = BK * 2, B_ROWB = BN * 2;
-    static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BK * B_ROWB;
+    static constexpr int A_ROWB = BK * 2, B_ROWB = BT ? BK * 2 : BN * 2;
+    static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BT ? BN * B_ROWB : BK * B_ROWB;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_SLOTS = A_BYTES / 16, B_SLOTS = B_BYTES / 16;
     static constexpr int A_GROUPS = A_SLOTS / 64, B_GROUPS = B_SLOTS / 64;   // 1 KB each
@@ -112,6 +116,13 @@ __device__ __forceinline__ void slotB(int p, int& k, int& col) {
     k = p / (T::BN / 8);
     const int pq = p % (T::BN / 8);
     col = ((((pq >> 1) ^ swzB<T::BN, T::MF>(k)) << 1) | (pq & 1)) * 8;
+}
+
+// LDS slot -> (row n, first K element) of a B tile stored N x K.
+template <class T>
+__device__ __forceinline__ void slotBt(int p, int& n, int& col) {
+    n = p / (T::BK / 8);
+    col = ((p % (T::BK / 8)) ^ swzA<T::BK>(n)) * 8;
 }
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
@@ -179,18 +190,25 @@ struct DmaOffsets {
 #pragma unroll
         for (int i = 0; i < T::B_IPW; ++i) {
             const int g = i * T::NW + wave;
-            int k, col;
-            slotB<T>(g * 64 + lane, k, col);
-            col = min(col, c.Nr - 8);
             const bool real = (T::B_GROUPS % T::NW == 0) || g < T::B_GROUPS;
-            b[i] = real ? (uint32_t)(k * c.ldb + col) : 0u;
+            if constexpr (T::BT) {
+                int n, col;
+                slotBt<T>(g * 64 + lane, n, col);
+                n = min(n, c.Nr - 1);
+                b[i] = real ? (uint32_t)(n * c.ldb + col) : 0u;
+            } else {
+                int k, col;
+                slotB<T>(g * 64 + lane, k, col);
+                col = min(col, c.Nr - 8);
+                b[i] = real ? (uint32_t)(k * c.ldb + col) : 0u;
+            }
         }
     }
 
     // Direct global->LDS loads of one full K step.
     __device__ __forceinline__ void issue(const TileCtx& c, int k0, lds_t* stage, lds_t* junk, int wave) const {
         const uint16_t* ab = c.A + k0;
-        const uint16_t* bb = c.B + (int64_t)k0 * c.ldb;
+        const uint16_t* bb = T::BT ? c.B + k0 : c.B + (int64_t)k0 * c.ldb;
 #pragma unroll
         for (int i = 0; i < T::A_IPW; ++i) {
             const int g = i * T::NW + wave;
@@ -225,6 +243,16 @@ __device__ __forceinline__ u32x4 reg_load_a(const TileCtx& c, int k0, int p) {
 
 template <class T>
 __device__ __forceinline__ u32x4 reg_load_b(const TileCtx& c, int k0, int p) {
+    if constexpr (T::BT) {
+        int n, col;
+        slotBt<T>(p, n, col);
+        const int k = k0 + col;
+        if (n < c.Nr && k < c.kend) {
+            const uint16_t* src = c.B + (int64_t)n * c.ldb + k;
+            return (c.vecB && k + 8 <= c.kend) ? *(const u32x4*)src : load8_elems(src, c.kend - k);
+        }
+        return zero4();
+    }
     int k, col;
     slotB<T>(p, k, col);
     const int kk = k0 + k;
@@ -263,16 +291,28 @@ __device__ __forceinline__ void read_frags32(const lds_t* sa, const lds_t* sb, i
     // lane = 32h + 16cs + s16: K half h, column half cs
     const int h = lane >> 5, cs = (lane >> 4) & 1, s16 = lane & 15;
     const int kk = ks * 16;
+    if constexpr (T::BT) {
+        // N x K tile: the lane takes column n = lane & 31 of the block, K
+        // columns 16ks + 8h .. +7 (the A fragments' K assignment)
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-        const int seg = ((wn * T::WTN + j * 32) >> 4) + cs;
-        const int k1 = kk + 8 * h + (s16 >> 2), k2 = k1 + 4;
-        const int o = (s16 & 3) * 8;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(sb + k1 * T::B_ROWB + ((seg ^ swzB<T::BN, 32>(k1)) << 5) + o));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(sb + k2 * T::B_ROWB + ((seg ^ swzB<T::BN, 32>(k2)) << 5) + o));
-        xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int j = 0; j < T::FN; ++j) {
+            const int n = wn * T::WTN + j * 32 + (lane & 31);
+            const int c1 = (kk >> 3) + h;
+            xb[j] = __builtin_bit_cast(bf16x8, *(const u32x4 __attribute__((address_space(3)))*)(
+                                                   sb + n * T::B_ROWB + ((c1 ^ swzA<T::BK>(n)) << 4)));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            const int seg = ((wn * T::WTN + j * 32) >> 4) + cs;
+            const int k1 = kk + 8 * h + (s16 >> 2), k2 = k1 + 4;
+            const int o = (s16 & 3) * 8;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
+                sb + k1 * T::B_ROWB + ((seg ^ swzB<T::BN, 32>(k1)) << 5) + o));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
+                sb + k2 * T::B_ROWB + ((seg ^ swzB<T::BN, 32>(k2)) << 5) + o));
+            xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
     }
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
@@ -370,7 +410,8 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     TileCtx c;
     c.A = args.A + (int64_t)b * args.sA + (int64_t)m0 * args.lda;
-    c.B = args.B + (int64_t)b * args.sB + n0;
+    // B tile origin: column n0 of a K x N matrix, or row n0 of an N x K one
+    c.B = args.B + (int64_t)b * args.sB + (T::BT ? (int64_t)n0 * args.ldb : (int64_t)n0);
     c.lda = args.lda;
     c.ldb = args.ldb;
     c.Mr = args.M - m0;
@@ -421,6 +462,17 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
                 bf16x8 xb[T::FN], ya[T::FM];
 #pragma unroll
                 for (int j = 0; j < T::FN; ++j) {
+                    if constexpr (T::BT) {
+                        // N x K tile: the A fragments' K assignment
+                        const int n = wn * T::WTN + j * 16 + s16;
+                        const int c1 = (kk >> 3) + (g4 >> 1), hb = (g4 & 1) * 8;
+                        const u32x2 lo = *(const u32x2 __attribute__((address_space(3)))*)(
+                            sb + n * T::B_ROWB + ((c1 ^ swzA<T::BK>(n)) << 4) + hb);
+                        const u32x2 hi = *(const u32x2 __attribute__((address_space(3)))*)(
+                            sb + n * T::B_ROWB + (((c1 + 2) ^ swzA<T::BK>(n)) << 4) + hb);
+                        xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+                        continue;
+                    }
                     const int seg = (wn * T::WTN + j * 16) >> 4;
                     const int k1 = kk + 4 * g4 + (s16 >> 2), k2 = k1 + 16;
                     const int o = (s16 & 3) * 8;
@@ -718,9 +770,24 @@ using T_32x128 = Tile<32, 128, 64, 1, 4, 4>;
 using T_16x128 = Tile<16, 128, 64, 1, 4, 4>;
 using T_16x256 = Tile<16, 256, 64, 1, 4, 4>;
 using T_32x64 = Tile<32, 64, 64, 2, 2, 4>;
+// the same tiles for B given as N x K
+using U_256x256 = Tile<256, 256, 64, 4, 2, 2, false, true>;
+using U_256x128 = Tile<256, 128, 64, 4, 2, 2, true, true>;
+using U_128x256 = Tile<128, 256, 64, 2, 4, 2, false, true>;
+using U_128x128 = Tile<128, 128, 64, 2, 2, 2, false, true>;
+using U_128x64 = Tile<128, 64, 64, 2, 2, 3, false, true>;
+using U_64x128 = Tile<64, 128, 64, 2, 2, 3, false, true>;
+using U_64x64 = Tile<64, 64, 64, 2, 2, 4, false, true>;
+using U_32x128 = Tile<32, 128, 64, 1, 4, 4, false, true>;
+using U_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true>;
+using U_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true>;
+using U_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true>;
 
-#define MKP_KERNEL(NAME, T) \
-    { NAME, T::BM, T::BN, T::BK, T::NT, T::LDS, T::FUSED, (const void*)&gemm_tile_kernel<T>, &launch_tile<T> }
+#define MKP_KERNEL(NAME, T)                                                                               \
+    {                                                                                                      \
+        NAME, T::BM, T::BN, T::BK, T::NT, T::LDS, T::FUSED, T::BT, (const void*)&gemm_tile_kernel<T>, \
+            &launch_tile<T>                                                                                \
+    }
 
 const KernelInfo g_kernels[] = {
     MKP_KERNEL("m256n256k64", T_256x256),
@@ -734,6 +801,17 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m16n128k64", T_16x128),
     MKP_KERNEL("m16n256k64", T_16x256),
     MKP_KERNEL("m32n64k64", T_32x64),
+    MKP_KERNEL("m256n256k64_nk", U_256x256),
+    MKP_KERNEL("m256n128k64_nk", U_256x128),
+    MKP_KERNEL("m128n256k64_nk", U_128x256),
+    MKP_KERNEL("m128n128k64_nk", U_128x128),
+    MKP_KERNEL("m128n64k64_nk", U_128x64),
+    MKP_KERNEL("m64n128k64_nk", U_64x128),
+    MKP_KERNEL("m64n64k64_nk", U_64x64),
+    MKP_KERNEL("m32n128k64_nk", U_32x128),
+    MKP_KERNEL("m16n128k64_nk", U_16x128),
+    MKP_KERNEL("m16n256k64_nk", U_16x256),
+    MKP_KERNEL("m32n64k64_nk", U_32x64),
 };
 
 }  // namespace

@@ -59,6 +59,11 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
         } else if (key == "kernel") {
             TableKernel k;
             if (!(ls >> k.name >> k.uM >> k.uN >> k.uK >> k.wg_per_cu)) return fail("bad kernel line");
+            std::string layout;   // optional: kn (B is K x N, the default) or nk
+            if (ls >> layout) {
+                if (layout == "nk") k.bt = true;
+                else if (layout != "kn") return fail("kernel layout must be kn or nk");
+            }
             if (k.uM <= 0 || k.uN <= 0 || k.uK <= 0 || k.wg_per_cu <= 0) return fail("bad kernel tile");
             for (auto& e : t.kernels)
                 if (e.name == k.name) return fail("duplicate kernel");
@@ -149,7 +154,8 @@ std::string table_to_text(const PerfTable& t) {
       << "\n";
     if (t.mfma_tflops > 0 || t.hbm_gbps > 0) o << "measured " << t.mfma_tflops << " " << t.hbm_gbps << "\n";
     for (auto& k : t.kernels)
-        o << "kernel " << k.name << " " << k.uM << " " << k.uN << " " << k.uK << " " << k.wg_per_cu << "\n";
+        o << "kernel " << k.name << " " << k.uM << " " << k.uN << " " << k.uK << " " << k.wg_per_cu
+          << (k.bt ? " nk" : "") << "\n";
     for (auto& k : t.kernels) {
         o << "g " << k.name;
         for (auto& p : k.pts) o << " " << p.first << ":" << p.second;
@@ -320,7 +326,9 @@ struct Searcher {
         }
     }
 
-    bool kernel_allowed(int k) const { return opt.force_kernel < 0 || opt.force_kernel == k; }
+    bool kernel_allowed(int k) const {
+        return tab.kernels[k].bt == opt.bt && (opt.force_kernel < 0 || opt.force_kernel == k);
+    }
 
     double cost(int ki, const SplitChoice& c, int64_t m, int64_t n, Region* r) {
         ++evaluated;
@@ -394,6 +402,7 @@ struct Searcher {
                 if (dir == 1 && !tab.pat_IIN) continue;
                 const int64_t ext = dir == 0 ? M : N;
                 for (int a = 0; a < nk; ++a) {
+                    if (!kernel_allowed(a)) continue;
                     const TableKernel& ka = tab.kernels[a];
                     const int64_t step = dir == 0 ? ka.uM : ka.uN;
                     const int64_t across = dir == 0 ? ceil_div(N, ka.uN) : ceil_div(M, ka.uM);
@@ -409,7 +418,7 @@ struct Searcher {
                             const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
                             const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
                             for (int b = 0; b < nk; ++b) {
-                                if (b == a) continue;
+                                if (b == a || !kernel_allowed(b)) continue;
                                 for (auto& c2s : sc[b]) {
                                     Cand x{0.0, dir == 0 ? PAT_IIM : PAT_IIN, {}, {}};
                                     x.cost = cost(a, c1s, m1, n1, &x.r1) + cost(b, c2s, m2, n2, &x.r2);
@@ -464,6 +473,7 @@ struct Searcher {
             if (dir == 1 && !tab.pat_IIN) continue;
             const int64_t ext = dir == 0 ? M : N;
             for (int a = 0; a < nk; ++a) {
+                if (!kernel_allowed(a)) continue;
                 const TableKernel& ka = tab.kernels[a];
                 const int64_t step = dir == 0 ? ka.uM : ka.uN;
                 // tiles across the uncut dimension
@@ -488,7 +498,7 @@ struct Searcher {
                                 best.cost_us)
                             continue;
                         for (int b = 0; b < nk; ++b) {
-                            if (b == a) continue;
+                            if (b == a || !kernel_allowed(b)) continue;
                             if (prune() && c1 + lb(b, m2, n2) >= best.cost_us) continue;
                             Region r2;
                             const double c2 = dir == 0 ? best_region(b, M - cut, N, &r2) : best_region(b, M, N - cut, &r2);

@@ -25,6 +25,7 @@ struct TableKernel {
     std::string name;
     int uM = 0, uN = 0, uK = 0;
     int wg_per_cu = 1;                               // resident workgroups per CU
+    bool bt = false;                                 // serves B given as N x K
     std::vector<std::pair<double, double>> pts;      // (t, us), sorted by t
     // Partial last wave: (fraction f of the slots filled, time of that wave
     // relative to a full one), sorted by f; empty = every wave costs a full g.
@@ -85,6 +86,7 @@ struct SearchOptions {
     bool allow_II = true;
     int cost_mode = COST_FULL;
     int plan_rank = 0;       // >0: return the rank-th cheapest candidate of the whole space
+    bool bt = false;         // B is N x K: only kernels of that layout take part
 };
 
 // Parse the text form of a table.  Returns false and sets err on bad input.

@@ -46,6 +46,12 @@ enum {
     MKP_ERR_BUFFER = -5       /* output text buffer too small */
 };
 
+/* flags of mkp_plan_describe (align_flags) and mkp_plan_with_table (flags) */
+enum {
+    MKP_PLAN_EXHAUSTIVE = 1,  /* mkp_plan_with_table: score every candidate */
+    MKP_PLAN_B_NK = 8         /* plan for B given as N x K (mkp_gemm_bt) */
+};
+
 /*
  * C[M x N] := A[M x K] . B[K x N].
  *   lda >= K, ldb >= N, ldc >= N (elements).  A, B, C may be NULL only when
@@ -76,11 +82,38 @@ int mkp_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                      void *stream);
 
 /*
+ * C[M x N] := A[M x K] . B^T with B given as N x K (row n holds the K values
+ * of output column n; ldb >= K), the layout in which a linear layer keeps
+ * its weights and attention keeps K.  Otherwise as mkp_gemm: same C, errors
+ * (ldb < K is MKP_ERR_INVALID_ARG), alignment freedom and stream semantics.
+ * The polymerizer composes it from the library's N x K micro-kernels (names
+ * ending in "_nk"), whose B fragments come from LDS like A's.  Source: the
+ * MikPoly page's GEMM (part 1 item 2) with B read through its transpose; the
+ * layout is the workloads' (Korch page's and BladeDISC page's linear and
+ * attention layers).
+ */
+int mkp_gemm_bt(int64_t M, int64_t N, int64_t K,
+                const void *A, int64_t lda,
+                const void *B, int64_t ldb,
+                float *C, int64_t ldc,
+                void *stream);
+
+/* Batched mkp_gemm_bt: entry b at A + b*strideA, B + b*strideB (N x K),
+ * C + b*strideC; as mkp_gemm_batched otherwise. */
+int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K,
+                        const void *A, int64_t lda, int64_t strideA,
+                        const void *B, int64_t ldb, int64_t strideB,
+                        float *C, int64_t ldc, int64_t strideC,
+                        void *stream);
+
+/*
  * Describe the plan the polymerizer picks for a shape, without launching.
  * align_flags: bit0 = A rows 16-byte aligned, bit1 = B rows, bit2 = C rows
- * (pass 7 for aligned operands).  Writes NUL-terminated JSON into buf:
+ * (pass 7 for aligned operands); MKP_PLAN_B_NK plans for mkp_gemm_bt.
+ * Writes NUL-terminated JSON into buf:
  *   {"pattern":..., "cost_us":..., "plan_us":..., "regions":[{"m0","n0","m",
- *    "n","kernel","uM","uN","uK","s","steps","tasks","waves"}...]}
+ *    "n","kernel","uM","uN","uK","s","steps","tasks","waves","wave_factor",
+ *    "cost_us"}...]}
  * Uses the active performance table (calibrated, or the built-in analytic
  * one).  Pure host code: needs no GPU.  Returns MKP_OK, MKP_ERR_INVALID_ARG
  * or MKP_ERR_BUFFER.
@@ -91,11 +124,13 @@ int mkp_plan_describe(int64_t batch, int64_t M, int64_t N, int64_t K, int align_
 /*
  * As mkp_plan_describe but with a caller-given performance table (text, the
  * format read by mkp_load_calibration) and the pruned or the exhaustive
- * search (exhaustive != 0: every candidate is scored, the page's ORACLE
- * variant of section 5 "cost-model effectiveness").  Kernel names in the
- * table need not exist in the library: nothing is launched.  Pure host code.
+ * search (flags & MKP_PLAN_EXHAUSTIVE: every candidate is scored, the
+ * modelled side of the page's ORACLE variant of section 5 "cost-model
+ * effectiveness"); flags & MKP_PLAN_B_NK restricts the search to the
+ * table's N x K kernels.  Kernel names in the table need not exist in the
+ * library: nothing is launched.  Pure host code.
  */
-int mkp_plan_with_table(const char *table_text, int exhaustive,
+int mkp_plan_with_table(const char *table_text, int flags,
                         int64_t batch, int64_t M, int64_t N, int64_t K,
                         char *buf, size_t len);
 
@@ -105,9 +140,15 @@ int mkp_plan_with_table(const char *table_text, int exhaustive,
  * file; path NULL reloads the table that ships with the library.  Lines:
  *   device <cus>                     launch_us <us>
  *   reduce <launch_us> <GB/s>        splitk <s1> <s2> ...
- *   patterns I II-M II-N             kernel <name> <uM> <uN> <uK> <wg_per_cu>
- *   g <name> <t>:<us> <t>:<us> ...
- * Kernels named here must exist in the library.  Clears the plan cache.
+ *   patterns I II-M II-N             kernel <name> <uM> <uN> <uK> <wg_per_cu> [kn|nk]
+ *   g <name> <t>:<us> <t>:<us> ...   measured <TFLOP/s> <GB/s>
+ *   tail <name> <f>:<r> ...          tailx <name> <f>:<r> ...
+ * (kn / nk: the kernel takes B as K x N, the default, or as N x K; tail and
+ * tailx: time of a wave filling a fraction f < 1 of the slots, on its own or
+ * after full waves, relative to a full wave.)  Kernels named here must exist
+ * in the library with the same tile and layout; a table with no kernel of
+ * one layout gets analytic estimates for that layout's kernels.  Clears the
+ * plan cache.
  */
 int mkp_load_calibration(const char *path);
 

@@ -58,6 +58,7 @@ class Kernel:
     uK: int
     wg_per_cu: int
     pts: List[Tuple[float, float]]  # (t, microseconds) sorted by t
+    bt: bool = False  # serves B given as N x K
     tail: List[Tuple[float, float]] = dataclasses.field(default_factory=list)   # (fill, ratio), alone
     tailx: List[Tuple[float, float]] = dataclasses.field(default_factory=list)  # after full waves
 
@@ -106,7 +107,10 @@ def parse_table(text: str) -> Table:
         elif key == "measured":
             pass  # sustained-rate figures: reported, not part of the cost model
         elif key == "kernel":
-            kernels[tok[1]] = Kernel(tok[1], int(tok[2]), int(tok[3]), int(tok[4]), int(tok[5]), [])
+            layout = tok[6] if len(tok) > 6 else "kn"
+            if layout not in ("kn", "nk"):
+                raise ValueError(f"bad kernel layout: {raw!r}")
+            kernels[tok[1]] = Kernel(tok[1], int(tok[2]), int(tok[3]), int(tok[4]), int(tok[5]), [], layout == "nk")
         elif key == "g":
             pts = []
             for p in tok[2:]:
@@ -215,9 +219,10 @@ def _valid_splits(tab: Table, k: Kernel, K: int) -> List[int]:
     return [s for s in tab.splits if 1 <= s <= max(t3, 1)]
 
 
-def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1):
-    """Every candidate strategy of the search space, no pruning."""
-    names = sorted(tab.kernels)
+def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1, bt: bool = False):
+    """Every candidate strategy of the search space, no pruning; only the
+    kernels that take B in the call's layout (K x N, or N x K when bt)."""
+    names = sorted(n for n, k in tab.kernels.items() if k.bt == bt)
     if "I" in tab.patterns:
         for a in names:
             for s in _valid_splits(tab, tab.kernels[a], K):
@@ -256,11 +261,11 @@ def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1):
                             yield pat, (r1, r2)
 
 
-def exhaustive_best(tab: Table, M: int, N: int, K: int, batch: int = 1, mode: str = "full"):
+def exhaustive_best(tab: Table, M: int, N: int, K: int, batch: int = 1, mode: str = "full", bt: bool = False):
     """Minimum modelled cost over the whole space (the page's ORACLE variant
     searches exhaustively; here only the modelled cost is minimised)."""
     best: Optional[Tuple[float, str, tuple]] = None
-    for pat, regs in enumerate_plans(tab, M, N, K, batch):
+    for pat, regs in enumerate_plans(tab, M, N, K, batch, bt):
         c = plan_cost(tab, regs, K, batch, mode)
         if best is None or c < best[0]:
             best = (c, pat, regs)

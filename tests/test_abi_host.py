@@ -31,8 +31,25 @@ def test_kernel_library_listing(mkp):
     names = mkp.mkp_kernel_names()
     assert len(names) == len(set(names)) >= 8
     for n in names:
-        m = re.fullmatch(r"m(\d+)n(\d+)k(\d+)", n)
+        m = re.fullmatch(r"m(\d+)n(\d+)k(\d+)(_nk)?", n)
         assert m, n
+    # every tile exists for both B layouts
+    kn = sorted(n for n in names if not n.endswith("_nk"))
+    nk = sorted(n[:-3] for n in names if n.endswith("_nk"))
+    assert kn == nk
+
+
+def test_bt_entry_points_check_arguments(mkp):
+    # B given as N x K needs ldb >= K; errors come back before any launch
+    assert mkp.mkp_gemm_bt_raw(4, 4, 8, 1, 8, 1, 7, 1, 4, 0) == mkp.MKP_ERR_INVALID_ARG
+    assert "ldb < K" in mkp.last_error()
+    assert mkp.mkp_gemm_bt_raw(4, 4, 8, 0, 8, 1, 8, 1, 4, 0) == mkp.MKP_ERR_INVALID_ARG
+    assert mkp.mkp_gemm_batched_bt_raw(-1, 4, 4, 8, 1, 8, 32, 1, 8, 32, 1, 4, 16, 0) == mkp.MKP_ERR_INVALID_ARG
+    assert mkp.mkp_gemm_bt_raw(0, 4, 8, 0, 8, 0, 8, 0, 4, 0) == mkp.MKP_OK
+    # N x K plans use N x K kernels only, and K x N plans K x N kernels only
+    for bt in (False, True):
+        p = mkp.mkp_plan_describe(1, 1000, 700, 300, bt=bt)
+        assert p["regions"] and all(r["kernel"].endswith("_nk") == bt for r in p["regions"])
 
 
 def test_invalid_arguments_fail_before_any_launch(mkp):
@@ -118,3 +135,15 @@ def test_force_kernel_and_split(mkp):
     finally:
         mkp.mkp_set_option("force_kernel", "")
         mkp.mkp_set_option("force_splitk", 0)
+
+
+def test_shipped_table_loads(mkp):
+    """The calibrated table that ships with the library fits its kernels
+    (tiles and B layouts) and is the one in use."""
+    mkp.mkp_load_calibration(None)
+    table = mkp.mkp_stats()["table"]
+    assert table.endswith("gfx950.tbl"), table
+    names = set(mkp.mkp_kernel_names())
+    text = open(table).read()
+    listed = {line.split()[1] for line in text.splitlines() if line.startswith("kernel ")}
+    assert listed == names

@@ -201,3 +201,29 @@ def test_partial_wave_search_is_exact(mkp):
         regs = to_regions(plan)
         assert cm.plan_cost(tab, regs, K, batch) == pytest.approx(plan["cost_us"], rel=1e-9)
         assert cm.covers_exactly(M, N, regs, {n: (k.uM, k.uN) for n, k in tab.kernels.items()})
+
+
+def test_layout_restricts_the_search(mkp):
+    """A table holding kernels for both B layouts: the search for B given as
+    N x K uses only the nk kernels and reaches the oracle's exhaustive
+    minimum over them (and likewise for K x N)."""
+    rng = np.random.default_rng(91)
+    for trial in range(25):
+        text = random_table(rng, int(rng.integers(2, 4)), tails=bool(trial % 2))
+        # a second family of kernels, marked nk, with their own timings
+        extra = random_table(rng, int(rng.integers(1, 4)), tails=bool(trial % 2))
+        lines = []
+        for line in extra.splitlines():
+            tok = line.split()
+            if tok[0] == "kernel":
+                lines.append(" ".join(["kernel", tok[1] + "_nk"] + tok[2:] + ["nk"]))
+            elif tok[0] in ("g", "tail", "tailx"):
+                lines.append(" ".join([tok[0], tok[1] + "_nk"] + tok[2:]))
+        text = text + "\n".join(lines) + "\n"
+        tab = cm.parse_table(text)
+        M, N, K = (int(x) for x in rng.integers(1, 200, size=3))
+        for bt in (False, True):
+            plan = mkp.mkp_plan_with_table(text, 1, M, N, K, bt=bt)
+            best = cm.exhaustive_best(tab, M, N, K, 1, bt=bt)
+            assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (trial, bt)
+            assert all(r["kernel"].endswith("_nk") == bt for r in plan["regions"])
