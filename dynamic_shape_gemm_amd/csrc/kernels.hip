@@ -758,8 +758,10 @@ __global__ __launch_bounds__(256) void fill_random_bf16_kernel(uint16_t* p, int6
 
 // The library: tile shapes, wave layouts and LDS stage counts.  The large
 // tiles run 8 waves (two per SIMD) so one wave's LDS waits overlap the
-// other's MFMAs; 128x128 runs two 4-wave workgroups per CU.
-using T_256x256 = Tile<256, 256, 64, 4, 2, 2>;
+// other's MFMAs; 128x128 runs two 4-wave workgroups per CU.  With B as K x N
+// the 256x256 tile uses 128 x 64 wave tiles: each wave then takes half as
+// many B fragments through the slower transposed LDS reads as with 64 x 128.
+using T_256x256 = Tile<256, 256, 64, 2, 4, 2>;
 using T_256x128 = Tile<256, 128, 64, 4, 2, 2, true>;
 using T_128x256 = Tile<128, 256, 64, 2, 4, 2>;
 using T_128x128 = Tile<128, 128, 64, 2, 2, 2>;
