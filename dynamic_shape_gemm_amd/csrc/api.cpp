@@ -103,6 +103,7 @@ struct Library {
 
     std::atomic<bool> fused_reduce{false};        // split-K: fused last-arrival sum (else 2 passes)
     std::atomic<bool> pack_unaligned{true};       // stage unaligned re-read operands aligned
+    std::atomic<int> transpose_b{1};              // K x N calls as transpose + N x K: 0 no, 1 by cost, 2 always
     std::atomic<bool> trace{false};               // time every launch with events
     std::atomic<int64_t> calls{0};                // C-ABI GEMM calls so far
     std::mutex trace_mu;
@@ -266,7 +267,8 @@ std::shared_ptr<const Plan> get_plan(const Key& key) {
     }
     SearchOptions o = L.opts;
     o.bt = key.bt;
-    auto plan = std::make_shared<Plan>(polymerize(L.table, key.batch, key.M, key.N, key.K, o));
+    const int tmode = key.batch <= 65535 ? L.transpose_b.load(std::memory_order_relaxed) : 0;
+    auto plan = std::make_shared<Plan>(plan_call(L.table, key.batch, key.M, key.N, key.K, o, tmode));
     L.misses.fetch_add(1, std::memory_order_relaxed);
     L.plan_ns.fetch_add((int64_t)(plan->plan_us * 1000.0), std::memory_order_relaxed);
     if (L.cache.size() >= L.cache_cap) L.cache.clear();
@@ -409,18 +411,22 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
             part_bytes = std::max(part_bytes, (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float));
         }
     const bool pack_on = L.pack_unaligned.load(std::memory_order_relaxed);
+    // A K x N B the plan runs on N x K kernels is first transposed into the
+    // workspace (rows of K padded to 8 elements, aligned)
+    const bool tr = plan->transpose_b && !bt;
+    const int64_t ldt = (K + 7) & ~int64_t(7);
     // B rows: N long for a K x N B, K long for an N x K one
     const int64_t b_rows = bt ? N : K, b_cols = bt ? K : N;
     const int64_t ldap = (K + 7) & ~int64_t(7), ldbp = (b_cols + 7) & ~int64_t(7);
     // (a copy pays off once several tile rows/columns re-read the operand)
     const bool packA = pack_on && !vA && N > 192 && ldap < (int64_t(1) << 23);
-    const bool packB = pack_on && !vB && M > 192 && ldbp < (int64_t(1) << (bt ? 23 : 25));
+    const bool packB = !tr && pack_on && !vB && M > 192 && ldbp < (int64_t(1) << (bt ? 23 : 25));
     auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t offA = kCounterBytes + round256(part_bytes);
     const size_t bytesA = packA ? (size_t)batch * M * ldap * 2 : 0;
     const size_t offB = offA + round256(bytesA);
-    const size_t bytesB = packB ? (size_t)batch * b_rows * ldbp * 2 : 0;
-    const size_t ws_bytes = (part_bytes || packA || packB) ? offB + bytesB : 0;
+    const size_t bytesB = tr ? (size_t)batch * N * ldt * 2 : packB ? (size_t)batch * b_rows * ldbp * 2 : 0;
+    const size_t ws_bytes = (part_bytes || packA || packB || tr) ? offB + bytesB : 0;
     void* ws = nullptr;
     if (ws_bytes) {
         int rc = get_workspace(dev, st, ws_bytes, &ws);
@@ -436,6 +442,19 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         sA = M * ldap;
         vA = true;
     }
+    if (tr) {
+        uint16_t* dst = (uint16_t*)((char*)ws + offB);
+        he = traced(L, st, -4, 0.0, (double)batch * (2.0 * K * N + 2.0 * N * ldt), [&] {
+            return launch_transpose_bf16(B, ldb, sB, dst, ldt, N * ldt, (int)K, (int)N, (int)batch, vB, st);
+        });
+        if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("transpose launch: ") + hipGetErrorString(he));
+        L.launches.fetch_add(1, std::memory_order_relaxed);
+        B = dst;
+        ldb = ldt;
+        sB = N * ldt;
+        vB = true;
+    }
+    const bool kbt = bt || tr;   // the regions' kernels take B as N x K
     if (packB) {
         uint16_t* dst = (uint16_t*)((char*)ws + offB);
         he = traced(L, st, -3, 0.0, (double)batch * b_rows * (2.0 * b_cols + 2.0 * ldbp), [&] {
@@ -453,10 +472,10 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         const int li = r.lib;
         if (li < 0 || li >= kernel_count()) return fail(MKP_ERR_UNSUPPORTED, "plan kernel is not launchable");
         const KernelInfo& ki = kernel_info(li);
-        if (ki.bt != bt) return fail(MKP_ERR_UNSUPPORTED, "plan kernel has the other B layout");
+        if (ki.bt != kbt) return fail(MKP_ERR_UNSUPPORTED, "plan kernel has the other B layout");
         KArgs a{};
         a.A = A + r.m0 * lda;
-        a.B = bt ? B + r.n0 * ldb : B + r.n0;
+        a.B = kbt ? B + r.n0 * ldb : B + r.n0;
         a.lda = lda;
         a.ldb = ldb;
         a.sA = sA;
@@ -581,7 +600,7 @@ int mkp_plan_describe(int64_t batch, int64_t M, int64_t N, int64_t K, int align_
     std::shared_lock<std::shared_mutex> lk(L.mu);
     SearchOptions o = L.opts;
     o.bt = (align_flags & MKP_PLAN_B_NK) != 0;
-    Plan p = polymerize(L.table, batch, M, N, K, o);
+    Plan p = plan_call(L.table, batch, M, N, K, o, batch <= 65535 ? L.transpose_b.load() : 0);
     return write_out(plan_to_json(p, L.table), buf, len);
 }
 
@@ -604,7 +623,7 @@ int mkp_plan_with_table(const char* table_text, int flags, int64_t batch, int64_
         o.cost_mode = L.opts.cost_mode;
         o.plan_rank = L.opts.plan_rank;
     }
-    Plan p = polymerize(t, batch, M, N, K, o);
+    Plan p = plan_call(t, batch, M, N, K, o, batch <= 65535 ? 1 : 0);
     return write_out(plan_to_json(p, t), buf, len);
 }
 
@@ -644,6 +663,10 @@ int mkp_set_option(const char* key, const char* value) {
         if (v == "I") L.opts.allow_II = false;
         else if (v == "I,II" || v == "II") L.opts.allow_II = true;
         else return fail(MKP_ERR_INVALID_ARG, "patterns must be I or I,II");
+    } else if (k == "transpose_b") {
+        const int x = std::atoi(v.c_str());
+        if (x < 0 || x > 2) return fail(MKP_ERR_INVALID_ARG, "transpose_b must be 0, 1 or 2");
+        L.transpose_b.store(x);
     } else if (k == "pack_unaligned") {
         L.pack_unaligned.store(std::atoi(v.c_str()) != 0);
         return MKP_OK;
@@ -728,7 +751,11 @@ int mkp_trace_dump(char* buf, size_t len) {
         (void)hipEventDestroy(recs[i].e0);
         (void)hipEventDestroy(recs[i].e1);
         const int k = recs[i].kernel;
-        const char* name = k >= 0 ? kernel_info(k).name : k == -1 ? "splitk_reduce" : k == -2 ? "zero_fill" : "pack_rows";
+        const char* name = k >= 0    ? kernel_info(k).name
+                           : k == -1 ? "splitk_reduce"
+                           : k == -2 ? "zero_fill"
+                           : k == -3 ? "pack_rows"
+                                     : "transpose_b";
         if (i) o << ",";
         o << "{\"kernel\":\"" << name << "\",\"call\":" << recs[i].call << ",\"us\":" << 1000.0 * ms
           << ",\"flops\":" << recs[i].flops
@@ -842,6 +869,27 @@ int mkp_calibrate(const char* path, int max_points) {
             }
             (void)hipFree(W);
         }
+    }
+    // transpose of a K x N B into N x K: fixed cost and bandwidth fitted to
+    // two sizes, in the cost model's byte count 4*K*N; source and target
+    // rotate through the pool like the kernels' operands
+    {
+        int64_t slot = 0;
+        auto run = [&](int K, int N) {
+            const size_t bytes = round256((size_t)K * N * 2);
+            const size_t nslots = std::max<size_t>(2, pool_ab / bytes);
+            return time_launches([&] {
+                char* src = pAB + (size_t)(slot % nslots) * bytes;
+                char* dst = pAB + (size_t)((slot + 1) % nslots) * bytes;
+                slot += 2;
+                return launch_transpose_bf16((const uint16_t*)src, N, 0, (uint16_t*)dst, K, 0, K, N, 1, true, nullptr);
+            }, 10, 30, &err);
+        };
+        const double ta = run(768, 768), tb = run(4096, 4096);
+        const double ba = 4.0 * 768 * 768, bb = 4.0 * 4096 * 4096;
+        const double bw = (bb - ba) / std::max(tb - ta, 0.1);   // bytes per us
+        t.tr_gbps = bw / 1e3;
+        t.tr_launch_us = std::max(ta - ba / bw, 0.0);
     }
     for (int i = 0; i < kernel_count() && err == hipSuccess; ++i) {
         const KernelInfo& ki = kernel_info(i);

@@ -69,6 +69,13 @@ hipError_t launch_zero_fill(float* C, int64_t ldc, int64_t sC, int M, int N, int
 hipError_t launch_pack_rows(const uint16_t* src, int64_t ld_src, int64_t stride_src, uint16_t* dst, int64_t ld_dst,
                             int rows, int cols, int batch, hipStream_t st);
 
+// Batch K x N bf16 matrices (leading dimension ld_src, batch stride s_src) into
+// N x K (ld_dst >= K, a multiple of 8, dst 16-byte aligned; padding columns
+// zeroed).  src_vec: source rows 16-byte aligned (128-bit loads).  Fails with
+// hipErrorInvalidValue beyond 65535 batch entries or K tiles.
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t ld_src, int64_t s_src, uint16_t* dst, int64_t ld_dst,
+                                 int64_t s_dst, int K, int N, int batch, bool src_vec, hipStream_t st);
+
 // Calibration probes: MFMA rate on random operands (blocks x 4 waves, each
 // 64*iters 32x32x16 MFMAs) and a streaming copy of `bytes` (multiple of 16).
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);

@@ -676,6 +676,49 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restri
     *(u32x4*)(dst + (int64_t)b * rows * ld_dst + (int64_t)r * ld_dst + c) = load8_elems(s, cols - c);
 }
 
+// dst[b][n][k] = src[b][k][n] for a K x N bf16 matrix (leading dimension
+// ld_src) into N x K (leading dimension ld_dst >= K, a multiple of 8, rows
+// 16-byte aligned; columns K..ld_dst-1 are zeroed).  One 64 x 64 tile per
+// workgroup through LDS: 16-byte loads along the rows of the source (element
+// loads when its rows are not 16-byte aligned) and 16-byte stores along the
+// rows of the target.
+template <bool VEC>
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                                             int64_t s_src, uint16_t* __restrict__ dst,
+                                                             int64_t ld_dst, int64_t s_dst, int K, int N) {
+    __shared__ __attribute__((aligned(16))) uint16_t t[64][72];   // [k][n], rows of 144 bytes
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+    const uint16_t* sb = src + (int64_t)blockIdx.z * s_src;
+    uint16_t* db = dst + (int64_t)blockIdx.z * s_dst;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int q = it * 256 + tid, r = q >> 3, c8 = (q & 7) * 8;
+        const int k = k0 + r, n = n0 + c8;
+        u32x4 v = zero4();
+        if (k < K) {
+            const uint16_t* p = sb + (int64_t)k * ld_src + n;
+            v = (VEC && n + 8 <= N) ? *(const u32x4*)p : load8_elems(p, N - n);
+        }
+        *(u32x4*)&t[r][c8] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int q = it * 256 + tid, r = q >> 3, c8 = (q & 7) * 8;
+        const int n = n0 + r, k = k0 + c8;
+        if (n >= N || k >= ld_dst) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = k + 2 * e < K ? t[c8 + 2 * e][r] : 0u;
+            const uint32_t hi = k + 2 * e + 1 < K ? t[c8 + 2 * e + 1][r] : 0u;
+            w[e] = lo | (hi << 16);
+        }
+        *(u32x4*)(db + (int64_t)n * ld_dst + k) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
 __global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ C, int64_t ldc, int64_t sC, int M,
                                                         int N, int batch) {
     const int64_t per = (int64_t)M * N;
@@ -832,6 +875,19 @@ hipError_t launch_splitk_reduce(const float* W, int splits, int64_t sWsplit, int
     dim3 grid((unsigned)((items + 255) / 256));
     hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, W, splits, sWsplit, sWbatch, ldw, C, ldc, sC, M,
                        N, batch, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t ld_src, int64_t s_src, uint16_t* dst, int64_t ld_dst,
+                                 int64_t s_dst, int K, int N, int batch, bool src_vec, hipStream_t st) {
+    if (batch > 65535 || (ld_dst + 63) / 64 > 65535 || ld_dst % 8 != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((ld_dst + 63) / 64), (unsigned)batch);
+    if (src_vec)
+        hipLaunchKernelGGL(transpose_bf16_kernel<true>, grid, dim3(256), 0, st, src, ld_src, s_src, dst, ld_dst, s_dst,
+                           K, N);
+    else
+        hipLaunchKernelGGL(transpose_bf16_kernel<false>, grid, dim3(256), 0, st, src, ld_src, s_src, dst, ld_dst,
+                           s_dst, K, N);
     return hipGetLastError();
 }
 

@@ -36,6 +36,10 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
             if (!(ls >> t.launch_us) || t.launch_us < 0) return fail("bad launch_us");
         } else if (key == "reduce") {
             if (!(ls >> t.red_launch_us >> t.red_gbps) || t.red_gbps <= 0) return fail("bad reduce line");
+        } else if (key == "transpose") {
+            // transpose <launch_us> <GB/s>: K x N -> N x K copy of B
+            if (!(ls >> t.tr_launch_us >> t.tr_gbps) || t.tr_gbps <= 0 || t.tr_launch_us < 0)
+                return fail("bad transpose line");
         } else if (key == "splitk") {
             t.splits.clear();
             int s;
@@ -148,6 +152,7 @@ std::string table_to_text(const PerfTable& t) {
     o << "device " << t.cus << "\n";
     o << "launch_us " << t.launch_us << "\n";
     o << "reduce " << t.red_launch_us << " " << t.red_gbps << "\n";
+    if (t.tr_gbps > 0) o << "transpose " << t.tr_launch_us << " " << t.tr_gbps << "\n";
     o << "splitk";
     for (int s : t.splits) o << " " << s;
     o << "\npatterns" << (t.pat_I ? " I" : "") << (t.pat_IIM ? " II-M" : "") << (t.pat_IIN ? " II-N" : "")
@@ -540,6 +545,38 @@ Plan polymerize(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64
     return p;
 }
 
+double transpose_cost(const PerfTable& tab, int64_t batch, int64_t N, int64_t K) {
+    if (!(tab.tr_gbps > 0)) return std::numeric_limits<double>::infinity();
+    return tab.tr_launch_us + 4.0 * (double)K * (double)N * (double)batch / (tab.tr_gbps * 1e3);
+}
+
+Plan plan_call(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_t K, const SearchOptions& opt,
+               int transpose_mode) {
+    Plan p = polymerize(tab, batch, M, N, K, opt);
+    if (opt.bt || transpose_mode == 0 || p.pattern == PAT_EMPTY || p.pattern == PAT_ZERO || opt.plan_rank > 0 ||
+        opt.force_kernel >= 0 || opt.cost_mode != COST_FULL)
+        return p;
+    double tc = transpose_cost(tab, batch, N, K);
+    if (!std::isfinite(tc)) {
+        if (transpose_mode != 2) return p;
+        tc = 0.0;   // forced without figures: the copy goes unpriced
+    }
+    SearchOptions o = opt;
+    o.bt = true;
+    Plan q = polymerize(tab, batch, M, N, K, o);
+    if (q.regions.empty() || !(transpose_mode == 2 || q.cost_us + tc < p.cost_us || p.regions.empty())) {
+        p.plan_us += q.plan_us;
+        p.evaluated += q.evaluated;
+        return p;
+    }
+    q.transpose_b = true;
+    q.transpose_us = tc;
+    q.cost_us += tc;
+    q.plan_us += p.plan_us;
+    q.evaluated += p.evaluated;
+    return q;
+}
+
 std::string plan_to_json(const Plan& p, const PerfTable& tab) {
     static const char* names[] = {"empty", "zero", "I", "II-M", "II-N"};
     std::ostringstream o;
@@ -547,6 +584,8 @@ std::string plan_to_json(const Plan& p, const PerfTable& tab) {
     o << "{\"pattern\":\"" << names[p.pattern] << "\",\"cost_us\":" << (p.regions.empty() ? 0.0 : p.cost_us)
       << ",\"plan_us\":" << p.plan_us << ",\"evaluated\":" << p.evaluated;
     if (p.rank > 0) o << ",\"rank\":" << p.rank << ",\"candidates\":" << p.candidates;
+    o << ",\"transpose_b\":" << (p.transpose_b ? "true" : "false");
+    if (p.transpose_b) o << ",\"transpose_us\":" << p.transpose_us;
     o << ",\"regions\":[";
     for (size_t i = 0; i < p.regions.size(); ++i) {
         const Region& r = p.regions[i];

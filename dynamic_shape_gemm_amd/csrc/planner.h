@@ -41,6 +41,10 @@ struct PerfTable {
     double launch_us = 0.0;       // per launch (per region)
     double red_launch_us = 0.0;   // split-K reduction: fixed part
     double red_gbps = 1000.0;     // split-K reduction: bandwidth
+    // transposing a K x N B into an N x K copy (so that a K x N call can run
+    // on the N x K kernels): fixed part and bandwidth; tr_gbps 0 = never
+    double tr_launch_us = 0.0;
+    double tr_gbps = 0.0;
     std::vector<int> splits{1};
     bool pat_I = true, pat_IIM = true, pat_IIN = true;
     double mfma_tflops = 0.0;     // measured sustained bf16 MFMA rate (0: unknown)
@@ -70,6 +74,8 @@ struct Plan {
     int64_t evaluated = 0;   // candidate regions scored
     int rank = 0;            // >0: this is the rank-th cheapest candidate
     int64_t candidates = 0;  // size of the ranked candidate list (rank > 0 only)
+    bool transpose_b = false;  // a K x N B is first copied to N x K; regions use N x K kernels
+    double transpose_us = 0.0; // modelled time of that copy (included in cost_us)
 };
 
 // Which factors of the cost model the search scores (MikPoly page, section 4
@@ -105,6 +111,17 @@ double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64
 
 Plan polymerize(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_t K,
                 const SearchOptions& opt);
+
+// Modelled time of transposing batch K x N bf16 matrices (reads and writes
+// 2*K*N bytes each); infinite when the table has no transpose figures.
+double transpose_cost(const PerfTable& tab, int64_t batch, int64_t N, int64_t K);
+
+// The plan for a call: for B given as N x K the N x K search; for B given as
+// K x N the cheaper of the K x N search and a transpose of B followed by the
+// N x K search.  transpose_mode: 0 never transpose, 1 by modelled cost (when
+// the table prices the copy), 2 always (when an N x K plan exists).
+Plan plan_call(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_t K, const SearchOptions& opt,
+               int transpose_mode);
 
 std::string plan_to_json(const Plan& p, const PerfTable& tab);
 

@@ -113,7 +113,9 @@ int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K,
  * Writes NUL-terminated JSON into buf:
  *   {"pattern":..., "cost_us":..., "plan_us":..., "regions":[{"m0","n0","m",
  *    "n","kernel","uM","uN","uK","s","steps","tasks","waves","wave_factor",
- *    "cost_us"}...]}
+ *    "cost_us"}...], "transpose_b": bool [, "transpose_us"]}
+ * transpose_b: a K x N B is first copied into N x K workspace rows and the
+ * regions run on N x K kernels (the cheaper plan by the cost model).
  * Uses the active performance table (calibrated, or the built-in analytic
  * one).  Pure host code: needs no GPU.  Returns MKP_OK, MKP_ERR_INVALID_ARG
  * or MKP_ERR_BUFFER.
@@ -143,6 +145,7 @@ int mkp_plan_with_table(const char *table_text, int flags,
  *   patterns I II-M II-N             kernel <name> <uM> <uN> <uK> <wg_per_cu> [kn|nk]
  *   g <name> <t>:<us> <t>:<us> ...   measured <TFLOP/s> <GB/s>
  *   tail <name> <f>:<r> ...          tailx <name> <f>:<r> ...
+ *   transpose <launch_us> <GB/s>     (copy of a K x N B into N x K)
  * (kn / nk: the kernel takes B as K x N, the default, or as N x K; tail and
  * tailx: time of a wave filling a fraction f < 1 of the slots, on its own or
  * after full waves, relative to a full wave.)  Kernels named here must exist
@@ -169,6 +172,10 @@ int mkp_calibrate(const char *path, int max_points);
  * whose rows are not 16-byte aligned and that several tiles re-read is
  * first copied into aligned workspace rows, the default; 0 = such operands
  * are read element by element).
+ * "transpose_b" (0 = K x N calls always run on K x N kernels; 1 = the
+ * default: a K x N call may copy B into N x K workspace rows and run on the
+ * N x K kernels, when the table prices the copy and the model finds it
+ * cheaper; 2 = always, whenever an N x K plan exists).
  * Cost-model evaluation (MikPoly page, section 5 "cost-model effectiveness":
  * the WAVE and PIPE ablations and the ORACLE that measures candidates):
  * "cost_model" ("full" = f_wave * f_pipe, the default; "wave" = f_wave with
@@ -198,7 +205,7 @@ void mkp_cache_clear(void);
 int mkp_stats(char *buf, size_t len);
 
 /* Launch trace (option "trace" = 1): every kernel launch (micro-kernels,
- * "splitk_reduce", "zero_fill", "pack_rows") is bracketed by
+ * "splitk_reduce", "zero_fill", "pack_rows", "transpose_b") is bracketed by
  * HIP events on its stream.  Waits for the recorded launches, writes a JSON
  * list [{"kernel","call","us","flops","bytes"}...] ("call": sequence number
  * of the GEMM call that made the launch; algorithmic work per launch:

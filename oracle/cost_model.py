@@ -36,6 +36,10 @@ Readings where the page is silent (each is listed in the design doc):
   * the ablations of section 5 "cost-model effectiveness" (MikPoly-WAVE,
     MikPoly-PIPE) keep one factor of the product and take the other as 1
     (f_pipe = 1 us, resp. f_wave = 1); the launch and reduction terms stay.
+  * B layouts (not on the page): a kernel takes B as K x N or as N x K; a
+    call searches the kernels of its layout.  A K x N call may instead pay
+    for a transpose of B (launch + 4*K*N*batch bytes / bandwidth) and run
+    the N x K search; the cheaper of the two is the plan.
   * Pattern I: one region = whole output, one kernel.  Pattern II-M (II-N):
     a cut of the M (N) extent, the two parts on two different kernels (the
     case study's 3072 | 1024 split).  The cut is a wave boundary of the
@@ -72,6 +76,8 @@ class Table:
     splits: List[int]
     patterns: List[str]
     kernels: Dict[str, Kernel]
+    tr_launch_us: float = 0.0
+    tr_gbps: float = 0.0
 
     def slots(self, k: Kernel) -> int:
         return self.cus * k.wg_per_cu
@@ -82,6 +88,7 @@ def parse_table(text: str) -> Table:
     cus = 0
     launch = 0.0
     red_l, red_bw = 0.0, 1.0
+    tr_l, tr_bw = 0.0, 0.0
     splits = [1]
     patterns = ["I", "II-M", "II-N"]
     kernels: Dict[str, Kernel] = {}
@@ -100,6 +107,8 @@ def parse_table(text: str) -> Table:
             launch = float(tok[1])
         elif key == "reduce":
             red_l, red_bw = float(tok[1]), float(tok[2])
+        elif key == "transpose":
+            tr_l, tr_bw = float(tok[1]), float(tok[2])
         elif key == "splitk":
             splits = [int(x) for x in tok[1:]]
         elif key == "patterns":
@@ -132,7 +141,7 @@ def parse_table(text: str) -> Table:
     for k in kernels.values():
         if not k.pts:
             raise ValueError(f"kernel {k.name} has no g points")
-    return Table(cus, launch, red_l, red_bw, splits, patterns, kernels)
+    return Table(cus, launch, red_l, red_bw, splits, patterns, kernels, tr_l, tr_bw)
 
 
 def g_predict(k: Kernel, t: float) -> float:
@@ -299,3 +308,23 @@ def covers_exactly(M: int, N: int, regions: Sequence[Region], tiles: Dict[str, T
             for j0 in range(r.n0, r.n0 + r.n, uN):
                 cnt[i0:min(i0 + uM, r.m0 + r.m), j0:min(j0 + uN, r.n0 + r.n)] += 1
     return bool((cnt == 1).all())
+
+
+def transpose_cost(tab: Table, batch: int, N: int, K: int) -> float:
+    """Modelled time of copying a K x N B to N x K (infinite without figures)."""
+    if tab.tr_gbps <= 0:
+        return float("inf")
+    return tab.tr_launch_us + 4.0 * K * N * batch / (tab.tr_gbps * 1e3)
+
+
+def best_call(tab: Table, M: int, N: int, K: int, batch: int = 1, bt: bool = False):
+    """(cost, transposed?) of the best plan of a call: for B given as K x N,
+    the K x N plan or a transpose followed by the N x K plan."""
+    direct = exhaustive_best(tab, M, N, K, batch, bt=bt)
+    if bt:
+        return (direct[0] if direct else float("inf")), False
+    via = exhaustive_best(tab, M, N, K, batch, bt=True)
+    tc = transpose_cost(tab, batch, N, K)
+    if via is not None and (direct is None or via[0] + tc < direct[0]):
+        return via[0] + tc, True
+    return (direct[0] if direct else float("inf")), False

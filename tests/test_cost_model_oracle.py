@@ -184,3 +184,13 @@ tailx k 0.5:0.2
     # without tail lines the full model is the page's ceil
     tab0 = cm.parse_table(text.replace("tail k 0.25:0.4 0.5:0.7\n", "").replace("tailx k 0.5:0.2\n", ""))
     assert cm.region_cost(tab0, r, 160, 1) == pytest.approx(0.5 + 2 * 11)
+
+
+def test_transpose_cost_closed_form():
+    """The copy of a K x N B to N x K costs launch + 4*K*N*batch bytes at the
+    table's bandwidth; without a transpose line it is never taken."""
+    tab = cm.parse_table("device 4\ntranspose 1.5 2000\nkernel k 16 16 16 1\ng k 1:1\n")
+    assert cm.transpose_cost(tab, 3, 1000, 500) == pytest.approx(1.5 + 4.0 * 500 * 1000 * 3 / 2e6)
+    tab0 = cm.parse_table("device 4\nkernel k 16 16 16 1\ng k 1:1\n")
+    assert cm.transpose_cost(tab0, 1, 64, 64) == float("inf")
+    assert cm.best_call(tab0, 64, 64, 64)[1] is False

@@ -227,3 +227,36 @@ def test_layout_restricts_the_search(mkp):
             best = cm.exhaustive_best(tab, M, N, K, 1, bt=bt)
             assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (trial, bt)
             assert all(r["kernel"].endswith("_nk") == bt for r in plan["regions"])
+
+
+def test_transpose_then_nk_choice_matches_oracle(mkp):
+    """With N x K kernels and transpose figures in the table, a K x N call
+    takes the cheaper of its own plan and transpose + N x K plan, as the
+    oracle computes it."""
+    rng = np.random.default_rng(123)
+    chosen = {False: 0, True: 0}
+    for trial in range(30):
+        text = random_table(rng, int(rng.integers(2, 4)))
+        extra = random_table(rng, int(rng.integers(1, 3)))
+        lines = [f"transpose {rng.uniform(0.5, 5):.3f} {rng.uniform(200, 20000):.1f}"]
+        for line in extra.splitlines():
+            tok = line.split()
+            if tok[0] == "kernel":
+                lines.append(" ".join(["kernel", tok[1] + "_nk"] + tok[2:] + ["nk"]))
+            elif tok[0] == "g":
+                # the N x K family runs 0.3x - 1.5x the time of its K x N draw
+                scale = rng.uniform(0.3, 1.5)
+                pts = " ".join(f"{p.split(':')[0]}:{float(p.split(':')[1]) * scale:.4f}" for p in tok[2:])
+                lines.append(f"g {tok[1]}_nk {pts}")
+        text = text + "\n".join(lines) + "\n"
+        tab = cm.parse_table(text)
+        M, N, K = (int(x) for x in rng.integers(1, 300, size=3))
+        plan = mkp.mkp_plan_with_table(text, 1, M, N, K)
+        cost, transposed = cm.best_call(tab, M, N, K, 1)
+        assert plan["cost_us"] == pytest.approx(cost, rel=1e-9), (trial, M, N, K)
+        assert plan["transpose_b"] == transposed
+        assert all(r["kernel"].endswith("_nk") == transposed for r in plan["regions"])
+        if transposed:
+            assert plan["transpose_us"] == pytest.approx(cm.transpose_cost(tab, 1, N, K), rel=1e-9)
+        chosen[transposed] += 1
+    assert chosen[True] > 0 and chosen[False] > 0
