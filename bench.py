@@ -43,11 +43,15 @@ def log(msg):
 class Workload:
     """Device-resident operands for one sweep of a config."""
 
-    def __init__(self, cfg: int, copies: int = 1, b_layout: str = "kn"):
+    def __init__(self, cfg: int, copies: int = 1, b_layout: str = "kn", qkv: str = "merged"):
         import torch
         import workloads
 
         self.cfg = cfg
+        # the query/key/value projection (N = 3 x 768 of the encoder linears):
+        # merged = one call over the side-by-side weights; grouped = one
+        # grouped call over three 768-wide weights; separate = three calls
+        self.qkv = qkv if cfg == 2 else "merged"
         # kn: B is K x N (mkp_gemm); nk: B is kept as N x K, a linear layer's
         # weight layout (mkp_gemm_bt) -- the same products either way
         self.bt = b_layout == "nk"
@@ -82,9 +86,33 @@ class Workload:
         t = torch.from_numpy(b.view(np.int16)).cuda()
         return t.transpose(-1, -2).contiguous() if self.bt else t
 
+    def is_qkv(self, case) -> bool:
+        return self.qkv != "merged" and case.N == 2304 and case.batch == 1
+
+    def calls_per_case(self):
+        return [3 if self.qkv == "separate" and self.is_qkv(c) else 1 for c in self.cases]
+
+    def _qkv_step(self, mkp, case, pa, pb, tc, stream):
+        """The 2304-wide product as three 768-wide ones: B_g and C_g are
+        the g-th column blocks (or, for N x K weights, row blocks of B)."""
+        M, K, n = case.M, case.K, 768
+        pc = tc.data_ptr()
+        pbs = [pb + 2 * g * (n * K if self.bt else n) for g in range(3)]
+        ldb = K if self.bt else case.N
+        pcs = [pc + 4 * g * n for g in range(3)]
+        if self.qkv == "grouped":
+            fn = mkp.mkp_gemm_grouped_bt if self.bt else mkp.mkp_gemm_grouped
+            fn(M, K, pa, K, [n] * 3, pbs, [ldb] * 3, pcs, [case.N] * 3, stream)
+        else:
+            fn = mkp.mkp_gemm_bt if self.bt else mkp.mkp_gemm
+            for g in range(3):
+                fn(M, n, K, pa, K, pbs[g], ldb, pcs[g], case.N, stream)
+
     def step(self, mkp, stream):
         for case, pa, pb, tc in self.calls:
-            if self.bt:
+            if self.is_qkv(case):
+                self._qkv_step(mkp, case, pa, pb, tc, stream)
+            elif self.bt:
                 mkp.mkp_gemm_batched_bt(case.batch, case.M, case.N, case.K, pa, case.K, case.M * case.K, pb, case.K,
                                         case.N * case.K, tc, case.N, case.M * case.N, stream)
             elif case.batch == 1:
@@ -234,6 +262,9 @@ def main():
     ap.add_argument("--detail", action="store_true", help="per-GEMM timings to stderr")
     ap.add_argument("--b-layout", choices=["kn", "nk"], default="kn",
                     help="B as K x N (default) or kept N x K, a linear layer's weight layout")
+    ap.add_argument("--qkv", choices=["merged", "grouped", "separate"], default="merged",
+                    help="encoder linears: run the query/key/value projection as one call (default), "
+                         "one grouped call over three weights, or three calls")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of MiB (to scale rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -252,7 +283,7 @@ def main():
 
     torch.cuda.set_device(0)
     log(f"[bench] generating config {args.config} inputs")
-    wl = Workload(args.config, copies=4, b_layout=args.b_layout)
+    wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv)
     stream = torch.cuda.current_stream().cuda_stream
     mkp.mkp_cache_clear()
 
@@ -291,13 +322,23 @@ def main():
         for r in recs:
             by_call[r["call"]] = by_call.get(r["call"], 0.0) + r["us"]
         calls = [by_call[k] for k in sorted(by_call)]
-        assert len(calls) == len(wl.cases), (len(calls), len(wl.cases))
-        per_step.append(calls)
+        counts = wl.calls_per_case()
+        assert len(calls) == sum(counts), (len(calls), sum(counts))
+        per_case, i = [], 0
+        for c in counts:   # a case made of several library calls sums them
+            per_case.append(sum(calls[i:i + c]))
+            i += c
+        per_step.append(per_case)
     per_call = [float(np.median(v)) for v in zip(*per_step)]
     fr = sweep_fraction(per_call, wl)
     if args.detail:
         for case, us, f in zip(wl.cases, per_call, fr):
-            plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K, bt=wl.bt)
+            if wl.is_qkv(case):
+                plan = mkp.mkp_plan_describe_grouped(case.M, case.K, [768] * 3, bt=wl.bt)
+                if wl.qkv == "separate":
+                    plan = dict(mkp.mkp_plan_describe(1, case.M, 768, case.K, bt=wl.bt), pattern="3x")
+            else:
+                plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K, bt=wl.bt)
             ks = "+".join(f"{r['kernel']}/s{r['s']}" for r in plan["regions"])
             log(f"  {case.tag:>14} {case.M:5d}x{case.N:5d}x{case.K:5d} b{case.batch:<3d} {us:9.2f} us "
                 f"{case.flops / us / 1e6:8.1f} TF/s  {100 * f:5.1f}% of R  {plan['pattern']:4s} {ks}")
@@ -319,6 +360,7 @@ def main():
             "workload": workloads.CONFIG_NAMES[args.config],
             "config_index": args.config,
             "b_layout": args.b_layout,
+            "qkv": wl.qkv,
             "gemms_per_step": len(wl.cases),
             "flops_per_step": wl.flops,
             "bytes_per_step": wl.bytes,

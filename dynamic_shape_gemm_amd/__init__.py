@@ -56,6 +56,13 @@ _lib.mkp_gemm_bt.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.mkp_gemm_bt.restype = _int
 _lib.mkp_gemm_batched_bt.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
 _lib.mkp_gemm_batched_bt.restype = _int
+_grp_args = [_i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p]
+_lib.mkp_gemm_grouped.argtypes = _grp_args
+_lib.mkp_gemm_grouped.restype = _int
+_lib.mkp_gemm_grouped_bt.argtypes = _grp_args
+_lib.mkp_gemm_grouped_bt.restype = _int
+_lib.mkp_plan_describe_grouped.argtypes = [_i64, _i64, _i64, _p, _int, ctypes.c_char_p, ctypes.c_size_t]
+_lib.mkp_plan_describe_grouped.restype = _int
 _lib.mkp_plan_describe.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.c_char_p, ctypes.c_size_t]
 _lib.mkp_plan_describe.restype = _int
 _lib.mkp_plan_with_table.argtypes = [ctypes.c_char_p, _int, _i64, _i64, _i64, _i64, ctypes.c_char_p, ctypes.c_size_t]
@@ -79,7 +86,9 @@ _lib.mkp_trace_dump.restype = _int
 _lib.mkp_last_error.argtypes = []
 _lib.mkp_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_plan_describe", "mkp_plan_with_table", "mkp_load_calibration",
+EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_grouped",
+            "mkp_gemm_grouped_bt", "mkp_plan_describe", "mkp_plan_describe_grouped", "mkp_plan_with_table",
+            "mkp_load_calibration",
             "mkp_calibrate", "mkp_set_option", "mkp_kernel_count", "mkp_kernel_name", "mkp_cache_clear",
             "mkp_stats", "mkp_trace_dump", "mkp_last_error"]
 
@@ -150,6 +159,44 @@ def mkp_gemm_bt_raw(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 def mkp_gemm_batched_bt_raw(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream) -> int:
     return _lib.mkp_gemm_batched_bt(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC,
                                     stream or 0)
+
+
+def _i64_array(values):
+    return (ctypes.c_int64 * max(len(values), 1))(*[int(v) for v in values])
+
+
+def _ptr_array(values):
+    return (ctypes.c_void_p * max(len(values), 1))(*[_addr(v) for v in values])
+
+
+def _grouped_call(fn, M, K, A, lda, N, B, ldb, C, ldc, stream):
+    g = len(N)
+    if not (len(B) == len(ldb) == len(C) == len(ldc) == g):
+        raise ValueError("N, B, ldb, C and ldc must have one entry per group")
+    return fn(g, M, K, _addr(A), lda, ctypes.cast(_i64_array(N), _p), ctypes.cast(_ptr_array(B), _p),
+              ctypes.cast(_i64_array(ldb), _p), ctypes.cast(_ptr_array(C), _p), ctypes.cast(_i64_array(ldc), _p),
+              stream)
+
+
+def mkp_gemm_grouped(M, K, A, lda, N, B, ldb, C, ldc, stream=None) -> int:
+    """C[g][M x N[g]] := A[M x K] . B[g] (B[g] K x N[g]) for every group, in
+    one launch.  N, B, ldb, C, ldc are sequences with one entry per group."""
+    return _check(_grouped_call(_lib.mkp_gemm_grouped, M, K, A, lda, N, B, ldb, C, ldc, _stream(stream)))
+
+
+def mkp_gemm_grouped_bt(M, K, A, lda, N, B, ldb, C, ldc, stream=None) -> int:
+    """As mkp_gemm_grouped with each B[g] given as N[g] x K (ldb[g] >= K)."""
+    return _check(_grouped_call(_lib.mkp_gemm_grouped_bt, M, K, A, lda, N, B, ldb, C, ldc, _stream(stream)))
+
+
+def mkp_gemm_grouped_raw(M, K, A, lda, N, B, ldb, C, ldc, stream, bt=False) -> int:
+    fn = _lib.mkp_gemm_grouped_bt if bt else _lib.mkp_gemm_grouped
+    return _grouped_call(fn, M, K, A, lda, N, B, ldb, C, ldc, stream or 0)
+
+
+def mkp_plan_describe_grouped(M, K, N, bt=False) -> dict:
+    return json.loads(_text_call(_lib.mkp_plan_describe_grouped, len(N), M, K,
+                                 ctypes.cast(_i64_array(N), _p), MKP_PLAN_B_NK if bt else 0))
 
 
 def _text_call(fn, *args, size=1 << 16):
@@ -247,3 +294,26 @@ def gemm_bt(a, w, out=None, stream=None):
         raise ValueError("out rows must be contiguous")
     mkp_gemm_bt(M, N, K, a, max(a.stride(0), 1), w, max(w.stride(0), 1), out, max(out.stride(0), 1), stream)
     return out
+
+
+def gemm_grouped(a, ws, outs=None, stream=None, bt=False):
+    """torch convenience: one A (M,K) bf16 against several weights in one
+    launch.  ws: list of (K,N_g) bf16 tensors, or (N_g,K) with bt=True.
+    Returns (or fills) the list of (M,N_g) fp32 outputs."""
+    import torch
+    if a.dtype != torch.bfloat16 or any(w.dtype != torch.bfloat16 for w in ws):
+        raise TypeError("a and the weights must be bfloat16")
+    if a.stride(1) != 1 or any(w.stride(1) != 1 for w in ws):
+        raise ValueError("rows must be contiguous (unit column stride)")
+    M, K = a.shape
+    Ns = [w.shape[0] if bt else w.shape[1] for w in ws]
+    if any((w.shape[1] if bt else w.shape[0]) != K for w in ws):
+        raise ValueError("inner dimensions differ")
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.float32, device=a.device) for n in Ns]
+    if any(o.stride(1) != 1 for o in outs):
+        raise ValueError("out rows must be contiguous")
+    fn = mkp_gemm_grouped_bt if bt else mkp_gemm_grouped
+    fn(M, K, a, max(a.stride(0), 1), Ns, ws, [max(w.stride(0), 1) for w in ws], outs,
+       [max(o.stride(0), 1) for o in outs], stream)
+    return outs

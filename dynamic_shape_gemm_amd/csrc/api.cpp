@@ -93,6 +93,7 @@ struct Library {
     std::string table_origin = "analytic";
     SearchOptions opts;
     std::unordered_map<Key, std::shared_ptr<const Plan>, KeyHash> cache;
+    std::map<std::vector<int64_t>, std::shared_ptr<const Plan>> gcache;   // grouped calls
     size_t cache_cap = 1 << 16;
 
     std::mutex ws_mu;
@@ -207,6 +208,7 @@ int load_table_locked(Library& L, const char* path, bool quiet_missing) {
             L.table = analytic_table();
             L.table_origin = "analytic";
             L.cache.clear();
+    L.gcache.clear();
             return MKP_OK;
         }
         return fail(MKP_ERR_INVALID_ARG, "cannot read performance table " + p);
@@ -217,6 +219,7 @@ int load_table_locked(Library& L, const char* path, bool quiet_missing) {
     L.table = t;
     L.table_origin = p;
     L.cache.clear();
+    L.gcache.clear();
     return MKP_OK;
 }
 
@@ -272,6 +275,7 @@ std::shared_ptr<const Plan> get_plan(const Key& key) {
     L.misses.fetch_add(1, std::memory_order_relaxed);
     L.plan_ns.fetch_add((int64_t)(plan->plan_us * 1000.0), std::memory_order_relaxed);
     if (L.cache.size() >= L.cache_cap) L.cache.clear();
+    L.gcache.clear();
     L.cache.emplace(key, plan);
     return plan;
 }
@@ -532,6 +536,144 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     return MKP_OK;
 }
 
+// C_g := A . B_g for g < G (shared A, K; B_g K x N_g, or N_g x K when bt).
+int run_grouped(int64_t G, int64_t M, int64_t K, const void* Av, int64_t lda, const int64_t* Ns,
+                const void* const* Bs, const int64_t* ldbs, float* const* Cs, const int64_t* ldcs, void* stream_v,
+                bool bt) {
+    if (G < 1 || G > kMaxGroups) return fail(MKP_ERR_INVALID_ARG, "groups must be 1.." + std::to_string(kMaxGroups));
+    if (!Ns || !Bs || !ldbs || !Cs || !ldcs) return fail(MKP_ERR_INVALID_ARG, "group arrays are NULL");
+    if (M < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
+    if (M > INT_MAX || K > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "dimension exceeds 2^31-1");
+    for (int64_t g = 0; g < G; ++g) {
+        const int64_t N = Ns[g];
+        if (N < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
+        if (N > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "dimension exceeds 2^31-1");
+        if (N == 0 || M == 0) continue;
+        if (K > 0 && (bt ? ldbs[g] < K : ldbs[g] < N)) return fail(MKP_ERR_INVALID_ARG, bt ? "ldb < K" : "ldb < N");
+        if (ldcs[g] < N) return fail(MKP_ERR_INVALID_ARG, "ldc < N");
+        if (!Cs[g]) return fail(MKP_ERR_INVALID_ARG, "C is NULL");
+        if (K > 0 && !Bs[g]) return fail(MKP_ERR_INVALID_ARG, "B is NULL");
+    }
+    if (K > 0 && M > 0 && lda < K) return fail(MKP_ERR_INVALID_ARG, "lda < K");
+    if (K > 0 && M > 0 && !Av) return fail(MKP_ERR_INVALID_ARG, "A is NULL");
+    // the groups that have work
+    std::vector<int64_t> live;
+    for (int64_t g = 0; g < G; ++g)
+        if (Ns[g] > 0) live.push_back(g);
+    if (M == 0 || live.empty()) return MKP_OK;
+    ensure_init();
+    t_call = lib().calls.fetch_add(1, std::memory_order_relaxed);
+    hipStream_t st = (hipStream_t)stream_v;
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
+    Library& L = lib();
+    if (K == 0) {
+        for (int64_t g : live) {
+            he = traced(L, st, -2, 0.0, 4.0 * M * Ns[g],
+                        [&] { return launch_zero_fill(Cs[g], ldcs[g], 0, (int)M, (int)Ns[g], 1, st); });
+            if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("zero fill launch: ") + hipGetErrorString(he));
+            L.launches.fetch_add(1, std::memory_order_relaxed);
+        }
+        return MKP_OK;
+    }
+    // plan (cached by M, K, layout, device and the group widths)
+    std::vector<int64_t> key{M, K, bt ? 1 : 0, dev};
+    std::vector<int64_t> widths;
+    for (int64_t g : live) {
+        key.push_back(Ns[g]);
+        widths.push_back(Ns[g]);
+    }
+    std::shared_ptr<const Plan> plan;
+    {
+        std::shared_lock<std::shared_mutex> lk(L.mu);
+        auto it = L.gcache.find(key);
+        if (it != L.gcache.end()) plan = it->second;
+    }
+    if (plan) {
+        L.hits.fetch_add(1, std::memory_order_relaxed);
+    } else {
+        std::unique_lock<std::shared_mutex> lk(L.mu);
+        SearchOptions o = L.opts;
+        o.bt = bt;
+        auto p = std::make_shared<Plan>(polymerize_grouped(L.table, M, K, widths, o));
+        L.misses.fetch_add(1, std::memory_order_relaxed);
+        L.plan_ns.fetch_add((int64_t)(p->plan_us * 1000.0), std::memory_order_relaxed);
+        if (L.gcache.size() >= L.cache_cap) L.gcache.clear();
+        L.gcache.emplace(key, p);
+        plan = p;
+    }
+    if (plan->regions.empty()) return fail(MKP_ERR_UNSUPPORTED, "no plan for this grouped call");
+    const Region& r = plan->regions[0];
+    if (r.lib < 0 || r.lib >= kernel_count()) return fail(MKP_ERR_UNSUPPORTED, "plan kernel is not launchable");
+    const KernelInfo& ki = kernel_info(r.lib);
+    if (ki.bt != bt) return fail(MKP_ERR_UNSUPPORTED, "plan kernel has the other B layout");
+
+    const uint16_t* A = (const uint16_t*)Av;
+    const bool vA = aligned16(A) && lda % 8 == 0 && lda < (int64_t(1) << 23);
+    KArgs a{};
+    a.A = A;
+    a.lda = lda;
+    a.M = (int)M;
+    a.K = (int)K;
+    a.tiles_m = (int)ceil_div(M, ki.uM);
+    a.steps_per_split = r.steps;
+    a.splits = r.s;
+    a.batch = 1;
+    a.flags = vA ? KF_VEC_A : 0;
+    a.ngroups = (int)live.size();
+    int tile0 = 0;
+    double flops = 0, bytes = 2.0 * M * K;
+    for (size_t i = 0; i < live.size(); ++i) {
+        const int64_t g = live[i];
+        KGroup& G_ = a.group[i];
+        G_.B = (const uint16_t*)Bs[g];
+        G_.C = Cs[g];
+        G_.ldb = ldbs[g];
+        G_.ldc = ldcs[g];
+        G_.N = (int)Ns[g];
+        G_.tile0 = tile0;
+        const bool vB = aligned16(Bs[g]) && ldbs[g] % 8 == 0 && ldbs[g] < (int64_t(1) << (bt ? 23 : 25));
+        const bool vC = aligned16(Cs[g]) && ldcs[g] % 4 == 0;
+        G_.flags = (vB ? KF_VEC_B : 0) | (vC ? KF_VEC_C : 0);
+        tile0 += (int)ceil_div(Ns[g], ki.uN);
+        flops += 2.0 * M * Ns[g] * K;
+        bytes += 2.0 * K * Ns[g] + 4.0 * M * Ns[g];
+    }
+    a.tiles_n = tile0;
+    // split-K partials: one workspace whose columns follow the launch's tile columns
+    const int64_t ldw = (int64_t)tile0 * ki.uN;
+    float* W = nullptr;
+    if (r.s > 1) {
+        void* ws = nullptr;
+        int rc = get_workspace(dev, st, kCounterBytes + (size_t)r.s * M * ldw * sizeof(float), &ws);
+        if (rc != MKP_OK) return rc;
+        W = (float*)((char*)ws + kCounterBytes);
+        a.C = W;
+        a.ldc = ldw;
+        a.sC = M * ldw;
+        a.sCsplit = M * ldw;
+        a.flags |= KF_VEC_C;
+    }
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
+    if (grid > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
+    he = traced(L, st, r.lib, flops, bytes, [&] { return ki.launch(a, dim3((unsigned)grid), st); });
+    if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
+    L.launches.fetch_add(1, std::memory_order_relaxed);
+    if (r.s > 1) {
+        for (size_t i = 0; i < live.size(); ++i) {
+            const KGroup& G_ = a.group[i];
+            he = traced(L, st, -1, 0.0, (double)(r.s + 1) * 4.0 * M * G_.N, [&] {
+                return launch_splitk_reduce(W + (int64_t)G_.tile0 * ki.uN, r.s, M * ldw, 0, ldw, G_.C, G_.ldc, 0,
+                                            (int)M, G_.N, 1, (G_.flags & KF_VEC_C) ? 1 : 0, st);
+            });
+            if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
+            L.launches.fetch_add(1, std::memory_order_relaxed);
+        }
+    }
+    return MKP_OK;
+}
+
 int write_out(const std::string& s, char* buf, size_t len) {
     if (!buf || len == 0) return fail(MKP_ERR_BUFFER, "output buffer is empty");
     if (s.size() + 1 > len) {
@@ -591,6 +733,36 @@ int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K, const vo
                         int64_t strideA, const void* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc,
                         int64_t strideC, void* stream) {
     return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream, true);
+}
+
+int mkp_gemm_grouped(int64_t groups, int64_t M, int64_t K, const void* A, int64_t lda, const int64_t* N,
+                     const void* const* B, const int64_t* ldb, float* const* C, const int64_t* ldc, void* stream) {
+    return run_grouped(groups, M, K, A, lda, N, B, ldb, C, ldc, stream, false);
+}
+
+int mkp_gemm_grouped_bt(int64_t groups, int64_t M, int64_t K, const void* A, int64_t lda, const int64_t* N,
+                        const void* const* B, const int64_t* ldb, float* const* C, const int64_t* ldc,
+                        void* stream) {
+    return run_grouped(groups, M, K, A, lda, N, B, ldb, C, ldc, stream, true);
+}
+
+int mkp_plan_describe_grouped(int64_t groups, int64_t M, int64_t K, const int64_t* N, int flags, char* buf,
+                              size_t len) {
+    if (groups < 1 || groups > kMaxGroups || !N) return fail(MKP_ERR_INVALID_ARG, "bad group count or widths");
+    if (M < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
+    std::vector<int64_t> widths;
+    for (int64_t g = 0; g < groups; ++g) {
+        if (N[g] < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
+        if (N[g] > 0) widths.push_back(N[g]);
+    }
+    ensure_init();
+    Library& L = lib();
+    std::shared_lock<std::shared_mutex> lk(L.mu);
+    SearchOptions o = L.opts;
+    o.bt = (flags & MKP_PLAN_B_NK) != 0;
+    Plan p;
+    if (M > 0 && K > 0 && !widths.empty()) p = polymerize_grouped(L.table, M, K, widths, o);
+    return write_out(plan_to_json(p, L.table), buf, len);
 }
 
 int mkp_plan_describe(int64_t batch, int64_t M, int64_t N, int64_t K, int align_flags, char* buf, size_t len) {
@@ -695,6 +867,7 @@ int mkp_set_option(const char* key, const char* value) {
         return fail(MKP_ERR_INVALID_ARG, "unknown option " + k);
     }
     L.cache.clear();
+    L.gcache.clear();
     return MKP_OK;
 }
 
@@ -711,6 +884,7 @@ void mkp_cache_clear(void) {
         Library& L = lib();
         std::unique_lock<std::shared_mutex> lk(L.mu);
         L.cache.clear();
+    L.gcache.clear();
     }
     free_workspaces();
 }
@@ -1014,6 +1188,7 @@ int mkp_calibrate(const char* path, int max_points) {
     L.table_origin = path;
     L.opts.force_kernel = -1;
     L.cache.clear();
+    L.gcache.clear();
     return MKP_OK;
 }
 

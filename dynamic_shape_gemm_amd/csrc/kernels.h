@@ -19,6 +19,18 @@ enum : int {
     KF_VEC_COUT = 8,  // final C rows (fused split-K) 16-byte aligned
 };
 
+// One group of a grouped call: C_g = A . B_g over the tile columns
+// [tile0, tile0 + ceil(N / uN)) of the launch (groups share A and K).
+struct KGroup {
+    const uint16_t* B;
+    float* C;
+    int64_t ldb, ldc;
+    int N;
+    int tile0;
+    int flags;   // this group's KF_VEC_B / KF_VEC_C bits
+};
+enum : int { kMaxGroups = 4 };
+
 struct KArgs {
     const uint16_t* A;    // region origin in A (row m0, column 0)
     const uint16_t* B;    // B (row 0, column 0 of a K x N matrix, or of an N x K one); the kernel adds n0
@@ -39,6 +51,12 @@ struct KArgs {
     int* counters;
     float* Cout;
     int64_t ldcout, sCout;
+    // Grouped call (ngroups > 0, batch 1, no fused reduction): tile columns
+    // are dealt group after group; B, N and (with one split) C, ldc come from
+    // the tile's group.  With several splits C above is the partial
+    // workspace, whose columns follow the launch's tile columns.
+    int ngroups;
+    KGroup group[kMaxGroups];
 };
 
 struct KernelInfo {

@@ -50,8 +50,6 @@ template <int BK>
 __device__ __forceinline__ int swzA(int row);
 template <>
 __device__ __forceinline__ int swzA<64>(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-template <>
-__device__ __forceinline__ int swzA<128>(int row) { return row & 15; }
 
 // B rows (uN*2 bytes) are XOR swizzled in 32-byte segments so that one
 // transposed read never hits a 32-byte bank window twice in a 32-lane pass.
@@ -407,6 +405,27 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
 
     int tm, tn, split, b;
     map_tile<8>(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, args.splits, tm, tn, split, b);
+    if (args.ngroups > 0) {
+        // grouped call: switch to the B, N and C of the tile column's group
+        // (constant indices only, so the argument block stays in registers)
+        KGroup G = args.group[0];
+#pragma unroll
+        for (int i = 1; i < kMaxGroups; ++i)
+            if (i < args.ngroups && tn >= args.group[i].tile0) G = args.group[i];
+        tn -= G.tile0;
+        args.B = G.B;
+        args.ldb = G.ldb;
+        args.N = G.N;
+        args.flags = (args.flags & ~KF_VEC_B) | (G.flags & KF_VEC_B);
+        if (args.splits == 1) {
+            args.C = G.C;
+            args.ldc = G.ldc;
+            args.flags = (args.flags & ~KF_VEC_C) | (G.flags & KF_VEC_C);
+        } else {
+            args.C += (int64_t)G.tile0 * T::BN;   // the group's workspace columns
+        }
+        args.counters = nullptr;
+    }
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     TileCtx c;
     c.A = args.A + (int64_t)b * args.sA + (int64_t)m0 * args.lda;

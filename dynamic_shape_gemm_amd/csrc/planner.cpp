@@ -545,6 +545,63 @@ Plan polymerize(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64
     return p;
 }
 
+Plan polymerize_grouped(const PerfTable& tab, int64_t M, int64_t K, const std::vector<int64_t>& Ns,
+                        const SearchOptions& opt) {
+    auto t0 = std::chrono::steady_clock::now();
+    Plan best;
+    best.pattern = PAT_I;
+    best.cost_us = std::numeric_limits<double>::infinity();
+    int64_t Nsum = 0;
+    for (int64_t n : Ns) Nsum += n;
+    std::vector<int> req;
+    if (opt.force_splitk > 0) {
+        req.push_back(opt.force_splitk);
+    } else {
+        for (int s : tab.splits)
+            if (s <= opt.splitk_max) req.push_back(s);
+        if (req.empty()) req.push_back(1);
+    }
+    for (size_t ki = 0; ki < tab.kernels.size(); ++ki) {
+        const TableKernel& k = tab.kernels[ki];
+        if (k.bt != opt.bt || (opt.force_kernel >= 0 && opt.force_kernel != (int)ki)) continue;
+        const int64_t t3 = ceil_div(K, k.uK);
+        int64_t cols = 0;
+        for (int64_t n : Ns) cols += ceil_div(n, k.uN);
+        const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
+        for (int s_req : req) {
+            if (s_req > 1 && s_req > t3 && opt.force_splitk <= 0) continue;
+            const int64_t sr = std::min<int64_t>(s_req, std::max<int64_t>(t3, 1));
+            const int64_t per = ceil_div(t3, sr);
+            const int64_t s_eff = ceil_div(t3, per);
+            const int64_t tasks = ceil_div(M, k.uM) * cols * s_eff;
+            const double wf = wave_factor(k, tasks, slots);
+            double c = tab.launch_us + wf * g_predict(k, (double)per);
+            if (s_eff > 1)
+                for (int64_t n : Ns)
+                    c += tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)M * (double)n / (tab.red_gbps * 1e3);
+            ++best.evaluated;
+            if (c < best.cost_us) {
+                Region r;
+                r.m = M;
+                r.n = Nsum;
+                r.kernel = (int)ki;
+                r.lib = k.lib_index;
+                r.s = (int)s_eff;
+                r.steps = (int)per;
+                r.tasks = tasks;
+                r.waves = ceil_div(tasks, slots);
+                r.wave_factor = wf;
+                r.cost = c;
+                best.cost_us = c;
+                best.regions.assign(1, r);
+            }
+        }
+    }
+    auto t1 = std::chrono::steady_clock::now();
+    best.plan_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+    return best;
+}
+
 double transpose_cost(const PerfTable& tab, int64_t batch, int64_t N, int64_t K) {
     if (!(tab.tr_gbps > 0)) return std::numeric_limits<double>::infinity();
     return tab.tr_launch_us + 4.0 * (double)K * (double)N * (double)batch / (tab.tr_gbps * 1e3);

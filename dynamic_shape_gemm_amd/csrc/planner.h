@@ -112,6 +112,13 @@ double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64
 Plan polymerize(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_t K,
                 const SearchOptions& opt);
 
+// Grouped call C_g = A . B_g (g < G, shared A and K): Pattern I over the
+// tile columns of all groups -- one kernel and one split factor, tasks =
+// ceil(M/uM) * sum_g ceil(N_g/uN) * s, one launch, and with s > 1 one
+// reduction per group.
+Plan polymerize_grouped(const PerfTable& tab, int64_t M, int64_t K, const std::vector<int64_t>& Ns,
+                        const SearchOptions& opt);
+
 // Modelled time of transposing batch K x N bf16 matrices (reads and writes
 // 2*K*N bytes each); infinite when the table has no transpose figures.
 double transpose_cost(const PerfTable& tab, int64_t batch, int64_t N, int64_t K);

@@ -107,6 +107,35 @@ int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K,
                         void *stream);
 
 /*
+ * Grouped call: C_g[M x N_g] := A[M x K] . B_g for g < groups (1..4), the
+ * products sharing A -- the merge of GEMMs that share an operand into one
+ * product with the other operands side by side (BladeDISC page, GEMM merge,
+ * first kind; e.g. the query, key and value projections of one input).  N, B, ldb, C, ldc are host arrays of
+ * `groups` entries; B_g is K x N_g (ldb_g >= N_g).  One launch serves every
+ * group: its tile columns are dealt group after group, so the widths need
+ * not be tile multiples; the plan (one kernel and split factor over all
+ * groups' tiles) is cached by M, K and the widths.  Groups with N_g == 0
+ * are skipped; errors as for mkp_gemm, before anything is written.
+ */
+int mkp_gemm_grouped(int64_t groups, int64_t M, int64_t K,
+                     const void *A, int64_t lda,
+                     const int64_t *N, const void *const *B, const int64_t *ldb,
+                     float *const *C, const int64_t *ldc,
+                     void *stream);
+
+/* As mkp_gemm_grouped with each B_g given as N_g x K (ldb_g >= K). */
+int mkp_gemm_grouped_bt(int64_t groups, int64_t M, int64_t K,
+                        const void *A, int64_t lda,
+                        const int64_t *N, const void *const *B, const int64_t *ldb,
+                        float *const *C, const int64_t *ldc,
+                        void *stream);
+
+/* The plan of a grouped call (JSON as mkp_plan_describe; one region spanning
+ * the sum of the widths).  flags: MKP_PLAN_B_NK for mkp_gemm_grouped_bt. */
+int mkp_plan_describe_grouped(int64_t groups, int64_t M, int64_t K, const int64_t *N, int flags,
+                              char *buf, size_t len);
+
+/*
  * Describe the plan the polymerizer picks for a shape, without launching.
  * align_flags: bit0 = A rows 16-byte aligned, bit1 = B rows, bit2 = C rows
  * (pass 7 for aligned operands); MKP_PLAN_B_NK plans for mkp_gemm_bt.

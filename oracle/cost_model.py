@@ -310,6 +310,37 @@ def covers_exactly(M: int, N: int, regions: Sequence[Region], tiles: Dict[str, T
     return bool((cnt == 1).all())
 
 
+def grouped_cost(tab: Table, kernel: str, s: int, M: int, K: int, Ns: Sequence[int]) -> float:
+    """Modelled time of one launch computing A.B_g for every width N_g in Ns
+    (BladeDISC page, GEMM merge of the first kind: products that share A
+    run as A times the B_g placed side by side).  The launch holds every
+    group's tiles: sum over g of ceil(M/uM) * ceil(N_g/uN) * s_eff tasks, one
+    wave term and one g_predict over them (MikPoly page, section 3 cost, one
+    Pattern I region); with split-K each group has its own reduction."""
+    k = tab.kernels[kernel]
+    t3 = ceil_div(K, k.uK)
+    per, s_eff = split_steps(t3, s)
+    columns = sum(ceil_div(n, k.uN) for n in Ns)
+    tasks = ceil_div(M, k.uM) * columns * s_eff
+    c = tab.launch_us + wave_term(k, tasks, tab.slots(k)) * g_predict(k, per)
+    if s_eff > 1:
+        for n in Ns:
+            c += tab.red_launch_us + (2 * s_eff + 1) * 4.0 * M * n / (tab.red_gbps * 1e3)
+    return c
+
+
+def grouped_best(tab: Table, M: int, K: int, Ns: Sequence[int], bt: bool = False):
+    """(cost, kernel, split) minimising grouped_cost over the kernels of the
+    call's B layout and every split factor, by enumeration."""
+    best = None
+    for name in sorted(n for n, k in tab.kernels.items() if k.bt == bt):
+        for s in _valid_splits(tab, tab.kernels[name], K):
+            c = grouped_cost(tab, name, s, M, K, Ns)
+            if best is None or c < best[0]:
+                best = (c, name, s)
+    return best
+
+
 def transpose_cost(tab: Table, batch: int, N: int, K: int) -> float:
     """Modelled time of copying a K x N B to N x K (infinite without figures)."""
     if tab.tr_gbps <= 0:

@@ -147,3 +147,46 @@ def test_shipped_table_loads(mkp):
     text = open(table).read()
     listed = {line.split()[1] for line in text.splitlines() if line.startswith("kernel ")}
     assert listed == names
+
+
+def test_grouped_argument_errors(mkp):
+    """Bad grouped calls are refused on the host before any launch (no GPU
+    needed: every check precedes the first device call)."""
+    fake = 1 << 20  # never dereferenced: each call fails its checks first
+    ok = dict(M=64, K=64, A=fake, lda=64, N=[64, 32], B=[fake, fake], ldb=[64, 32], C=[fake, fake], ldc=[64, 32])
+
+    def call(bt=False, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return mkp.mkp_gemm_grouped_raw(a["M"], a["K"], a["A"], a["lda"], a["N"], a["B"], a["ldb"], a["C"],
+                                        a["ldc"], 0, bt=bt)
+
+    E = mkp.MKP_ERR_INVALID_ARG
+    assert call(N=[64] * 5, B=[fake] * 5, ldb=[64] * 5, C=[fake] * 5, ldc=[64] * 5) == E   # > 4 groups
+    assert call(N=[], B=[], ldb=[], C=[], ldc=[]) == E
+    assert call(M=-1) == E
+    assert call(N=[64, -1]) == E
+    assert call(ldb=[64, 31]) == E          # ldb < N
+    assert call(ldc=[63, 32]) == E          # ldc < N
+    assert call(lda=63) == E                # lda < K
+    assert call(A=0) == E
+    assert call(B=[fake, 0]) == E
+    assert call(C=[0, fake]) == E
+    assert call(bt=True, ldb=[64, 63]) == E  # N x K: ldb < K
+    assert "ldb" in mkp.last_error()
+    # nothing to do: no launch, success
+    assert call(M=0) == mkp.MKP_OK
+    assert call(N=[0, 0]) == mkp.MKP_OK
+    with pytest.raises(ValueError):
+        mkp.mkp_gemm_grouped(64, 64, fake, 64, [64], [fake, fake], [64], [fake], [64], stream=0)
+
+
+def test_grouped_plan_describe(mkp):
+    p = mkp.mkp_plan_describe_grouped(4096, 768, [768, 768, 768], bt=True)
+    (r,) = p["regions"]
+    assert r["n"] == 3 * 768 and r["kernel"].endswith("_nk")
+    p = mkp.mkp_plan_describe_grouped(100, 300, [5, 0, 700])
+    assert p["regions"][0]["n"] == 705 and not p["regions"][0]["kernel"].endswith("_nk")
+    assert mkp.mkp_plan_describe_grouped(0, 300, [5])["regions"] == []
+    with pytest.raises(mkp.MkpError):
+        mkp.mkp_plan_describe_grouped(10, 10, [1, 2, 3, 4, 5])

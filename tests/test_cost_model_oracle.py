@@ -194,3 +194,83 @@ def test_transpose_cost_closed_form():
     tab0 = cm.parse_table("device 4\nkernel k 16 16 16 1\ng k 1:1\n")
     assert cm.transpose_cost(tab0, 1, 64, 64) == float("inf")
     assert cm.best_call(tab0, 64, 64, 64)[1] is False
+
+
+# ---- grouped calls (BladeDISC page, GEMM merge of the first kind) ----------
+
+def _grouped_table(cus=3, wg=2, launch=1.5, red=(0.7, 900.0)):
+    return cm.parse_table(f"""device {cus}
+launch_us {launch}
+splitk 1 2 4
+reduce {red[0]} {red[1]}
+kernel a 64 64 32 {wg}
+kernel b 32 128 32 1
+kernel c 128 256 32 1
+g a 1:0.9 4:2.0 16:6.5
+g b 1:0.5 4:1.7 16:5.0
+g c 1:2.0 4:4.5 16:13.0
+tail a 0.25:0.4 0.5:0.7
+tailx a 0.5:0.6
+""")
+
+
+def test_grouped_equals_concatenated_gemm_for_tile_multiples():
+    """Merging products that share A is the product with the B_g side by
+    side: when every width is a multiple of every kernel's uN, the grouped
+    launch has exactly the tasks of one GEMM of width sum(N_g), so its cost
+    is that Pattern I region's, plus one more reduction launch per extra
+    group when split."""
+    tab = _grouped_table()
+    for Ns in ([256], [256, 512], [768, 256, 256], [256, 256, 256, 1024]):
+        for M, K in ((64, 96), (300, 512), (1000, 40)):
+            for name in tab.kernels:
+                for s in (1, 2, 4):
+                    g = cm.grouped_cost(tab, name, s, M, K, Ns)
+                    one = cm.region_cost(tab, cm.Region(0, 0, M, sum(Ns), name, s), K, 1)
+                    s_eff = cm.split_steps(cm.ceil_div(K, tab.kernels[name].uK), s)[1]
+                    extra = (len(Ns) - 1) * tab.red_launch_us if s_eff > 1 else 0.0
+                    assert g == pytest.approx(one + extra, rel=1e-12), (Ns, M, K, name, s)
+
+
+def test_grouped_single_group_is_pattern_one():
+    tab = _grouped_table()
+    for M, N, K in ((1, 1, 1), (77, 130, 200), (513, 37, 4096)):
+        for name in tab.kernels:
+            for s in (1, 2, 4):
+                assert cm.grouped_cost(tab, name, s, M, K, [N]) == pytest.approx(
+                    cm.region_cost(tab, cm.Region(0, 0, M, N, name, s), K, 1), rel=1e-12)
+
+
+def test_grouped_task_count_by_brute_force():
+    """With one slot, no launch cost and g = 1 per wave at one K step, the
+    cost is the task count; count the tiles by walking every output element
+    of every group and collecting the distinct (group, tile row, tile col)."""
+    tab = cm.parse_table("""device 1
+launch_us 0
+splitk 1
+reduce 0 1
+kernel k 48 40 64 1
+g k 1:1 2:2
+""")
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        M = int(rng.integers(1, 120))
+        Ns = [int(x) for x in rng.integers(1, 150, size=int(rng.integers(1, 5)))]
+        tiles = set()
+        for g, n in enumerate(Ns):
+            for i in range(M):
+                for j in range(n):
+                    tiles.add((g, i // 48, j // 40))
+        assert cm.grouped_cost(tab, "k", 1, M, 64, Ns) == pytest.approx(len(tiles)), (M, Ns)
+
+
+def test_grouped_best_is_minimum_over_enumeration():
+    tab = _grouped_table()
+    rng = np.random.default_rng(17)
+    for _ in range(30):
+        M, K = (int(x) for x in rng.integers(1, 700, size=2))
+        Ns = [int(x) for x in rng.integers(1, 700, size=int(rng.integers(1, 5)))]
+        best = cm.grouped_best(tab, M, K, Ns)
+        costs = [cm.grouped_cost(tab, n, s, M, K, Ns) for n in tab.kernels for s in (1, 2, 4)
+                 if s <= max(cm.ceil_div(K, tab.kernels[n].uK), 1)]
+        assert best[0] == pytest.approx(min(costs), rel=1e-12)

@@ -396,3 +396,59 @@ def test_transposed_b_path(mkp):
     finally:
         mkp.mkp_set_option("transpose_b", 1)
         mkp.mkp_set_option("force_splitk", 0)
+
+
+def test_concurrent_callers_on_separate_streams(mkp):
+    """Two host threads call the library at once, each on its own stream with
+    its own shapes (split-K workspaces are per stream, the plan cache is
+    shared): every result matches the oracle."""
+    import threading
+
+    import torch
+
+    rng = np.random.default_rng(99)
+    jobs = []
+    for t in range(2):
+        cases = []
+        for i in range(6):
+            M, N, K = int(rng.integers(50, 700)), int(rng.integers(50, 700)), int(rng.integers(64, 3000))
+            cases.append((rand_bits(rng, (M, K)), rand_bits(rng, (K, N))))
+        jobs.append(cases)
+    results = [[None] * 6 for _ in range(2)]
+    errors = []
+    print("[case] two threads, two streams", flush=True)
+
+    def worker(t):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                outs = []
+                for i, (a, b) in enumerate(jobs[t]):
+                    M, K = a.shape
+                    N = b.shape[1]
+                    ta, pa = dev_bf16(a)
+                    tb, pb = dev_bf16(b)
+                    tc = torch.empty((M, N), dtype=torch.float32, device="cuda")
+                    for _ in range(3):   # repeated calls: cache hits and workspace reuse
+                        mkp.mkp_gemm(M, N, K, pa, K, pb, N, tc, N, stream.cuda_stream)
+                    outs.append((ta, tb, tc))
+                stream.synchronize()
+                for i, (_, _, tc) in enumerate(outs):
+                    results[t][i] = tc.cpu().numpy().astype(np.float64)
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    try:
+        mkp.mkp_set_option("force_splitk", 4)
+        threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+    finally:
+        mkp.mkp_set_option("force_splitk", 0)
+    assert not errors, errors
+    for t in range(2):
+        for i, (a, b) in enumerate(jobs[t]):
+            ref, refabs = oracle.gemm(a, b, with_abs=True)
+            assert_close(results[t][i], ref, refabs, a.shape[1], f"thread {t} case {i}")

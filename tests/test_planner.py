@@ -260,3 +260,66 @@ def test_transpose_then_nk_choice_matches_oracle(mkp):
             assert plan["transpose_us"] == pytest.approx(cm.transpose_cost(tab, 1, N, K), rel=1e-9)
         chosen[transposed] += 1
     assert chosen[True] > 0 and chosen[False] > 0
+
+
+SHIPPED = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "dynamic_shape_gemm_amd", "calib", "gfx950.tbl")
+
+
+def _check_grouped(mkp, tab, M, K, Ns, bt):
+    plan = mkp.mkp_plan_describe_grouped(M, K, Ns, bt=bt)
+    best = cm.grouped_best(tab, M, K, Ns, bt=bt)
+    assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (M, K, Ns, bt)
+    (r,) = plan["regions"]
+    assert r["n"] == sum(Ns) and r["m"] == M
+    assert tab.kernels[r["kernel"]].bt == bt
+    # the chosen (kernel, split) is priced by the oracle at the same cost
+    assert cm.grouped_cost(tab, r["kernel"], r["s"], M, K, Ns) == pytest.approx(plan["cost_us"], rel=1e-9)
+
+
+def test_grouped_plan_matches_oracle_on_shipped_table(mkp):
+    """Grouped calls (BladeDISC page, GEMM merge of the first kind) are
+    planned as one launch over every group's tiles; the library's choice
+    is the oracle's minimum over kernels x splits."""
+    mkp.mkp_load_calibration(None)
+    tab = cm.parse_table(open(SHIPPED).read())
+    rng = np.random.default_rng(8)
+    for _ in range(40):
+        M = int(rng.choice([1, 16, 100, 512, 2048, 8192]))
+        K = int(rng.choice([64, 200, 768, 1024, 4096]))
+        Ns = [int(x) for x in rng.integers(1, 5000, size=int(rng.integers(1, 5)))]
+        for bt in (False, True):
+            _check_grouped(mkp, tab, M, K, Ns, bt)
+    # the attention projections of a 768-wide model
+    for M in (128, 4096):
+        _check_grouped(mkp, tab, M, 768, [768, 768, 768], True)
+
+
+def test_grouped_plan_matches_oracle_on_random_tables(mkp, tmp_path):
+    shipped = cm.parse_table(open(SHIPPED).read())
+    rng = np.random.default_rng(44)
+    try:
+        for trial in range(12):
+            lines = [f"device {int(rng.integers(4, 300))}", f"launch_us {rng.uniform(0, 3):.3f}",
+                     "splitk 1 2 3 4 8", f"reduce {rng.uniform(0, 2):.3f} {rng.uniform(100, 20000):.1f}"]
+            for name, k in shipped.kernels.items():
+                lines.append(f"kernel {name} {k.uM} {k.uN} {k.uK} {int(rng.integers(1, 3))} "
+                             f"{'nk' if k.bt else 'kn'}")
+                base, slope = rng.uniform(1, 20), rng.uniform(0.1, 3)
+                lines.append(f"g {name} " + " ".join(f"{t}:{base + slope * t * rng.uniform(0.9, 1.1):.4f}"
+                                                      for t in (1, 4, 16, 64)))
+                if trial % 2:
+                    fs = sorted(rng.uniform(0.05, 0.95, size=2))
+                    lines.append(f"tail {name} " + " ".join(f"{f:.3f}:{rng.uniform(0.1, 1):.3f}" for f in fs))
+                    lines.append(f"tailx {name} " + " ".join(f"{f:.3f}:{rng.uniform(0.1, 1):.3f}" for f in fs))
+            text = "\n".join(lines) + "\n"
+            path = tmp_path / f"t{trial}.tbl"
+            path.write_text(text)
+            mkp.mkp_load_calibration(str(path))
+            tab = cm.parse_table(text)
+            for _ in range(6):
+                M, K = (int(x) for x in rng.integers(1, 3000, size=2))
+                Ns = [int(x) for x in rng.integers(1, 3000, size=int(rng.integers(1, 5)))]
+                _check_grouped(mkp, tab, M, K, Ns, bool(rng.integers(0, 2)))
+    finally:
+        mkp.mkp_load_calibration(None)
