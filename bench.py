@@ -43,11 +43,18 @@ def log(msg):
 class Workload:
     """Device-resident operands for one sweep of a config."""
 
-    def __init__(self, cfg: int, copies: int = 1, b_layout: str = "kn", qkv: str = "merged"):
+    def __init__(self, cfg: int, copies: int = 1, b_layout: str = "kn", qkv: str = "merged",
+                 epilogue: str = "none"):
         import torch
         import workloads
 
         self.cfg = cfg
+        # epilogue: none; bias = every GEMM adds a bias vector; bias_gelu = and
+        # the FFN-up GEMMs (N = 3072) apply GELU, fused into the GEMM;
+        # bias_gelu_unfused = the same done by separate elementwise passes
+        # after the GEMM (torch), for comparison
+        self.epilogue = epilogue
+        self.biases = {}
         # the query/key/value projection (N = 3 x 768 of the encoder linears):
         # merged = one call over the side-by-side weights; grouped = one
         # grouped call over three 768-wide weights; separate = three calls
@@ -81,6 +88,13 @@ class Workload:
             self.host.append((case, a, b))
         self.flops = sum(c.flops for c in self.cases)
         self.bytes = sum(c.bytes for c in self.cases)
+        if epilogue != "none":
+            if cfg != 2:
+                raise SystemExit("--epilogue applies to the encoder linears (config 2)")
+            rng = np.random.default_rng(202)
+            for case in self.cases:
+                if case.N not in self.biases:
+                    self.biases[case.N] = torch.from_numpy(rng.uniform(-1, 1, case.N).astype(np.float32)).cuda()
 
     def _dev_b(self, torch, b):
         t = torch.from_numpy(b.view(np.int16)).cuda()
@@ -108,9 +122,28 @@ class Workload:
             for g in range(3):
                 fn(M, n, K, pa, K, pbs[g], ldb, pcs[g], case.N, stream)
 
+    def _epilogue_step(self, mkp, case, pa, pb, tc, stream):
+        import torch
+
+        act = "gelu" if self.epilogue.startswith("bias_gelu") and case.N == 3072 else "none"
+        bias = self.biases[case.N]
+        if self.epilogue.endswith("_unfused"):
+            if self.bt:
+                mkp.mkp_gemm_bt(case.M, case.N, case.K, pa, case.K, pb, case.K, tc, case.N, stream)
+            else:
+                mkp.mkp_gemm(case.M, case.N, case.K, pa, case.K, pb, case.N, tc, case.N, stream)
+            tc.add_(bias)
+            if act == "gelu":
+                tc.copy_(torch.nn.functional.gelu(tc))
+            return
+        mkp.mkp_gemm_ex(1, case.M, case.N, case.K, pa, case.K, 0, pb, case.K if self.bt else case.N, 0,
+                        mkp.MKP_B_NK if self.bt else mkp.MKP_B_KN, tc, case.N, 0, 1.0, 0.0, bias, act, stream)
+
     def step(self, mkp, stream):
         for case, pa, pb, tc in self.calls:
-            if self.is_qkv(case):
+            if self.epilogue != "none":
+                self._epilogue_step(mkp, case, pa, pb, tc, stream)
+            elif self.is_qkv(case):
                 self._qkv_step(mkp, case, pa, pb, tc, stream)
             elif self.bt:
                 mkp.mkp_gemm_batched_bt(case.batch, case.M, case.N, case.K, pa, case.K, case.M * case.K, pb, case.K,
@@ -265,6 +298,9 @@ def main():
     ap.add_argument("--qkv", choices=["merged", "grouped", "separate"], default="merged",
                     help="encoder linears: run the query/key/value projection as one call (default), "
                          "one grouped call over three weights, or three calls")
+    ap.add_argument("--epilogue", choices=["none", "bias", "bias_gelu", "bias_gelu_unfused"], default="none",
+                    help="encoder linears with a bias on every GEMM (and GELU on the FFN-up GEMMs), fused into the "
+                         "GEMM epilogue or, for comparison, as separate passes")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of MiB (to scale rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -283,7 +319,9 @@ def main():
 
     torch.cuda.set_device(0)
     log(f"[bench] generating config {args.config} inputs")
-    wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv)
+    if args.epilogue != "none" and args.qkv != "merged":
+        raise SystemExit("--epilogue and --qkv are separate experiments")
+    wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv, epilogue=args.epilogue)
     stream = torch.cuda.current_stream().cuda_stream
     mkp.mkp_cache_clear()
 
@@ -361,6 +399,7 @@ def main():
             "config_index": args.config,
             "b_layout": args.b_layout,
             "qkv": wl.qkv,
+            "epilogue": wl.epilogue,
             "gemms_per_step": len(wl.cases),
             "flops_per_step": wl.flops,
             "bytes_per_step": wl.bytes,

@@ -25,6 +25,15 @@ MKP_ERR_HIP = -4
 MKP_ERR_BUFFER = -5
 MKP_PLAN_EXHAUSTIVE = 1
 MKP_PLAN_B_NK = 8
+MKP_B_KN = 0
+MKP_B_NK = 1
+MKP_ACT_NONE = 0
+MKP_ACT_RELU = 1
+MKP_ACT_GELU = 2
+MKP_ACT_GELU_TANH = 3
+MKP_ACT_SILU = 4
+ACTIVATIONS = {None: MKP_ACT_NONE, "none": MKP_ACT_NONE, "relu": MKP_ACT_RELU, "gelu": MKP_ACT_GELU,
+               "gelu_tanh": MKP_ACT_GELU_TANH, "silu": MKP_ACT_SILU}
 
 
 class MkpError(RuntimeError):
@@ -56,6 +65,9 @@ _lib.mkp_gemm_bt.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.mkp_gemm_bt.restype = _int
 _lib.mkp_gemm_batched_bt.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
 _lib.mkp_gemm_batched_bt.restype = _int
+_lib.mkp_gemm_ex.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _int, _p, _i64, _i64,
+                             ctypes.c_float, ctypes.c_float, _p, _int, _p]
+_lib.mkp_gemm_ex.restype = _int
 _grp_args = [_i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p]
 _lib.mkp_gemm_grouped.argtypes = _grp_args
 _lib.mkp_gemm_grouped.restype = _int
@@ -86,7 +98,7 @@ _lib.mkp_trace_dump.restype = _int
 _lib.mkp_last_error.argtypes = []
 _lib.mkp_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_grouped",
+EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_ex", "mkp_gemm_grouped",
             "mkp_gemm_grouped_bt", "mkp_plan_describe", "mkp_plan_describe_grouped", "mkp_plan_with_table",
             "mkp_load_calibration",
             "mkp_calibrate", "mkp_set_option", "mkp_kernel_count", "mkp_kernel_name", "mkp_cache_clear",
@@ -159,6 +171,22 @@ def mkp_gemm_bt_raw(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 def mkp_gemm_batched_bt_raw(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream) -> int:
     return _lib.mkp_gemm_batched_bt(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC,
                                     stream or 0)
+
+
+def mkp_gemm_ex(batch, M, N, K, A, lda, strideA, B, ldb, strideB, b_layout, C, ldc, strideC,
+                alpha=1.0, beta=0.0, bias=None, act=MKP_ACT_NONE, stream=None) -> int:
+    """C_b := act(alpha * A_b . op(B_b) + beta * C_b + bias) with op(B) = B
+    (b_layout MKP_B_KN) or B^T (MKP_B_NK); act an MKP_ACT_* code or name."""
+    return _check(mkp_gemm_ex_raw(batch, M, N, K, A, lda, strideA, B, ldb, strideB, b_layout, C, ldc, strideC,
+                                  alpha, beta, bias, act, _stream(stream)))
+
+
+def mkp_gemm_ex_raw(batch, M, N, K, A, lda, strideA, B, ldb, strideB, b_layout, C, ldc, strideC,
+                    alpha, beta, bias, act, stream) -> int:
+    if not isinstance(act, int):
+        act = ACTIVATIONS[act]
+    return _lib.mkp_gemm_ex(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB, b_layout, _addr(C), ldc,
+                            strideC, alpha, beta, _addr(bias), act, stream or 0)
 
 
 def _i64_array(values):
@@ -317,3 +345,30 @@ def gemm_grouped(a, ws, outs=None, stream=None, bt=False):
     fn(M, K, a, max(a.stride(0), 1), Ns, ws, [max(w.stride(0), 1) for w in ws], outs,
        [max(o.stride(0), 1) for o in outs], stream)
     return outs
+
+
+def linear(a, w, bias=None, act=None, out=None, beta=0.0, stream=None):
+    """torch convenience for a linear layer: out = act(a . w^T + bias (+ beta
+    * out)), a (M,K) bf16, w (N,K) bf16 (the layer's weight), bias (N,) fp32
+    or None, act None/"relu"/"gelu"/"gelu_tanh"/"silu"; all in one launch
+    sequence of the library (the epilogue runs inside the GEMM)."""
+    import torch
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("a and w must be bfloat16")
+    if bias is not None and (bias.dtype != torch.float32 or bias.stride(0) != 1):
+        raise TypeError("bias must be a contiguous float32 vector")
+    if a.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("rows must be contiguous (unit column stride)")
+    M, K = a.shape
+    N, K2 = w.shape
+    if K2 != K or (bias is not None and bias.shape[0] != N):
+        raise ValueError("shapes differ")
+    if out is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs out")
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    mkp_gemm_ex(1, M, N, K, a, max(a.stride(0), 1), 0, w, max(w.stride(0), 1), 0, MKP_B_NK, out,
+                max(out.stride(0), 1), 0, 1.0, beta, bias, act, stream)
+    return out

@@ -353,9 +353,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // C = A . B with B given as K x N (bt false) or as N x K (bt true, C = A . B^T
 // of the stored matrix).
+// With `epi` (non-null) every final value goes through the fused epilogue.
 int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int64_t lda, int64_t sA,
              const void* Bv, int64_t ldb, int64_t sB, float* C, int64_t ldc, int64_t sC, void* stream_v,
-             bool bt = false) {
+             bool bt = false, const KEpi* epi = nullptr) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "dimension exceeds 2^31-1");
     if (batch == 0 || M == 0 || N == 0) return MKP_OK;
@@ -374,9 +375,21 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
 
     Library& L = lib();
+    // bytes the epilogue adds: the old C (beta != 0) and the bias vector
+    const double epi_bytes =
+        epi ? (epi->beta != 0.0f ? 4.0 * M * N * batch : 0.0) + (epi->bias ? 4.0 * N : 0.0) : 0.0;
     if (K == 0) {
-        he = traced(L, st, -2, 0.0, 4.0 * M * N * batch,
-                    [&] { return launch_zero_fill(C, ldc, sC, (int)M, (int)N, (int)batch, st); });
+        if (epi) {
+            // empty sum: C := act(beta * C + bias)
+            const bool vC0 = aligned16(C) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
+            he = traced(L, st, -2, 0.0, 4.0 * M * N * batch + epi_bytes, [&] {
+                return launch_splitk_reduce(nullptr, 0, 0, 0, 0, C, ldc, sC, (int)M, (int)N, (int)batch,
+                                            vC0 ? 1 : 0, st, epi);
+            });
+        } else {
+            he = traced(L, st, -2, 0.0, 4.0 * M * N * batch,
+                        [&] { return launch_zero_fill(C, ldc, sC, (int)M, (int)N, (int)batch, st); });
+        }
         if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("zero fill launch: ") + hipGetErrorString(he));
         L.launches.fetch_add(1, std::memory_order_relaxed);
         return MKP_OK;
@@ -516,17 +529,31 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         a.ldcout = ldc;
         a.sCout = sC;
         if (vC) a.flags |= KF_VEC_COUT;
+        // the epilogue's bias starts at the region's first column; it runs in
+        // the micro-kernel unless a second pass reduces the splits
+        KEpi e{};
+        if (epi) {
+            e = *epi;
+            if (e.bias) e.bias += r.n0;
+            if (r.s == 1 || fused) {
+                a.flags |= KF_EPI;
+                a.epi = e;
+            }
+        }
+        const double r_epi = epi ? (epi->beta != 0.0f ? 4.0 * r.m * r.n * batch : 0.0) + (epi->bias ? 4.0 * r.n : 0.0)
+                                 : 0.0;
         const int64_t G = (int64_t)a.tiles_m * a.tiles_n * a.splits * batch;
         if (G > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
         const double flops = 2.0 * r.m * r.n * K * batch;
-        const double bytes = (double)batch * (2.0 * r.m * K + 2.0 * K * r.n + 4.0 * r.m * r.n);
+        const double bytes = (double)batch * (2.0 * r.m * K + 2.0 * K * r.n + 4.0 * r.m * r.n) +
+                             ((a.flags & KF_EPI) ? r_epi : 0.0);
         he = traced(L, st, li, flops, bytes, [&] { return ki.launch(a, dim3((unsigned)G), st); });
         if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
         L.launches.fetch_add(1, std::memory_order_relaxed);
         if (r.s > 1 && !fused) {
-            he = traced(L, st, -1, 0.0, (double)(r.s + 1) * 4.0 * r.m * r.n * batch, [&] {
+            he = traced(L, st, -1, 0.0, (double)(r.s + 1) * 4.0 * r.m * r.n * batch + (epi ? r_epi : 0.0), [&] {
                 return launch_splitk_reduce(a.C, r.s, batch * r.m * ldw, r.m * ldw, ldw, Creg, ldc, sC,
-                                            (int)r.m, (int)r.n, (int)batch, vC ? 1 : 0, st);
+                                            (int)r.m, (int)r.n, (int)batch, vC ? 1 : 0, st, epi ? &e : nullptr);
             });
             if (he != hipSuccess)
                 return fail(MKP_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
@@ -733,6 +760,23 @@ int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K, const vo
                         int64_t strideA, const void* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc,
                         int64_t strideC, void* stream) {
     return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream, true);
+}
+
+static_assert(MKP_ACT_NONE == ACT_NONE && MKP_ACT_RELU == ACT_RELU && MKP_ACT_GELU == ACT_GELU &&
+                  MKP_ACT_GELU_TANH == ACT_GELU_TANH && MKP_ACT_SILU == ACT_SILU && ACT_COUNT == 5,
+              "activation codes of the C ABI and the kernels differ");
+
+int mkp_gemm_ex(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t strideA,
+                const void* B, int64_t ldb, int64_t strideB, int b_layout, float* C, int64_t ldc, int64_t strideC,
+                float alpha, float beta, const float* bias, int act, void* stream) {
+    if (b_layout != MKP_B_KN && b_layout != MKP_B_NK) return fail(MKP_ERR_INVALID_ARG, "b_layout must be 0 or 1");
+    if (act < 0 || act >= ACT_COUNT) return fail(MKP_ERR_INVALID_ARG, "unknown activation");
+    if (!std::isfinite(alpha) || !std::isfinite(beta)) return fail(MKP_ERR_INVALID_ARG, "alpha and beta must be finite");
+    const KEpi e{bias, alpha, beta, act};
+    // the identity epilogue is the plain product
+    const bool plain = alpha == 1.0f && beta == 0.0f && bias == nullptr && act == ACT_NONE;
+    return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream,
+                    b_layout == MKP_B_NK, plain ? nullptr : &e);
 }
 
 int mkp_gemm_grouped(int64_t groups, int64_t M, int64_t K, const void* A, int64_t lda, const int64_t* N,

@@ -17,6 +17,19 @@ enum : int {
     KF_VEC_B = 2,   // B rows 16-byte aligned
     KF_VEC_C = 4,   // C rows 16-byte aligned: 128-bit stores allowed
     KF_VEC_COUT = 8,  // final C rows (fused split-K) 16-byte aligned
+    KF_EPI = 16,      // apply the epilogue below to the final C values
+};
+
+// Fused epilogue (Bolt page, epilogue fusion, and its persistent-kernel
+// form D = alpha.A.W + beta.C): each final value becomes
+//   act(alpha * acc + beta * C_old + bias[n]),
+// C_old read from the output itself (only when beta != 0), bias indexed by
+// the region's column.  Split-K partials never see it: the reduction does.
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4, ACT_COUNT = 5 };
+struct KEpi {
+    const float* bias;   // region column 0 of the bias vector, or null
+    float alpha, beta;
+    int act;
 };
 
 // One group of a grouped call: C_g = A . B_g over the tile columns
@@ -57,6 +70,7 @@ struct KArgs {
     // workspace, whose columns follow the launch's tile columns.
     int ngroups;
     KGroup group[kMaxGroups];
+    KEpi epi;             // used when flags has KF_EPI
 };
 
 struct KernelInfo {
@@ -75,9 +89,11 @@ const KernelInfo& kernel_info(int i);
 int kernel_find(const char* name);
 
 // Sum of `splits` partials W[z] (z ascending) into C; W is [splits][batch][M][ldw].
+// With an epilogue (epi non-null) the sum goes through it; splits == 0 is an
+// empty sum (W unused), which with the epilogue serves K == 0.
 hipError_t launch_splitk_reduce(const float* W, int splits, int64_t sWsplit, int64_t sWbatch, int64_t ldw,
                                 float* C, int64_t ldc, int64_t sC, int M, int N, int batch, int vec,
-                                hipStream_t st);
+                                hipStream_t st, const KEpi* epi = nullptr);
 // C := 0 for batch matrices of M x N (K == 0: empty sum).
 hipError_t launch_zero_fill(float* C, int64_t ldc, int64_t sC, int M, int N, int batch, hipStream_t st);
 

@@ -44,6 +44,112 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_t;
 
+// ---- fused epilogue -------------------------------------------------------
+
+// Activations, branch-free on the native 2^x and reciprocal instructions.
+//   sigmoid(z) = 1 / (1 + e^-z)
+//   silu(x) = x sigmoid(x); the tanh form of GELU, x/2 (1 + tanh u), equals
+//   x sigmoid(2u) since (1 + tanh u) / 2 = sigmoid(2u)
+//   GELU, x Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf from Abramowitz &
+//   Stegun, Handbook of Mathematical Functions, formula 7.1.26 (absolute
+//   error <= 1.5e-7): for a >= 0, 1 - erf(a) = q(a) = P(t) e^{-a^2},
+//   t = 1 / (1 + p a), P a degree-5 polynomial without constant term; so
+//   1 + erf(x / sqrt 2) is q(|x| / sqrt 2) for x < 0 (no cancellation in the
+//   negative tail) and 2 - q for x >= 0.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
+__device__ __forceinline__ float gelu_erf_fast(float x) {
+    const float a = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
+    float poly = 1.061405429f;
+    poly = fmaf(poly, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    const float q = poly * t * __builtin_amdgcn_exp2f(-1.4426950408889634f * a * a);
+    return 0.5f * x * (x < 0.0f ? q : 2.0f - q);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_t(float v) {
+    if constexpr (ACT == ACT_RELU) return v > 0.0f ? v : 0.0f;
+    if constexpr (ACT == ACT_GELU) return gelu_erf_fast(v);
+    if constexpr (ACT == ACT_GELU_TANH)
+        return v * sigmoid_fast(2.0f * 0.79788456080286536f * (v + 0.044715f * v * v * v));
+    if constexpr (ACT == ACT_SILU) return v * sigmoid_fast(v);
+    return v;
+}
+
+__device__ __forceinline__ float act_apply(int act, float v) {
+    switch (act) {
+        case ACT_RELU: return act_t<ACT_RELU>(v);
+        case ACT_GELU: return act_t<ACT_GELU>(v);
+        case ACT_GELU_TANH: return act_t<ACT_GELU_TANH>(v);
+        case ACT_SILU: return act_t<ACT_SILU>(v);
+        default: return v;
+    }
+}
+
+// bias[n..n+3] (zeros past nvalid, or without a bias)
+__device__ __forceinline__ f32x4 load_bias4(const KEpi& e, int n, int nvalid) {
+    f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (e.bias != nullptr) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (r < nvalid) b[r] = e.bias[n + r];
+    }
+    return b;
+}
+
+// The output's current values at p[0..3] (zeros past nvalid); vec allows a
+// 128-bit read.
+__device__ __forceinline__ f32x4 read_old4(const float* p, bool vec, int nvalid) {
+    f32x4 old = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (vec && nvalid >= 4) {
+        old = *(const f32x4*)p;
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (r < nvalid) old[r] = p[r];
+    }
+    return old;
+}
+
+// Four consecutive values through the epilogue with the activation fixed at
+// compile time (no beta term).
+template <int ACT>
+__device__ __forceinline__ f32x4 epi_apply4_t(float alpha, f32x4 b4, f32x4 v) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = act_t<ACT>(fmaf(alpha, v[r], b4[r]));
+    return v;
+}
+
+// Four consecutive values through the epilogue, given the old output values
+// (used only when beta != 0) and the bias (load_bias4).
+__device__ __forceinline__ f32x4 epi_apply4(const KEpi& e, f32x4 old, f32x4 b4, f32x4 v) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float x = e.alpha * v[r];
+        if (e.beta != 0.0f) x += e.beta * old[r];
+        v[r] = act_apply(e.act, x + b4[r]);
+    }
+    return v;
+}
+
+// Four consecutive columns of one row at p (nvalid of them exist).
+__device__ __forceinline__ f32x4 epi4(const KEpi& e, const float* p, bool vec, int nvalid, f32x4 b4, f32x4 v) {
+    const f32x4 old = e.beta != 0.0f ? read_old4(p, vec, nvalid) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    return epi_apply4(e, old, b4, v);
+}
+
+__device__ __forceinline__ float epi1(const KEpi& e, const float* p, float bias, float v) {
+    float x = e.alpha * v;
+    if (e.beta != 0.0f) x += e.beta * *p;
+    return act_apply(e.act, x + bias);
+}
+
 // A rows (uK*2 bytes) are XOR swizzled in 16-byte chunks: the 16 rows one
 // fragment read touches land in 16 distinct 16-byte bank windows.
 template <int BK>
@@ -535,6 +641,14 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
                 if (n + r < c.Nr) p[r] = v[r];
         }
     };
+    // final values go through the fused epilogue (one split, or the fused
+    // reduction's sum; two-pass split-K leaves it to the reduction)
+    const bool epi = args.flags & KF_EPI;
+    auto emit4 = [&](float* base, int64_t ld, bool vec, int m, int n, f32x4 v) {
+        if (m >= c.Mr) return;
+        if (epi) v = epi4(args.epi, base + (int64_t)m * ld + n, vec, c.Nr - n, load_bias4(args.epi, n0 + n, c.Nr - n), v);
+        store4(base, ld, vec, m, n, v);
+    };
     // visit every (row, first column, 4 values) the lane holds
     auto for_each4 = [&](auto&& fn) {
 #pragma unroll
@@ -588,13 +702,29 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
             f32x4 sum = split == 0 ? own : *(const f32x4*)w;
             for (int z = 1; z < args.splits; ++z)
                 sum += z == split ? own : *(const f32x4*)(w + (int64_t)z * args.sCsplit);
-            store4(Co, args.ldcout, vecCo, m, n, sum);
+            emit4(Co, args.ldcout, vecCo, m, n, sum);
         });
         if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
     // Plain epilogue: the tile goes through LDS one fragment row at a time
     // so that every store instruction writes contiguous row segments.
+    const bool epi_here = epi && args.splits == 1;
+    const int col0 = wn * T::WTN;   // first tile column of this wave
+    constexpr int C4 = T::WTN / 4;  // 16-byte chunks per staged row
+    static_assert(64 % C4 == 0, "a lane's chunk column must not change across the store loop");
+    // with the epilogue, each lane's bias chunk is loaded once: its column is
+    // the same in every row it stores
+    f32x4 bias4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    float bias1[(T::WTN + 63) / 64] = {};
+    if (epi_here) {
+        const int cl = col0 + (lane % C4) * 4;
+        bias4 = load_bias4(args.epi, n0 + cl, c.Nr - cl);
+#pragma unroll
+        for (int c0 = 0; c0 < T::WTN; c0 += 64)
+            bias1[c0 / 64] = (args.epi.bias != nullptr && col0 + c0 + lane < c.Nr) ? args.epi.bias[n0 + col0 + c0 + lane]
+                                                                                  : 0.0f;
+    }
     __syncthreads();   // every wave is done with the K-loop stages
     float __attribute__((address_space(3)))* stg =
         (float __attribute__((address_space(3)))*)(smem + wave * T::EPI_WAVE_BYTES);
@@ -616,11 +746,62 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes land before its reads
         const int row0 = wm * T::WTM + i * T::MF;             // tile row of staged row 0
-        const int col0 = wn * T::WTN;
-        if (vecC) {
-            constexpr int C4 = T::WTN / 4;                    // 16-byte chunks per staged row
+        constexpr int ITS = (T::MF * C4 + 63) / 64;
+        if (vecC && epi_here && args.epi.beta == 0.0f) {
+            // no reads in this loop (a load would make the compiler wait for
+            // every earlier store, vmcnt counting both, before its use), and
+            // the activation chosen once, outside it
+            const int n = col0 + (lane % C4) * 4;
+            auto rows = [&](auto act_tag) {
+                constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll 1
-            for (int it = 0; it < (T::MF * C4 + 63) / 64; ++it) {
+                for (int it = 0; it < ITS; ++it) {
+                    const int id = it * 64 + lane;
+                    if ((T::MF * C4) % 64 == 0 || id < T::MF * C4) {
+                        const int r = id / C4;
+                        const f32x4 v =
+                            *(const f32x4 __attribute__((address_space(3)))*)(stg + r * T::EPI_LD + (n - col0));
+                        if (row0 + r < c.Mr)
+                            store4(C, args.ldc, true, row0 + r, n, epi_apply4_t<ACT>(args.epi.alpha, bias4, v));
+                    }
+                }
+            };
+            switch (args.epi.act) {
+                case ACT_RELU: rows(std::integral_constant<int, ACT_RELU>{}); break;
+                case ACT_GELU: rows(std::integral_constant<int, ACT_GELU>{}); break;
+                case ACT_GELU_TANH: rows(std::integral_constant<int, ACT_GELU_TANH>{}); break;
+                case ACT_SILU: rows(std::integral_constant<int, ACT_SILU>{}); break;
+                default: rows(std::integral_constant<int, ACT_NONE>{}); break;
+            }
+        } else if (vecC && epi_here) {
+            // the lane's column n is fixed; the old values of the next row
+            // are read one iteration ahead
+            const int n = col0 + (lane % C4) * 4;
+            const bool rd = true;
+            auto old_at = [&](int it) -> f32x4 {
+                const int id = it * 64 + lane;
+                const int m = row0 + id / C4;
+                if (!rd || it >= ITS || ((T::MF * C4) % 64 != 0 && id >= T::MF * C4) || m >= c.Mr)
+                    return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                return read_old4(C + (int64_t)m * args.ldc + n, true, c.Nr - n);
+            };
+            f32x4 old_next = old_at(0);
+#pragma unroll 1
+            for (int it = 0; it < ITS; ++it) {
+                const f32x4 old = old_next;
+                old_next = old_at(it + 1);
+                const int id = it * 64 + lane;
+                if ((T::MF * C4) % 64 == 0 || id < T::MF * C4) {
+                    const int r = id / C4;
+                    if (row0 + r < c.Mr) {
+                        f32x4 v = *(const f32x4 __attribute__((address_space(3)))*)(stg + r * T::EPI_LD + (n - col0));
+                        store4(C, args.ldc, true, row0 + r, n, epi_apply4(args.epi, old, bias4, v));
+                    }
+                }
+            }
+        } else if (vecC) {
+#pragma unroll 1
+            for (int it = 0; it < ITS; ++it) {
                 const int id = it * 64 + lane;
                 if ((T::MF * C4) % 64 == 0 || id < T::MF * C4) {
                     const int r = id / C4, c4 = (id % C4) * 4;
@@ -638,7 +819,10 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
 #pragma unroll
                 for (int c0 = 0; c0 < T::WTN; c0 += 64) {
                     const int col = c0 + lane;
-                    if ((T::WTN % 64 == 0 || col < T::WTN) && col0 + col < c.Nr) dst[col] = stg[r * T::EPI_LD + col];
+                    if ((T::WTN % 64 == 0 || col < T::WTN) && col0 + col < c.Nr) {
+                        const float v = stg[r * T::EPI_LD + col];
+                        dst[col] = epi_here ? epi1(args.epi, dst + col, bias1[c0 / 64], v) : v;
+                    }
                 }
             }
         }
@@ -652,10 +836,11 @@ hipError_t launch_tile(const KArgs& a, dim3 grid, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <bool EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ W, int splits, int64_t sWs,
                                                             int64_t sWb, int64_t ldw, float* __restrict__ C,
                                                             int64_t ldc, int64_t sC, int M, int N, int batch,
-                                                            int vec) {
+                                                            int vec, KEpi epi) {
     const int nq = (N + 3) >> 2;
     const int64_t per = (int64_t)M * nq;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -664,10 +849,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const int64_t e = idx % per;
     const int m = (int)(e / nq);
     const int n = (int)(e % nq) * 4;
-    const float* w = W + (int64_t)b * sWb + (int64_t)m * ldw + n;
-    f32x4 s = *(const f32x4*)w;
-    for (int z = 1; z < splits; ++z) s += *(const f32x4*)(w + (int64_t)z * sWs);
+    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (splits > 0) {
+        const float* w = W + (int64_t)b * sWb + (int64_t)m * ldw + n;
+        s = *(const f32x4*)w;
+        for (int z = 1; z < splits; ++z) s += *(const f32x4*)(w + (int64_t)z * sWs);
+    }
     float* p = C + (int64_t)b * sC + (int64_t)m * ldc + n;
+    if (EPI) s = epi4(epi, p, vec, N - n, load_bias4(epi, n, N - n), s);
     if (vec && n + 4 <= N) {
         *(f32x4*)p = s;
     } else {
@@ -889,11 +1078,18 @@ int kernel_find(const char* name) {
 }
 
 hipError_t launch_splitk_reduce(const float* W, int splits, int64_t sWsplit, int64_t sWbatch, int64_t ldw, float* C,
-                                int64_t ldc, int64_t sC, int M, int N, int batch, int vec, hipStream_t st) {
+                                int64_t ldc, int64_t sC, int M, int N, int batch, int vec, hipStream_t st,
+                                const KEpi* epi) {
     const int64_t items = (int64_t)M * ((N + 3) / 4) * batch;
+    if (items == 0) return hipSuccess;
+    if (items > (int64_t)UINT32_MAX * 256) return hipErrorInvalidValue;
     dim3 grid((unsigned)((items + 255) / 256));
-    hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, W, splits, sWsplit, sWbatch, ldw, C, ldc, sC, M,
-                       N, batch, vec);
+    if (epi)
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, st, W, splits, sWsplit, sWbatch, ldw, C,
+                           ldc, sC, M, N, batch, vec, *epi);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, st, W, splits, sWsplit, sWbatch, ldw, C,
+                           ldc, sC, M, N, batch, vec, KEpi{});
     return hipGetLastError();
 }
 

@@ -46,6 +46,21 @@ enum {
     MKP_ERR_BUFFER = -5       /* output text buffer too small */
 };
 
+/* b_layout of mkp_gemm_ex */
+enum {
+    MKP_B_KN = 0,             /* B is K x N, ldb >= N */
+    MKP_B_NK = 1              /* B is N x K, ldb >= K: C = A . B^T of the stored matrix */
+};
+
+/* activations of mkp_gemm_ex's epilogue */
+enum {
+    MKP_ACT_NONE = 0,
+    MKP_ACT_RELU = 1,         /* max(x, 0) */
+    MKP_ACT_GELU = 2,         /* x * Phi(x), Phi the standard normal distribution (erf form) */
+    MKP_ACT_GELU_TANH = 3,    /* x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))) */
+    MKP_ACT_SILU = 4          /* x * sigmoid(x) */
+};
+
 /* flags of mkp_plan_describe (align_flags) and mkp_plan_with_table (flags) */
 enum {
     MKP_PLAN_EXHAUSTIVE = 1,  /* mkp_plan_with_table: score every candidate */
@@ -105,6 +120,27 @@ int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K,
                         const void *B, int64_t ldb, int64_t strideB,
                         float *C, int64_t ldc, int64_t strideC,
                         void *stream);
+
+/*
+ * General form with a fused epilogue (Bolt page, epilogue fusion; its
+ * persistent-kernel section writes the GEMM as D = alpha.A.W + beta.C):
+ *   C_b := act(alpha * A_b . op(B_b) + beta * C_b + bias)   for b < batch,
+ * op(B) = B for b_layout MKP_B_KN (B_b K x N), B^T for MKP_B_NK (B_b N x K).
+ * bias: N fp32 values (device memory) added to every row, or NULL.  act: one
+ * of MKP_ACT_*.  C is read only when beta != 0 (then it must hold values).
+ * The epilogue runs where the final value is made -- in the micro-kernel's
+ * store, or in the split-K reduction -- so it adds no pass over C.  With
+ * alpha = 1, beta = 0, bias = NULL and MKP_ACT_NONE this is mkp_gemm_batched
+ * (or _bt).  K == 0: C := act(beta * C + bias).  Batch strides as in
+ * mkp_gemm_batched (ignored when batch == 1).  Errors as for mkp_gemm, plus
+ * an unknown b_layout or act, or a non-finite alpha or beta.
+ */
+int mkp_gemm_ex(int64_t batch, int64_t M, int64_t N, int64_t K,
+                const void *A, int64_t lda, int64_t strideA,
+                const void *B, int64_t ldb, int64_t strideB, int b_layout,
+                float *C, int64_t ldc, int64_t strideC,
+                float alpha, float beta, const float *bias, int act,
+                void *stream);
 
 /*
  * Grouped call: C_g[M x N_g] := A[M x K] . B_g for g < groups (1..4), the

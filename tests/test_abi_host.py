@@ -190,3 +190,28 @@ def test_grouped_plan_describe(mkp):
     assert mkp.mkp_plan_describe_grouped(0, 300, [5])["regions"] == []
     with pytest.raises(mkp.MkpError):
         mkp.mkp_plan_describe_grouped(10, 10, [1, 2, 3, 4, 5])
+
+
+def test_gemm_ex_argument_errors(mkp):
+    fake = 1 << 20  # never dereferenced: each call fails its checks first
+
+    def call(**kw):
+        a = dict(batch=1, M=8, N=8, K=8, A=fake, lda=8, sA=0, B=fake, ldb=8, sB=0, lay=0, C=fake, ldc=8, sC=0,
+                 alpha=1.0, beta=0.0, bias=None, act=0)
+        a.update(kw)
+        return mkp.mkp_gemm_ex_raw(a["batch"], a["M"], a["N"], a["K"], a["A"], a["lda"], a["sA"], a["B"], a["ldb"],
+                                   a["sB"], a["lay"], a["C"], a["ldc"], a["sC"], a["alpha"], a["beta"], a["bias"],
+                                   a["act"], 0)
+
+    E = mkp.MKP_ERR_INVALID_ARG
+    assert call(lay=2) == E
+    assert call(act=5) == E and "activation" in mkp.last_error()
+    assert call(act=-1) == E
+    assert call(alpha=float("nan")) == E
+    assert call(beta=float("inf")) == E
+    assert call(lda=7) == E
+    assert call(lay=1, ldb=7) == E          # N x K needs ldb >= K
+    assert call(ldc=7) == E
+    assert call(M=0, act=2, beta=1.0) == mkp.MKP_OK   # empty output: nothing to do
+    with pytest.raises(KeyError):
+        call(act="tanh")
