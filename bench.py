@@ -301,6 +301,8 @@ def main():
     ap.add_argument("--epilogue", choices=["none", "bias", "bias_gelu", "bias_gelu_unfused"], default="none",
                     help="encoder linears with a bias on every GEMM (and GELU on the FFN-up GEMMs), fused into the "
                          "GEMM epilogue or, for comparison, as separate passes")
+    ap.add_argument("--fuse-regions", type=int, choices=[0, 1], default=0,
+                    help="one-launch Pattern II plans over kernel pairs when the model prefers them (1) or never (0)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of MiB (to scale rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -323,6 +325,7 @@ def main():
         raise SystemExit("--epilogue and --qkv are separate experiments")
     wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv, epilogue=args.epilogue)
     stream = torch.cuda.current_stream().cuda_stream
+    mkp.mkp_set_option("fuse_regions", args.fuse_regions)
     mkp.mkp_cache_clear()
 
     # first step: plan misses (polymerization) + launches, timed on its own
@@ -377,7 +380,8 @@ def main():
                     plan = dict(mkp.mkp_plan_describe(1, case.M, 768, case.K, bt=wl.bt), pattern="3x")
             else:
                 plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K, bt=wl.bt)
-            ks = "+".join(f"{r['kernel']}/s{r['s']}" for r in plan["regions"])
+            ks = "+".join(f"{r['kernel']}/s{r['s']}" for r in plan["regions"]) + (" (1 launch)" if plan.get("fused")
+                                                                                    else "")
             log(f"  {case.tag:>14} {case.M:5d}x{case.N:5d}x{case.K:5d} b{case.batch:<3d} {us:9.2f} us "
                 f"{case.flops / us / 1e6:8.1f} TF/s  {100 * f:5.1f}% of R  {plan['pattern']:4s} {ks}")
 
@@ -400,6 +404,7 @@ def main():
             "b_layout": args.b_layout,
             "qkv": wl.qkv,
             "epilogue": wl.epilogue,
+            "fuse_regions": args.fuse_regions,
             "gemms_per_step": len(wl.cases),
             "flops_per_step": wl.flops,
             "bytes_per_step": wl.bytes,

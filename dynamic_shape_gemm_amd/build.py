@@ -14,7 +14,16 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmkp.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["kernels.hip", "planner.cpp", "api.cpp"]
+# (source, object, extra flags): the kernel file builds as three translation
+# units (single-tile kernels; two-tile kernels per B layout), compiled side by side
+UNITS = [
+    ("kernels.hip", "kernels_p1.o", ["-DMKP_PART=1"]),
+    ("kernels.hip", "kernels_p2.o", ["-DMKP_PART=2"]),
+    ("kernels.hip", "kernels_p3.o", ["-DMKP_PART=3"]),
+    ("planner.cpp", "planner.o", []),
+    ("api.cpp", "api.o", []),
+]
+SOURCES = sorted({u[0] for u in UNITS})
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -59,36 +68,43 @@ def parse_resource_usage(remarks: str) -> dict:
 
 
 def build_library(verbose: bool = False) -> str:
-    objs = []
     obj_dir = os.path.join(HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    for src in SOURCES:
-        obj = os.path.join(obj_dir, src.rsplit(".", 1)[0] + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+    jobs = []
+    for src, obj_name, extra in UNITS:
+        obj = os.path.join(obj_dir, obj_name)
+        cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if src.endswith(".hip"):
             cmd += ["-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics"]
         if verbose:
             print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
-        usage = parse_resource_usage(res.stderr) if src.endswith(".hip") else {}
-        other = "\n".join(l for l in res.stderr.splitlines()
+        jobs.append((src, obj, cmd, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))
+    usage, objs, failed = {}, [], None
+    for src, obj, cmd, proc in jobs:
+        _, err = proc.communicate()
+        if src.endswith(".hip"):
+            usage.update(parse_resource_usage(err))
+        other = "\n".join(l for l in err.splitlines()
                           if "kernel-resource-usage" not in l and "packed-fp32-ops" not in l)
         if other.strip():
             print(other, file=sys.stderr, flush=True)
-        if res.returncode != 0:
-            raise subprocess.CalledProcessError(res.returncode, cmd)
-        if usage:
-            with open(RESOURCE_REPORT, "w") as f:
-                for k in sorted(usage):
-                    u = usage[k]
-                    f.write(f"{k} vgpr={u.get('vgpr')} agpr={u.get('agpr')} scratch={u.get('scratch')} "
-                            f"lds={u.get('lds')} occupancy={u.get('occupancy')}\n")
-            # a GEMM micro-kernel that spills to scratch has lost its register
-            # tiling; refuse to ship it
-            spills = [k for k, u in usage.items() if "gemm_tile_kernel" in k and u.get("scratch", 0) > 0]
-            if spills:
-                raise RuntimeError("GEMM micro-kernels use scratch memory: " + ", ".join(spills))
+        if proc.returncode != 0 and failed is None:
+            failed = subprocess.CalledProcessError(proc.returncode, cmd)
         objs.append(obj)
+    if failed is not None:
+        raise failed
+    with open(RESOURCE_REPORT, "w") as f:
+        for k in sorted(usage):
+            u = usage[k]
+            f.write(f"{k} vgpr={u.get('vgpr')} agpr={u.get('agpr')} scratch={u.get('scratch')} "
+                    f"lds={u.get('lds')} occupancy={u.get('occupancy')}\n")
+    # a GEMM micro-kernel that spills to scratch has lost its register
+    # tiling; refuse to ship it
+    spills = [k for k, u in usage.items()
+              if ("gemm_tile_kernel" in k or "gemm_dual_kernel" in k) and u.get("scratch", 0) > 0]
+    if spills:
+        raise RuntimeError("GEMM micro-kernels use scratch memory: " + ", ".join(spills))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-ldl"]
     if verbose:

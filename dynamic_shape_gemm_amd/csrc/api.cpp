@@ -153,6 +153,17 @@ PerfTable analytic_table() {
 }
 
 // Resolve table kernel names to library kernels.
+// Library index of the two-tile kernel running kernels a then b (library
+// indices) in one launch, or -1.
+int dual_find(int a, int b) {
+    if (a < 0 || b < 0) return -1;
+    for (int i = 0; i < dual_count(); ++i) {
+        const DualInfo& d = dual_info(i);
+        if (kernel_find(d.first) == a && kernel_find(d.second) == b) return i;
+    }
+    return -1;
+}
+
 bool bind_table(PerfTable& t, std::string& err) {
     for (auto& k : t.kernels) {
         k.lib_index = kernel_find(k.name.c_str());
@@ -175,7 +186,35 @@ bool bind_table(PerfTable& t, std::string& err) {
         for (auto& k : analytic_table().kernels)
             if (k.bt == (layout == 1)) t.kernels.push_back(k);
     }
+    // kernel pairs: each listed pair must have a two-tile kernel; a table
+    // without pair lines gets every pair the library has whose kernels it
+    // prices with the same workgroups per CU
+    for (auto& pr : t.pairs)
+        if (dual_find(t.kernels[pr.first].lib_index, t.kernels[pr.second].lib_index) < 0) {
+            err = "table pairs " + t.kernels[pr.first].name + " and " + t.kernels[pr.second].name +
+                  ", which the library cannot run in one launch";
+            return false;
+        }
+    if (t.pairs.empty())
+        for (int d = 0; d < dual_count(); ++d) {
+            int ia = -1, ib = -1;
+            for (size_t i = 0; i < t.kernels.size(); ++i) {
+                if (t.kernels[i].name == dual_info(d).first) ia = (int)i;
+                if (t.kernels[i].name == dual_info(d).second) ib = (int)i;
+            }
+            if (ia >= 0 && ib >= 0 && t.kernels[ia].wg_per_cu == t.kernels[ib].wg_per_cu &&
+                t.kernels[ia].bt == t.kernels[ib].bt)
+                t.pairs.emplace_back(ia, ib);
+        }
     return true;
+}
+
+// The analytic estimates with the library's kernel pairs bound.
+PerfTable bound_analytic_table() {
+    PerfTable t = analytic_table();
+    std::string err;
+    (void)bind_table(t, err);
+    return t;
 }
 
 std::string default_table_path() {
@@ -205,10 +244,10 @@ int load_table_locked(Library& L, const char* path, bool quiet_missing) {
     std::string text, err;
     if (!read_file(p, text)) {
         if (quiet_missing) {
-            L.table = analytic_table();
+            L.table = bound_analytic_table();
             L.table_origin = "analytic";
             L.cache.clear();
-    L.gcache.clear();
+            L.gcache.clear();
             return MKP_OK;
         }
         return fail(MKP_ERR_INVALID_ARG, "cannot read performance table " + p);
@@ -243,7 +282,7 @@ void ensure_init() {
             // a shipped table that does not fit the library is a build error:
             // say so once, and plan with the analytic estimates
             std::fprintf(stderr, "libmkp: %s; planning with analytic estimates\n", t_last_error.c_str());
-            L.table = analytic_table();
+            L.table = bound_analytic_table();
             L.table_origin = "analytic";
         }
         read_env_options(L);
@@ -421,12 +460,24 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     // (as the Bolt page pads kernels to alignment 8), so the micro-kernels
     // take the direct-load path.  Workspace layout, regions in order on one
     // stream sharing it: [split-K counters][split-K partials][A copy][B copy].
+    // The two regions of a one-launch plan run together: each gets its own
+    // partial area and its own range of counters.
+    const bool one_launch = plan->fused && plan->regions.size() == 2;
+    auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
     size_t part_bytes = 0;
-    for (auto& r : plan->regions)
-        if (r.s > 1) {
-            const int64_t ldw = (r.n + 3) & ~int64_t(3);
-            part_bytes = std::max(part_bytes, (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float));
+    size_t part_off[2] = {0, 0};
+    for (size_t i = 0; i < plan->regions.size() && i < 2; ++i) {
+        const Region& r = plan->regions[i];
+        if (r.s <= 1) continue;
+        const int64_t ldw = (r.n + 3) & ~int64_t(3);
+        const size_t bytes = (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float);
+        if (one_launch) {
+            part_off[i] = i == 0 ? 0 : round256(part_bytes);
+            part_bytes = part_off[i] + bytes;
+        } else {
+            part_bytes = std::max(part_bytes, bytes);
         }
+    }
     const bool pack_on = L.pack_unaligned.load(std::memory_order_relaxed);
     // A K x N B the plan runs on N x K kernels is first transposed into the
     // workspace (rows of K padded to 8 elements, aligned)
@@ -438,7 +489,6 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     // (a copy pays off once several tile rows/columns re-read the operand)
     const bool packA = pack_on && !vA && N > 192 && ldap < (int64_t(1) << 23);
     const bool packB = !tr && pack_on && !vB && M > 192 && ldbp < (int64_t(1) << (bt ? 23 : 25));
-    auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t offA = kCounterBytes + round256(part_bytes);
     const size_t bytesA = packA ? (size_t)batch * M * ldap * 2 : 0;
     const size_t offB = offA + round256(bytesA);
@@ -484,13 +534,24 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         vB = true;
     }
 
-    for (size_t i = 0; i < plan->regions.size(); ++i) {
+    // One region's launch arguments; `counter0`: its first split-K counter.
+    struct RegionLaunch {
+        KArgs a{};
+        KEpi e{};
+        const KernelInfo* ki = nullptr;
+        bool fused_red = false;   // split-K reduced by the last-arriving split
+        float* Creg = nullptr;
+        int64_t ldw = 0, G = 0;
+        double flops = 0, bytes = 0, red_bytes = 0;
+    };
+    auto setup = [&](size_t i, int64_t counter0, int64_t counter_cap, RegionLaunch& R) -> int {
         const Region& r = plan->regions[i];
         const int li = r.lib;
         if (li < 0 || li >= kernel_count()) return fail(MKP_ERR_UNSUPPORTED, "plan kernel is not launchable");
         const KernelInfo& ki = kernel_info(li);
         if (ki.bt != kbt) return fail(MKP_ERR_UNSUPPORTED, "plan kernel has the other B layout");
-        KArgs a{};
+        R.ki = &ki;
+        KArgs& a = R.a;
         a.A = A + r.m0 * lda;
         a.B = kbt ? B + r.n0 * ldb : B + r.n0;
         a.lda = lda;
@@ -506,59 +567,91 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         a.splits = r.s;
         a.batch = (int)batch;
         a.flags = (vA ? KF_VEC_A : 0) | (vB ? KF_VEC_B : 0);
-        float* Creg = C + r.m0 * ldc + r.n0;
-        const int64_t ldw = (r.n + 3) & ~int64_t(3);
+        R.Creg = C + r.m0 * ldc + r.n0;
+        R.ldw = (r.n + 3) & ~int64_t(3);
         if (r.s == 1) {
-            a.C = Creg;
+            a.C = R.Creg;
             a.ldc = ldc;
             a.sC = sC;
             a.sCsplit = 0;
             a.flags |= vC ? KF_VEC_C : 0;
         } else {
-            a.C = (float*)((char*)ws + kCounterBytes);
-            a.ldc = ldw;
-            a.sC = r.m * ldw;
-            a.sCsplit = batch * r.m * ldw;
+            a.C = (float*)((char*)ws + kCounterBytes + part_off[i < 2 ? i : 0]);
+            a.ldc = R.ldw;
+            a.sC = r.m * R.ldw;
+            a.sCsplit = batch * r.m * R.ldw;
             a.flags |= KF_VEC_C;
         }
         // fused reduction when the per-tile counters fit, else a second pass
-        const bool fused = r.s > 1 && ki.fused_ok && L.fused_reduce.load(std::memory_order_relaxed) &&
-                           (int64_t)a.tiles_m * a.tiles_n * batch <= kCounterCap;
-        a.counters = fused ? (int*)ws : nullptr;
-        a.Cout = Creg;
+        const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n * batch;
+        R.fused_red = r.s > 1 && ki.fused_ok && L.fused_reduce.load(std::memory_order_relaxed) &&
+                      counter0 + ntiles <= counter_cap;
+        a.counters = R.fused_red ? (int*)ws + counter0 : nullptr;
+        a.Cout = R.Creg;
         a.ldcout = ldc;
         a.sCout = sC;
         if (vC) a.flags |= KF_VEC_COUT;
         // the epilogue's bias starts at the region's first column; it runs in
         // the micro-kernel unless a second pass reduces the splits
-        KEpi e{};
         if (epi) {
-            e = *epi;
-            if (e.bias) e.bias += r.n0;
-            if (r.s == 1 || fused) {
+            R.e = *epi;
+            if (R.e.bias) R.e.bias += r.n0;
+            if (r.s == 1 || R.fused_red) {
                 a.flags |= KF_EPI;
-                a.epi = e;
+                a.epi = R.e;
             }
         }
         const double r_epi = epi ? (epi->beta != 0.0f ? 4.0 * r.m * r.n * batch : 0.0) + (epi->bias ? 4.0 * r.n : 0.0)
                                  : 0.0;
-        const int64_t G = (int64_t)a.tiles_m * a.tiles_n * a.splits * batch;
+        R.G = (int64_t)a.tiles_m * a.tiles_n * a.splits * batch;
+        if (R.G > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
+        R.flops = 2.0 * r.m * r.n * K * batch;
+        R.bytes = (double)batch * (2.0 * r.m * K + 2.0 * K * r.n + 4.0 * r.m * r.n) + ((a.flags & KF_EPI) ? r_epi : 0.0);
+        R.red_bytes = (double)(r.s + 1) * 4.0 * r.m * r.n * batch + (epi ? r_epi : 0.0);
+        return MKP_OK;
+    };
+    auto reduce = [&](size_t i, RegionLaunch& R) -> int {
+        const Region& r = plan->regions[i];
+        if (r.s <= 1 || R.fused_red) return MKP_OK;
+        he = traced(L, st, -1, 0.0, R.red_bytes, [&] {
+            return launch_splitk_reduce(R.a.C, r.s, batch * r.m * R.ldw, r.m * R.ldw, R.ldw, R.Creg, ldc, sC, (int)r.m,
+                                        (int)r.n, (int)batch, vC ? 1 : 0, st, epi ? &R.e : nullptr);
+        });
+        if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
+        L.launches.fetch_add(1, std::memory_order_relaxed);
+        return MKP_OK;
+    };
+
+    if (one_launch) {
+        // both regions in one launch of the pair's two-tile kernel
+        RegionLaunch R[2];
+        int rc = setup(0, 0, kCounterCap, R[0]);
+        if (rc != MKP_OK) return rc;
+        const int64_t used = R[0].fused_red ? (int64_t)R[0].a.tiles_m * R[0].a.tiles_n * batch : 0;
+        rc = setup(1, used, kCounterCap, R[1]);
+        if (rc != MKP_OK) return rc;
+        const int d = dual_find(plan->regions[0].lib, plan->regions[1].lib);
+        if (d < 0) return fail(MKP_ERR_UNSUPPORTED, "plan pairs kernels that have no one-launch form");
+        const int64_t G = R[0].G + R[1].G;
         if (G > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
-        const double flops = 2.0 * r.m * r.n * K * batch;
-        const double bytes = (double)batch * (2.0 * r.m * K + 2.0 * K * r.n + 4.0 * r.m * r.n) +
-                             ((a.flags & KF_EPI) ? r_epi : 0.0);
-        he = traced(L, st, li, flops, bytes, [&] { return ki.launch(a, dim3((unsigned)G), st); });
+        he = traced(L, st, -100 - d, R[0].flops + R[1].flops, R[0].bytes + R[1].bytes, [&] {
+            return dual_info(d).launch(R[0].a, R[1].a, (int)R[0].G, dim3((unsigned)G), st);
+        });
         if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
         L.launches.fetch_add(1, std::memory_order_relaxed);
-        if (r.s > 1 && !fused) {
-            he = traced(L, st, -1, 0.0, (double)(r.s + 1) * 4.0 * r.m * r.n * batch + (epi ? r_epi : 0.0), [&] {
-                return launch_splitk_reduce(a.C, r.s, batch * r.m * ldw, r.m * ldw, ldw, Creg, ldc, sC,
-                                            (int)r.m, (int)r.n, (int)batch, vC ? 1 : 0, st, epi ? &e : nullptr);
-            });
-            if (he != hipSuccess)
-                return fail(MKP_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
-            L.launches.fetch_add(1, std::memory_order_relaxed);
-        }
+        for (size_t i = 0; i < 2; ++i)
+            if ((rc = reduce(i, R[i])) != MKP_OK) return rc;
+        return MKP_OK;
+    }
+    for (size_t i = 0; i < plan->regions.size(); ++i) {
+        RegionLaunch R;
+        int rc = setup(i, 0, kCounterCap, R);
+        if (rc != MKP_OK) return rc;
+        he = traced(L, st, plan->regions[i].lib, R.flops, R.bytes,
+                    [&] { return R.ki->launch(R.a, dim3((unsigned)R.G), st); });
+        if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
+        L.launches.fetch_add(1, std::memory_order_relaxed);
+        if ((rc = reduce(i, R)) != MKP_OK) return rc;
     }
     return MKP_OK;
 }
@@ -838,6 +931,7 @@ int mkp_plan_with_table(const char* table_text, int flags, int64_t batch, int64_
         std::shared_lock<std::shared_mutex> lk(L.mu);
         o.cost_mode = L.opts.cost_mode;
         o.plan_rank = L.opts.plan_rank;
+        o.fuse = L.opts.fuse;
     }
     Plan p = plan_call(t, batch, M, N, K, o, batch <= 65535 ? 1 : 0);
     return write_out(plan_to_json(p, t), buf, len);
@@ -903,6 +997,12 @@ int mkp_set_option(const char* key, const char* value) {
         int r = std::atoi(v.c_str());
         if (r < 0) return fail(MKP_ERR_INVALID_ARG, "plan_rank < 0");
         L.opts.plan_rank = r;
+    } else if (k == "fuse_regions") {
+        // one-launch Pattern II plans over kernel pairs: 0 off (the default:
+        // measured no faster on the encoder linears), 1 by modelled cost
+        const int x = std::atoi(v.c_str());
+        if (x < 0 || x > 1) return fail(MKP_ERR_INVALID_ARG, "fuse_regions must be 0 or 1");
+        L.opts.fuse = x == 1;
     } else if (k == "splitk_max") {
         int s = std::atoi(v.c_str());
         if (s < 1) return fail(MKP_ERR_INVALID_ARG, "splitk_max < 1");
@@ -969,11 +1069,13 @@ int mkp_trace_dump(char* buf, size_t len) {
         (void)hipEventDestroy(recs[i].e0);
         (void)hipEventDestroy(recs[i].e1);
         const int k = recs[i].kernel;
-        const char* name = k >= 0    ? kernel_info(k).name
-                           : k == -1 ? "splitk_reduce"
-                           : k == -2 ? "zero_fill"
-                           : k == -3 ? "pack_rows"
-                                     : "transpose_b";
+        // -100 - d: both regions in one launch of two-tile kernel d
+        const std::string name = k >= 0       ? std::string(kernel_info(k).name)
+                                 : k <= -100 ? std::string(dual_info(-100 - k).first) + "+" + dual_info(-100 - k).second
+                                 : k == -1   ? "splitk_reduce"
+                                 : k == -2   ? "zero_fill"
+                                 : k == -3   ? "pack_rows"
+                                             : "transpose_b";
         if (i) o << ",";
         o << "{\"kernel\":\"" << name << "\",\"call\":" << recs[i].call << ",\"us\":" << 1000.0 * ms
           << ",\"flops\":" << recs[i].flops
@@ -1218,6 +1320,11 @@ int mkp_calibrate(const char* path, int max_points) {
     (void)hipFree(pAB);
     (void)hipFree(pC);
     if (err != hipSuccess) return fail(MKP_ERR_HIP, std::string("calibration launch: ") + hipGetErrorString(err));
+    {
+        // the library's one-launch kernel pairs, written out with the table
+        std::string berr;
+        if (!bind_table(t, berr)) return fail(MKP_ERR_UNSUPPORTED, "calibrated table: " + berr);
+    }
 
     std::string text = "# measured by mkp_calibrate on " + std::string(prop.name) + " (" +
                        std::string(prop.gcnArchName) + "), " + std::to_string(cus) + " CUs\n" + table_to_text(t);

@@ -88,6 +88,18 @@ int kernel_count();
 const KernelInfo& kernel_info(int i);
 int kernel_find(const char* name);
 
+// A pair of micro-kernels compiled into one launch: the first `n1`
+// workgroups run kernel `first` over one region, the others kernel `second`
+// over another (grid = n1 + the second region's workgroups).
+struct DualInfo {
+    const char* first;
+    const char* second;
+    const void* func;
+    hipError_t (*launch)(const KArgs& a1, const KArgs& a2, int n1, dim3 grid, hipStream_t);
+};
+int dual_count();
+const DualInfo& dual_info(int i);
+
 // Sum of `splits` partials W[z] (z ascending) into C; W is [splits][batch][M][ldw].
 // With an epilogue (epi non-null) the sum goes through it; splits == 0 is an
 // empty sum (W unused), which with the epilogue serves K == 0.

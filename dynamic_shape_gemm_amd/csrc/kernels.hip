@@ -31,6 +31,14 @@
 
 #include <hip/hip_runtime.h>
 
+// The file builds as three translation units compiled side by side: part 1
+// holds the single-tile kernels, the helper kernels and their launchers,
+// parts 2 and 3 the two-tile kernels for B as K x N and as N x K; without
+// MKP_PART it holds everything.
+#ifndef MKP_PART
+#define MKP_PART 0
+#endif
+
 #include <type_traits>
 
 namespace mkp {
@@ -500,17 +508,18 @@ __device__ __forceinline__ void map_tile(int bid, int G, int tiles_m, int tiles_
     tn = in_g / gsz;
 }
 
+// One pipeline task of tile T: workgroup `bid` of the `nblk` workgroups that
+// serve the region described by args; smem is the workgroup's LDS (T::LDS
+// bytes).
 template <class T>
-__global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[T::LDS];
-    lds_t* smem = (lds_t*)smem_raw;
+__device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* smem) {
     lds_t* junk = smem + T::S * T::STAGE;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % T::WGM, wn = wave / T::WGM;
 
     int tm, tn, split, b;
-    map_tile<8>(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, args.splits, tm, tn, split, b);
+    map_tile<8>(bid, nblk, args.tiles_m, args.tiles_n, args.splits, tm, tn, split, b);
     if (args.ngroups > 0) {
         // grouped call: switch to the B, N and C of the tile column's group
         // (constant indices only, so the argument block stays in registers)
@@ -677,7 +686,9 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
         // arrival.  The last split to arrive makes the other splits' partials
         // visible (one L2/L1 invalidate) and sums them in split order -- the
         // same order whichever split arrives last.
-        __shared__ int s_last;
+        // the arrival flag lives in the stage memory, idle after the K loop
+        // (every wave is past its last stage read once the barrier below is passed)
+        int __attribute__((address_space(3)))* s_last_p = (int __attribute__((address_space(3)))*)smem;
         float* Wt = args.C + (int64_t)b * args.sC + (int64_t)m0 * args.ldc + n0;   // split 0's tile
         for_each4([&](int m, int n, f32x4 v) { store4(C, args.ldc, vecC, m, n, v); });
         __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
@@ -690,10 +701,10 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
                 last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.splits - 1;
             last = __builtin_amdgcn_readfirstlane(last);
             if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (lane == 0) s_last = last;
+            if (lane == 0) *s_last_p = last;
         }
         __syncthreads();
-        if (!s_last) return;
+        if (!*s_last_p) return;
         float* Co = args.Cout + (int64_t)b * args.sCout + (int64_t)m0 * args.ldcout + n0;
         const bool vecCo = args.flags & KF_VEC_COUT;
         for_each4([&](int m, int n, f32x4 own) {
@@ -831,11 +842,45 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
 }
 
 template <class T>
+__global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[T::LDS];
+    tile_task<T>(args, blockIdx.x, gridDim.x, (lds_t*)smem_raw);
+}
+
+template <class T>
 hipError_t launch_tile(const KArgs& a, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL(gemm_tile_kernel<T>, grid, dim3(T::NT), 0, st, a);
     return hipGetLastError();
 }
 
+// The two regions of a plan in one launch: workgroups [0, n1) run tile T1
+// over region a1, the others tile T2 over region a2.  The hardware hands out
+// workgroups in order, so the second region's tiles start as soon as slots
+// free up in the first region's last wave (the merged-wave view of the
+// MikPoly page's case study).  Both tiles use the same workgroup size, and
+// the LDS of the larger one leaves the number of resident workgroups per CU
+// of each unchanged.
+template <class T1, class T2>
+__global__ __launch_bounds__(T1::NT) void gemm_dual_kernel(KArgs a1, KArgs a2, int n1) {
+    static_assert(T1::NT == T2::NT, "both tiles must use the same workgroup size");
+    constexpr int L = T1::LDS > T2::LDS ? T1::LDS : T2::LDS;
+    constexpr int kLdsPerCu = 160 * 1024;
+    static_assert(kLdsPerCu / (L + 16) >= (kLdsPerCu / (T1::LDS + 16) < kLdsPerCu / (T2::LDS + 16)
+                                              ? kLdsPerCu / (T1::LDS + 16)
+                                              : kLdsPerCu / (T2::LDS + 16)),
+                  "pairing must not lower the resident workgroups per CU");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[L];
+    if ((int)blockIdx.x < n1) tile_task<T1>(a1, blockIdx.x, n1, (lds_t*)smem_raw);
+    else tile_task<T2>(a2, (int)blockIdx.x - n1, (int)gridDim.x - n1, (lds_t*)smem_raw);
+}
+
+template <class T1, class T2>
+hipError_t launch_dual(const KArgs& a1, const KArgs& a2, int n1, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_dual_kernel<T1, T2>), grid, dim3(T1::NT), 0, st, a1, a2, n1);
+    return hipGetLastError();
+}
+
+#if MKP_PART == 0 || MKP_PART == 1
 template <bool EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ W, int splits, int64_t sWs,
                                                             int64_t sWb, int64_t ldw, float* __restrict__ C,
@@ -1007,6 +1052,8 @@ __global__ __launch_bounds__(256) void fill_random_bf16_kernel(uint16_t* p, int6
     }
 }
 
+#endif  // helper kernels
+
 // The library: tile shapes, wave layouts and LDS stage counts.  The large
 // tiles run 8 waves (two per SIMD) so one wave's LDS waits overlap the
 // other's MFMAs; 128x128 runs two 4-wave workgroups per CU.  With B as K x N
@@ -1036,6 +1083,7 @@ using U_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true>;
 using U_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true>;
 using U_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true>;
 
+#if MKP_PART == 0 || MKP_PART == 1
 #define MKP_KERNEL(NAME, T)                                                                               \
     {                                                                                                      \
         NAME, T::BM, T::BN, T::BK, T::NT, T::LDS, T::FUSED, T::BT, (const void*)&gemm_tile_kernel<T>, \
@@ -1067,8 +1115,72 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m32n64k64_nk", U_32x64),
 };
 
+#endif  // single-tile registry
+
+// Pairs of tiles that can share a launch (same workgroup size and resident
+// workgroups per CU): a large tile for the region of whole waves and a
+// smaller one for the rest, in both B layouts.
+#define MKP_DUAL(N1, T1, N2, T2) \
+    { N1, N2, (const void*)&gemm_dual_kernel<T1, T2>, &launch_dual<T1, T2> }
+
+#if MKP_PART == 0 || MKP_PART == 2
+const DualInfo g_duals_kn[] = {
+    MKP_DUAL("m128n128k64", T_128x128, "m64n64k64", T_64x64),
+    MKP_DUAL("m128n128k64", T_128x128, "m64n128k64", T_64x128),
+    MKP_DUAL("m128n128k64", T_128x128, "m128n64k64", T_128x64),
+    MKP_DUAL("m128n128k64", T_128x128, "m16n128k64", T_16x128),
+    MKP_DUAL("m128n64k64", T_128x64, "m64n64k64", T_64x64),
+    MKP_DUAL("m64n128k64", T_64x128, "m64n64k64", T_64x64),
+    MKP_DUAL("m256n256k64", T_256x256, "m256n128k64", T_256x128),
+    MKP_DUAL("m256n256k64", T_256x256, "m128n256k64", T_128x256),
+};
+#endif
+#if MKP_PART == 0 || MKP_PART == 3
+const DualInfo g_duals_nk[] = {
+    MKP_DUAL("m128n128k64_nk", U_128x128, "m64n64k64_nk", U_64x64),
+    MKP_DUAL("m128n128k64_nk", U_128x128, "m64n128k64_nk", U_64x128),
+    MKP_DUAL("m128n128k64_nk", U_128x128, "m128n64k64_nk", U_128x64),
+    MKP_DUAL("m128n128k64_nk", U_128x128, "m16n128k64_nk", U_16x128),
+    MKP_DUAL("m128n64k64_nk", U_128x64, "m64n64k64_nk", U_64x64),
+    MKP_DUAL("m64n128k64_nk", U_64x128, "m64n64k64_nk", U_64x64),
+    MKP_DUAL("m256n256k64_nk", U_256x256, "m256n128k64_nk", U_256x128),
+    MKP_DUAL("m256n256k64_nk", U_256x256, "m128n256k64_nk", U_128x256),
+};
+#endif
+
 }  // namespace
 
+// the pair tables of the two-tile translation units
+const DualInfo* duals_kn(int* n);
+const DualInfo* duals_nk(int* n);
+#if MKP_PART == 0 || MKP_PART == 2
+const DualInfo* duals_kn(int* n) {
+    *n = (int)(sizeof(g_duals_kn) / sizeof(g_duals_kn[0]));
+    return g_duals_kn;
+}
+#endif
+#if MKP_PART == 0 || MKP_PART == 3
+const DualInfo* duals_nk(int* n) {
+    *n = (int)(sizeof(g_duals_nk) / sizeof(g_duals_nk[0]));
+    return g_duals_nk;
+}
+#endif
+#if MKP_PART == 0 || MKP_PART == 1
+int dual_count() {
+    int a = 0, b = 0;
+    duals_kn(&a);
+    duals_nk(&b);
+    return a + b;
+}
+const DualInfo& dual_info(int i) {
+    int a = 0, b = 0;
+    const DualInfo* kn = duals_kn(&a);
+    const DualInfo* nk = duals_nk(&b);
+    return i < a ? kn[i] : nk[i - a];
+}
+#endif
+
+#if MKP_PART == 0 || MKP_PART == 1
 int kernel_count() { return (int)(sizeof(g_kernels) / sizeof(g_kernels[0])); }
 const KernelInfo& kernel_info(int i) { return g_kernels[i]; }
 int kernel_find(const char* name) {
@@ -1135,5 +1247,7 @@ hipError_t launch_fill_random_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStr
     hipLaunchKernelGGL(fill_random_bf16_kernel, dim3(1024), dim3(256), 0, st, p, n, seed);
     return hipGetLastError();
 }
+
+#endif  // part 1
 
 }  // namespace mkp

@@ -19,6 +19,7 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
     std::string raw;
     int lineno = 0;
     std::vector<std::pair<std::string, std::vector<std::pair<double, double>>>> gs, tails, tailxs;
+    std::vector<std::pair<std::string, std::string>> pair_names;
     while (std::getline(in, raw)) {
         ++lineno;
         auto hash = raw.find('#');
@@ -86,6 +87,11 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
                 pts.emplace_back(f, r);
             }
             (key == "tail" ? tails : tailxs).emplace_back(name, pts);
+        } else if (key == "pair") {
+            // pair <kernel a> <kernel b>: a and b can share one launch
+            std::string a, b;
+            if (!(ls >> a >> b) || a == b) return fail("bad pair line");
+            pair_names.emplace_back(a, b);
         } else if (key == "g") {
             std::string name, tok;
             if (!(ls >> name)) return fail("bad g line");
@@ -142,6 +148,22 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
         err = "table has no kernels";
         return false;
     }
+    for (auto& pn : pair_names) {
+        int ia = -1, ib = -1;
+        for (size_t i = 0; i < t.kernels.size(); ++i) {
+            if (t.kernels[i].name == pn.first) ia = (int)i;
+            if (t.kernels[i].name == pn.second) ib = (int)i;
+        }
+        if (ia < 0 || ib < 0) {
+            err = "pair line names an unknown kernel: " + pn.first + " " + pn.second;
+            return false;
+        }
+        if (t.kernels[ia].bt != t.kernels[ib].bt || t.kernels[ia].wg_per_cu != t.kernels[ib].wg_per_cu) {
+            err = "pair " + pn.first + " " + pn.second + " differs in B layout or workgroups per CU";
+            return false;
+        }
+        t.pairs.emplace_back(ia, ib);
+    }
     out = t;
     return true;
 }
@@ -174,7 +196,42 @@ std::string table_to_text(const PerfTable& t) {
             for (auto& p : pts) o << " " << p.first << ":" << p.second;
             o << "\n";
         }
+    for (auto& pr : t.pairs) o << "pair " << t.kernels[pr.first].name << " " << t.kernels[pr.second].name << "\n";
     return o.str();
+}
+
+double merged_makespan(int64_t S, int64_t n1, double d1, int64_t n2, double d2) {
+    if (n1 <= 0) return (double)((n2 + S - 1) / S) * d2;
+    const int64_t w1 = n1 / S, r1 = n1 % S;
+    const double t0 = (double)w1 * d1;
+    if (n2 <= 0) return r1 ? t0 + d1 : t0;
+    if (r1 == 0) return t0 + (double)((n2 + S - 1) / S) * d2;
+    // after w1 full waves, a = S - r1 slots are free at t0 and the r1 slots
+    // of the first region's last wave at t1 = t0 + d1; the second region's
+    // tasks take them in order, so its last task starts at the n2-th
+    // smallest value of {t0 + i d2 (a of each)} u {t1 + j d2 (b of each)}
+    const int64_t a = S - r1, b = r1;
+    const double t1 = t0 + d1;
+    const double q = d1 / d2;   // (t1 - t0) / d2
+    const double eps = 1e-9;
+    // starts at or before t0 + i d2: a (i + 1) + b (floor(i - q) + 1)_+
+    auto count_a = [&](int64_t i) {
+        const double jb = std::floor((double)i - q + eps);
+        return a * (i + 1) + (jb >= 0 ? b * ((int64_t)jb + 1) : 0);
+    };
+    // starts at or before t1 + j d2: b (j + 1) + a (floor(j + q) + 1)
+    auto count_b = [&](int64_t j) { return b * (j + 1) + a * ((int64_t)std::floor((double)j + q + eps) + 1); };
+    auto first = [&](auto&& cnt) {   // smallest index whose count reaches n2
+        int64_t lo = 0, hi = (n2 + std::min(a, b) - 1) / std::min(a, b);
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) / 2;
+            if (cnt(mid) >= n2) hi = mid;
+            else lo = mid + 1;
+        }
+        return lo;
+    };
+    const double start = std::min(t0 + (double)first(count_a) * d2, t1 + (double)first(count_b) * d2);
+    return std::max(t1, start + d2);
 }
 
 // Piecewise-linear in t between measured points; the first point's value
@@ -364,6 +421,88 @@ struct Searcher {
         return v;
     }
 
+    // Both regions of a Pattern II cut in one launch over a kernel pair:
+    // launch + the merged-wave makespan of the two task lists (each task as
+    // long as its kernel's full-wave time g) + each region's split-K
+    // reduction.  Not additive over the regions.
+    double fused_cost(int a, const SplitChoice& c1, int64_t m1, int64_t n1, int b, const SplitChoice& c2,
+                      int64_t m2, int64_t n2, Region* r1, Region* r2) {
+        const double v1 = cost(a, c1, m1, n1, r1);
+        const double v2 = cost(b, c2, m2, n2, r2);
+        (void)v1;
+        (void)v2;
+        const TableKernel& ka = tab.kernels[a];
+        const int64_t S = (int64_t)tab.cus * ka.wg_per_cu;
+        double v = tab.launch_us + merged_makespan(S, r1->tasks, c1.g, r2->tasks, c2.g);
+        for (const Region* r : {r1, r2})
+            if (r->s > 1)
+                v += tab.red_launch_us +
+                     (double)(2 * r->s + 1) * 4.0 * (double)r->m * (double)r->n * (double)batch / (tab.red_gbps * 1e3);
+        return v;
+    }
+
+    bool fuse_allowed() const {
+        return opt.fuse && opt.cost_mode == COST_FULL && opt.force_kernel < 0 && opt.allow_II && !tab.pairs.empty();
+    }
+
+    // Visit every one-launch Pattern II candidate: for each kernel pair
+    // (a, b), direction, split of a and wave-boundary cut (as for Pattern
+    // II), and split of b.  fn(cost, r1, r2, dir) sees each; it returns true
+    // when the candidate became the best so far.  With use_bound, candidates
+    // whose lower bound reaches `bound` are skipped: the makespan is at
+    // least the first region's own waves, ceil(n1/S) d1 (which only grows
+    // with the cut), and at least the total work over the slots.
+    template <class F>
+    void fused_candidates(double bound, bool use_bound, F&& fn) {
+        auto red = [&](int s_eff, int64_t m, int64_t n) {
+            return s_eff > 1 ? tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)m * (double)n *
+                                                       (double)batch / (tab.red_gbps * 1e3)
+                             : 0.0;
+        };
+        for (auto& pr : tab.pairs) {
+            const int a = pr.first, b = pr.second;
+            if (!kernel_allowed(a) || !kernel_allowed(b)) continue;
+            const TableKernel& ka = tab.kernels[a];
+            const TableKernel& kb = tab.kernels[b];
+            const int64_t S = (int64_t)tab.cus * ka.wg_per_cu;
+            for (int dir = 0; dir < 2; ++dir) {
+                if (dir == 0 && !tab.pat_IIM) continue;
+                if (dir == 1 && !tab.pat_IIN) continue;
+                const int64_t ext = dir == 0 ? M : N;
+                const int64_t step = dir == 0 ? ka.uM : ka.uN;
+                const int64_t across = dir == 0 ? ceil_div(N, ka.uN) : ceil_div(M, ka.uM);
+                for (auto& c1s : sc[a]) {
+                    const int64_t per_line = across * c1s.s_eff * batch;
+                    int64_t prev_cut = 0;
+                    for (int64_t w = 1;; ++w) {
+                        const int64_t cut = (w * S / per_line) * step;
+                        if (cut >= ext) break;
+                        if (cut == 0 || cut == prev_cut) continue;
+                        prev_cut = cut;
+                        const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
+                        const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
+                        const int64_t t1 = ceil_div(m1, ka.uM) * ceil_div(n1, ka.uN) * c1s.s_eff * batch;
+                        const double own1 = (double)ceil_div(t1, S) * c1s.g;
+                        const double red1 = red(c1s.s_eff, m1, n1);
+                        if (use_bound && tab.launch_us + own1 + red1 >= bound) break;
+                        for (auto& c2s : sc[b]) {
+                            const int64_t t2 = ceil_div(m2, kb.uM) * ceil_div(n2, kb.uN) * c2s.s_eff * batch;
+                            const double lbv = tab.launch_us + red1 + red(c2s.s_eff, m2, n2) +
+                                               std::max(own1, ((double)t1 * c1s.g + (double)t2 * c2s.g) / (double)S);
+                            if (use_bound && lbv >= bound) continue;
+                            Region r1, r2;
+                            const double v = fused_cost(a, c1s, m1, n1, b, c2s, m2, n2, &r1, &r2);
+                            r1.m0 = r1.n0 = 0;
+                            r2.m0 = dir == 0 ? cut : 0;
+                            r2.n0 = dir == 0 ? 0 : cut;
+                            if (fn(v, r1, r2, dir)) bound = std::min(bound, v);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
     double best_region(int ki, int64_t m, int64_t n, Region* r) {
         double best = std::numeric_limits<double>::infinity();
         for (auto& c : sc[ki]) {
@@ -389,6 +528,7 @@ struct Searcher {
             double cost;
             int pattern;
             Region r1, r2;
+            bool fused = false;
         };
         std::vector<Cand> all;
         const int nk = (int)tab.kernels.size();
@@ -436,6 +576,12 @@ struct Searcher {
                     }
                 }
             }
+        if (fuse_allowed())
+            fused_candidates(0.0, false, [&](double v, const Region& r1, const Region& r2, int dir) {
+                Cand x{v, dir == 0 ? PAT_IIM : PAT_IIN, r1, r2, true};
+                all.push_back(x);
+                return false;
+            });
         std::stable_sort(all.begin(), all.end(), [](const Cand& x, const Cand& y) { return x.cost < y.cost; });
         Plan p;
         p.rank = rank;
@@ -448,6 +594,7 @@ struct Searcher {
         const Cand& c = all[rank - 1];
         p.pattern = c.pattern;
         p.cost_us = c.cost;
+        p.fused = c.fused;
         p.regions.push_back(c.r1);
         if (c.pattern != PAT_I) p.regions.push_back(c.r2);
         p.regions[0].m0 = p.regions[0].n0 = 0;
@@ -521,6 +668,17 @@ struct Searcher {
                 }
             }
         }
+        // one-launch Pattern II over kernel pairs (not additive: scored
+        // whole, bounded by the first region's full waves)
+        if (fuse_allowed())
+            fused_candidates(best.cost_us, prune(), [&](double v, const Region& r1, const Region& r2, int dir) {
+                if (!(v < best.cost_us)) return false;
+                best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
+                best.cost_us = v;
+                best.fused = true;
+                best.regions.assign({r1, r2});
+                return true;
+            });
         return best;
     }
 };
@@ -642,6 +800,7 @@ std::string plan_to_json(const Plan& p, const PerfTable& tab) {
       << ",\"plan_us\":" << p.plan_us << ",\"evaluated\":" << p.evaluated;
     if (p.rank > 0) o << ",\"rank\":" << p.rank << ",\"candidates\":" << p.candidates;
     o << ",\"transpose_b\":" << (p.transpose_b ? "true" : "false");
+    o << ",\"fused\":" << (p.fused ? "true" : "false");
     if (p.transpose_b) o << ",\"transpose_us\":" << p.transpose_us;
     o << ",\"regions\":[";
     for (size_t i = 0; i < p.regions.size(); ++i) {

@@ -50,6 +50,10 @@ struct PerfTable {
     double mfma_tflops = 0.0;     // measured sustained bf16 MFMA rate (0: unknown)
     double hbm_gbps = 0.0;        // measured streaming-copy bandwidth (0: unknown)
     std::vector<TableKernel> kernels;
+    // Kernel pairs (indices into kernels) compiled into one launch: a Pattern
+    // II plan over such a pair may run both regions in one launch.  Both
+    // kernels of a pair share layout and resident workgroups per CU.
+    std::vector<std::pair<int, int>> pairs;
 };
 
 enum PatternKind { PAT_EMPTY = 0, PAT_ZERO = 1, PAT_I = 2, PAT_IIM = 3, PAT_IIN = 4 };
@@ -76,6 +80,7 @@ struct Plan {
     int64_t candidates = 0;  // size of the ranked candidate list (rank > 0 only)
     bool transpose_b = false;  // a K x N B is first copied to N x K; regions use N x K kernels
     double transpose_us = 0.0; // modelled time of that copy (included in cost_us)
+    bool fused = false;        // the two regions run in one launch (a kernel pair)
 };
 
 // Which factors of the cost model the search scores (MikPoly page, section 4
@@ -93,6 +98,7 @@ struct SearchOptions {
     int cost_mode = COST_FULL;
     int plan_rank = 0;       // >0: return the rank-th cheapest candidate of the whole space
     bool bt = false;         // B is N x K: only kernels of that layout take part
+    bool fuse = false;       // consider one-launch Pattern II plans over kernel pairs
 };
 
 // Parse the text form of a table.  Returns false and sets err on bad input.
@@ -108,6 +114,13 @@ double tail_ratio(const std::vector<std::pair<double, double>>& pts, double f);
 double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots);
 double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K,
                    int64_t batch, int s_req, Region* out);
+
+// Time to run n1 tasks of duration d1 and then n2 tasks of duration d2 on S
+// slots, each task starting on the earliest free slot in that order (the
+// merged-wave view of one launch holding two regions): the second region's
+// tasks fill the slots the first region's last wave leaves free.  With
+// d1 == d2 it is ceil((n1 + n2) / S) * d1.
+double merged_makespan(int64_t S, int64_t n1, double d1, int64_t n2, double d2);
 
 Plan polymerize(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_t K,
                 const SearchOptions& opt);

@@ -250,7 +250,8 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("planner_eval needs a GPU")
     torch.cuda.init()
-    kernels = mkp.mkp_kernel_names()
+    # the calls give B as K x N: the fixed-kernel baselines are the K x N kernels
+    kernels = [k for k in mkp.mkp_kernel_names() if not k.endswith("_nk")]
     splits = table_splits(os.environ.get("MKP_CALIB", os.path.join(HERE, "calib", "gfx950.tbl")))
     seen, cases = set(), []
     for c in workloads.config_cases(a.config):

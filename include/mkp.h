@@ -178,9 +178,11 @@ int mkp_plan_describe_grouped(int64_t groups, int64_t M, int64_t K, const int64_
  * Writes NUL-terminated JSON into buf:
  *   {"pattern":..., "cost_us":..., "plan_us":..., "regions":[{"m0","n0","m",
  *    "n","kernel","uM","uN","uK","s","steps","tasks","waves","wave_factor",
- *    "cost_us"}...], "transpose_b": bool [, "transpose_us"]}
+ *    "cost_us"}...], "transpose_b": bool [, "transpose_us"], "fused": bool}
  * transpose_b: a K x N B is first copied into N x K workspace rows and the
  * regions run on N x K kernels (the cheaper plan by the cost model).
+ * fused: the two regions of a Pattern II plan run in one launch of a
+ * two-tile kernel (option "fuse_regions").
  * Uses the active performance table (calibrated, or the built-in analytic
  * one).  Pure host code: needs no GPU.  Returns MKP_OK, MKP_ERR_INVALID_ARG
  * or MKP_ERR_BUFFER.
@@ -211,12 +213,16 @@ int mkp_plan_with_table(const char *table_text, int flags,
  *   g <name> <t>:<us> <t>:<us> ...   measured <TFLOP/s> <GB/s>
  *   tail <name> <f>:<r> ...          tailx <name> <f>:<r> ...
  *   transpose <launch_us> <GB/s>     (copy of a K x N B into N x K)
+ *   pair <name a> <name b>           (a and b can share one launch)
  * (kn / nk: the kernel takes B as K x N, the default, or as N x K; tail and
  * tailx: time of a wave filling a fraction f < 1 of the slots, on its own or
  * after full waves, relative to a full wave.)  Kernels named here must exist
  * in the library with the same tile and layout; a table with no kernel of
- * one layout gets analytic estimates for that layout's kernels.  Clears the
- * plan cache.
+ * one layout gets analytic estimates for that layout's kernels.  Each pair
+ * must be one the library compiles into a two-tile kernel (same layout and
+ * resident workgroups per CU); a table without pair lines gets all of the
+ * library's pairs whose kernels it prices with equal workgroups per CU.
+ * Clears the plan cache.
  */
 int mkp_load_calibration(const char *path);
 
@@ -241,6 +247,13 @@ int mkp_calibrate(const char *path, int max_points);
  * default: a K x N call may copy B into N x K workspace rows and run on the
  * N x K kernels, when the table prices the copy and the model finds it
  * cheaper; 2 = always, whenever an N x K plan exists).
+ * "fuse_regions" (0 = the default: every region of a plan is a launch of its
+ * own; 1 = a Pattern II plan over a kernel pair may run both regions in one
+ * launch, the second region's workgroups taking the slots the first
+ * region's last wave leaves free, when the cost model -- launch + the
+ * merged-wave makespan of both regions' tasks + reductions -- finds it
+ * cheaper; off by default because on the encoder-linear sweep it measured no
+ * faster than two launches).
  * Cost-model evaluation (MikPoly page, section 5 "cost-model effectiveness":
  * the WAVE and PIPE ablations and the ORACLE that measures candidates):
  * "cost_model" ("full" = f_wave * f_pipe, the default; "wave" = f_wave with
@@ -270,6 +283,7 @@ void mkp_cache_clear(void);
 int mkp_stats(char *buf, size_t len);
 
 /* Launch trace (option "trace" = 1): every kernel launch (micro-kernels,
+ * "<a>+<b>" for both regions in one launch of a kernel pair,
  * "splitk_reduce", "zero_fill", "pack_rows", "transpose_b") is bracketed by
  * HIP events on its stream.  Waits for the recorded launches, writes a JSON
  * list [{"kernel","call","us","flops","bytes"}...] ("call": sequence number

@@ -40,6 +40,12 @@ Readings where the page is silent (each is listed in the design doc):
     call searches the kernels of its layout.  A K x N call may instead pay
     for a transpose of B (launch + 4*K*N*batch bytes / bandwidth) and run
     the N x K search; the cheaper of the two is the plan.
+  * one launch for both regions (not on the page as an interface; its case
+    study merges the two regions' warps into common waves): for a kernel
+    pair listed in the table, a Pattern II candidate may run as one launch
+    whose tasks are taken in order by the earliest free slot; its cost is
+    launch + the makespan of that schedule (each task lasting its kernel's
+    full-wave time) + the reductions.  Not additive over the regions.
   * Pattern I: one region = whole output, one kernel.  Pattern II-M (II-N):
     a cut of the M (N) extent, the two parts on two different kernels (the
     case study's 3072 | 1024 split).  The cut is a wave boundary of the
@@ -78,6 +84,7 @@ class Table:
     kernels: Dict[str, Kernel]
     tr_launch_us: float = 0.0
     tr_gbps: float = 0.0
+    pairs: List[Tuple[str, str]] = dataclasses.field(default_factory=list)  # one-launch kernel pairs
 
     def slots(self, k: Kernel) -> int:
         return self.cus * k.wg_per_cu
@@ -93,6 +100,7 @@ def parse_table(text: str) -> Table:
     patterns = ["I", "II-M", "II-N"]
     kernels: Dict[str, Kernel] = {}
     gpts: Dict[str, List[Tuple[float, float]]] = {}
+    pairs: List[Tuple[str, str]] = []
     tails: Dict[str, List[Tuple[float, float]]] = {}
     tailxs: Dict[str, List[Tuple[float, float]]] = {}
     for raw in text.splitlines():
@@ -126,6 +134,8 @@ def parse_table(text: str) -> Table:
                 t, v = p.split(":")
                 pts.append((float(t), float(v)))
             gpts.setdefault(tok[1], []).extend(pts)
+        elif key == "pair":
+            pairs.append((tok[1], tok[2]))
         elif key in ("tail", "tailx"):
             for p in tok[2:]:
                 f, r = p.split(":")
@@ -141,7 +151,11 @@ def parse_table(text: str) -> Table:
     for k in kernels.values():
         if not k.pts:
             raise ValueError(f"kernel {k.name} has no g points")
-    return Table(cus, launch, red_l, red_bw, splits, patterns, kernels, tr_l, tr_bw)
+    for a, b in pairs:
+        ka, kb = kernels[a], kernels[b]
+        if a == b or ka.bt != kb.bt or ka.wg_per_cu != kb.wg_per_cu:
+            raise ValueError(f"bad pair {a} {b}")
+    return Table(cus, launch, red_l, red_bw, splits, patterns, kernels, tr_l, tr_bw, pairs)
 
 
 def g_predict(k: Kernel, t: float) -> float:
@@ -228,9 +242,54 @@ def _valid_splits(tab: Table, k: Kernel, K: int) -> List[int]:
     return [s for s in tab.splits if 1 <= s <= max(t3, 1)]
 
 
-def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1, bt: bool = False):
+def makespan_sim(S: int, n1: int, d1: float, n2: int, d2: float) -> float:
+    """Finish time of n1 tasks of duration d1 followed by n2 tasks of
+    duration d2 on S slots, each task taken in order by the earliest free
+    slot -- simulated task by task (the merged-wave view of one launch that
+    holds two regions, MikPoly page case study: the second region's warps
+    fill the waves the first leaves free)."""
+    import heapq
+
+    free = [0.0] * S
+    end = 0.0
+    for d, n in ((d1, n1), (d2, n2)):
+        for _ in range(n):
+            t = heapq.heappop(free)
+            heapq.heappush(free, t + d)
+            end = max(end, t + d)
+    return end
+
+
+def fused_cost(tab: Table, regions: Sequence[Region], K: int, batch: int) -> float:
+    """Both regions of a Pattern II plan in one launch over a kernel pair:
+    launch + the simulated makespan of the two task lists, each task taking
+    its kernel's full-wave time g(f_num), + each region's split-K reduction."""
+    r1, r2 = regions
+    k1, k2 = tab.kernels[r1.kernel], tab.kernels[r2.kernel]
+    S = tab.slots(k1)
+    parts = []
+    c = tab.launch_us
+    for r, k in ((r1, k1), (r2, k2)):
+        per, s_eff = split_steps(ceil_div(K, k.uK), r.s)
+        parts.append((ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch, g_predict(k, per)))
+        if s_eff > 1:
+            c += tab.red_launch_us + (2 * s_eff + 1) * 4.0 * r.m * r.n * batch / (tab.red_gbps * 1e3)
+    return c + makespan_sim(S, parts[0][0], parts[0][1], parts[1][0], parts[1][1])
+
+
+def candidate_cost(tab: Table, pat: str, regions: Sequence[Region], K: int, batch: int, mode: str = "full") -> float:
+    """Modelled cost of one candidate: one-launch candidates (pattern names
+    ending in '+1') are scored whole, the others region by region."""
+    if pat.endswith("+1"):
+        return fused_cost(tab, regions, K, batch)
+    return plan_cost(tab, regions, K, batch, mode)
+
+
+def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1, bt: bool = False, fused: bool = False):
     """Every candidate strategy of the search space, no pruning; only the
-    kernels that take B in the call's layout (K x N, or N x K when bt)."""
+    kernels that take B in the call's layout (K x N, or N x K when bt).
+    With `fused`, also the one-launch form ('II-M+1', 'II-N+1') of every
+    Pattern II candidate over a kernel pair of the table."""
     names = sorted(n for n, k in tab.kernels.items() if k.bt == bt)
     if "I" in tab.patterns:
         for a in names:
@@ -268,14 +327,16 @@ def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1, bt: bool
                                 r1 = Region(0, 0, M, cut, a, s1)
                                 r2 = Region(0, cut, M, N - cut, b, s2)
                             yield pat, (r1, r2)
+                            if fused and (a, b) in tab.pairs:
+                                yield pat + "+1", (r1, r2)
 
 
 def exhaustive_best(tab: Table, M: int, N: int, K: int, batch: int = 1, mode: str = "full", bt: bool = False):
     """Minimum modelled cost over the whole space (the page's ORACLE variant
     searches exhaustively; here only the modelled cost is minimised)."""
     best: Optional[Tuple[float, str, tuple]] = None
-    for pat, regs in enumerate_plans(tab, M, N, K, batch, bt):
-        c = plan_cost(tab, regs, K, batch, mode)
+    for pat, regs in enumerate_plans(tab, M, N, K, batch, bt, fused=mode == "full"):
+        c = candidate_cost(tab, pat, regs, K, batch, mode)
         if best is None or c < best[0]:
             best = (c, pat, regs)
     return best
@@ -286,14 +347,14 @@ def distinct_candidates(tab: Table, M: int, N: int, K: int, batch: int = 1, mode
     same number of splits are one candidate) with its modelled cost, sorted
     by cost."""
     seen = {}
-    for pat, regs in enumerate_plans(tab, M, N, K, batch):
+    for pat, regs in enumerate_plans(tab, M, N, K, batch, fused=mode == "full"):
         key = [pat]
         for r in regs:
             t3 = ceil_div(K, tab.kernels[r.kernel].uK)
             key.append((r.m0, r.n0, r.m, r.n, r.kernel, split_steps(t3, r.s)[1]))
         key = tuple(key)
         if key not in seen:
-            seen[key] = (plan_cost(tab, regs, K, batch, mode), pat, regs)
+            seen[key] = (candidate_cost(tab, pat, regs, K, batch, mode), pat, regs)
     return sorted(seen.values(), key=lambda x: x[0])
 
 

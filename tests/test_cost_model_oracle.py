@@ -274,3 +274,62 @@ def test_grouped_best_is_minimum_over_enumeration():
         costs = [cm.grouped_cost(tab, n, s, M, K, Ns) for n in tab.kernels for s in (1, 2, 4)
                  if s <= max(cm.ceil_div(K, tab.kernels[n].uK), 1)]
         assert best[0] == pytest.approx(min(costs), rel=1e-12)
+
+
+# ---- one launch for two regions: the merged-wave schedule ------------------
+
+def test_makespan_hand_worked():
+    # S = 4 slots, 6 tasks of 3 us then 5 of 1 us: the first wave of 4 ends
+    # at 3; two slots finish region 1 (3..6), the other two run region 2 at
+    # 3, 3, 4, 4, 5 -> the last ends at 6
+    assert cm.makespan_sim(4, 6, 3.0, 5, 1.0) == 6.0
+    # S = 3, 4 tasks of 2 then 7 of 1: starts 2, 2, 3, 3, 4, 4 (two slots)
+    # and 4 (the third slot, free at 4): last start 4, end 5
+    assert cm.makespan_sim(3, 4, 2.0, 7, 1.0) == 5.0
+    # the second region shorter than the first's last wave: the first region decides
+    assert cm.makespan_sim(4, 5, 10.0, 3, 1.0) == 20.0
+
+
+def test_makespan_equal_durations_is_merged_waves():
+    """With equal task times the launch runs ceil((n1 + n2) / S) waves --
+    the page's merged-warp count (its case study: 1792 warps in waves of
+    864 -> 3 waves)."""
+    assert cm.makespan_sim(864, 768, 1.0, 1024, 1.0) == 3.0
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        S = int(rng.integers(1, 40))
+        n1, n2 = (int(x) for x in rng.integers(0, 200, size=2))
+        assert cm.makespan_sim(S, n1, 2.5, n2, 2.5) == pytest.approx(math.ceil((n1 + n2) / S) * 2.5)
+
+
+def test_makespan_whole_waves_are_additive():
+    """When the first region fills whole waves the second starts on all
+    slots at once: the serial sum of the two regions' waves."""
+    rng = np.random.default_rng(13)
+    for _ in range(50):
+        S = int(rng.integers(1, 30))
+        w = int(rng.integers(0, 5))
+        n2 = int(rng.integers(1, 100))
+        d1, d2 = rng.uniform(0.5, 4, size=2)
+        assert cm.makespan_sim(S, w * S, d1, n2, d2) == pytest.approx(w * d1 + math.ceil(n2 / S) * d2)
+
+
+def test_fused_candidates_only_for_pairs():
+    text = """device 2
+launch_us 1
+splitk 1
+kernel a 32 32 32 1
+kernel b 16 16 32 1
+kernel c 16 32 32 2
+g a 1:4
+g b 1:1
+g c 1:1
+pair a b
+"""
+    tab = cm.parse_table(text)
+    pats = [p for p, _ in cm.enumerate_plans(tab, 100, 64, 32, fused=True)]
+    fused = [p for p in pats if p.endswith("+1")]
+    assert fused and len(fused) == sum(1 for p, r in cm.enumerate_plans(tab, 100, 64, 32, fused=True)
+                                      if p.endswith("+1") and r[0].kernel == "a" and r[1].kernel == "b")
+    with pytest.raises(ValueError):
+        cm.parse_table(text + "pair a c\n")   # different workgroups per CU

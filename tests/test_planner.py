@@ -83,6 +83,9 @@ def random_table(rng, nk, tails=False):
 
 
 def test_pruned_search_is_exact(mkp):
+    """Also: one-launch candidates stay out of the search unless enabled."""
+    text = _with_pairs(np.random.default_rng(1), random_table(np.random.default_rng(1), 3))
+    assert not mkp.mkp_plan_with_table(text, 1, 300, 300, 300)["fused"]
     rng = np.random.default_rng(2024)
     checked = 0
     for trial in range(40):
@@ -323,3 +326,78 @@ def test_grouped_plan_matches_oracle_on_random_tables(mkp, tmp_path):
                 _check_grouped(mkp, tab, M, K, Ns, bool(rng.integers(0, 2)))
     finally:
         mkp.mkp_load_calibration(None)
+
+
+def _with_pairs(rng, text):
+    """Append pair lines for kernels of equal workgroups per CU (and layout)."""
+    tab = cm.parse_table(text)
+    names = sorted(tab.kernels)
+    lines = []
+    for a in names:
+        for b in names:
+            ka, kb = tab.kernels[a], tab.kernels[b]
+            if a != b and ka.wg_per_cu == kb.wg_per_cu and ka.bt == kb.bt and rng.uniform() < 0.7:
+                lines.append(f"pair {a} {b}")
+    return text + "\n".join(lines) + "\n"
+
+
+@pytest.fixture
+def fuse_on(mkp):
+    mkp.mkp_set_option("fuse_regions", 1)
+    yield
+    mkp.mkp_set_option("fuse_regions", 0)
+
+
+def test_one_launch_plans_match_oracle(mkp, fuse_on):
+    """Tables with kernel pairs: the planner's choice (one-launch Pattern II
+    plans scored by the merged-wave makespan, with its bounds) reaches the
+    oracle's exhaustive minimum, whose makespan is simulated task by task."""
+    rng = np.random.default_rng(77)
+    fused_seen = 0
+    for trial in range(60):
+        text = random_table(rng, int(rng.integers(2, 5)), tails=bool(trial % 2))
+        # equal workgroups per CU for most kernels, so that pairs exist
+        text = "\n".join(l if not l.startswith("kernel") else " ".join(l.split()[:5] + ["2"])
+                         for l in text.splitlines()) + "\n"
+        text = _with_pairs(rng, text)
+        tab = cm.parse_table(text)
+        M, N, K = (int(x) for x in rng.integers(1, 400, size=3))
+        batch = int(rng.choice([1, 1, 2]))
+        plan = mkp.mkp_plan_with_table(text, batch, M, N, K)
+        ex = mkp.mkp_plan_with_table(text, batch, M, N, K, exhaustive=True)
+        best = cm.exhaustive_best(tab, M, N, K, batch)
+        assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (trial, M, N, K, batch, best[1])
+        assert ex["cost_us"] == pytest.approx(best[0], rel=1e-9)
+        regs = to_regions(plan)
+        pat = plan["pattern"] + ("+1" if plan["fused"] else "")
+        assert cm.candidate_cost(tab, pat, regs, K, batch) == pytest.approx(plan["cost_us"], rel=1e-9)
+        if plan["fused"]:
+            fused_seen += 1
+            assert (regs[0].kernel, regs[1].kernel) in tab.pairs
+        assert cm.covers_exactly(M, N, regs, {n: (k.uM, k.uN) for n, k in tab.kernels.items()})
+    assert fused_seen >= 5
+
+
+def test_ranked_list_includes_one_launch_candidates(mkp, fuse_on):
+    """With kernel pairs the ranked space holds the one-launch form of each
+    paired Pattern II candidate; plan_rank walks it in the oracle's order."""
+    rng = np.random.default_rng(78)
+    try:
+        for trial in range(8):
+            text = random_table(rng, 3)
+            text = "\n".join(l if not l.startswith("kernel") else " ".join(l.split()[:5] + ["1"])
+                             for l in text.splitlines()) + "\n"
+            text = _with_pairs(rng, text)
+            tab = cm.parse_table(text)
+            M, N, K = (int(x) for x in rng.integers(20, 150, size=3))
+            cands = cm.distinct_candidates(tab, M, N, K, 1)
+            n = len(cands)
+            assert any(c[1].endswith("+1") for c in cands)
+            for r in sorted({1, 2, max(1, n // 3), n}):
+                mkp.mkp_set_option("plan_rank", str(r))
+                p = mkp.mkp_plan_with_table(text, 1, M, N, K)
+                assert p["candidates"] == n and p["cost_us"] == pytest.approx(cands[r - 1][0], rel=1e-9), (trial, r)
+                pat = p["pattern"] + ("+1" if p["fused"] else "")
+                assert cm.candidate_cost(tab, pat, to_regions(p), K, 1) == pytest.approx(p["cost_us"], rel=1e-9)
+    finally:
+        mkp.mkp_set_option("plan_rank", "0")
