@@ -155,6 +155,108 @@ class Workload:
                                      case.K * case.N, tc, case.N, case.M * case.N, stream)
 
 
+class ConvWorkload:
+    """Device-resident operands for the convolution sweep (NHWC inputs, KRSC
+    filters, NPQK fp32 outputs), each call through mkp_conv2d."""
+
+    bt = True
+    qkv = "merged"
+    epilogue = "none"
+
+    def __init__(self):
+        import torch
+        import workloads
+
+        self.cfg = "conv"
+        self.cases = workloads.conv_cases()
+        self.calls, self.host, self.keep = [], [], []
+        for case in self.cases:
+            x, w = workloads.make_conv_operands(case)
+            tx = torch.from_numpy(x.view(np.int16)).cuda()
+            tw = torch.from_numpy(w.view(np.int16)).cuda()
+            ty = torch.empty((case.N, case.P, case.Q, case.K), dtype=torch.float32, device="cuda")
+            self.keep += [tx, tw]
+            self.calls.append((case, tx.data_ptr(), tw.data_ptr(), ty))
+            self.host.append((case, x, w))
+        self.flops = sum(c.flops for c in self.cases)
+        self.bytes = sum(c.bytes for c in self.cases)
+
+    def is_qkv(self, case) -> bool:
+        return False
+
+    def calls_per_case(self):
+        return [1] * len(self.cases)
+
+    def step(self, mkp, stream):
+        for c, px, pw, ty in self.calls:
+            mkp.mkp_conv2d(c.N, c.H, c.W, c.C, c.K, c.R, c.S, c.stride, c.stride, c.pad, c.pad, 1, 1, px, pw, ty,
+                           None, 0, stream)
+
+
+def conv_vs_gemm(wl, mkp, stream):
+    """Each convolution against a plain N x K GEMM of the same M = N P Q,
+    N = K, K = R S C (A a zero-filled M x K buffer), both through the
+    library: mean of 50 back-to-back calls after 20 warm-up, between two HIP
+    events on the launch stream.  Returns [(tag, M, N, K, conv us, GEMM us)]."""
+    import torch
+
+    cur = torch.cuda.current_stream()
+
+    def timeit(fn):
+        for _ in range(20):
+            fn()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(cur)
+        for _ in range(50):
+            fn()
+        e.record(cur)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / 50
+
+    rows = []
+    for c, px, pw, ty in wl.calls:
+        M, N, K = c.M, c.K, c.Kg
+        ta = torch.zeros((M, K), dtype=torch.int16, device="cuda")
+        tc = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        t_conv = timeit(lambda: mkp.mkp_conv2d(c.N, c.H, c.W, c.C, c.K, c.R, c.S, c.stride, c.stride, c.pad, c.pad,
+                                               1, 1, px, pw, ty, None, 0, stream))
+        t_gemm = timeit(lambda: mkp.mkp_gemm_bt(M, N, K, ta, K, pw, K, tc, N, stream))
+        rows.append((c.tag, M, N, K, round(t_conv, 3), round(t_gemm, 3)))
+        del ta, tc
+    return rows
+
+
+def conv_cpu_baseline(wl, budget_s: float):
+    """The convolution oracle as it stands on the first image of each call in
+    order, until `budget_s` seconds have elapsed."""
+    from oracle import conv as ocv
+
+    t0 = time.perf_counter()
+    flops, n = 0, 0
+    img = 0
+    while time.perf_counter() - t0 < budget_s:
+        done = False
+        for case, x, w in wl.host:
+            if time.perf_counter() - t0 >= budget_s:
+                break
+            if img >= case.N:
+                continue
+            ocv.conv2d(x[img:img + 1], w, (case.stride, case.stride), (case.pad, case.pad))
+            flops += case.flops // case.N
+            n += 1
+            done = True
+        img += 1
+        if not done:
+            break
+    dt = time.perf_counter() - t0
+    import os as _os
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": len(_os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"binary64 convolution oracle (numpy), one image at a time over the calls in order, {n} images, "
+                      f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+
+
 def timed_steps(wl, mkp, steps, stream):
     import torch
     torch.cuda.synchronize()
@@ -290,6 +392,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", choices=["gemm", "conv"], default="gemm",
+                    help="the GEMM sweep of --config (default) or the ResNet-50 convolution sweep")
+    ap.add_argument("--vs-gemm", action="store_true",
+                    help="with --workload conv: also time each convolution against the plain GEMM of its shape "
+                         "(reported under config.conv_vs_gemm)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail", action="store_true", help="per-GEMM timings to stderr")
@@ -320,10 +427,13 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
-    log(f"[bench] generating config {args.config} inputs")
+    log(f"[bench] generating {'convolution sweep' if args.workload == 'conv' else f'config {args.config}'} inputs")
     if args.epilogue != "none" and args.qkv != "merged":
         raise SystemExit("--epilogue and --qkv are separate experiments")
-    wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv, epilogue=args.epilogue)
+    if args.workload == "conv":
+        wl = ConvWorkload()
+    else:
+        wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv, epilogue=args.epilogue)
     stream = torch.cuda.current_stream().cuda_stream
     mkp.mkp_set_option("fuse_regions", args.fuse_regions)
     mkp.mkp_cache_clear()
@@ -355,7 +465,7 @@ def main():
         recs_all.append(mkp.mkp_trace_dump())
     mkp.mkp_set_option("trace", 0)
     roof, per_kernel = roofline_from_trace([r for recs in recs_all for r in recs])
-    roof["traffic"] = recorded_traffic(roof["kernel"], args.config)
+    roof["traffic"] = recorded_traffic(roof["kernel"], args.config) if args.workload == "gemm" else None
     # per-call durations (a call may hold several launches), median of the traced steps
     per_step = []
     for recs in recs_all:
@@ -374,15 +484,17 @@ def main():
     fr = sweep_fraction(per_call, wl)
     if args.detail:
         for case, us, f in zip(wl.cases, per_call, fr):
+            # the GEMM view of the call (a convolution: N P Q x K x R S C)
+            gm, gn, gk = (case.M, case.K, case.Kg) if wl.cfg == "conv" else (case.M, case.N, case.K)
             if wl.is_qkv(case):
                 plan = mkp.mkp_plan_describe_grouped(case.M, case.K, [768] * 3, bt=wl.bt)
                 if wl.qkv == "separate":
                     plan = dict(mkp.mkp_plan_describe(1, case.M, 768, case.K, bt=wl.bt), pattern="3x")
             else:
-                plan = mkp.mkp_plan_describe(case.batch, case.M, case.N, case.K, bt=wl.bt)
+                plan = mkp.mkp_plan_describe(case.batch, gm, gn, gk, bt=wl.bt)
             ks = "+".join(f"{r['kernel']}/s{r['s']}" for r in plan["regions"]) + (" (1 launch)" if plan.get("fused")
                                                                                     else "")
-            log(f"  {case.tag:>14} {case.M:5d}x{case.N:5d}x{case.K:5d} b{case.batch:<3d} {us:9.2f} us "
+            log(f"  {case.tag:>14} {gm:5d}x{gn:5d}x{gk:5d} b{case.batch:<3d} {us:9.2f} us "
                 f"{case.flops / us / 1e6:8.1f} TF/s  {100 * f:5.1f}% of R  {plan['pattern']:4s} {ks}")
 
     out = {
@@ -399,9 +511,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": workloads.CONFIG_NAMES[args.config],
-            "config_index": args.config,
-            "b_layout": args.b_layout,
+            "workload": workloads.CONV_NAME if args.workload == "conv" else workloads.CONFIG_NAMES[args.config],
+            "config_index": None if args.workload == "conv" else args.config,
+            "b_layout": "nk" if args.workload == "conv" else args.b_layout,
             "qkv": wl.qkv,
             "epilogue": wl.epilogue,
             "fuse_regions": args.fuse_regions,
@@ -421,9 +533,13 @@ def main():
         },
         "roofline": roof,
     }
+    if args.vs_gemm and args.workload == "conv":
+        log("[bench] each convolution against the GEMM of its shape")
+        out["config"]["conv_vs_gemm"] = conv_vs_gemm(wl, mkp, stream)
     if not args.no_cpu:
         log(f"[bench] CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline"] = (conv_cpu_baseline(wl, args.cpu_seconds) if args.workload == "conv"
+                               else cpu_baseline(wl, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 

@@ -68,6 +68,8 @@ _lib.mkp_gemm_batched_bt.restype = _int
 _lib.mkp_gemm_ex.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _int, _p, _i64, _i64,
                              ctypes.c_float, ctypes.c_float, _p, _int, _p]
 _lib.mkp_gemm_ex.restype = _int
+_lib.mkp_conv2d.argtypes = [_i64] * 13 + [_p, _p, _p, _p, _int, _p]
+_lib.mkp_conv2d.restype = _int
 _grp_args = [_i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p]
 _lib.mkp_gemm_grouped.argtypes = _grp_args
 _lib.mkp_gemm_grouped.restype = _int
@@ -98,7 +100,7 @@ _lib.mkp_trace_dump.restype = _int
 _lib.mkp_last_error.argtypes = []
 _lib.mkp_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_ex", "mkp_gemm_grouped",
+EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_ex", "mkp_conv2d", "mkp_gemm_grouped",
             "mkp_gemm_grouped_bt", "mkp_plan_describe", "mkp_plan_describe_grouped", "mkp_plan_with_table",
             "mkp_load_calibration",
             "mkp_calibrate", "mkp_set_option", "mkp_kernel_count", "mkp_kernel_name", "mkp_cache_clear",
@@ -187,6 +189,25 @@ def mkp_gemm_ex_raw(batch, M, N, K, A, lda, strideA, B, ldb, strideB, b_layout, 
         act = ACTIVATIONS[act]
     return _lib.mkp_gemm_ex(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB, b_layout, _addr(C), ldc,
                             strideC, alpha, beta, _addr(bias), act, stream or 0)
+
+
+def mkp_conv2d_raw(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, x, w, y, bias=None,
+                   act=MKP_ACT_NONE, stream=0) -> int:
+    if not isinstance(act, int):
+        act = ACTIVATIONS[act]
+    return _lib.mkp_conv2d(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, _addr(x), _addr(w),
+                           _addr(y), _addr(bias), act, stream or 0)
+
+
+def mkp_conv2d(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, x, w, y, bias=None,
+               act=MKP_ACT_NONE, stream=None) -> int:
+    """y (N,P,Q,K) fp32 := act(conv2d(x (N,H,W,C) bf16, w (K,R,S,C) bf16) + bias)."""
+    return _check(mkp_conv2d_raw(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, x, w, y,
+                                 bias, act, _stream(stream)))
+
+
+def conv_out_size(H, R, stride, pad, dil):
+    return (H + 2 * pad - dil * (R - 1) - 1) // stride + 1
 
 
 def _i64_array(values):
@@ -371,4 +392,26 @@ def linear(a, w, bias=None, act=None, out=None, beta=0.0, stream=None):
         raise ValueError("out rows must be contiguous")
     mkp_gemm_ex(1, M, N, K, a, max(a.stride(0), 1), 0, w, max(w.stride(0), 1), 0, MKP_B_NK, out,
                 max(out.stride(0), 1), 0, 1.0, beta, bias, act, stream)
+    return out
+
+
+def conv2d(x, w, bias=None, act=None, stride=1, padding=0, dilation=1, out=None, stream=None):
+    """torch convenience: x (N,H,W,C) bf16 NHWC, w (K,R,S,C) bf16, contiguous;
+    returns (or fills) y (N,P,Q,K) fp32 = act(conv2d(x, w) + bias)."""
+    import torch
+    sh, sw = (stride, stride) if isinstance(stride, int) else stride
+    ph, pw = (padding, padding) if isinstance(padding, int) else padding
+    dh, dw = (dilation, dilation) if isinstance(dilation, int) else dilation
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bfloat16")
+    if not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x and w must be contiguous (NHWC and KRSC)")
+    N, H, W, C = x.shape
+    K, R, S, C2 = w.shape
+    if C2 != C:
+        raise ValueError("channel counts differ")
+    P, Q = conv_out_size(H, R, sh, ph, dh), conv_out_size(W, S, sw, pw, dw)
+    if out is None:
+        out = torch.empty((N, P, Q, K), dtype=torch.float32, device=x.device)
+    mkp_conv2d(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, x, w, out, bias, act, stream)
     return out

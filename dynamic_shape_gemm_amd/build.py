@@ -14,12 +14,14 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmkp.so")
 ROOT = os.path.dirname(HERE)
 
-# (source, object, extra flags): the kernel file builds as three translation
-# units (single-tile kernels; two-tile kernels per B layout), compiled side by side
+# (source, object, extra flags): the kernel file builds as four translation
+# units (single-tile kernels; two-tile kernels per B layout; convolution
+# kernels), compiled side by side
 UNITS = [
     ("kernels.hip", "kernels_p1.o", ["-DMKP_PART=1"]),
     ("kernels.hip", "kernels_p2.o", ["-DMKP_PART=2"]),
     ("kernels.hip", "kernels_p3.o", ["-DMKP_PART=3"]),
+    ("kernels.hip", "kernels_p4.o", ["-DMKP_PART=4"]),
     ("planner.cpp", "planner.o", []),
     ("api.cpp", "api.o", []),
 ]

@@ -25,6 +25,7 @@
 #include <shared_mutex>
 #include <sstream>
 #include <string>
+#include <tuple>
 #include <unordered_map>
 #include <vector>
 
@@ -47,9 +48,10 @@ struct Key {
     int64_t batch, M, N, K;
     int align, device;
     bool bt;   // B given as N x K
+    bool conv = false;   // implicit-GEMM convolution: single-tile plans, B as N x K, no transpose
     bool operator==(const Key& o) const {
         return batch == o.batch && M == o.M && N == o.N && K == o.K && align == o.align && device == o.device &&
-               bt == o.bt;
+               bt == o.bt && conv == o.conv;
     }
 };
 struct KeyHash {
@@ -66,6 +68,7 @@ struct KeyHash {
         mix((uint64_t)k.align);
         mix((uint64_t)k.device);
         mix((uint64_t)k.bt);
+        mix((uint64_t)k.conv);
         return (size_t)h;
     }
 };
@@ -97,7 +100,11 @@ struct Library {
     size_t cache_cap = 1 << 16;
 
     std::mutex ws_mu;
-    std::map<std::pair<int, void*>, Workspace> workspaces;
+    // per device: 256 zero bytes, the source of a convolution's padding
+    std::map<int, void*> zero_pages;
+    // per (device, stream, slot): slot 0 serves the GEMM launches, slot 1
+    // a convolution's channel-padded copies, which outlive slot 0's use
+    std::map<std::tuple<int, void*, int>, Workspace> workspaces;
 
     std::atomic<int64_t> hits{0}, misses{0}, launches{0};
     std::atomic<int64_t> plan_ns{0};
@@ -309,22 +316,22 @@ std::shared_ptr<const Plan> get_plan(const Key& key) {
     }
     SearchOptions o = L.opts;
     o.bt = key.bt;
-    const int tmode = key.batch <= 65535 ? L.transpose_b.load(std::memory_order_relaxed) : 0;
+    if (key.conv) o.fuse = false;   // no two-tile form of the convolution kernels
+    const int tmode = key.conv ? 0 : key.batch <= 65535 ? L.transpose_b.load(std::memory_order_relaxed) : 0;
     auto plan = std::make_shared<Plan>(plan_call(L.table, key.batch, key.M, key.N, key.K, o, tmode));
     L.misses.fetch_add(1, std::memory_order_relaxed);
     L.plan_ns.fetch_add((int64_t)(plan->plan_us * 1000.0), std::memory_order_relaxed);
     if (L.cache.size() >= L.cache_cap) L.cache.clear();
-    L.gcache.clear();
     L.cache.emplace(key, plan);
     return plan;
 }
 
 // ---- workspaces -------------------------------------------------------------
 
-int get_workspace(int dev, hipStream_t st, size_t bytes, void** out) {
+int get_workspace(int dev, hipStream_t st, size_t bytes, void** out, int slot = 0) {
     Library& L = lib();
     std::lock_guard<std::mutex> lk(L.ws_mu);
-    Workspace& w = L.workspaces[{dev, (void*)st}];
+    Workspace& w = L.workspaces[{dev, (void*)st, slot}];
     if (w.bytes < bytes) {
         size_t want = std::max(bytes, w.bytes * 2);
         want = (want + 4095) & ~(size_t)4095;
@@ -362,7 +369,7 @@ void free_workspaces() {
     (void)hipGetDevice(&cur);
     for (auto& kv : L.workspaces) {
         if (!kv.second.ptr) continue;
-        (void)hipSetDevice(kv.first.first);
+        (void)hipSetDevice(std::get<0>(kv.first));
         (void)hipDeviceSynchronize();
         (void)hipFree(kv.second.ptr);
     }
@@ -392,10 +399,20 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // C = A . B with B given as K x N (bt false) or as N x K (bt true, C = A . B^T
 // of the stored matrix).
+// Index of the convolution form of N x K kernel `lib`, or -1.
+int conv_for(int lib) {
+    if (lib < 0 || lib >= kernel_count()) return -1;
+    for (int i = 0; i < conv_count(); ++i)
+        if (std::strcmp(conv_info(i).twin, kernel_info(lib).name) == 0) return i;
+    return -1;
+}
+
 // With `epi` (non-null) every final value goes through the fused epilogue.
+// With `conv` (non-null) A is the NHWC input of an implicit-GEMM
+// convolution (bt must be set: B is the KRSC filter bank).
 int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int64_t lda, int64_t sA,
              const void* Bv, int64_t ldb, int64_t sB, float* C, int64_t ldc, int64_t sC, void* stream_v,
-             bool bt = false, const KEpi* epi = nullptr) {
+             bool bt = false, const KEpi* epi = nullptr, const KConv* conv = nullptr) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "dimension exceeds 2^31-1");
     if (batch == 0 || M == 0 || N == 0) return MKP_OK;
@@ -440,13 +457,16 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     // 128-bit loads need 16-byte aligned rows; the direct-load path also
     // keeps per-tile offsets (<= 256 rows of A, <= 64 rows of a K x N B,
     // <= 256 rows of an N x K B) in 32 bits
-    bool vA = aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0) && lda < (int64_t(1) << 23);
+    // (convolution: 16-byte aligned input with C % 8 == 0, so 8 channels of
+    // one tap are 16 aligned bytes)
+    bool vA = conv ? aligned16(A) && conv->C % 8 == 0
+                   : aligned16(A) && lda % 8 == 0 && (batch == 1 || sA % 8 == 0) && lda < (int64_t(1) << 23);
     bool vB = aligned16(B) && ldb % 8 == 0 && (batch == 1 || sB % 8 == 0) &&
               ldb < (int64_t(1) << (bt ? 23 : 25));
     const bool vC = aligned16(C) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
     const int align = (vA ? 1 : 0) | (vB ? 2 : 0) | (vC ? 4 : 0);
 
-    Key key{batch, M, N, K, align, dev, bt};
+    Key key{batch, M, N, K, align, dev, bt, conv != nullptr};
     std::shared_ptr<const Plan> plan = get_plan(key);
     if (plan->regions.empty()) {
         if (plan->rank > 0)
@@ -462,7 +482,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     // stream sharing it: [split-K counters][split-K partials][A copy][B copy].
     // The two regions of a one-launch plan run together: each gets its own
     // partial area and its own range of counters.
-    const bool one_launch = plan->fused && plan->regions.size() == 2;
+    const bool one_launch = !conv && plan->fused && plan->regions.size() == 2;
     auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
     size_t part_bytes = 0;
     size_t part_off[2] = {0, 0};
@@ -471,7 +491,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         if (r.s <= 1) continue;
         const int64_t ldw = (r.n + 3) & ~int64_t(3);
         const size_t bytes = (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float);
-        if (one_launch) {
+        if (one_launch && !conv) {
             part_off[i] = i == 0 ? 0 : round256(part_bytes);
             part_bytes = part_off[i] + bytes;
         } else {
@@ -487,7 +507,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     const int64_t b_rows = bt ? N : K, b_cols = bt ? K : N;
     const int64_t ldap = (K + 7) & ~int64_t(7), ldbp = (b_cols + 7) & ~int64_t(7);
     // (a copy pays off once several tile rows/columns re-read the operand)
-    const bool packA = pack_on && !vA && N > 192 && ldap < (int64_t(1) << 23);
+    const bool packA = !conv && pack_on && !vA && N > 192 && ldap < (int64_t(1) << 23);
     const bool packB = !tr && pack_on && !vB && M > 192 && ldbp < (int64_t(1) << (bt ? 23 : 25));
     const size_t offA = kCounterBytes + round256(part_bytes);
     const size_t bytesA = packA ? (size_t)batch * M * ldap * 2 : 0;
@@ -552,7 +572,11 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         if (ki.bt != kbt) return fail(MKP_ERR_UNSUPPORTED, "plan kernel has the other B layout");
         R.ki = &ki;
         KArgs& a = R.a;
-        a.A = A + r.m0 * lda;
+        a.A = conv ? A : A + r.m0 * lda;
+        if (conv) {
+            a.conv = *conv;
+            a.conv.m0 = (int)r.m0;
+        }
         a.B = kbt ? B + r.n0 * ldb : B + r.n0;
         a.lda = lda;
         a.ldb = ldb;
@@ -567,6 +591,15 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         a.splits = r.s;
         a.batch = (int)batch;
         a.flags = (vA ? KF_VEC_A : 0) | (vB ? KF_VEC_B : 0);
+        // (the direct-load gather keeps input offsets in 32 bits: from tap
+        // (0, 0) of the first pixel, up to pad rows/columns before the
+        // image, to the last tap of the last one)
+        if (conv && vA && conv->C % ki.uK == 0) {
+            const int64_t imgs = M / ((int64_t)conv->P * conv->Q);
+            const int64_t span = imgs * ((int64_t)conv->H + 2 * conv->ph + (int64_t)conv->dh * conv->R) *
+                                 ((int64_t)conv->W + 2 * conv->pw + (int64_t)conv->dw * conv->S) * conv->C;
+            if (span < INT_MAX / 2) a.flags |= KF_CONV_DMA;
+        }
         R.Creg = C + r.m0 * ldc + r.n0;
         R.ldw = (r.n + 3) & ~int64_t(3);
         if (r.s == 1) {
@@ -607,6 +640,9 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         if (R.G > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
         R.flops = 2.0 * r.m * r.n * K * batch;
         R.bytes = (double)batch * (2.0 * r.m * K + 2.0 * K * r.n + 4.0 * r.m * r.n) + ((a.flags & KF_EPI) ? r_epi : 0.0);
+        if (conv)   // the region's share of the input, its filters and its output, once each
+            R.bytes = 2.0 * (double)(M / ((int64_t)conv->P * conv->Q)) * conv->H * conv->W * conv->C * r.m / M +
+                      2.0 * K * r.n + 4.0 * r.m * r.n + ((a.flags & KF_EPI) ? r_epi : 0.0);
         R.red_bytes = (double)(r.s + 1) * 4.0 * r.m * r.n * batch + (epi ? r_epi : 0.0);
         return MKP_OK;
     };
@@ -647,8 +683,14 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         RegionLaunch R;
         int rc = setup(i, 0, kCounterCap, R);
         if (rc != MKP_OK) return rc;
+        auto launch = R.ki->launch;
+        if (conv) {
+            const int ci = conv_for(plan->regions[i].lib);
+            if (ci < 0) return fail(MKP_ERR_UNSUPPORTED, "plan kernel has no convolution form");
+            launch = conv_info(ci).launch;
+        }
         he = traced(L, st, plan->regions[i].lib, R.flops, R.bytes,
-                    [&] { return R.ki->launch(R.a, dim3((unsigned)R.G), st); });
+                    [&] { return launch(R.a, dim3((unsigned)R.G), st); });
         if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he));
         L.launches.fetch_add(1, std::memory_order_relaxed);
         if ((rc = reduce(i, R)) != MKP_OK) return rc;
@@ -855,6 +897,101 @@ int mkp_gemm_batched_bt(int64_t batch, int64_t M, int64_t N, int64_t K, const vo
     return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream, true);
 }
 
+// 256 zero bytes on device `dev` (allocated and cleared on first use).
+int zero_page(int dev, const uint16_t** out) {
+    Library& L = lib();
+    std::lock_guard<std::mutex> lk(L.ws_mu);
+    void*& p = L.zero_pages[dev];
+    if (!p) {
+        void* q = nullptr;
+        hipError_t e = hipMalloc(&q, 256);
+        if (e != hipSuccess || !q) {
+            (void)hipGetLastError();
+            return fail(MKP_ERR_OOM, "zero page: allocation failed");
+        }
+        e = hipMemset(q, 0, 256);
+        if (e != hipSuccess) {
+            (void)hipFree(q);
+            return fail(MKP_ERR_HIP, std::string("zero page: ") + hipGetErrorString(e));
+        }
+        p = q;
+    }
+    *out = (const uint16_t*)p;
+    return MKP_OK;
+}
+
+int mkp_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S, int64_t stride_h,
+               int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w, const void* x,
+               const void* w, float* y, const float* bias, int act, void* stream) {
+    if (N < 0 || K < 0 || H < 1 || W < 1 || C < 1 || R < 1 || S < 1)
+        return fail(MKP_ERR_INVALID_ARG, "bad dimension (H, W, C, R, S >= 1; N, K >= 0)");
+    if (stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || pad_h < 0 || pad_w < 0)
+        return fail(MKP_ERR_INVALID_ARG, "strides and dilations must be >= 1, padding >= 0");
+    if (act < 0 || act >= ACT_COUNT) return fail(MKP_ERR_INVALID_ARG, "unknown activation");
+    const int64_t span_h = dil_h * (R - 1) + 1, span_w = dil_w * (S - 1) + 1;
+    if (H + 2 * pad_h < span_h || W + 2 * pad_w < span_w)
+        return fail(MKP_ERR_INVALID_ARG, "filter larger than the padded input");
+    const int64_t P = (H + 2 * pad_h - span_h) / stride_h + 1, Q = (W + 2 * pad_w - span_w) / stride_w + 1;
+    if (N == 0 || K == 0) return MKP_OK;
+    const int64_t M = N * P * Q, Kg = R * S * C;
+    if (M > INT_MAX || Kg > INT_MAX || N * H > INT_MAX || H > INT_MAX / 4 || W > INT_MAX / 4 || C > INT_MAX / 4 ||
+        pad_h > INT_MAX / 4 || pad_w > INT_MAX / 4 || stride_h * P > INT_MAX / 4 || stride_w * Q > INT_MAX / 4 ||
+        dil_h * R > INT_MAX / 4 || dil_w * S > INT_MAX / 4)
+        return fail(MKP_ERR_INVALID_ARG, "convolution extents exceed the 32-bit index range");
+    if (!x || !w || !y) return fail(MKP_ERR_INVALID_ARG, "x, w or y is NULL");
+    const KEpi e{bias, 1.0f, 0.0f, act};
+    const KEpi* epi = (bias || act != ACT_NONE) ? &e : nullptr;
+    if (R == 1 && S == 1 && stride_h == 1 && stride_w == 1 && pad_h == 0 && pad_w == 0)
+        // a 1 x 1 convolution over every pixel: A is the input itself, an
+        // (N H W) x C matrix -- a plain GEMM with B given as K x C rows
+        return run_gemm(1, M, K, C, x, C, 0, w, C, 0, y, K, 0, stream, true, epi);
+    ensure_init();
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he));
+    const uint16_t* zero = nullptr;
+    int rc = zero_page(dev, &zero);
+    if (rc != MKP_OK) return rc;
+    // Channels not a multiple of 8 (or an unaligned input) would leave the
+    // gathers element by element: pad the channels of the input and of the
+    // filters to a multiple of 8 with zeros (the Bolt page pads kernels to
+    // alignment 8) -- the same convolution with C8 channels.
+    const uint16_t* xs = (const uint16_t*)x;
+    const uint16_t* ws = (const uint16_t*)w;
+    int64_t Cc = C;
+    if (C % 8 != 0 || !aligned16(x)) {
+        hipStream_t st = (hipStream_t)stream;
+        const int64_t C8 = (C + 7) & ~int64_t(7);
+        const int64_t xrows = N * H * W, wrows = K * R * S;
+        const size_t xbytes = ((size_t)xrows * C8 * 2 + 255) & ~size_t(255);
+        if (xrows > INT_MAX || wrows > INT_MAX || R * S * C8 > INT_MAX)
+            return fail(MKP_ERR_INVALID_ARG, "convolution extents exceed the 32-bit index range");
+        void* buf = nullptr;
+        t_call = lib().calls.load(std::memory_order_relaxed);   // the copies belong to this call's trace record
+        rc = get_workspace(dev, st, xbytes + (size_t)wrows * C8 * 2, &buf, 1);
+        if (rc != MKP_OK) return rc;
+        uint16_t* xp = (uint16_t*)buf;
+        uint16_t* wp = (uint16_t*)((char*)buf + xbytes);
+        Library& L = lib();
+        hipError_t e1 = traced(L, st, -3, 0.0, (double)xrows * (2.0 * C + 2.0 * C8), [&] {
+            return launch_pack_rows((const uint16_t*)x, C, 0, xp, C8, (int)xrows, (int)C, 1, st);
+        });
+        if (e1 != hipSuccess) return fail(MKP_ERR_HIP, std::string("pack launch: ") + hipGetErrorString(e1));
+        e1 = traced(L, st, -3, 0.0, (double)wrows * (2.0 * C + 2.0 * C8), [&] {
+            return launch_pack_rows((const uint16_t*)w, C, 0, wp, C8, (int)wrows, (int)C, 1, st);
+        });
+        if (e1 != hipSuccess) return fail(MKP_ERR_HIP, std::string("pack launch: ") + hipGetErrorString(e1));
+        xs = xp;
+        ws = wp;
+        Cc = C8;
+    }
+    const int64_t Kc = R * S * Cc;
+    const KConv cv{zero, 0, (int)H, (int)W, (int)Cc, (int)S, (int)P, (int)Q, (int)stride_h, (int)stride_w,
+                   (int)pad_h, (int)pad_w, (int)dil_h, (int)dil_w, (int)R};
+    // GEMM view: A (N P Q) x (R S C), B the filters as K x (R S C) rows, C the NPQK output
+    return run_gemm(1, M, K, Kc, xs, Kc, 0, ws, Kc, 0, y, K, 0, stream, true, epi, &cv);
+}
+
 static_assert(MKP_ACT_NONE == ACT_NONE && MKP_ACT_RELU == ACT_RELU && MKP_ACT_GELU == ACT_GELU &&
                   MKP_ACT_GELU_TANH == ACT_GELU_TANH && MKP_ACT_SILU == ACT_SILU && ACT_COUNT == 5,
               "activation codes of the C ABI and the kernels differ");
@@ -1028,7 +1165,7 @@ void mkp_cache_clear(void) {
         Library& L = lib();
         std::unique_lock<std::shared_mutex> lk(L.mu);
         L.cache.clear();
-    L.gcache.clear();
+        L.gcache.clear();
     }
     free_workspaces();
 }

@@ -18,6 +18,21 @@ enum : int {
     KF_VEC_C = 4,   // C rows 16-byte aligned: 128-bit stores allowed
     KF_VEC_COUT = 8,  // final C rows (fused split-K) 16-byte aligned
     KF_EPI = 16,      // apply the epilogue below to the final C values
+    KF_CONV_DMA = 32, // convolution with C % uK == 0 (a K step stays in one filter tap) and every
+                      // input offset, padding included, within 32 bits: direct loads
+};
+
+// Implicit-GEMM convolution (the MikPoly page runs convolutions as GEMMs):
+// A is never stored.  Row m of A is output pixel (n, p, q) of an NHWC input
+// and column k is filter tap (r, s) and input channel c, k = (r S + s) C + c;
+// A(m, k) = x[n][p sh - ph + r dh][q sw - pw + s dw][c], zero outside the
+// image.  B is the KRSC filter bank (an N x K matrix), C the NPQK output.
+struct KConv {
+    const uint16_t* zero;   // 16 zero bytes: where padded input is read from
+    int m0;                 // first A row of the launch's region
+    int H, W, C, S, P, Q;
+    int sh, sw, ph, pw, dh, dw;
+    int R;                  // filter height (bounds of the 32-bit direct-load offsets)
 };
 
 // Fused epilogue (Bolt page, epilogue fusion, and its persistent-kernel
@@ -71,6 +86,7 @@ struct KArgs {
     int ngroups;
     KGroup group[kMaxGroups];
     KEpi epi;             // used when flags has KF_EPI
+    KConv conv;           // convolution kernels only: A is the NHWC input
 };
 
 struct KernelInfo {
@@ -99,6 +115,16 @@ struct DualInfo {
 };
 int dual_count();
 const DualInfo& dual_info(int i);
+
+// The convolution form of an N x K micro-kernel (same tile; A gathered from
+// an NHWC input through KArgs::conv).
+struct ConvInfo {
+    const char* twin;     // name of the N x K kernel with the same tile
+    const void* func;
+    hipError_t (*launch)(const KArgs&, dim3 grid, hipStream_t);
+};
+int conv_count();
+const ConvInfo& conv_info(int i);
 
 // Sum of `splits` partials W[z] (z ascending) into C; W is [splits][batch][M][ldw].
 // With an epilogue (epi non-null) the sum goes through it; splits == 0 is an

@@ -31,10 +31,10 @@
 
 #include <hip/hip_runtime.h>
 
-// The file builds as three translation units compiled side by side: part 1
+// The file builds as four translation units compiled side by side: part 1
 // holds the single-tile kernels, the helper kernels and their launchers,
-// parts 2 and 3 the two-tile kernels for B as K x N and as N x K; without
-// MKP_PART it holds everything.
+// parts 2 and 3 the two-tile kernels for B as K x N and as N x K, part 4 the
+// convolution kernels; without MKP_PART it holds everything.
 #ifndef MKP_PART
 #define MKP_PART 0
 #endif
@@ -175,7 +175,8 @@ __device__ __forceinline__ int swzB(int k) {
     else return BN >= 128 ? ((k & 3) << 1) : (((k >> 1) & 1) << 1);
 }
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_, bool PREREAD_ = false, bool BT_ = false>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int S_, bool PREREAD_ = false, bool BT_ = false,
+          bool CONV_ = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, S = S_;
     static constexpr bool PREREAD = PREREAD_;   // read a whole stage's fragments before its MFMAs
@@ -183,6 +184,9 @@ struct Tile {
     // weights): its tile is stored like A's and read with the same 128-bit
     // fragment reads instead of the transposed ones
     static constexpr bool BT = BT_;
+    // A gathered from an NHWC input (implicit-GEMM convolution, KArgs::conv)
+    static constexpr bool CONV = CONV_;
+    static_assert(!CONV || BT, "convolution kernels take the filters as an N x K matrix");
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -272,13 +276,25 @@ __device__ __forceinline__ void wait_step(int ahead) {
 }
 
 struct TileCtx {
-    const uint16_t* A;   // tile origin row m0 (row 0 of the tile), column 0
+    const uint16_t* A;   // tile origin row m0 (row 0 of the tile), column 0; convolution: the input
     const uint16_t* B;   // tile origin column n0, row 0
     int64_t lda, ldb;
     int Mr, Nr;          // rows/columns of the tile inside the region
     int kend;            // end of this split's K range
     bool vecA, vecB;
+    int row0;            // convolution: A row of the tile's row 0
+    KConv cv;            // convolution geometry
 };
+
+// Convolution: offset of A(m, k) in the input, or -1 where it is padding.
+[[maybe_unused]] __device__ __forceinline__ int64_t conv_offset(const KConv& v, int m, int k) {
+    const int pq = v.P * v.Q;
+    const int n = m / pq, pr = m - n * pq, p = pr / v.Q, q = pr - p * v.Q;
+    const int rs = k / v.C, ch = k - rs * v.C, r = rs / v.S, s = rs - r * v.S;
+    const int h = p * v.sh - v.ph + r * v.dh, w = q * v.sw - v.pw + s * v.dw;
+    if ((unsigned)h >= (unsigned)v.H || (unsigned)w >= (unsigned)v.W) return -1;
+    return (((int64_t)n * v.H + h) * v.W + w) * v.C + ch;
+}
 
 // Per-lane element offsets of the direct loads, fixed for a tile: rows and
 // columns past the tile's valid extent are clamped to valid ones (they only
@@ -288,8 +304,21 @@ struct TileCtx {
 template <class T>
 struct DmaOffsets {
     uint32_t a[T::A_IPW], b[T::B_IPW];
+    // convolution: per A chunk, the input offset of its pixel's tap (0, 0)
+    // plus the chunk's channel, and that tap's input row and column; the
+    // current filter tap (r, s) and first channel c0 of the step, advanced
+    // one step at a time (the direct-load steps come in order)
+    int cbase[T::CONV ? T::A_IPW : 1];   // (32 bits: the host enables this path only when offsets fit)
+    int ch0[T::CONV ? T::A_IPW : 1], cw0[T::CONV ? T::A_IPW : 1];
+    int tr = 0, ts = 0, tc0 = 0;
 
-    __device__ __forceinline__ void init(const TileCtx& c, int wave, int lane) {
+    __device__ __forceinline__ void init(const TileCtx& c, int wave, int lane, int kbeg = 0) {
+        if constexpr (T::CONV) {
+            const int rs = kbeg / c.cv.C;
+            tc0 = kbeg - rs * c.cv.C;
+            tr = rs / c.cv.S;
+            ts = rs - tr * c.cv.S;
+        }
 #pragma unroll
         for (int i = 0; i < T::A_IPW; ++i) {
             const int g = i * T::NW + wave;
@@ -297,7 +326,17 @@ struct DmaOffsets {
             slotA<T>(g * 64 + lane, row, col);
             row = min(row, c.Mr - 1);
             const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
-            a[i] = real ? (uint32_t)(row * c.lda + col) : 0u;
+            if constexpr (T::CONV) {
+                const KConv& v = c.cv;
+                const int m = c.row0 + row, pq = v.P * v.Q;
+                const int n = m / pq, pr = m - n * pq, p = pr / v.Q, q = pr - p * v.Q;
+                ch0[i] = p * v.sh - v.ph;
+                cw0[i] = q * v.sw - v.pw;
+                cbase[i] = ((n * v.H + ch0[i]) * v.W + cw0[i]) * v.C + col;
+                a[i] = 0u;
+            } else {
+                a[i] = real ? (uint32_t)(row * c.lda + col) : 0u;
+            }
         }
 #pragma unroll
         for (int i = 0; i < T::B_IPW; ++i) {
@@ -317,16 +356,41 @@ struct DmaOffsets {
         }
     }
 
-    // Direct global->LDS loads of one full K step.
-    __device__ __forceinline__ void issue(const TileCtx& c, int k0, lds_t* stage, lds_t* junk, int wave) const {
+    // Direct global->LDS loads of one full K step (convolution: the steps in
+    // order, from the one init was given).
+    __device__ __forceinline__ void issue(const TileCtx& c, int k0, lds_t* stage, lds_t* junk, int wave) {
         const uint16_t* ab = c.A + k0;
         const uint16_t* bb = T::BT ? c.B + k0 : c.B + (int64_t)k0 * c.ldb;
+        if constexpr (T::CONV) {
+            // the step's K columns are channels tc0.. of filter tap (tr, ts):
+            // one uniform offset from each chunk's tap-(0, 0) position
+            const KConv& v = c.cv;
+            const int dr = tr * v.dh, ds = ts * v.dw;
+            const int tap = (dr * v.W + ds) * v.C + tc0;
 #pragma unroll
-        for (int i = 0; i < T::A_IPW; ++i) {
-            const int g = i * T::NW + wave;
-            const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
-            __builtin_amdgcn_global_load_lds((const void*)(ab + a[i]), (void*)(real ? stage + g * 1024 : junk), 16,
-                                             0, 0);
+            for (int i = 0; i < T::A_IPW; ++i) {
+                const int g = i * T::NW + wave;
+                const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
+                const bool in = (unsigned)(ch0[i] + dr) < (unsigned)v.H && (unsigned)(cw0[i] + ds) < (unsigned)v.W;
+                const uint16_t* src = in ? c.A + (int64_t)(cbase[i] + tap) : v.zero;
+                __builtin_amdgcn_global_load_lds((const void*)src, (void*)(real ? stage + g * 1024 : junk), 16, 0, 0);
+            }
+            tc0 += T::BK;   // C is a multiple of uK on this path
+            if (tc0 == v.C) {
+                tc0 = 0;
+                if (++ts == v.S) {
+                    ts = 0;
+                    ++tr;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::A_IPW; ++i) {
+                const int g = i * T::NW + wave;
+                const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
+                __builtin_amdgcn_global_load_lds((const void*)(ab + a[i]), (void*)(real ? stage + g * 1024 : junk),
+                                                 16, 0, 0);
+            }
         }
 #pragma unroll
         for (int i = 0; i < T::B_IPW; ++i) {
@@ -346,6 +410,28 @@ __device__ __forceinline__ u32x4 reg_load_a(const TileCtx& c, int k0, int p) {
     int row, col;
     slotA<T>(p, row, col);
     const int k = k0 + col;
+    if constexpr (T::CONV) {
+        if (row >= c.Mr || k >= c.kend) return zero4();
+        const int m = c.row0 + row;
+        if (c.vecA) {
+            // C % 8 == 0: the 8 columns are 8 channels of one tap, 16 aligned bytes
+            const int64_t off = conv_offset(c.cv, m, k);
+            return off < 0 ? zero4() : *(const u32x4*)(c.A + off);
+        }
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t v2[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kk = k + 2 * e + h;
+                const int64_t off = kk < c.kend ? conv_offset(c.cv, m, kk) : -1;
+                v2[h] = off < 0 ? 0u : (uint32_t)c.A[off];
+            }
+            wd[e] = v2[0] | (v2[1] << 16);
+        }
+        return u32x4{wd[0], wd[1], wd[2], wd[3]};
+    }
     if (row < c.Mr && k < c.kend) {
         const uint16_t* src = c.A + (int64_t)row * c.lda + k;
         return (c.vecA && k + 8 <= c.kend) ? *(const u32x4*)src : load8_elems(src, c.kend - k);
@@ -543,7 +629,13 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     }
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     TileCtx c;
-    c.A = args.A + (int64_t)b * args.sA + (int64_t)m0 * args.lda;
+    if constexpr (T::CONV) {
+        c.A = args.A;   // the input; rows are gathered
+        c.row0 = args.conv.m0 + m0;
+        c.cv = args.conv;
+    } else {
+        c.A = args.A + (int64_t)b * args.sA + (int64_t)m0 * args.lda;
+    }
     // B tile origin: column n0 of a K x N matrix, or row n0 of an N x K one
     c.B = args.B + (int64_t)b * args.sB + (T::BT ? (int64_t)n0 * args.ldb : (int64_t)n0);
     c.lda = args.lda;
@@ -558,11 +650,12 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     // direct loads need 16-byte aligned rows, 32-bit tile offsets (host
     // clears the vector flags for leading dimensions too large for them)
     // and, on the last tile column, N a multiple of 8
-    const bool dma_tile = c.vecA && c.vecB && (c.Nr >= T::BN || (args.N & 7) == 0);
+    const bool dma_tile = c.vecA && c.vecB && (c.Nr >= T::BN || (args.N & 7) == 0) &&
+                          (!T::CONV || (args.flags & KF_CONV_DMA));
     const int dma_steps = dma_tile ? (c.kend - kbeg) / T::BK : 0;   // full steps
 
     DmaOffsets<T> dma;
-    if (dma_tile) dma.init(c, wave, lane);
+    if (dma_tile) dma.init(c, wave, lane, kbeg);
     auto load_step = [&](int s) {
         lds_t* st = smem + (s % T::S) * T::STAGE;
         const int k0 = kbeg + s * T::BK;
@@ -1117,6 +1210,32 @@ const KernelInfo g_kernels[] = {
 
 #endif  // single-tile registry
 
+// The convolution forms of the N x K tiles (implicit GEMM; same tiles).
+using V_256x256 = Tile<256, 256, 64, 4, 2, 2, false, true, true>;
+using V_256x128 = Tile<256, 128, 64, 4, 2, 2, true, true, true>;
+using V_128x256 = Tile<128, 256, 64, 2, 4, 2, false, true, true>;
+using V_128x128 = Tile<128, 128, 64, 2, 2, 2, false, true, true>;
+using V_128x64 = Tile<128, 64, 64, 2, 2, 3, false, true, true>;
+using V_64x128 = Tile<64, 128, 64, 2, 2, 3, false, true, true>;
+using V_64x64 = Tile<64, 64, 64, 2, 2, 4, false, true, true>;
+using V_32x128 = Tile<32, 128, 64, 1, 4, 4, false, true, true>;
+using V_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true, true>;
+using V_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true, true>;
+using V_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true, true>;
+
+#if MKP_PART == 0 || MKP_PART == 4
+#define MKP_CONV(TWIN, T) \
+    { TWIN, (const void*)&gemm_tile_kernel<T>, &launch_tile<T> }
+const ConvInfo g_conv[] = {
+    MKP_CONV("m256n256k64_nk", V_256x256), MKP_CONV("m256n128k64_nk", V_256x128),
+    MKP_CONV("m128n256k64_nk", V_128x256), MKP_CONV("m128n128k64_nk", V_128x128),
+    MKP_CONV("m128n64k64_nk", V_128x64),   MKP_CONV("m64n128k64_nk", V_64x128),
+    MKP_CONV("m64n64k64_nk", V_64x64),     MKP_CONV("m32n128k64_nk", V_32x128),
+    MKP_CONV("m16n128k64_nk", V_16x128),   MKP_CONV("m16n256k64_nk", V_16x256),
+    MKP_CONV("m32n64k64_nk", V_32x64),
+};
+#endif
+
 // Pairs of tiles that can share a launch (same workgroup size and resident
 // workgroups per CU): a large tile for the region of whole waves and a
 // smaller one for the rest, in both B layouts.
@@ -1149,6 +1268,11 @@ const DualInfo g_duals_nk[] = {
 #endif
 
 }  // namespace
+
+#if MKP_PART == 0 || MKP_PART == 4
+int conv_count() { return (int)(sizeof(g_conv) / sizeof(g_conv[0])); }
+const ConvInfo& conv_info(int i) { return g_conv[i]; }
+#endif
 
 // the pair tables of the two-tile translation units
 const DualInfo* duals_kn(int* n);

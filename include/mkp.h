@@ -143,6 +143,35 @@ int mkp_gemm_ex(int64_t batch, int64_t M, int64_t N, int64_t K,
                 void *stream);
 
 /*
+ * Convolution as an implicit GEMM (the MikPoly page runs convolutions as
+ * GEMMs on the same micro-kernels): y = act(conv2d(x, w) + bias), with
+ *   x: N x H x W x C bf16 input (NHWC, contiguous),
+ *   w: K x R x S x C bf16 filters (KRSC, contiguous: the K x (R S C) matrix
+ *      of the GEMM's B, stored N x K),
+ *   y: N x P x Q x K fp32 output (NPQK, contiguous),
+ *   P = (H + 2 pad_h - dil_h (R - 1) - 1) / stride_h + 1, Q likewise;
+ *   y[n][p][q][k] = sum over r, s, c of
+ *     x[n][p stride_h - pad_h + r dil_h][q stride_w - pad_w + s dil_w][c] * w[k][r][s][c]
+ *   (input outside the image reads as zero).
+ * The GEMM is M = N P Q rows, N = K columns and K = R S C depth; it is
+ * planned like mkp_gemm_bt and runs on the convolution form of the chosen
+ * N x K micro-kernels, whose A loader gathers input rows (a K step of
+ * channels within one filter tap when C is a multiple of 64 -- direct loads,
+ * padding read from a zero page -- else 8 channels, or one element, at a
+ * time; a 1 x 1 convolution with stride 1 and no padding is the plain GEMM
+ * of the input as an (N H W) x C matrix).  bias: K fp32 values or NULL;
+ * act: an MKP_ACT_* code.  Errors: bad
+ * extents or a filter larger than the padded input (MKP_ERR_INVALID_ARG),
+ * before anything is written; N == 0 or K == 0: nothing is launched.
+ */
+int mkp_conv2d(int64_t N, int64_t H, int64_t W, int64_t C,
+               int64_t K, int64_t R, int64_t S,
+               int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+               int64_t dil_h, int64_t dil_w,
+               const void *x, const void *w, float *y,
+               const float *bias, int act, void *stream);
+
+/*
  * Grouped call: C_g[M x N_g] := A[M x K] . B_g for g < groups (1..4), the
  * products sharing A -- the merge of GEMMs that share an operand into one
  * product with the other operands side by side (BladeDISC page, GEMM merge,

@@ -215,3 +215,29 @@ def test_gemm_ex_argument_errors(mkp):
     assert call(M=0, act=2, beta=1.0) == mkp.MKP_OK   # empty output: nothing to do
     with pytest.raises(KeyError):
         call(act="tanh")
+
+
+def test_conv2d_argument_errors(mkp):
+    fake = 1 << 20  # never dereferenced: each call fails its checks first
+
+    def call(**kw):
+        a = dict(N=1, H=8, W=8, C=16, K=8, R=3, S=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, x=fake, w=fake, y=fake,
+                 bias=None, act=0)
+        a.update(kw)
+        return mkp.mkp_conv2d_raw(a["N"], a["H"], a["W"], a["C"], a["K"], a["R"], a["S"], a["sh"], a["sw"], a["ph"],
+                                  a["pw"], a["dh"], a["dw"], a["x"], a["w"], a["y"], a["bias"], a["act"], 0)
+
+    E = mkp.MKP_ERR_INVALID_ARG
+    assert call(H=0) == E
+    assert call(C=0) == E
+    assert call(R=0) == E
+    assert call(sh=0) == E
+    assert call(dw=0) == E
+    assert call(ph=-1) == E
+    assert call(R=11, ph=0) == E and "filter larger" in mkp.last_error()   # 11 > 8 + 0
+    assert call(S=3, dw=5, pw=0) == E                                       # span 11 > 8
+    assert call(act=9) == E
+    assert call(x=0) == E
+    assert call(N=0) == mkp.MKP_OK   # nothing to do
+    assert call(K=0) == mkp.MKP_OK
+    assert mkp.conv_out_size(224, 7, 2, 3, 1) == 112

@@ -156,3 +156,84 @@ def digest(*arrays: np.ndarray) -> str:
     for a in arrays:
         h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()[:16]
+
+
+# ---- convolution sweep -------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class ConvCase:
+    """One convolution call: NHWC input, KRSC filters, NPQK output."""
+    N: int
+    H: int
+    W: int
+    C: int
+    K: int
+    R: int
+    S: int
+    stride: int
+    pad: int
+    seed_x: tuple
+    seed_w: tuple
+    tag: str
+
+    @property
+    def P(self) -> int:
+        return (self.H + 2 * self.pad - self.R) // self.stride + 1
+
+    @property
+    def Q(self) -> int:
+        return (self.W + 2 * self.pad - self.S) // self.stride + 1
+
+    # the GEMM view: M = N P Q, N = K, K = R S C
+    @property
+    def M(self) -> int:
+        return self.N * self.P * self.Q
+
+    @property
+    def Kg(self) -> int:
+        return self.R * self.S * self.C
+
+    batch = 1
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.K * self.Kg
+
+    @property
+    def bytes(self) -> int:
+        # input, filters and output once each
+        return 2 * self.N * self.H * self.W * self.C + 2 * self.K * self.Kg + 4 * self.M * self.K
+
+
+# Distinct convolution layers of a ResNet-50 (bottleneck blocks, stride on the
+# 3 x 3 convolution, 224 x 224 input): (H, C, K, R, stride, pad).
+RESNET50_LAYERS = [
+    (224, 3, 64, 7, 2, 3),                                                   # stem
+    (56, 64, 64, 1, 1, 0), (56, 64, 64, 3, 1, 1), (56, 64, 256, 1, 1, 0), (56, 256, 64, 1, 1, 0),
+    (56, 256, 128, 1, 1, 0), (56, 128, 128, 3, 2, 1), (28, 128, 512, 1, 1, 0), (56, 256, 512, 1, 2, 0),
+    (28, 512, 128, 1, 1, 0), (28, 128, 128, 3, 1, 1),
+    (28, 512, 256, 1, 1, 0), (28, 256, 256, 3, 2, 1), (14, 256, 1024, 1, 1, 0), (28, 512, 1024, 1, 2, 0),
+    (14, 1024, 256, 1, 1, 0), (14, 256, 256, 3, 1, 1),
+    (14, 1024, 512, 1, 1, 0), (14, 512, 512, 3, 2, 1), (7, 512, 2048, 1, 1, 0), (14, 1024, 2048, 1, 2, 0),
+    (7, 2048, 512, 1, 1, 0), (7, 512, 512, 3, 1, 1),
+]
+
+CONV_NAME = "ResNet-50 conv layers (23 distinct), batch N~U{1..32} per call, NHWC bf16"
+
+
+def conv_cases() -> List[ConvCase]:
+    """Every distinct ResNet-50 convolution once, each with its own batch
+    size drawn from seed 106 (the dynamic dimension of CNN inference)."""
+    rng = np.random.default_rng(106)
+    Ns = rng.integers(1, 32, size=len(RESNET50_LAYERS), endpoint=True)
+    out = []
+    for i, ((H, C, K, R, stride, pad), N) in enumerate(zip(RESNET50_LAYERS, Ns)):
+        out.append(ConvCase(int(N), H, H, C, K, R, R, stride, pad, (106, i, 0), (106, i, 1), f"conv[{i}]"))
+    return out
+
+
+def make_conv_operands(case: ConvCase) -> Tuple[np.ndarray, np.ndarray]:
+    """bf16 bits of x (N,H,W,C) ~ U[-1,1] and w (K,R,S,C) ~ U[-1,1]."""
+    x = _draw(_U11, case.seed_x, case.N * case.H * case.W * case.C).reshape(case.N, case.H, case.W, case.C)
+    w = _draw(_U11, case.seed_w, case.K * case.R * case.S * case.C).reshape(case.K, case.R, case.S, case.C)
+    return x, w
