@@ -24,7 +24,8 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), \d+, \d+, \d+, (?:true|false), (true|false)>")
+# Tile<uM, uN, uK, waves_m, waves_n, stages, preread, N x K B[, convolution]>
+TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), \d+, \d+, \d+, (?:true|false), (true|false)(?:, (true|false))?>")
 
 
 def read_counter(d: str, counter: str):
@@ -45,8 +46,10 @@ def lib_name(kernel_name: str):
     m = TILE.search(kernel_name)
     if not m or "gemm_tile_kernel" not in kernel_name:
         return None
-    # the last template flag marks the kernels that take B as N x K
-    return f"m{m.group(1)}n{m.group(2)}k{m.group(3)}" + ("_nk" if m.group(4) == "true" else "")
+    # the N x K flag marks the kernels that take B as N x K; the convolution
+    # forms of those count apart
+    name = f"m{m.group(1)}n{m.group(2)}k{m.group(3)}" + ("_nk" if m.group(4) == "true" else "")
+    return name + ("_conv" if m.group(5) == "true" else "")
 
 
 def copy_scale(d: str, counter: str, nbytes: float) -> float:
