@@ -1,4 +1,6 @@
-"""Turn rocprofv3 byte counters into HBM traffic per launch.
+"""Turn rocprofv3 counters into per-kernel figures.
+
+HBM traffic per launch (the default mode):
 
     python -m dynamic_shape_gemm_amd.pmc --config 2 \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
@@ -11,6 +13,13 @@ each counter: scale = bytes the copy moved / bytes the counter reports.  For
 every library micro-kernel the record holds the scaled fetch + write bytes
 averaged per dispatch, tagged with the hash of the kernel source it was
 measured on (bench.py reports it only while that source is unchanged).
+
+Counter summary (`python -m dynamic_shape_gemm_amd.pmc counters --dirs D1 D2
+--out FILE`): per library kernel, MFMA busy cycles over the SIMD cycles of
+the dispatch (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x 4)), LDS
+bank-conflict cycles per LDS-active cycle, the share of wave cycles waiting
+on any dependency and waiting to issue LDS instructions, and the L2 hit
+rate.
 """
 from __future__ import annotations
 
@@ -22,6 +31,7 @@ import hashlib
 import json
 import os
 import re
+import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Tile<uM, uN, uK, waves_m, waves_n, stages, preread, N x K B[, convolution]>
@@ -60,7 +70,68 @@ def copy_scale(d: str, counter: str, nbytes: float) -> float:
     return nbytes / (per_dispatch_kib * 1024.0), name, per_dispatch_kib
 
 
+def read_all(dirs):
+    """{library kernel: {counter: per-dispatch mean}} over every counter of
+    the given rocprofv3 --pmc output directories."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                ln = lib_name(row["Kernel_Name"])
+                if ln is None:
+                    continue
+                per[(ln, row["Counter_Name"])][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        for (ln, cn), vals in per.items():
+            acc[ln][cn].extend(vals.values())
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}, \
+        {k: max(len(v) for v in cs.values()) for k, cs in acc.items()}
+
+
+def counters_markdown(dirs, cus: int, command: str, xcds: int = 8) -> str:
+    """Per-kernel counter summary: MFMA busy share of the SIMD cycles while
+    the GPU is active (GRBM_GUI_ACTIVE counts the active cycles of every XCD,
+    so one XCD's are GRBM_GUI_ACTIVE / xcds), LDS bank-conflict cycles per
+    LDS-active cycle, share of wave time waiting on LDS, and the L2 hit
+    rate."""
+    vals, n = read_all(dirs)
+    out = ["| kernel | dispatches | MFMA busy | LDS bank conflicts / LDS active | waves waiting (any) | "
+           "waves waiting to issue LDS | L2 hit rate |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+
+    def ratio(a, b):
+        return f"{100.0 * a / b:.1f}%" if b else "n/a"
+
+    for k in sorted(vals, key=lambda k: -n[k]):
+        v = vals[k]
+        gui = v.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        mfma = ratio(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), gui * cus * 4)
+        bank = ratio(v.get("SQ_LDS_BANK_CONFLICT", 0.0), v.get("SQ_LDS_IDX_ACTIVE", 0.0))
+        wait = ratio(v.get("SQ_WAIT_INST_LDS", 0.0), v.get("SQ_WAVE_CYCLES", 0.0))
+        wany = ratio(v.get("SQ_WAIT_ANY", 0.0), v.get("SQ_WAVE_CYCLES", 0.0))
+        hit, miss = v.get("TCC_HIT_sum", 0.0), v.get("TCC_MISS_sum", 0.0)
+        out.append(f"| `{k}` | {n[k]} | {mfma} | {bank} | {wany} | {wait} | {ratio(hit, hit + miss)} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        ap = argparse.ArgumentParser(prog="pmc counters")
+        ap.add_argument("counters")
+        ap.add_argument("--dirs", nargs="+", required=True)
+        ap.add_argument("--cus", type=int, default=256)
+        ap.add_argument("--xcds", type=int, default=8)
+        ap.add_argument("--out", required=True)
+        ap.add_argument("--command", default="")
+        a = ap.parse_args()
+        text = counters_markdown(a.dirs, a.cus, a.command, a.xcds)
+        os.makedirs(os.path.dirname(a.out) or ".", exist_ok=True)
+        open(a.out, "w").write(text)
+        print(text)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, required=True)
     ap.add_argument("--fetch", required=True)
