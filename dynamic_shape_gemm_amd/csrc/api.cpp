@@ -184,14 +184,12 @@ bool bind_table(PerfTable& t, std::string& err) {
             return false;
         }
     }
-    // a table without any kernel for one B layout (written before the
-    // library had them) gets the analytic estimates of that layout's kernels
-    for (int layout = 0; layout < 2; ++layout) {
-        bool any = false;
-        for (auto& k : t.kernels) any |= k.bt == (layout == 1);
-        if (any) continue;
-        for (auto& k : analytic_table().kernels)
-            if (k.bt == (layout == 1)) t.kernels.push_back(k);
+    // library kernels the table does not price (it was written before the
+    // library had them) get the analytic estimates
+    for (auto& k : analytic_table().kernels) {
+        bool listed = false;
+        for (auto& e : t.kernels) listed |= e.name == k.name;
+        if (!listed) t.kernels.push_back(k);
     }
     // kernel pairs: each listed pair must have a two-tile kernel; a table
     // without pair lines gets every pair the library has whose kernels it

@@ -1163,6 +1163,10 @@ using T_32x128 = Tile<32, 128, 64, 1, 4, 4>;
 using T_16x128 = Tile<16, 128, 64, 1, 4, 4>;
 using T_16x256 = Tile<16, 256, 64, 1, 4, 4>;
 using T_32x64 = Tile<32, 64, 64, 2, 2, 4>;
+// 128 x 128 with four LDS stages: one workgroup per CU with three K steps of
+// loads in flight instead of two workgroups with one each -- faster where K
+// is deep or the tiles are few, slower on many shallow tiles
+using T_128x128x4 = Tile<128, 128, 64, 2, 2, 4>;
 // the same tiles for B given as N x K
 using U_256x256 = Tile<256, 256, 64, 4, 2, 2, false, true>;
 using U_256x128 = Tile<256, 128, 64, 4, 2, 2, true, true>;
@@ -1175,6 +1179,7 @@ using U_32x128 = Tile<32, 128, 64, 1, 4, 4, false, true>;
 using U_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true>;
 using U_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true>;
 using U_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true>;
+using U_128x128x4 = Tile<128, 128, 64, 2, 2, 4, false, true>;
 
 #if MKP_PART == 0 || MKP_PART == 1
 #define MKP_KERNEL(NAME, T)                                                                               \
@@ -1195,6 +1200,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m16n128k64", T_16x128),
     MKP_KERNEL("m16n256k64", T_16x256),
     MKP_KERNEL("m32n64k64", T_32x64),
+    MKP_KERNEL("m128n128k64x4", T_128x128x4),
     MKP_KERNEL("m256n256k64_nk", U_256x256),
     MKP_KERNEL("m256n128k64_nk", U_256x128),
     MKP_KERNEL("m128n256k64_nk", U_128x256),
@@ -1206,6 +1212,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m16n128k64_nk", U_16x128),
     MKP_KERNEL("m16n256k64_nk", U_16x256),
     MKP_KERNEL("m32n64k64_nk", U_32x64),
+    MKP_KERNEL("m128n128k64x4_nk", U_128x128x4),
 };
 
 #endif  // single-tile registry
@@ -1222,6 +1229,7 @@ using V_32x128 = Tile<32, 128, 64, 1, 4, 4, false, true, true>;
 using V_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true, true>;
 using V_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true, true>;
 using V_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true, true>;
+using V_128x128x4 = Tile<128, 128, 64, 2, 2, 4, false, true, true>;
 
 #if MKP_PART == 0 || MKP_PART == 4
 #define MKP_CONV(TWIN, T) \
@@ -1232,7 +1240,7 @@ const ConvInfo g_conv[] = {
     MKP_CONV("m128n64k64_nk", V_128x64),   MKP_CONV("m64n128k64_nk", V_64x128),
     MKP_CONV("m64n64k64_nk", V_64x64),     MKP_CONV("m32n128k64_nk", V_32x128),
     MKP_CONV("m16n128k64_nk", V_16x128),   MKP_CONV("m16n256k64_nk", V_16x256),
-    MKP_CONV("m32n64k64_nk", V_32x64),
+    MKP_CONV("m32n64k64_nk", V_32x64),     MKP_CONV("m128n128k64x4_nk", V_128x128x4),
 };
 #endif
 

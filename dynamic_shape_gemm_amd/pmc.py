@@ -35,7 +35,9 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Tile<uM, uN, uK, waves_m, waves_n, stages, preread, N x K B[, convolution]>
-TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), \d+, \d+, \d+, (?:true|false), (true|false)(?:, (true|false))?>")
+TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), \d+, \d+, (\d+), (?:true|false), (true|false)(?:, (true|false))?>")
+# tiles the library also has in a deeper-pipelined form, named with "x<stages>"
+DEEP = {(128, 128, 4)}
 
 
 def read_counter(d: str, counter: str):
@@ -58,8 +60,10 @@ def lib_name(kernel_name: str):
         return None
     # the N x K flag marks the kernels that take B as N x K; the convolution
     # forms of those count apart
-    name = f"m{m.group(1)}n{m.group(2)}k{m.group(3)}" + ("_nk" if m.group(4) == "true" else "")
-    return name + ("_conv" if m.group(5) == "true" else "")
+    bm, bn, stages = int(m.group(1)), int(m.group(2)), int(m.group(4))
+    name = f"m{bm}n{bn}k{m.group(3)}" + (f"x{stages}" if (bm, bn, stages) in DEEP else "")
+    name += "_nk" if m.group(5) == "true" else ""
+    return name + ("_conv" if m.group(6) == "true" else "")
 
 
 def copy_scale(d: str, counter: str, nbytes: float) -> float:

@@ -246,8 +246,8 @@ int mkp_plan_with_table(const char *table_text, int flags,
  * (kn / nk: the kernel takes B as K x N, the default, or as N x K; tail and
  * tailx: time of a wave filling a fraction f < 1 of the slots, on its own or
  * after full waves, relative to a full wave.)  Kernels named here must exist
- * in the library with the same tile and layout; a table with no kernel of
- * one layout gets analytic estimates for that layout's kernels.  Each pair
+ * in the library with the same tile and layout; library kernels the table
+ * does not list get analytic estimates.  Each pair
  * must be one the library compiles into a two-tile kernel (same layout and
  * resident workgroups per CU); a table without pair lines gets all of the
  * library's pairs whose kernels it prices with equal workgroups per CU.
