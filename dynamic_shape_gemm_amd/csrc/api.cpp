@@ -248,7 +248,9 @@ int load_table_locked(Library& L, const char* path, bool quiet_missing) {
     std::string p = path ? std::string(path) : default_table_path();
     std::string text, err;
     if (!read_file(p, text)) {
-        if (quiet_missing) {
+        // only a missing shipped table is quiet; a path the caller or
+        // MKP_CALIB names must exist
+        if (quiet_missing && !std::getenv("MKP_CALIB")) {
             L.table = bound_analytic_table();
             L.table_origin = "analytic";
             L.cache.clear();

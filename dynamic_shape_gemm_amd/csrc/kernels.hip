@@ -1065,6 +1065,36 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
     }
 }
 
+// The same copy when K and N are multiples of 8 and the source rows are
+// 16-byte aligned: each lane transposes one 8 x 8 block in registers (eight
+// 16-byte loads along source rows, eight 16-byte stores along target rows),
+// with no LDS round trip or barrier; a one-wave workgroup covers 64 x 64, so
+// a small B still spreads over many CUs.
+__global__ __launch_bounds__(64) void transpose8_bf16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                                            int64_t s_src, uint16_t* __restrict__ dst,
+                                                            int64_t ld_dst, int64_t s_dst, int K, int N) {
+    const int lane = threadIdx.x;
+    const int n = blockIdx.x * 64 + (lane & 7) * 8;
+    const int k = blockIdx.y * 64 + (lane >> 3) * 8;
+    if (n >= N || k >= K) return;   // K, N multiples of 8: whole blocks only
+    const uint16_t* sb = src + (int64_t)blockIdx.z * s_src + (int64_t)k * ld_src + n;
+    uint16_t* db = dst + (int64_t)blockIdx.z * s_dst + (int64_t)n * ld_dst + k;
+    u32x4 v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = *(const u32x4*)(sb + (int64_t)r * ld_src);
+    // target row c holds source column c: its dword e packs rows 2e and 2e+1
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = v[2 * e][c >> 1], hi = v[2 * e + 1][c >> 1];
+            w[e] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        *(u32x4*)(db + (int64_t)c * ld_dst) = w;
+    }
+}
+
 __global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ C, int64_t ldc, int64_t sC, int M,
                                                         int N, int batch) {
     const int64_t per = (int64_t)M * N;
@@ -1341,7 +1371,10 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t ld_src, int64_t s_
                                  int64_t s_dst, int K, int N, int batch, bool src_vec, hipStream_t st) {
     if (batch > 65535 || (ld_dst + 63) / 64 > 65535 || ld_dst % 8 != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((ld_dst + 63) / 64), (unsigned)batch);
-    if (src_vec)
+    if (src_vec && K % 8 == 0 && N % 8 == 0 && ld_dst == K)
+        hipLaunchKernelGGL(transpose8_bf16_kernel, grid, dim3(64), 0, st, src, ld_src, s_src, dst, ld_dst, s_dst, K,
+                           N);
+    else if (src_vec)
         hipLaunchKernelGGL(transpose_bf16_kernel<true>, grid, dim3(256), 0, st, src, ld_src, s_src, dst, ld_dst, s_dst,
                            K, N);
     else

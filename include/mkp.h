@@ -235,7 +235,10 @@ int mkp_plan_with_table(const char *table_text, int flags,
 /*
  * Load a performance table (MikPoly page, section 3 "micro-kernel
  * performance model": g_predict per micro-kernel over t K-steps) from a text
- * file; path NULL reloads the table that ships with the library.  Lines:
+ * file; path NULL reloads the table that ships with the library, or the
+ * file the environment variable MKP_CALIB names (which must then be
+ * readable: only a missing shipped table falls back, silently, to analytic
+ * estimates).  Lines:
  *   device <cus>                     launch_us <us>
  *   reduce <launch_us> <GB/s>        splitk <s1> <s2> ...
  *   patterns I II-M II-N             kernel <name> <uM> <uN> <uK> <wg_per_cu> [kn|nk]

@@ -46,10 +46,18 @@ def test_bt_entry_points_check_arguments(mkp):
     assert mkp.mkp_gemm_bt_raw(4, 4, 8, 0, 8, 1, 8, 1, 4, 0) == mkp.MKP_ERR_INVALID_ARG
     assert mkp.mkp_gemm_batched_bt_raw(-1, 4, 4, 8, 1, 8, 32, 1, 8, 32, 1, 4, 16, 0) == mkp.MKP_ERR_INVALID_ARG
     assert mkp.mkp_gemm_bt_raw(0, 4, 8, 0, 8, 0, 8, 0, 4, 0) == mkp.MKP_OK
-    # N x K plans use N x K kernels only, and K x N plans K x N kernels only
+    # N x K plans use N x K kernels only; K x N plans use K x N kernels
+    # unless they first transpose B, and then N x K kernels only
     for bt in (False, True):
         p = mkp.mkp_plan_describe(1, 1000, 700, 300, bt=bt)
-        assert p["regions"] and all(r["kernel"].endswith("_nk") == bt for r in p["regions"])
+        nk = bt or p["transpose_b"]
+        assert p["regions"] and all(r["kernel"].endswith("_nk") == nk for r in p["regions"])
+    try:
+        mkp.mkp_set_option("transpose_b", 0)
+        p = mkp.mkp_plan_describe(1, 1000, 700, 300, bt=False)
+        assert not p["transpose_b"] and not any(r["kernel"].endswith("_nk") for r in p["regions"])
+    finally:
+        mkp.mkp_set_option("transpose_b", 1)
 
 
 def test_invalid_arguments_fail_before_any_launch(mkp):
@@ -241,3 +249,27 @@ def test_conv2d_argument_errors(mkp):
     assert call(N=0) == mkp.MKP_OK   # nothing to do
     assert call(K=0) == mkp.MKP_OK
     assert mkp.conv_out_size(224, 7, 2, 3, 1) == 112
+
+
+def test_table_named_by_environment_must_exist(tmp_path):
+    """A missing shipped table falls back to analytic estimates, but a table
+    that MKP_CALIB names and that cannot be read is an error (and a warning
+    on the first call), so a mistyped path is not silently replaced."""
+    import os
+    import subprocess
+    import sys
+
+    code = (
+        "import dynamic_shape_gemm_amd as m\n"
+        "try:\n"
+        "    m.mkp_load_calibration(None)\n"
+        "    print('loaded')\n"
+        "except m.MkpError as e:\n"
+        "    print('error', e.code, m.last_error())\n"
+    )
+    env = dict(os.environ, MKP_CALIB=str(tmp_path / "missing.tbl"))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "error -1" in r.stdout and "missing.tbl" in r.stdout, r.stdout
+    assert "missing.tbl" in r.stderr and "analytic" in r.stderr, r.stderr

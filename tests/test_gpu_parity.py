@@ -363,12 +363,12 @@ def test_transposed_b_path(mkp):
     """K x N calls run as a transpose of B into the workspace followed by the
     N x K kernels (forced here with transpose_b = 2): ragged, unaligned,
     split-K and batched cases."""
-    import torch
-
     rng = np.random.default_rng(4242)
     try:
         mkp.mkp_set_option("transpose_b", 2)
-        for (M, N, K) in [(1, 1, 1), (17, 33, 65), (300, 257, 129), (513, 1000, 777), (7, 300, 3000)]:
+        # K and N multiples of 8 (register-block transpose) and not
+        for (M, N, K) in [(1, 1, 1), (17, 33, 65), (300, 257, 129), (513, 1000, 777), (7, 300, 3000), (3, 8, 8),
+                          (100, 200, 136), (260, 768, 3072)]:
             plan = mkp.mkp_plan_describe(1, M, N, K)
             assert plan["transpose_b"] and all(r["kernel"].endswith("_nk") for r in plan["regions"]), plan
             run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), what=f"transposed B {M}x{N}x{K}")
@@ -378,24 +378,31 @@ def test_transposed_b_path(mkp):
         mkp.mkp_set_option("force_splitk", 4)
         run_case(mkp, rand_bits(rng, (200, 2000)), rand_bits(rng, (2000, 300)), what="transposed B, split 4")
         mkp.mkp_set_option("force_splitk", 0)
-        batch, M, N, K = 6, 90, 150, 64
-        a = rand_bits(rng, (batch, M, K))
-        b = rand_bits(rng, (batch, K, N))
-        print("[case] transposed B, batched", flush=True)
-        ta, pa = dev_bf16(a)
-        tb, pb = dev_bf16(b)
-        tc = torch.full((batch * M * N + 64,), float("nan"), dtype=torch.float32, device="cuda")
-        mkp.mkp_gemm_batched(batch, M, N, K, pa, K, M * K, pb, N, K * N, tc.data_ptr(), N, M * N)
-        torch.cuda.synchronize()
-        h = tc.cpu().numpy()
-        assert np.isnan(h[batch * M * N:]).all()
-        ref, refabs = oracle.gemm(a, b, with_abs=True)
-        got = h[:batch * M * N].reshape(batch, M, N).astype(np.float64)
-        for z in range(batch):
-            assert_close(got[z], ref[z], refabs[z], K, f"transposed B batched [{z}]")
+        for batch, M, N, K in [(6, 90, 150, 64), (5, 40, 200, 72)]:
+            _batched_transposed(mkp, rng, batch, M, N, K)
     finally:
         mkp.mkp_set_option("transpose_b", 1)
         mkp.mkp_set_option("force_splitk", 0)
+
+
+def _batched_transposed(mkp, rng, batch, M, N, K):
+    """One batched K x N call on the transposed-B path, NaN guard after C."""
+    import torch
+
+    a = rand_bits(rng, (batch, M, K))
+    b = rand_bits(rng, (batch, K, N))
+    print(f"[case] transposed B, batched {batch}x{M}x{N}x{K}", flush=True)
+    ta, pa = dev_bf16(a)
+    tb, pb = dev_bf16(b)
+    tc = torch.full((batch * M * N + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    mkp.mkp_gemm_batched(batch, M, N, K, pa, K, M * K, pb, N, K * N, tc.data_ptr(), N, M * N)
+    torch.cuda.synchronize()
+    h = tc.cpu().numpy()
+    assert np.isnan(h[batch * M * N:]).all()
+    ref, refabs = oracle.gemm(a, b, with_abs=True)
+    got = h[:batch * M * N].reshape(batch, M, N).astype(np.float64)
+    for z in range(batch):
+        assert_close(got[z], ref[z], refabs[z], K, f"transposed B batched [{z}]")
 
 
 def test_concurrent_callers_on_separate_streams(mkp):
