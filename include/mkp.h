@@ -272,9 +272,9 @@ int mkp_calibrate(const char *path, int max_points);
  * (0 = split-K partials summed by a second launch, the default; 1 = summed
  * by the last-arriving workgroup of each tile, which on MI355X costs more in
  * L2 write-back than the second launch), "pack_unaligned" (1 = an operand
- * whose rows are not 16-byte aligned and that several tiles re-read is
- * first copied into aligned workspace rows, the default; 0 = such operands
- * are read element by element).
+ * whose rows are not 16-byte aligned, that several tiles re-read and
+ * whose K is at least 512 is first copied into aligned workspace rows, the
+ * default; 0 = such operands are read element by element).
  * "transpose_b" (0 = K x N calls always run on K x N kernels; 1 = the
  * default: a K x N call may copy B into N x K workspace rows and run on the
  * N x K kernels, when the table prices the copy and the model finds it

@@ -159,8 +159,25 @@ def test_unaligned(mkp, pack):
         M, N, K = 300, 509, 64
         a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
         run_case(mkp, a, b, lda=K + 3, ldb=N, ldc=N, what=f"odd N, ldb=N pack={pack}")
+        # deep enough K for the staging copy of re-read unaligned operands
+        # (the launch trace shows whether the copy ran)
+        M, N, K = 260, 301, 520
+        a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+        mkp.mkp_set_option("trace", 1)
+        mkp.mkp_trace_dump()
+        run_case(mkp, a, b, lda=K + 1, ldb=N, ldc=N + 1, what=f"deep K, lda odd, odd N pack={pack}")
+        packed = [r for r in mkp.mkp_trace_dump() if r["kernel"] == "pack_rows"]
+        assert bool(packed) == bool(pack), packed
+        run_case(mkp, a, b, offA=1, offB=1, what=f"deep K, misaligned pointers pack={pack}")
+        M, N, K = 260, 301, 64   # shallow K: read in place either way
+        a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+        mkp.mkp_trace_dump()
+        run_case(mkp, a, b, lda=K + 1, what=f"shallow K, lda odd pack={pack}")
+        assert not [r for r in mkp.mkp_trace_dump() if r["kernel"] == "pack_rows"]
     finally:
         mkp.mkp_set_option("pack_unaligned", 1)
+        mkp.mkp_set_option("trace", 0)
+        mkp.mkp_trace_dump()
 
 
 def test_k0_and_empty(mkp):

@@ -113,6 +113,11 @@ def test_bt_unaligned(mkp, pack):
         M, N, K = 256, 256, 256
         a, w = rand_bits(rng, (M, K)), rand_bits(rng, (N, K))
         run_case_bt(mkp, a, w, offB=1, what=f"aligned shape, B pointer off by one pack={pack}")
+        # deep enough K for the staging copy of re-read unaligned operands
+        M, N, K = 300, 260, 777
+        a, w = rand_bits(rng, (M, K)), rand_bits(rng, (N, K))
+        run_case_bt(mkp, a, w, what=f"deep K odd pack={pack}")
+        run_case_bt(mkp, a, w, offA=1, offB=1, what=f"deep K, misaligned pointers pack={pack}")
     finally:
         mkp.mkp_set_option("pack_unaligned", 1)
 
