@@ -408,6 +408,9 @@ def main():
     ap.add_argument("--epilogue", choices=["none", "bias", "bias_gelu", "bias_gelu_unfused"], default="none",
                     help="encoder linears with a bias on every GEMM (and GELU on the FFN-up GEMMs), fused into the "
                          "GEMM epilogue or, for comparison, as separate passes")
+    ap.add_argument("--fused-reduce", type=int, choices=[0, 1], default=None,
+                    help="split-K partials summed by the last split of each tile (1) or by a second pass (0); "
+                         "default: the library's setting")
     ap.add_argument("--fuse-regions", type=int, choices=[0, 1], default=0,
                     help="one-launch Pattern II plans over kernel pairs when the model prefers them (1) or never (0)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
@@ -436,6 +439,8 @@ def main():
         wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv, epilogue=args.epilogue)
     stream = torch.cuda.current_stream().cuda_stream
     mkp.mkp_set_option("fuse_regions", args.fuse_regions)
+    if args.fused_reduce is not None:
+        mkp.mkp_set_option("fused_reduce", args.fused_reduce)
     mkp.mkp_cache_clear()
 
     # first step: plan misses (polymerization) + launches, timed on its own
@@ -517,6 +522,7 @@ def main():
             "qkv": wl.qkv,
             "epilogue": wl.epilogue,
             "fuse_regions": args.fuse_regions,
+            "fused_reduce": args.fused_reduce,
             "gemms_per_step": len(wl.cases),
             "flops_per_step": wl.flops,
             "bytes_per_step": wl.bytes,

@@ -256,6 +256,24 @@ __device__ __forceinline__ u32x4 load8_elems(const uint16_t* p, int nvalid) {
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// 8 consecutive bf16 values that are all inside the operand, from rows of
+// any alignment: 4-byte words, shifted by 16 bits when the first value sits
+// in the upper half of a word.  The words read never leave those holding
+// the 8 values (so never a page beyond them).
+__device__ __forceinline__ u32x4 load8_words(const uint16_t* p) {
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t* q = (const uint32_t*)(a & ~uintptr_t(3));
+    if ((a & 2) == 0) return u32x4{q[0], q[1], q[2], q[3]};
+    const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3], w4 = q[4];
+    return u32x4{__builtin_amdgcn_alignbit(w1, w0, 16), __builtin_amdgcn_alignbit(w2, w1, 16),
+                 __builtin_amdgcn_alignbit(w3, w2, 16), __builtin_amdgcn_alignbit(w4, w3, 16)};
+}
+
+// Up to 8 values: whole chunks by words, partial ones element by element.
+__device__ __forceinline__ u32x4 load8_any(const uint16_t* p, int nvalid) {
+    return nvalid >= 8 ? load8_words(p) : load8_elems(p, nvalid);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // and its LDS operations are done, then meet the other waves.
 template <int N>
@@ -434,7 +452,7 @@ __device__ __forceinline__ u32x4 reg_load_a(const TileCtx& c, int k0, int p) {
     }
     if (row < c.Mr && k < c.kend) {
         const uint16_t* src = c.A + (int64_t)row * c.lda + k;
-        return (c.vecA && k + 8 <= c.kend) ? *(const u32x4*)src : load8_elems(src, c.kend - k);
+        return (c.vecA && k + 8 <= c.kend) ? *(const u32x4*)src : load8_any(src, c.kend - k);
     }
     return zero4();
 }
@@ -447,7 +465,11 @@ __device__ __forceinline__ u32x4 reg_load_b(const TileCtx& c, int k0, int p) {
         const int k = k0 + col;
         if (n < c.Nr && k < c.kend) {
             const uint16_t* src = c.B + (int64_t)n * c.ldb + k;
-            return (c.vecB && k + 8 <= c.kend) ? *(const u32x4*)src : load8_elems(src, c.kend - k);
+            // (the convolution tiles keep element loads: word loads push the
+            // largest one's registers over the limit)
+            if constexpr (T::CONV)
+                return (c.vecB && k + 8 <= c.kend) ? *(const u32x4*)src : load8_elems(src, c.kend - k);
+            return (c.vecB && k + 8 <= c.kend) ? *(const u32x4*)src : load8_any(src, c.kend - k);
         }
         return zero4();
     }
@@ -456,7 +478,7 @@ __device__ __forceinline__ u32x4 reg_load_b(const TileCtx& c, int k0, int p) {
     const int kk = k0 + k;
     if (kk < c.kend && col < c.Nr) {
         const uint16_t* src = c.B + (int64_t)kk * c.ldb + col;
-        return (c.vecB && col + 8 <= c.Nr) ? *(const u32x4*)src : load8_elems(src, c.Nr - col);
+        return (c.vecB && col + 8 <= c.Nr) ? *(const u32x4*)src : load8_any(src, c.Nr - col);
     }
     return zero4();
 }
@@ -817,6 +839,9 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     const int col0 = wn * T::WTN;   // first tile column of this wave
     constexpr int C4 = T::WTN / 4;  // 16-byte chunks per staged row
     static_assert(64 % C4 == 0, "a lane's chunk column must not change across the store loop");
+    // 16-byte stores on unaligned rows (below) everywhere but in the
+    // convolution form of the largest tile, whose registers they would spill
+    constexpr bool kWideUnaligned = !(T::CONV && T::BM * T::BN >= 256 * 256);
     // with the epilogue, each lane's bias chunk is loaded once: its column is
     // the same in every row it stores
     f32x4 bias4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -913,8 +938,43 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
                     store4(C, args.ldc, true, row0 + r, col0 + c4, v);
                 }
             }
+        } else if (kWideUnaligned && !epi_here) {
+            // Unaligned rows (4-byte aligned only): each row's segment of
+            // this wave's columns is written with 16-byte stores from its
+            // first 16-byte boundary on, 4 columns per lane as in the
+            // aligned loop; the at most three columns before that boundary
+            // and three after the last whole chunk go out one by one below.
+            const int W = min(T::WTN, c.Nr - col0);   // valid columns of the strip
+            if (W > 0) {
+#pragma unroll 1
+                for (int it = 0; it < ITS; ++it) {
+                    const int id = it * 64 + lane;
+                    if ((T::MF * C4) % 64 == 0 || id < T::MF * C4) {
+                        const int r = id / C4, j = id % C4;
+                        const int m = row0 + r;
+                        float* d = C + (int64_t)m * args.ldc + col0;
+                        const int h = min((int)((0u - (uint32_t)(uintptr_t)d) >> 2) & 3, W);
+                        const int col = h + 4 * j;
+                        if (m < c.Mr && col + 4 <= W) {
+                            const float __attribute__((address_space(3)))* sr = stg + r * T::EPI_LD + col;
+                            *(f32x4*)(d + col) = f32x4{sr[0], sr[1], sr[2], sr[3]};
+                        }
+                    }
+                }
+#pragma unroll 1
+                for (int r0 = 0; r0 < T::MF; r0 += 8) {
+                    const int r = r0 + (lane >> 3), e = lane & 7;
+                    const int m = row0 + r;
+                    float* d = C + (int64_t)m * args.ldc + col0;
+                    const int h = min((int)((0u - (uint32_t)(uintptr_t)d) >> 2) & 3, W);
+                    const int t0 = h + ((W - h) & ~3);   // first column after the whole chunks
+                    const int col = e < h ? e : t0 + (e - h);
+                    if (m < c.Mr && (e < h || col < W)) d[col] = stg[r * T::EPI_LD + col];
+                }
+            }
         } else {
-            // unaligned rows: lanes walk one row's columns, one float each
+            // unaligned rows with the epilogue: lanes walk one row's
+            // columns, one float each
 #pragma unroll 1
             for (int r = 0; r < T::MF; ++r) {
                 const int m = row0 + r;

@@ -180,6 +180,30 @@ def test_unaligned(mkp, pack):
         mkp.mkp_trace_dump()
 
 
+UNALIGNED_C_KERNELS = ["m256n256k64", "m128n128k64", "m128n64k64", "m64n64k64", "m16n128k64", "m32n64k64"]
+
+
+@pytest.mark.parametrize("name", UNALIGNED_C_KERNELS)
+def test_unaligned_rows_every_phase(mkp, name):
+    """C rows that start at every 4-byte phase of a 16-byte boundary (the
+    stores go out as whole 16-byte chunks plus up to three floats at each
+    end), strips narrower than the head, and B rows at odd and even element
+    offsets (word loads shifted by 16 bits, or not)."""
+    rng = np.random.default_rng(500 + UNALIGNED_C_KERNELS.index(name))
+    try:
+        mkp.mkp_set_option("force_kernel", name)
+        mkp.mkp_set_option("pack_unaligned", 0)
+        for (M, N, K) in [(70, 67, 72), (33, 130, 64), (9, 3, 40), (150, 258, 136)]:
+            a, b = rand_bits(rng, (M, K)), rand_bits(rng, (K, N))
+            for ldc, offC, ldb, offB in [(N + 1, 0, N + 1, 0), (N + 2, 1, N, 1), (N + 3, 2, N + 2, 0),
+                                         (N, 3, N + 3, 1)]:
+                run_case(mkp, a, b, ldb=ldb, ldc=ldc, offB=offB, offC=offC,
+                         what=f"{name} ldc={ldc} offC={offC} ldb={ldb} offB={offB}")
+    finally:
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("pack_unaligned", 1)
+
+
 def test_k0_and_empty(mkp):
     import torch
 
