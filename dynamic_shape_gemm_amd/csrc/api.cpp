@@ -386,10 +386,22 @@ template <class F>
 hipError_t traced(Library& L, hipStream_t st, int kernel, double flops, double bytes, F&& fn) {
     if (!L.trace.load(std::memory_order_relaxed)) return fn();
     TraceRec r{kernel, t_call, flops, bytes, nullptr, nullptr};
-    if (hipEventCreate(&r.e0) != hipSuccess || hipEventCreate(&r.e1) != hipSuccess) return fn();
-    (void)hipEventRecord(r.e0, st);
+    if (hipEventCreate(&r.e0) != hipSuccess || hipEventCreate(&r.e1) != hipSuccess) {
+        if (r.e0) (void)hipEventDestroy(r.e0);
+        return fn();
+    }
+    // the launch stamps the kernel's own start and end into the events
+    // (the time between two events recorded on the stream around it would
+    // also hold the dispatch gap before the kernel starts)
+    launch_events() = LaunchEvents{r.e0, r.e1};
     hipError_t e = fn();
-    (void)hipEventRecord(r.e1, st);
+    const bool launched = launch_events().start == nullptr;
+    launch_events() = LaunchEvents{};
+    if (!launched || e != hipSuccess) {   // nothing was launched: no record
+        (void)hipEventDestroy(r.e0);
+        (void)hipEventDestroy(r.e1);
+        return e;
+    }
     std::lock_guard<std::mutex> lk(L.trace_mu);
     L.trace_recs.push_back(r);
     return e;

@@ -100,6 +100,15 @@ struct KernelInfo {
     hipError_t (*launch)(const KArgs&, dim3 grid, hipStream_t);
 };
 
+// Launch timing: while a thread's slot holds two events, the next library
+// launch on that thread records its kernel's own start and end in them
+// (hipExtLaunchKernel: timestamps of the dispatch itself, not of the stream
+// around it) and empties the slot.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
 int kernel_count();
 const KernelInfo& kernel_info(int i);
 int kernel_find(const char* name);

@@ -30,6 +30,7 @@
 #include "kernels.h"
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 // The file builds as four translation units compiled side by side: part 1
 // holds the single-tile kernels, the helper kernels and their launchers,
@@ -994,6 +995,21 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     }
 }
 
+// Every library launch goes through here: with the thread's launch-timing
+// slot set, the kernel's own start and end go into its events.
+template <typename F, typename... Args>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+    LaunchEvents& ev = launch_events();
+    if (ev.start != nullptr) {
+        const LaunchEvents use = ev;
+        ev = LaunchEvents{};
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, use.start, use.stop, 0, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+    }
+    return hipGetLastError();
+}
+
 template <class T>
 __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[T::LDS];
@@ -1002,8 +1018,7 @@ __global__ __launch_bounds__(T::NT) void gemm_tile_kernel(KArgs args) {
 
 template <class T>
 hipError_t launch_tile(const KArgs& a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL(gemm_tile_kernel<T>, grid, dim3(T::NT), 0, st, a);
-    return hipGetLastError();
+    return launch_kernel(gemm_tile_kernel<T>, grid, dim3(T::NT), st, a);
 }
 
 // The two regions of a plan in one launch: workgroups [0, n1) run tile T1
@@ -1029,8 +1044,7 @@ __global__ __launch_bounds__(T1::NT) void gemm_dual_kernel(KArgs a1, KArgs a2, i
 
 template <class T1, class T2>
 hipError_t launch_dual(const KArgs& a1, const KArgs& a2, int n1, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_dual_kernel<T1, T2>), grid, dim3(T1::NT), 0, st, a1, a2, n1);
-    return hipGetLastError();
+    return launch_kernel(gemm_dual_kernel<T1, T2>, grid, dim3(T1::NT), st, a1, a2, n1);
 }
 
 #if MKP_PART == 0 || MKP_PART == 1
@@ -1403,6 +1417,11 @@ const DualInfo& dual_info(int i) {
 #endif
 
 #if MKP_PART == 0 || MKP_PART == 1
+LaunchEvents& launch_events() {
+    thread_local LaunchEvents slot;
+    return slot;
+}
+
 int kernel_count() { return (int)(sizeof(g_kernels) / sizeof(g_kernels[0])); }
 const KernelInfo& kernel_info(int i) { return g_kernels[i]; }
 int kernel_find(const char* name) {
@@ -1419,12 +1438,10 @@ hipError_t launch_splitk_reduce(const float* W, int splits, int64_t sWsplit, int
     if (items > (int64_t)UINT32_MAX * 256) return hipErrorInvalidValue;
     dim3 grid((unsigned)((items + 255) / 256));
     if (epi)
-        hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, st, W, splits, sWsplit, sWbatch, ldw, C,
-                           ldc, sC, M, N, batch, vec, *epi);
-    else
-        hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, st, W, splits, sWsplit, sWbatch, ldw, C,
-                           ldc, sC, M, N, batch, vec, KEpi{});
-    return hipGetLastError();
+        return launch_kernel(splitk_reduce_kernel<true>, grid, dim3(256), st, W, splits, sWsplit, sWbatch, ldw, C, ldc,
+                             sC, M, N, batch, vec, *epi);
+    return launch_kernel(splitk_reduce_kernel<false>, grid, dim3(256), st, W, splits, sWsplit, sWbatch, ldw, C, ldc, sC,
+                         M, N, batch, vec, KEpi{});
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t ld_src, int64_t s_src, uint16_t* dst, int64_t ld_dst,
@@ -1432,30 +1449,25 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t ld_src, int64_t s_
     if (batch > 65535 || (ld_dst + 63) / 64 > 65535 || ld_dst % 8 != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((ld_dst + 63) / 64), (unsigned)batch);
     if (src_vec && K % 8 == 0 && N % 8 == 0 && ld_dst == K)
-        hipLaunchKernelGGL(transpose8_bf16_kernel, grid, dim3(64), 0, st, src, ld_src, s_src, dst, ld_dst, s_dst, K,
-                           N);
-    else if (src_vec)
-        hipLaunchKernelGGL(transpose_bf16_kernel<true>, grid, dim3(256), 0, st, src, ld_src, s_src, dst, ld_dst, s_dst,
-                           K, N);
-    else
-        hipLaunchKernelGGL(transpose_bf16_kernel<false>, grid, dim3(256), 0, st, src, ld_src, s_src, dst, ld_dst,
-                           s_dst, K, N);
-    return hipGetLastError();
+        return launch_kernel(transpose8_bf16_kernel, grid, dim3(64), st, src, ld_src, s_src, dst, ld_dst, s_dst, K, N);
+    if (src_vec)
+        return launch_kernel(transpose_bf16_kernel<true>, grid, dim3(256), st, src, ld_src, s_src, dst, ld_dst, s_dst, K,
+                             N);
+    return launch_kernel(transpose_bf16_kernel<false>, grid, dim3(256), st, src, ld_src, s_src, dst, ld_dst, s_dst, K,
+                         N);
 }
 
 hipError_t launch_zero_fill(float* C, int64_t ldc, int64_t sC, int M, int N, int batch, hipStream_t st) {
     const int64_t items = (int64_t)M * N * batch;
     dim3 grid((unsigned)((items + 255) / 256));
-    hipLaunchKernelGGL(zero_fill_kernel, grid, dim3(256), 0, st, C, ldc, sC, M, N, batch);
-    return hipGetLastError();
+    return launch_kernel(zero_fill_kernel, grid, dim3(256), st, C, ldc, sC, M, N, batch);
 }
 
 hipError_t launch_pack_rows(const uint16_t* src, int64_t ld_src, int64_t stride_src, uint16_t* dst, int64_t ld_dst,
                             int rows, int cols, int batch, hipStream_t st) {
     const int64_t items = (int64_t)rows * (ld_dst >> 3) * batch;
-    hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, src, ld_src,
-                       stride_src, dst, ld_dst, rows, cols, batch);
-    return hipGetLastError();
+    return launch_kernel(pack_rows_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), st, src, ld_src,
+                         stride_src, dst, ld_dst, rows, cols, batch);
 }
 
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st) {
