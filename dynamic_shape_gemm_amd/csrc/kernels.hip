@@ -1063,9 +1063,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const int n = (int)(e % nq) * 4;
     f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
     if (splits > 0) {
+        // partials in split order; eight loads are issued before the first
+        // add (a load per iteration would wait out one memory round trip
+        // per split)
         const float* w = W + (int64_t)b * sWb + (int64_t)m * ldw + n;
         s = *(const f32x4*)w;
-        for (int z = 1; z < splits; ++z) s += *(const f32x4*)(w + (int64_t)z * sWs);
+        for (int z0 = 1; z0 < splits; z0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (z0 + u < splits) v[u] = *(const f32x4*)(w + (int64_t)(z0 + u) * sWs);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (z0 + u < splits) s += v[u];
+        }
     }
     float* p = C + (int64_t)b * sC + (int64_t)m * ldc + n;
     if (EPI) s = epi4(epi, p, vec, N - n, load_bias4(epi, n, N - n), s);
