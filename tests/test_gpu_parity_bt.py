@@ -122,6 +122,30 @@ def test_bt_unaligned(mkp, pack):
         mkp.mkp_set_option("pack_unaligned", 1)
 
 
+BT_PHASE_KERNELS = ["m256n256k64_nk", "m128n128k64_nk", "m64n64k64_nk", "m32n128k64_nk"]
+
+
+@pytest.mark.parametrize("name", BT_PHASE_KERNELS)
+def test_bt_unaligned_rows_every_phase(mkp, name):
+    """N x K kernels on rows of every alignment: A and B rows at odd and even
+    element offsets (whole chunks read as shifted 4-byte words) and C rows at
+    every 4-byte phase of a 16-byte boundary (16-byte chunk stores plus up to
+    three floats at each end)."""
+    rng = np.random.default_rng(700 + BT_PHASE_KERNELS.index(name))
+    try:
+        mkp.mkp_set_option("force_kernel", name)
+        mkp.mkp_set_option("pack_unaligned", 0)
+        for (M, N, K) in [(70, 67, 72), (33, 130, 136), (9, 3, 40)]:
+            a, w = rand_bits(rng, (M, K)), rand_bits(rng, (N, K))
+            for lda, ldb, ldc, offA, offB, offC in [(K + 1, K + 1, N + 1, 0, 0, 0), (K, K + 2, N + 2, 1, 1, 1),
+                                                    (K + 3, K, N + 3, 0, 1, 2), (K + 1, K + 3, N, 1, 0, 3)]:
+                run_case_bt(mkp, a, w, lda=lda, ldb=ldb, ldc=ldc, offA=offA, offB=offB, offC=offC,
+                            what=f"{name} lda={lda} ldb={ldb} ldc={ldc} off=({offA},{offB},{offC})")
+    finally:
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("pack_unaligned", 1)
+
+
 def test_bt_k0_and_empty(mkp):
     import torch
 
