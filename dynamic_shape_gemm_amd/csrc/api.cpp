@@ -133,7 +133,7 @@ PerfTable analytic_table() {
     t.launch_us = 2.0;
     t.red_launch_us = 2.0;
     t.red_gbps = 4000.0;
-    t.splits = {1, 2, 4, 8, 16, 32};
+    t.splits = {1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32};
     for (int i = 0; i < kernel_count(); ++i) {
         const KernelInfo& ki = kernel_info(i);
         TableKernel k;
@@ -1313,7 +1313,7 @@ int mkp_calibrate(const char* path, int max_points) {
 
     PerfTable t;
     t.cus = cus;
-    t.splits = {1, 2, 4, 8, 16, 32};
+    t.splits = {1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32};
     hipError_t err = hipSuccess;
     // launch overhead: a one-workgroup kernel back to back
     t.launch_us = time_launches([&] { return launch_zero_fill(dC, 1, 0, 1, 1, 1, nullptr); }, 20, 200, &err);
