@@ -100,6 +100,18 @@ _lib.mkp_trace_dump.restype = _int
 _lib.mkp_last_error.argtypes = []
 _lib.mkp_last_error.restype = ctypes.c_char_p
 
+# The GEMM entry points through the CPython marshalling module built beside
+# the library (a ctypes call spends ~1.5 us converting 10-14 arguments, as
+# long as the smallest GEMMs take on the GPU); ctypes where it is absent.
+try:
+    from . import _mkpfast as _fast
+except ImportError:
+    _fast = None
+_f_gemm = _fast.gemm if _fast else _lib.mkp_gemm
+_f_gemm_bt = _fast.gemm_bt if _fast else _lib.mkp_gemm_bt
+_f_gemm_batched = _fast.gemm_batched if _fast else _lib.mkp_gemm_batched
+_f_gemm_batched_bt = _fast.gemm_batched_bt if _fast else _lib.mkp_gemm_batched_bt
+
 EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_ex", "mkp_conv2d", "mkp_gemm_grouped",
             "mkp_gemm_grouped_bt", "mkp_plan_describe", "mkp_plan_describe_grouped", "mkp_plan_with_table",
             "mkp_load_calibration",
@@ -138,41 +150,40 @@ def _stream(stream) -> int:
 def mkp_gemm(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     """C[MxN] := A[MxK] . B[KxN] (bf16 in, fp32 out), enqueued on `stream`
     (default: torch's current stream).  Raises MkpError on a bad argument."""
-    return _check(_lib.mkp_gemm(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)))
+    return _check(_f_gemm(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)))
 
 
 def mkp_gemm_batched(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream=None) -> int:
-    return _check(_lib.mkp_gemm_batched(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB, _addr(C),
-                                        ldc, strideC, _stream(stream)))
+    return _check(_f_gemm_batched(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB, _addr(C),
+                                  ldc, strideC, _stream(stream)))
 
 
 def mkp_gemm_raw(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
     """As mkp_gemm but returns the status code instead of raising."""
-    return _lib.mkp_gemm(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, stream or 0)
+    return _f_gemm(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, stream or 0)
 
 
 def mkp_gemm_batched_raw(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream) -> int:
-    return _lib.mkp_gemm_batched(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC,
-                                 stream or 0)
+    return _f_gemm_batched(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC, stream or 0)
 
 
 def mkp_gemm_bt(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     """C[MxN] := A[MxK] . B^T with B given as N x K (ldb >= K)."""
-    return _check(_lib.mkp_gemm_bt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)))
+    return _check(_f_gemm_bt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream)))
 
 
 def mkp_gemm_batched_bt(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream=None) -> int:
-    return _check(_lib.mkp_gemm_batched_bt(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB,
-                                           _addr(C), ldc, strideC, _stream(stream)))
+    return _check(_f_gemm_batched_bt(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB,
+                                     _addr(C), ldc, strideC, _stream(stream)))
 
 
 def mkp_gemm_bt_raw(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
-    return _lib.mkp_gemm_bt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, stream or 0)
+    return _f_gemm_bt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, stream or 0)
 
 
 def mkp_gemm_batched_bt_raw(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream) -> int:
-    return _lib.mkp_gemm_batched_bt(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC,
-                                    stream or 0)
+    return _f_gemm_batched_bt(batch, M, N, K, _addr(A), lda, sA, _addr(B), ldb, sB, _addr(C), ldc, sC,
+                              stream or 0)
 
 
 def mkp_gemm_ex(batch, M, N, K, A, lda, strideA, B, ldb, strideB, b_layout, C, ldc, strideC,

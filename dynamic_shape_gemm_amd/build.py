@@ -8,6 +8,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import sysconfig
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -113,7 +114,25 @@ def build_library(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_fast_binding(verbose)
     return LIB
+
+
+FAST = os.path.join(HERE, "_mkpfast" + (sysconfig.get_config_var("EXT_SUFFIX") or ".so"))
+
+
+def build_fast_binding(verbose: bool = False) -> str:
+    """The CPython marshalling module for the GEMM entry points (host C,
+    linked against libmkp.so next to it)."""
+    tmp = FAST + ".tmp"
+    cmd = [os.environ.get("CC", "gcc"), "-O2", "-shared", "-fPIC", "-Wall", "-I", sysconfig.get_paths()["include"],
+           "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "pymkp.c"), "-o", tmp, "-L", HERE, "-lmkp",
+           "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, FAST)
+    return FAST
 
 
 if __name__ == "__main__":

@@ -273,3 +273,24 @@ def test_table_named_by_environment_must_exist(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     assert "error -1" in r.stdout and "missing.tbl" in r.stdout, r.stdout
     assert "missing.tbl" in r.stderr and "analytic" in r.stderr, r.stderr
+
+
+def test_fast_marshalling_agrees_with_ctypes(mkp):
+    """The CPython marshalling module forwards to the same entry points as
+    ctypes: same status codes for argument errors and for empty calls."""
+    assert mkp._fast is not None, "the marshalling module was not built beside the library"
+    cases_gemm = [(-1, 4, 4, 1, 4, 1, 4, 1, 4, 0), (4, 4, 8, 1, 7, 1, 4, 1, 4, 0), (4, 4, 8, 0, 8, 1, 4, 1, 4, 0),
+                  (0, 4, 8, 0, 8, 0, 4, 0, 4, 0), (4, 4, 8, 1, 8, 1, 4, 1, 3, 0)]
+    for args in cases_gemm:
+        assert mkp._fast.gemm(*args) == mkp._lib.mkp_gemm(*args), args
+        assert mkp._fast.gemm_bt(*args) == mkp._lib.mkp_gemm_bt(*args), args
+    cases_batched = [(0, 17, 17, 64, 1, 64, 1088, 1, 17, 1088, 1, 17, 289, 0),
+                     (-2, 17, 17, 64, 1, 64, 1088, 1, 17, 1088, 1, 17, 289, 0),
+                     (2, 17, 17, 64, 1, 63, 1088, 1, 17, 1088, 1, 17, 289, 0)]
+    for args in cases_batched:
+        assert mkp._fast.gemm_batched(*args) == mkp._lib.mkp_gemm_batched(*args), args
+        assert mkp._fast.gemm_batched_bt(*args) == mkp._lib.mkp_gemm_batched_bt(*args), args
+    with pytest.raises(TypeError):
+        mkp._fast.gemm(1, 2, 3)
+    with pytest.raises(TypeError):
+        mkp._fast.gemm(1, 2, 3, "A", 4, 5, 6, 7, 8, 0)
