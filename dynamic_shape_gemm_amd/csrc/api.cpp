@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <deque>
 #include <fstream>
 #include <functional>
 #include <map>
@@ -73,7 +74,13 @@ struct KeyHash {
     }
 };
 
+// One stream's scratch buffer.  `mu` is held by a call from the moment it
+// takes the buffer until its last launch is enqueued, so calls that share a
+// stream (from several threads) never interleave their use of it: one
+// call's split-K partials cannot be overwritten, nor the buffer freed or
+// regrown, between another call's launches.  Entries are never erased.
 struct Workspace {
+    std::mutex mu;
     void* ptr = nullptr;
     size_t bytes = 0;
 };
@@ -91,12 +98,17 @@ struct TraceRec {
 };
 
 struct Library {
-    std::shared_mutex mu;                         // guards table, opts, cache
-    PerfTable table;
+    std::shared_mutex mu;                         // guards table, opts, caches, generation
+    // the active table: replaced whole (never modified), so a search can run
+    // on a snapshot without holding `mu`
+    std::shared_ptr<const PerfTable> table;
+    int64_t generation = 0;                       // bumped whenever plans may change
     std::string table_origin = "analytic";
     SearchOptions opts;
     std::unordered_map<Key, std::shared_ptr<const Plan>, KeyHash> cache;
+    std::deque<Key> cache_order;                  // insertion order: the oldest plan is evicted first
     std::map<std::vector<int64_t>, std::shared_ptr<const Plan>> gcache;   // grouped calls
+    std::deque<std::vector<int64_t>> gcache_order;
     size_t cache_cap = 1 << 16;
 
     std::mutex ws_mu;
@@ -104,6 +116,7 @@ struct Library {
     std::map<int, void*> zero_pages;
     // per (device, stream, slot): slot 0 serves the GEMM launches, slot 1
     // a convolution's channel-padded copies, which outlive slot 0's use
+    // (a call that holds both takes slot 1 first)
     std::map<std::tuple<int, void*, int>, Workspace> workspaces;
 
     std::atomic<int64_t> hits{0}, misses{0}, launches{0};
@@ -243,6 +256,16 @@ bool read_file(const std::string& path, std::string& out) {
     return true;
 }
 
+// Forget every cached plan (caller holds the lock exclusively); plans being
+// built on an older snapshot are then not cached.
+void clear_plans_locked(Library& L) {
+    L.cache.clear();
+    L.cache_order.clear();
+    L.gcache.clear();
+    L.gcache_order.clear();
+    ++L.generation;
+}
+
 // Load the table at `path` (or the shipped one) into the library; caller holds the lock.
 int load_table_locked(Library& L, const char* path, bool quiet_missing) {
     std::string p = path ? std::string(path) : default_table_path();
@@ -251,10 +274,9 @@ int load_table_locked(Library& L, const char* path, bool quiet_missing) {
         // only a missing shipped table is quiet; a path the caller or
         // MKP_CALIB names must exist
         if (quiet_missing && !std::getenv("MKP_CALIB")) {
-            L.table = bound_analytic_table();
+            L.table = std::make_shared<const PerfTable>(bound_analytic_table());
             L.table_origin = "analytic";
-            L.cache.clear();
-            L.gcache.clear();
+            clear_plans_locked(L);
             return MKP_OK;
         }
         return fail(MKP_ERR_INVALID_ARG, "cannot read performance table " + p);
@@ -262,10 +284,9 @@ int load_table_locked(Library& L, const char* path, bool quiet_missing) {
     PerfTable t;
     if (!parse_table(text, t, err) || !bind_table(t, err))
         return fail(MKP_ERR_INVALID_ARG, "performance table " + p + ": " + err);
-    L.table = t;
+    L.table = std::make_shared<const PerfTable>(std::move(t));
     L.table_origin = p;
-    L.cache.clear();
-    L.gcache.clear();
+    clear_plans_locked(L);
     return MKP_OK;
 }
 
@@ -275,8 +296,8 @@ void read_env_options(Library& L) {
     if (const char* e = std::getenv("MKP_FORCE_SPLITK")) L.opts.force_splitk = std::max(0, std::atoi(e));
     if (const char* e = std::getenv("MKP_CACHE_CAP")) L.cache_cap = (size_t)std::max(1, std::atoi(e));
     if (const char* e = std::getenv("MKP_FORCE_KERNEL")) {
-        for (size_t i = 0; i < L.table.kernels.size(); ++i)
-            if (L.table.kernels[i].name == e) L.opts.force_kernel = (int)i;
+        for (size_t i = 0; i < L.table->kernels.size(); ++i)
+            if (L.table->kernels[i].name == e) L.opts.force_kernel = (int)i;
     }
 }
 
@@ -289,7 +310,7 @@ void ensure_init() {
             // a shipped table that does not fit the library is a build error:
             // say so once, and plan with the analytic estimates
             std::fprintf(stderr, "libmkp: %s; planning with analytic estimates\n", t_last_error.c_str());
-            L.table = bound_analytic_table();
+            L.table = std::make_shared<const PerfTable>(bound_analytic_table());
             L.table_origin = "analytic";
         }
         read_env_options(L);
@@ -298,8 +319,20 @@ void ensure_init() {
 
 // ---- plans ------------------------------------------------------------------
 
+// A snapshot of what a search needs, taken under the shared lock.
+struct PlanInputs {
+    std::shared_ptr<const PerfTable> table;
+    SearchOptions opts;
+    int transpose_mode = 0;
+    int64_t generation = 0;
+};
+
+// Look the key up; on a miss, search on a snapshot with no lock held (so
+// lookups of other shapes never wait behind a search) and cache the plan
+// unless the table or the options changed meanwhile.
 std::shared_ptr<const Plan> get_plan(const Key& key) {
     Library& L = lib();
+    PlanInputs in;
     {
         std::shared_lock<std::shared_mutex> lk(L.mu);
         auto it = L.cache.find(key);
@@ -307,74 +340,105 @@ std::shared_ptr<const Plan> get_plan(const Key& key) {
             L.hits.fetch_add(1, std::memory_order_relaxed);
             return it->second;
         }
+        in.table = L.table;
+        in.opts = L.opts;
+        in.generation = L.generation;
     }
-    std::unique_lock<std::shared_mutex> lk(L.mu);
-    auto it = L.cache.find(key);
-    if (it != L.cache.end()) {
-        L.hits.fetch_add(1, std::memory_order_relaxed);
-        return it->second;
-    }
-    SearchOptions o = L.opts;
-    o.bt = key.bt;
-    if (key.conv) o.fuse = false;   // no two-tile form of the convolution kernels
-    const int tmode = key.conv ? 0 : key.batch <= 65535 ? L.transpose_b.load(std::memory_order_relaxed) : 0;
-    auto plan = std::make_shared<Plan>(plan_call(L.table, key.batch, key.M, key.N, key.K, o, tmode));
+    in.opts.bt = key.bt;
+    if (key.conv) in.opts.fuse = false;   // no two-tile form of the convolution kernels
+    in.transpose_mode = key.conv ? 0 : key.batch <= 65535 ? L.transpose_b.load(std::memory_order_relaxed) : 0;
+    auto plan = std::make_shared<const Plan>(
+        plan_call(*in.table, key.batch, key.M, key.N, key.K, in.opts, in.transpose_mode));
     L.misses.fetch_add(1, std::memory_order_relaxed);
     L.plan_ns.fetch_add((int64_t)(plan->plan_us * 1000.0), std::memory_order_relaxed);
-    if (L.cache.size() >= L.cache_cap) L.cache.clear();
-    L.cache.emplace(key, plan);
+    std::unique_lock<std::shared_mutex> lk(L.mu);
+    if (L.generation != in.generation) return plan;
+    auto ins = L.cache.emplace(key, plan);
+    if (!ins.second) return ins.first->second;   // another thread cached it first
+    L.cache_order.push_back(key);
+    while (L.cache.size() > L.cache_cap && !L.cache_order.empty()) {
+        L.cache.erase(L.cache_order.front());
+        L.cache_order.pop_front();
+    }
     return plan;
 }
 
 // ---- workspaces -------------------------------------------------------------
 
-int get_workspace(int dev, hipStream_t st, size_t bytes, void** out, int slot = 0) {
-    Library& L = lib();
-    std::lock_guard<std::mutex> lk(L.ws_mu);
-    Workspace& w = L.workspaces[{dev, (void*)st, slot}];
-    if (w.bytes < bytes) {
-        size_t want = std::max(bytes, w.bytes * 2);
-        want = (want + 4095) & ~(size_t)4095;
-        if (w.ptr) {
-            hipError_t e = hipFreeAsync(w.ptr, st);
-            w.ptr = nullptr;
-            w.bytes = 0;
-            if (e != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
-        }
-        void* p = nullptr;
-        hipError_t e = hipMallocAsync(&p, want, st);
-        if (e != hipSuccess || !p) {
-            (void)hipGetLastError();
-            return fail(MKP_ERR_OOM, "split-K workspace of " + std::to_string(want) + " bytes: allocation failed");
-        }
-        // the fused reduction's arrival counters start at zero (and every
-        // launch leaves them at zero)
-        e = launch_zero_fill((float*)p, kCounterCap, 0, 1, kCounterCap, 1, st);
-        if (e != hipSuccess) {
-            (void)hipFreeAsync(p, st);
-            return fail(MKP_ERR_HIP, std::string("workspace clear: ") + hipGetErrorString(e));
-        }
-        w.ptr = p;
-        w.bytes = want;
-    }
-    *out = w.ptr;
-    return MKP_OK;
-}
+// A call's hold on one stream's workspace: from acquire() until the lease
+// goes out of scope (after the call's last launch is enqueued), no other
+// call takes the same (device, stream, slot) buffer.
+class WsLease {
+   public:
+    WsLease() = default;
+    WsLease(const WsLease&) = delete;
+    WsLease& operator=(const WsLease&) = delete;
 
+    // The buffer, at least `bytes` long (grown stream-ordered when short).
+    int acquire(int dev, hipStream_t st, size_t bytes, void** out, int slot = 0) {
+        Library& L = lib();
+        if (!w_) {
+            std::lock_guard<std::mutex> lk(L.ws_mu);
+            w_ = &L.workspaces[{dev, (void*)st, slot}];
+        }
+        if (!lk_.owns_lock()) lk_ = std::unique_lock<std::mutex>(w_->mu);
+        Workspace& w = *w_;
+        if (w.bytes < bytes) {
+            size_t want = std::max(bytes, w.bytes * 2);
+            want = (want + 4095) & ~(size_t)4095;
+            if (w.ptr) {
+                hipError_t e = hipFreeAsync(w.ptr, st);
+                w.ptr = nullptr;
+                w.bytes = 0;
+                if (e != hipSuccess) return fail(MKP_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+            }
+            void* p = nullptr;
+            hipError_t e = hipMallocAsync(&p, want, st);
+            if (e != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return fail(MKP_ERR_OOM, "split-K workspace of " + std::to_string(want) + " bytes: allocation failed");
+            }
+            // the fused reduction's arrival counters start at zero (and every
+            // launch leaves them at zero)
+            e = launch_zero_fill((float*)p, kCounterCap, 0, 1, kCounterCap, 1, st);
+            if (e != hipSuccess) {
+                (void)hipFreeAsync(p, st);
+                return fail(MKP_ERR_HIP, std::string("workspace clear: ") + hipGetErrorString(e));
+            }
+            w.ptr = p;
+            w.bytes = want;
+        }
+        *out = w.ptr;
+        return MKP_OK;
+    }
+
+   private:
+    Workspace* w_ = nullptr;
+    std::unique_lock<std::mutex> lk_;
+};
+
+// Free every workspace (each after the calls holding it have enqueued their
+// launches, and after the device has finished them).
 void free_workspaces() {
     Library& L = lib();
-    std::lock_guard<std::mutex> lk(L.ws_mu);
-    if (L.workspaces.empty()) return;
+    std::vector<std::pair<int, Workspace*>> all;
+    {
+        std::lock_guard<std::mutex> lk(L.ws_mu);
+        for (auto& kv : L.workspaces) all.emplace_back(std::get<0>(kv.first), &kv.second);
+    }
+    if (all.empty()) return;
     int cur = 0;
     (void)hipGetDevice(&cur);
-    for (auto& kv : L.workspaces) {
-        if (!kv.second.ptr) continue;
-        (void)hipSetDevice(std::get<0>(kv.first));
+    for (auto& e : all) {
+        std::lock_guard<std::mutex> lk(e.second->mu);
+        if (!e.second->ptr) continue;
+        (void)hipSetDevice(e.first);
         (void)hipDeviceSynchronize();
-        (void)hipFree(kv.second.ptr);
+        (void)hipFree(e.second->ptr);
+        e.second->ptr = nullptr;
+        e.second->bytes = 0;
     }
     (void)hipSetDevice(cur);
-    L.workspaces.clear();
 }
 
 // ---- dispatch ---------------------------------------------------------------
@@ -531,8 +595,9 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     const size_t bytesB = tr ? (size_t)batch * N * ldt * 2 : packB ? (size_t)batch * b_rows * ldbp * 2 : 0;
     const size_t ws_bytes = (part_bytes || packA || packB || tr) ? offB + bytesB : 0;
     void* ws = nullptr;
+    WsLease lease;   // held until this call's last launch is enqueued
     if (ws_bytes) {
-        int rc = get_workspace(dev, st, ws_bytes, &ws);
+        int rc = lease.acquire(dev, st, ws_bytes, &ws);
         if (rc != MKP_OK) return rc;
     }
     if (packA) {
@@ -763,23 +828,36 @@ int run_grouped(int64_t G, int64_t M, int64_t K, const void* Av, int64_t lda, co
         widths.push_back(Ns[g]);
     }
     std::shared_ptr<const Plan> plan;
+    PlanInputs in;
     {
         std::shared_lock<std::shared_mutex> lk(L.mu);
         auto it = L.gcache.find(key);
         if (it != L.gcache.end()) plan = it->second;
+        in.table = L.table;
+        in.opts = L.opts;
+        in.generation = L.generation;
     }
     if (plan) {
         L.hits.fetch_add(1, std::memory_order_relaxed);
     } else {
-        std::unique_lock<std::shared_mutex> lk(L.mu);
-        SearchOptions o = L.opts;
-        o.bt = bt;
-        auto p = std::make_shared<Plan>(polymerize_grouped(L.table, M, K, widths, o));
+        // searched with no lock held, cached unless the table or options changed
+        in.opts.bt = bt;
+        plan = std::make_shared<const Plan>(polymerize_grouped(*in.table, M, K, widths, in.opts));
         L.misses.fetch_add(1, std::memory_order_relaxed);
-        L.plan_ns.fetch_add((int64_t)(p->plan_us * 1000.0), std::memory_order_relaxed);
-        if (L.gcache.size() >= L.cache_cap) L.gcache.clear();
-        L.gcache.emplace(key, p);
-        plan = p;
+        L.plan_ns.fetch_add((int64_t)(plan->plan_us * 1000.0), std::memory_order_relaxed);
+        std::unique_lock<std::shared_mutex> lk(L.mu);
+        if (L.generation == in.generation) {
+            auto ins = L.gcache.emplace(key, plan);
+            if (!ins.second) {
+                plan = ins.first->second;
+            } else {
+                L.gcache_order.push_back(key);
+                while (L.gcache.size() > L.cache_cap && !L.gcache_order.empty()) {
+                    L.gcache.erase(L.gcache_order.front());
+                    L.gcache_order.pop_front();
+                }
+            }
+        }
     }
     if (plan->regions.empty()) return fail(MKP_ERR_UNSUPPORTED, "no plan for this grouped call");
     const Region& r = plan->regions[0];
@@ -822,9 +900,10 @@ int run_grouped(int64_t G, int64_t M, int64_t K, const void* Av, int64_t lda, co
     // split-K partials: one workspace whose columns follow the launch's tile columns
     const int64_t ldw = (int64_t)tile0 * ki.uN;
     float* W = nullptr;
+    WsLease lease;   // held until this call's last launch is enqueued
     if (r.s > 1) {
         void* ws = nullptr;
-        int rc = get_workspace(dev, st, kCounterBytes + (size_t)r.s * M * ldw * sizeof(float), &ws);
+        int rc = lease.acquire(dev, st, kCounterBytes + (size_t)r.s * M * ldw * sizeof(float), &ws);
         if (rc != MKP_OK) return rc;
         W = (float*)((char*)ws + kCounterBytes);
         a.C = W;
@@ -975,6 +1054,9 @@ int mkp_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R,
     const uint16_t* xs = (const uint16_t*)x;
     const uint16_t* ws = (const uint16_t*)w;
     int64_t Cc = C;
+    // the padded copies (slot 1) stay this call's until the GEMM below has
+    // enqueued its launches on them
+    WsLease lease1;
     if (C % 8 != 0 || !aligned16(x)) {
         hipStream_t st = (hipStream_t)stream;
         const int64_t C8 = (C + 7) & ~int64_t(7);
@@ -984,7 +1066,7 @@ int mkp_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R,
             return fail(MKP_ERR_INVALID_ARG, "convolution extents exceed the 32-bit index range");
         void* buf = nullptr;
         t_call = lib().calls.load(std::memory_order_relaxed);   // the copies belong to this call's trace record
-        rc = get_workspace(dev, st, xbytes + (size_t)wrows * C8 * 2, &buf, 1);
+        rc = lease1.acquire(dev, st, xbytes + (size_t)wrows * C8 * 2, &buf, 1);
         if (rc != MKP_OK) return rc;
         uint16_t* xp = (uint16_t*)buf;
         uint16_t* wp = (uint16_t*)((char*)buf + xbytes);
@@ -1047,23 +1129,33 @@ int mkp_plan_describe_grouped(int64_t groups, int64_t M, int64_t K, const int64_
     }
     ensure_init();
     Library& L = lib();
-    std::shared_lock<std::shared_mutex> lk(L.mu);
-    SearchOptions o = L.opts;
+    std::shared_ptr<const PerfTable> tab;
+    SearchOptions o;
+    {
+        std::shared_lock<std::shared_mutex> lk(L.mu);
+        tab = L.table;
+        o = L.opts;
+    }
     o.bt = (flags & MKP_PLAN_B_NK) != 0;
     Plan p;
-    if (M > 0 && K > 0 && !widths.empty()) p = polymerize_grouped(L.table, M, K, widths, o);
-    return write_out(plan_to_json(p, L.table), buf, len);
+    if (M > 0 && K > 0 && !widths.empty()) p = polymerize_grouped(*tab, M, K, widths, o);
+    return write_out(plan_to_json(p, *tab), buf, len);
 }
 
 int mkp_plan_describe(int64_t batch, int64_t M, int64_t N, int64_t K, int align_flags, char* buf, size_t len) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
     ensure_init();
     Library& L = lib();
-    std::shared_lock<std::shared_mutex> lk(L.mu);
-    SearchOptions o = L.opts;
+    std::shared_ptr<const PerfTable> tab;
+    SearchOptions o;
+    {
+        std::shared_lock<std::shared_mutex> lk(L.mu);
+        tab = L.table;
+        o = L.opts;
+    }
     o.bt = (align_flags & MKP_PLAN_B_NK) != 0;
-    Plan p = plan_call(L.table, batch, M, N, K, o, batch <= 65535 ? L.transpose_b.load() : 0);
-    return write_out(plan_to_json(p, L.table), buf, len);
+    Plan p = plan_call(*tab, batch, M, N, K, o, batch <= 65535 ? L.transpose_b.load() : 0);
+    return write_out(plan_to_json(p, *tab), buf, len);
 }
 
 int mkp_plan_with_table(const char* table_text, int flags, int64_t batch, int64_t M, int64_t N, int64_t K,
@@ -1113,8 +1205,8 @@ int mkp_set_option(const char* key, const char* value) {
             L.opts.force_kernel = -1;
         } else {
             int idx = -1;
-            for (size_t i = 0; i < L.table.kernels.size(); ++i)
-                if (L.table.kernels[i].name == v) idx = (int)i;
+            for (size_t i = 0; i < L.table->kernels.size(); ++i)
+                if (L.table->kernels[i].name == v) idx = (int)i;
             if (idx < 0) return fail(MKP_ERR_UNSUPPORTED, "no kernel named " + v + " in the active table");
             L.opts.force_kernel = idx;
         }
@@ -1163,8 +1255,7 @@ int mkp_set_option(const char* key, const char* value) {
     } else {
         return fail(MKP_ERR_INVALID_ARG, "unknown option " + k);
     }
-    L.cache.clear();
-    L.gcache.clear();
+    clear_plans_locked(L);
     return MKP_OK;
 }
 
@@ -1180,8 +1271,7 @@ void mkp_cache_clear(void) {
     {
         Library& L = lib();
         std::unique_lock<std::shared_mutex> lk(L.mu);
-        L.cache.clear();
-        L.gcache.clear();
+        clear_plans_locked(L);
     }
     free_workspaces();
 }
@@ -1488,11 +1578,10 @@ int mkp_calibrate(const char* path, int max_points) {
     }
     Library& L = lib();
     std::unique_lock<std::shared_mutex> lk(L.mu);
-    L.table = t;
+    L.table = std::make_shared<const PerfTable>(std::move(t));
     L.table_origin = path;
     L.opts.force_kernel = -1;
-    L.cache.clear();
-    L.gcache.clear();
+    clear_plans_locked(L);
     return MKP_OK;
 }
 

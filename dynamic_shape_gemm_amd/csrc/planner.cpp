@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <limits>
 #include <sstream>
+#include <unordered_map>
 
 namespace mkp {
 
@@ -310,13 +311,16 @@ namespace {
 // GPU uses patterns I and II):
 //   I    : one region, one kernel, the whole M x N.
 //   II-M : rows [0, cut) on kernel a, rows [cut, M) on kernel b != a, where
-//          the cut is a wave boundary of region 1: the largest multiple of
-//          uM(a) whose tasks fill exactly w waves of kernel a (w = 1, 2, ...),
-//          as in the case study where region 1 is one full wave of kernel A.
+//          the cut is any multiple of uM(a) strictly inside M (region 1 is
+//          tile-aligned; region 2 carries the ragged edge).  In the case
+//          study region 1 is 3072 rows of kernel A: 96 of A's 108 slots.
 //   II-N : the same along N.
 // Every region takes its own split factor.  The search visits Pattern I
-// first (a tight bound), then the II cuts in increasing w, and stops as soon
-// as a partial cost plus a lower bound for the rest reaches the best found.
+// first (a tight bound), then the II cuts in increasing order, skipping a
+// cut whose region-1 cost plus a lower bound for region 2 reaches the best
+// found, and stopping once no larger cut can win.  The best region 2 for a
+// remaining extent e depends on e only (and on which kernel region 1 uses),
+// so it is computed once per e and kept.
 struct Searcher {
     const PerfTable& tab;
     const SearchOptions& opt;
@@ -331,14 +335,9 @@ struct Searcher {
     std::vector<std::vector<SplitChoice>> sc;   // per kernel: distinct usable splits
     std::vector<double> min_g;                   // per kernel: cheapest single (possibly partial) wave
     std::vector<double> rate;                    // per kernel: lowest cost per output element
+    std::vector<double> tmin_alone, tmin_after;  // per kernel: smallest partial-wave ratio (tail, tailx)
     double lb_region = 0.0;                      // lower bound of any region's cost
     double min_rate = 0.0;                       // lowest rate over allowed kernels
-
-    // Lower bound of a region of m x n on kernel b: its tasks fill at least
-    // m*n*s/(uM*uN*slots) (fractional) waves of g each; launch cost on top.
-    double lb(int b, int64_t m, int64_t n) const {
-        return tab.launch_us + std::max(min_g[b], (double)m * (double)n * (double)batch * rate[b]);
-    }
 
     Searcher(const PerfTable& t, const SearchOptions& o, int64_t b, int64_t m, int64_t n, int64_t k)
         : tab(t), opt(o), batch(b), M(m), N(n), K(k) {
@@ -350,23 +349,29 @@ struct Searcher {
                 if (s <= opt.splitk_max) req.push_back(s);
             if (req.empty()) req.push_back(1);
         }
-        sc.resize(tab.kernels.size());
-        min_g.assign(tab.kernels.size(), std::numeric_limits<double>::infinity());
-        rate.assign(tab.kernels.size(), std::numeric_limits<double>::infinity());
+        const size_t nk = tab.kernels.size();
+        sc.resize(nk);
+        min_g.assign(nk, std::numeric_limits<double>::infinity());
+        rate.assign(nk, std::numeric_limits<double>::infinity());
+        tmin_alone.assign(nk, 1.0);
+        tmin_after.assign(nk, 1.0);
         lb_region = std::numeric_limits<double>::infinity();
         min_rate = std::numeric_limits<double>::infinity();
-        for (size_t ki = 0; ki < tab.kernels.size(); ++ki) {
+        for (size_t ki = 0; ki < nk; ++ki) {
             const TableKernel& kk = tab.kernels[ki];
             const int64_t t3 = ceil_div(K, kk.uK);
             // a region's wave factor is at least tmin (one possibly partial
             // wave) and at least rho * tasks/slots (piecewise-linear ratios:
             // r(f)/f is smallest at a point or at f = 1)
-            double tmin = 1.0, rho = 1.0;
+            double rho = 1.0;
             for (auto& p : kk.tail) {
-                tmin = std::min(tmin, p.second);
+                tmin_alone[ki] = std::min(tmin_alone[ki], p.second);
                 rho = std::min(rho, p.second / p.first);
             }
-            for (auto& p : kk.tailx) rho = std::min(rho, p.second / p.first);
+            for (auto& p : kk.tailx) {
+                tmin_after[ki] = std::min(tmin_after[ki], p.second);
+                rho = std::min(rho, p.second / p.first);
+            }
             for (int s_req : req) {
                 // a factor above the K-step count is only kept when forced
                 if (s_req > 1 && s_req > t3 && opt.force_splitk <= 0) continue;
@@ -377,7 +382,7 @@ struct Searcher {
                 for (auto& c : sc[ki]) dup |= c.s_eff == s_eff;
                 if (dup) continue;
                 sc[ki].push_back({s_eff, (int)per, g_predict(kk, (double)per)});
-                min_g[ki] = std::min(min_g[ki], tmin * sc[ki].back().g);
+                min_g[ki] = std::min(min_g[ki], tmin_alone[ki] * sc[ki].back().g);
                 const double slots = (double)tab.cus * kk.wg_per_cu;
                 rate[ki] = std::min(rate[ki], rho * (double)s_eff * sc[ki].back().g / (slots * kk.uM * kk.uN));
             }
@@ -392,6 +397,12 @@ struct Searcher {
         return tab.kernels[k].bt == opt.bt && (opt.force_kernel < 0 || opt.force_kernel == k);
     }
 
+    double red_cost(int s_eff, int64_t m, int64_t n) const {
+        return s_eff > 1 ? tab.red_launch_us +
+                               (double)(2 * s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch / (tab.red_gbps * 1e3)
+                         : 0.0;
+    }
+
     double cost(int ki, const SplitChoice& c, int64_t m, int64_t n, Region* r) {
         ++evaluated;
         const TableKernel& k = tab.kernels[ki];
@@ -403,9 +414,7 @@ struct Searcher {
         if (opt.cost_mode == COST_WAVE) v += (double)waves;   // the page's f_wave alone
         else if (opt.cost_mode == COST_PIPE) v += c.g;
         else v += wf * c.g;
-        if (c.s_eff > 1)
-            v += tab.red_launch_us +
-                 (double)(2 * c.s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch / (tab.red_gbps * 1e3);
+        v += red_cost(c.s_eff, m, n);
         if (r) {
             r->kernel = ki;
             r->lib = k.lib_index;
@@ -421,24 +430,36 @@ struct Searcher {
         return v;
     }
 
+    // Lower bound of the cost of region 1 on kernel a with split c for every
+    // cut of at least m x n (a larger cut has at least as many full waves,
+    // a partial wave costs at least the kernel's smallest tail ratio, and
+    // the reduction grows with the area).
+    double lb_from(int a, const SplitChoice& c, int64_t m, int64_t n) const {
+        const TableKernel& k = tab.kernels[a];
+        const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * c.s_eff * batch;
+        const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
+        const int64_t full = tasks / slots;
+        const double part = tasks % slots ? (full ? tmin_after[a] : tmin_alone[a]) : 0.0;
+        return tab.launch_us + ((double)full + part) * c.g + red_cost(c.s_eff, m, n);
+    }
+
+    // Lower bound of any region 2 of m x n.
+    double lb2(int64_t m, int64_t n) const {
+        return tab.launch_us + std::max((double)m * (double)n * (double)batch * min_rate, lb_region - tab.launch_us);
+    }
+
     // Both regions of a Pattern II cut in one launch over a kernel pair:
     // launch + the merged-wave makespan of the two task lists (each task as
     // long as its kernel's full-wave time g) + each region's split-K
     // reduction.  Not additive over the regions.
     double fused_cost(int a, const SplitChoice& c1, int64_t m1, int64_t n1, int b, const SplitChoice& c2,
                       int64_t m2, int64_t n2, Region* r1, Region* r2) {
-        const double v1 = cost(a, c1, m1, n1, r1);
-        const double v2 = cost(b, c2, m2, n2, r2);
-        (void)v1;
-        (void)v2;
+        (void)cost(a, c1, m1, n1, r1);
+        (void)cost(b, c2, m2, n2, r2);
         const TableKernel& ka = tab.kernels[a];
         const int64_t S = (int64_t)tab.cus * ka.wg_per_cu;
-        double v = tab.launch_us + merged_makespan(S, r1->tasks, c1.g, r2->tasks, c2.g);
-        for (const Region* r : {r1, r2})
-            if (r->s > 1)
-                v += tab.red_launch_us +
-                     (double)(2 * r->s + 1) * 4.0 * (double)r->m * (double)r->n * (double)batch / (tab.red_gbps * 1e3);
-        return v;
+        return tab.launch_us + merged_makespan(S, r1->tasks, c1.g, r2->tasks, c2.g) + red_cost(r1->s, r1->m, r1->n) +
+               red_cost(r2->s, r2->m, r2->n);
     }
 
     bool fuse_allowed() const {
@@ -446,19 +467,15 @@ struct Searcher {
     }
 
     // Visit every one-launch Pattern II candidate: for each kernel pair
-    // (a, b), direction, split of a and wave-boundary cut (as for Pattern
-    // II), and split of b.  fn(cost, r1, r2, dir) sees each; it returns true
-    // when the candidate became the best so far.  With use_bound, candidates
+    // (a, b), direction, split of a, tile-aligned cut (as for Pattern II)
+    // and split of b.  fn(cost, r1, r2, dir) sees each; it returns true when
+    // the candidate became the best so far.  With use_bound, candidates
     // whose lower bound reaches `bound` are skipped: the makespan is at
     // least the first region's own waves, ceil(n1/S) d1 (which only grows
-    // with the cut), and at least the total work over the slots.
+    // with the cut, as does its reduction), and at least the total work over
+    // the slots.
     template <class F>
     void fused_candidates(double bound, bool use_bound, F&& fn) {
-        auto red = [&](int s_eff, int64_t m, int64_t n) {
-            return s_eff > 1 ? tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)m * (double)n *
-                                                       (double)batch / (tab.red_gbps * 1e3)
-                             : 0.0;
-        };
         for (auto& pr : tab.pairs) {
             const int a = pr.first, b = pr.second;
             if (!kernel_allowed(a) || !kernel_allowed(b)) continue;
@@ -470,24 +487,17 @@ struct Searcher {
                 if (dir == 1 && !tab.pat_IIN) continue;
                 const int64_t ext = dir == 0 ? M : N;
                 const int64_t step = dir == 0 ? ka.uM : ka.uN;
-                const int64_t across = dir == 0 ? ceil_div(N, ka.uN) : ceil_div(M, ka.uM);
                 for (auto& c1s : sc[a]) {
-                    const int64_t per_line = across * c1s.s_eff * batch;
-                    int64_t prev_cut = 0;
-                    for (int64_t w = 1;; ++w) {
-                        const int64_t cut = (w * S / per_line) * step;
-                        if (cut >= ext) break;
-                        if (cut == 0 || cut == prev_cut) continue;
-                        prev_cut = cut;
+                    for (int64_t cut = step; cut < ext; cut += step) {
                         const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
                         const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
                         const int64_t t1 = ceil_div(m1, ka.uM) * ceil_div(n1, ka.uN) * c1s.s_eff * batch;
                         const double own1 = (double)ceil_div(t1, S) * c1s.g;
-                        const double red1 = red(c1s.s_eff, m1, n1);
+                        const double red1 = red_cost(c1s.s_eff, m1, n1);
                         if (use_bound && tab.launch_us + own1 + red1 >= bound) break;
                         for (auto& c2s : sc[b]) {
                             const int64_t t2 = ceil_div(m2, kb.uM) * ceil_div(n2, kb.uN) * c2s.s_eff * batch;
-                            const double lbv = tab.launch_us + red1 + red(c2s.s_eff, m2, n2) +
+                            const double lbv = tab.launch_us + red1 + red_cost(c2s.s_eff, m2, n2) +
                                                std::max(own1, ((double)t1 * c1s.g + (double)t2 * c2s.g) / (double)S);
                             if (use_bound && lbv >= bound) continue;
                             Region r1, r2;
@@ -516,29 +526,74 @@ struct Searcher {
         return best;
     }
 
+    // Best region 2 for one remaining extent: the cheapest kernel and split,
+    // and the cheapest on a different kernel (region 2 may not reuse region
+    // 1's kernel).  Kernels are visited in table order, so ties keep the
+    // earliest, as in a plain scan.
+    struct Second {
+        double c1 = std::numeric_limits<double>::infinity(), c2 = std::numeric_limits<double>::infinity();
+        Region r1, r2;
+    };
+    Second second_for(int64_t m, int64_t n) {
+        Second out;
+        const int nk = (int)tab.kernels.size();
+        for (int b = 0; b < nk; ++b) {
+            if (!kernel_allowed(b)) continue;
+            Region r;
+            const double v = best_region(b, m, n, &r);
+            if (v < out.c1) {
+                if (out.r1.kernel >= 0 && out.r1.kernel != b) {
+                    out.c2 = out.c1;
+                    out.r2 = out.r1;
+                }
+                out.c1 = v;
+                out.r1 = r;
+            } else if (v < out.c2 && b != out.r1.kernel) {
+                out.c2 = v;
+                out.r2 = r;
+            }
+        }
+        return out;
+    }
+
     // The bounds below hold for the full model only; the ablations and the
     // ranked list score every candidate.
     bool prune() const { return !opt.exhaustive && opt.cost_mode == COST_FULL; }
 
     // Every candidate of the space (each region with each of its splits),
     // ordered by modelled cost (ties keep enumeration order); returns the
-    // rank-th (1-based) and the list size.
+    // rank-th (1-based) and the size of the space.  Only the `rank` cheapest
+    // are kept while the space is walked.
     Plan ranked(int rank) {
         struct Cand {
             double cost;
+            int64_t seq;
             int pattern;
             Region r1, r2;
             bool fused = false;
         };
-        std::vector<Cand> all;
+        auto worse = [](const Cand& x, const Cand& y) { return x.cost < y.cost || (x.cost == y.cost && x.seq < y.seq); };
+        std::vector<Cand> heap;   // max-heap under `worse`: the worst kept candidate on top
+        int64_t seq = 0;
+        auto offer = [&](Cand&& x) {
+            x.seq = seq++;
+            if ((int64_t)heap.size() < rank) {
+                heap.push_back(std::move(x));
+                std::push_heap(heap.begin(), heap.end(), worse);
+            } else if (!heap.empty() && worse(x, heap.front())) {
+                std::pop_heap(heap.begin(), heap.end(), worse);
+                heap.back() = std::move(x);
+                std::push_heap(heap.begin(), heap.end(), worse);
+            }
+        };
         const int nk = (int)tab.kernels.size();
         if (tab.pat_I)
             for (int a = 0; a < nk; ++a) {
                 if (!kernel_allowed(a)) continue;
                 for (auto& c : sc[a]) {
-                    Cand x{0.0, PAT_I, {}, {}};
+                    Cand x{0.0, 0, PAT_I, {}, {}};
                     x.cost = cost(a, c, M, N, &x.r1);
-                    all.push_back(x);
+                    offer(std::move(x));
                 }
             }
         if (opt.force_kernel < 0 && opt.allow_II)
@@ -550,26 +605,20 @@ struct Searcher {
                     if (!kernel_allowed(a)) continue;
                     const TableKernel& ka = tab.kernels[a];
                     const int64_t step = dir == 0 ? ka.uM : ka.uN;
-                    const int64_t across = dir == 0 ? ceil_div(N, ka.uN) : ceil_div(M, ka.uM);
-                    const int64_t slots = (int64_t)tab.cus * ka.wg_per_cu;
                     for (auto& c1s : sc[a]) {
-                        const int64_t per_line = across * c1s.s_eff * batch;
-                        int64_t prev_cut = 0;
-                        for (int64_t w = 1;; ++w) {
-                            const int64_t cut = (w * slots / per_line) * step;
-                            if (cut >= ext) break;
-                            if (cut == 0 || cut == prev_cut) continue;
-                            prev_cut = cut;
+                        for (int64_t cut = step; cut < ext; cut += step) {
                             const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
                             const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
+                            Region r1;
+                            const double c1 = cost(a, c1s, m1, n1, &r1);
                             for (int b = 0; b < nk; ++b) {
                                 if (b == a || !kernel_allowed(b)) continue;
                                 for (auto& c2s : sc[b]) {
-                                    Cand x{0.0, dir == 0 ? PAT_IIM : PAT_IIN, {}, {}};
-                                    x.cost = cost(a, c1s, m1, n1, &x.r1) + cost(b, c2s, m2, n2, &x.r2);
+                                    Cand x{0.0, 0, dir == 0 ? PAT_IIM : PAT_IIN, r1, {}};
+                                    x.cost = c1 + cost(b, c2s, m2, n2, &x.r2);
                                     x.r2.m0 = dir == 0 ? cut : 0;
                                     x.r2.n0 = dir == 0 ? 0 : cut;
-                                    all.push_back(x);
+                                    offer(std::move(x));
                                 }
                             }
                         }
@@ -578,20 +627,19 @@ struct Searcher {
             }
         if (fuse_allowed())
             fused_candidates(0.0, false, [&](double v, const Region& r1, const Region& r2, int dir) {
-                Cand x{v, dir == 0 ? PAT_IIM : PAT_IIN, r1, r2, true};
-                all.push_back(x);
+                offer(Cand{v, 0, dir == 0 ? PAT_IIM : PAT_IIN, r1, r2, true});
                 return false;
             });
-        std::stable_sort(all.begin(), all.end(), [](const Cand& x, const Cand& y) { return x.cost < y.cost; });
         Plan p;
         p.rank = rank;
-        p.candidates = (int64_t)all.size();
-        if (rank < 1 || rank > (int)all.size()) {
+        p.candidates = seq;
+        if (rank < 1 || rank > (int64_t)heap.size()) {
             p.pattern = PAT_I;
             p.cost_us = std::numeric_limits<double>::infinity();
             return p;   // no regions: the caller reports "no plan"
         }
-        const Cand& c = all[rank - 1];
+        std::sort_heap(heap.begin(), heap.end(), worse);
+        const Cand& c = heap[rank - 1];
         p.pattern = c.pattern;
         p.cost_us = c.cost;
         p.fused = c.fused;
@@ -624,46 +672,34 @@ struct Searcher {
             if (dir == 0 && !tab.pat_IIM) continue;
             if (dir == 1 && !tab.pat_IIN) continue;
             const int64_t ext = dir == 0 ? M : N;
+            std::unordered_map<int64_t, Second> seconds;   // remaining extent -> best region 2
             for (int a = 0; a < nk; ++a) {
                 if (!kernel_allowed(a)) continue;
                 const TableKernel& ka = tab.kernels[a];
                 const int64_t step = dir == 0 ? ka.uM : ka.uN;
-                // tiles across the uncut dimension
-                const int64_t across = dir == 0 ? ceil_div(N, ka.uN) : ceil_div(M, ka.uM);
-                const int64_t slots = (int64_t)tab.cus * ka.wg_per_cu;
                 for (auto& c1s : sc[a]) {
-                    const int64_t per_line = across * c1s.s_eff * batch;   // tasks per tile row (column)
-                    int64_t prev_cut = 0;
-                    for (int64_t w = 1;; ++w) {
-                        const int64_t lines = w * slots / per_line;
-                        const int64_t cut = lines * step;
-                        if (cut >= ext) break;
-                        if (cut == 0 || cut == prev_cut) continue;
-                        prev_cut = cut;
+                    for (int64_t cut = step; cut < ext; cut += step) {
+                        const int64_t e = ext - cut;
+                        const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
+                        const int64_t m2 = dir == 0 ? e : M, n2 = dir == 0 ? N : e;
+                        // no cut from here on can lead to a better plan
+                        if (prune() && lb_from(a, c1s, m1, n1) + lb_region >= best.cost_us) break;
                         Region r1;
-                        const double c1 = dir == 0 ? cost(a, c1s, cut, N, &r1) : cost(a, c1s, M, cut, &r1);
-                        // c1 grows with w: once it cannot lead to a better plan, stop
-                        if (prune() && c1 + lb_region >= best.cost_us) break;
-                        const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
-                        if (prune() &&
-                            c1 + tab.launch_us + std::max((double)m2 * n2 * batch * min_rate, lb_region - tab.launch_us) >=
-                                best.cost_us)
-                            continue;
-                        for (int b = 0; b < nk; ++b) {
-                            if (b == a || !kernel_allowed(b)) continue;
-                            if (prune() && c1 + lb(b, m2, n2) >= best.cost_us) continue;
-                            Region r2;
-                            const double c2 = dir == 0 ? best_region(b, M - cut, N, &r2) : best_region(b, M, N - cut, &r2);
-                            const double c = c1 + c2;
-                            if (c < best.cost_us) {
-                                best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
-                                best.cost_us = c;
-                                r1.m0 = r1.n0 = 0;
-                                r2.m0 = dir == 0 ? cut : 0;
-                                r2.n0 = dir == 0 ? 0 : cut;
-                                best.regions.assign({r1, r2});
-                            }
-                        }
+                        const double c1 = cost(a, c1s, m1, n1, &r1);
+                        if (prune() && c1 + lb2(m2, n2) >= best.cost_us) continue;
+                        auto it = seconds.find(e);
+                        if (it == seconds.end()) it = seconds.emplace(e, second_for(m2, n2)).first;
+                        const Second& sd = it->second;
+                        const bool own = sd.r1.kernel == a;
+                        const double c2 = own ? sd.c2 : sd.c1;
+                        if (!(c1 + c2 < best.cost_us)) continue;
+                        Region r2 = own ? sd.r2 : sd.r1;
+                        best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
+                        best.cost_us = c1 + c2;
+                        r1.m0 = r1.n0 = 0;
+                        r2.m0 = dir == 0 ? cut : 0;
+                        r2.n0 = dir == 0 ? 0 : cut;
+                        best.regions.assign({r1, r2});
                     }
                 }
             }

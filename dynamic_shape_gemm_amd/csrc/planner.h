@@ -83,7 +83,7 @@ struct Plan {
     bool fused = false;        // the two regions run in one launch (a kernel pair)
 };
 
-// Which factors of the cost model the search scores (MikPoly page, section 4
+// Which factors of the cost model the search scores (MikPoly page, section 5
 // ablation): the full product f_wave * f_pipe, f_wave alone (f_pipe taken as
 // 1 us), or f_pipe alone (f_wave taken as 1).  The launch and split-K
 // reduction terms stay in all three.

@@ -19,10 +19,16 @@
  * reported synchronously, before anything is written to C.  Faults inside a
  * kernel surface at the caller's next synchronisation of `stream`.
  *
- * Thread safety: every entry point may be called from several host threads;
- * the plan cache is shared under a lock and split-K workspaces are kept per
- * (device, stream).  Two calls that run concurrently on different streams
- * must not write the same C.  C must not alias A or B.
+ * Thread safety: every entry point may be called from several host threads,
+ * on the same stream or on different ones.  The plan cache is shared under
+ * a lock (a search on a miss runs outside it, so lookups of other shapes do
+ * not wait); split-K workspaces are kept per (device, stream), and a call
+ * holds its stream's workspace from the moment it takes it until its last
+ * launch is enqueued, so calls on one stream from several threads run one
+ * after the other on that stream without sharing partial results.  Two
+ * calls that run concurrently on different streams must not write the same
+ * C.  C must not alias A or B.  mkp_cache_clear() waits for the calls that
+ * hold workspaces and then for the device before freeing them.
  *
  * Status codes: MKP_OK (0) on success, negative on error; mkp_last_error()
  * returns a thread-local message for the last error raised on this thread.

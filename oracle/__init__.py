@@ -47,8 +47,8 @@ def _load():
         lib.oracle_gemm_entries.argtypes = [i64, i64, i64, p, i64, i64, p, i64, i64, i64, p, p, p, p, p,
                                             ctypes.c_int]
         lib.oracle_gemm_entries.restype = ctypes.c_int
-        lib.oracle_gemm_tiled.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i64]
-        lib.oracle_gemm_tiled.restype = ctypes.c_int
+        lib.oracle_gemm_outer.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+        lib.oracle_gemm_outer.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [ctypes.c_int]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -108,15 +108,16 @@ def gemm_entries(a: np.ndarray, b: np.ndarray, rows, cols, bidx=None, nthreads: 
     return out, outabs
 
 
-def gemm_tiled(a: np.ndarray, b: np.ndarray, tile: int = 32) -> np.ndarray:
+def gemm_outer(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """A.B accumulated as K ascending rank-1 updates (oracle_gemm_outer)."""
     lib = _load()
     a = np.ascontiguousarray(a, dtype=np.uint16)
     b = np.ascontiguousarray(b, dtype=np.uint16)
     M, K = a.shape
     N = b.shape[1]
     c = np.empty((M, N), dtype=np.float64)
-    if lib.oracle_gemm_tiled(M, N, K, _ptr(a), K, _ptr(b), N, _ptr(c), N, tile) != 0:
-        raise RuntimeError("oracle_gemm_tiled failed")
+    if lib.oracle_gemm_outer(M, N, K, _ptr(a), K, _ptr(b), N, _ptr(c), N) != 0:
+        raise RuntimeError("oracle_gemm_outer failed")
     return c
 
 

@@ -48,10 +48,11 @@ Readings where the page is silent (each is listed in the design doc):
     full-wave time) + the reductions.  Not additive over the regions.
   * Pattern I: one region = whole output, one kernel.  Pattern II-M (II-N):
     a cut of the M (N) extent, the two parts on two different kernels (the
-    case study's 3072 | 1024 split).  The cut is a wave boundary of the
-    first region: the largest multiple of kernel a's tile whose tasks fill
-    exactly w whole waves of a (w = 1, 2, ...), the case study's first region
-    being one full wave of kernel A.  Each region has its own split factor.
+    case study's 3072 | 1024 split).  The cut may be any multiple of kernel
+    a's tile height (width) strictly inside the extent, so the first region
+    is tile-aligned and only the second carries the ragged edge; in the case
+    study the first region holds 96 tasks of a 108-slot wave, which is not a
+    whole wave.  Each region has its own split factor.
 """
 from __future__ import annotations
 
@@ -302,20 +303,9 @@ def enumerate_plans(tab: Table, M: int, N: int, K: int, batch: int = 1, bt: bool
         for a in names:
             ka = tab.kernels[a]
             step = ka.uM if pat == "II-M" else ka.uN
-            across = ceil_div(N, ka.uN) if pat == "II-M" else ceil_div(M, ka.uM)
-            t3 = ceil_div(K, ka.uK)
             for s1 in _valid_splits(tab, ka, K):
-                s1_eff = split_steps(t3, s1)[1]
-                per_line = across * s1_eff * batch
-                prev, w = 0, 0
-                while True:
-                    w += 1
-                    cut = (w * tab.slots(ka) // per_line) * step
-                    if cut >= ext:
-                        break
-                    if cut == 0 or cut == prev:
-                        continue
-                    prev = cut
+                # every tile-aligned cut strictly inside the extent
+                for cut in range(step, ext, step):
                     for b in names:
                         if b == a:
                             continue

@@ -129,26 +129,29 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
 }
 
 /*
- * The page's loop-tiled form (same section, the tiled six-loop version with
- * square tiles of side `tile`), single batch entry, run serially.  Each
- * element still accumulates in ascending k from zero, so it must equal
- * oracle_gemm bit for bit; the self-test relies on that.  Edge tiles are cut
- * at M, N, K.
+ * The same product as a sum of K outer products (rank-1 updates): for
+ * k = 0, 1, ..., K-1 in ascending order, C += (column k of A) x (row k of
+ * B), every row and column of the update visited from the last to the
+ * first.  Each element still receives its K terms in ascending k starting
+ * from zero, so the result must equal oracle_gemm bit for bit whatever the
+ * order inside one update; the self-test relies on that (summation order
+ * per element, not the visiting order of elements, fixes the rounding).
+ * Single batch entry, run serially.
  */
-int oracle_gemm_tiled(int64_t M, int64_t N, int64_t K,
+int oracle_gemm_outer(int64_t M, int64_t N, int64_t K,
                       const uint16_t *A, int64_t lda,
                       const uint16_t *B, int64_t ldb,
-                      double *C, int64_t ldc, int64_t tile)
+                      double *C, int64_t ldc)
 {
-    if (M < 0 || N < 0 || K < 0 || tile <= 0) return -1;
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldc < N) return -1;
     for (int64_t i = 0; i < M; ++i)
-        for (int64_t j = 0; j < N; ++j) C[i * ldc + j] = 0.0;
-    for (int64_t i0 = 0; i0 < M; i0 += tile)
-        for (int64_t j0 = 0; j0 < N; j0 += tile)
-            for (int64_t k0 = 0; k0 < K; k0 += tile)
-                for (int64_t i = i0; i < i0 + tile && i < M; ++i)
-                    for (int64_t j = j0; j < j0 + tile && j < N; ++j)
-                        for (int64_t k = k0; k < k0 + tile && k < K; ++k)
-                            C[i * ldc + j] += widen_bf16(A[i * lda + k]) * widen_bf16(B[k * ldb + j]);
+        memset(C + i * ldc, 0, sizeof(double) * (size_t)N);
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t i = M - 1; i >= 0; --i) {
+            const double a = widen_bf16(A[i * lda + k]);
+            double *c = C + i * ldc;
+            for (int64_t j = N - 1; j >= 0; --j) c[j] += a * widen_bf16(B[k * ldb + j]);
+        }
+    }
     return 0;
 }

@@ -136,7 +136,10 @@ def test_ablation_costs_of_case_study():
 def test_distinct_candidates_brute_force():
     """The ranked list holds each distinct plan once, sorted, and its head is
     the exhaustive minimum; on the case study it holds exactly the plans a
-    hand count gives (2 Pattern I plans; Pattern II cuts at wave boundaries)."""
+    hand count gives: 2 Pattern I plans; II-M cuts at every multiple of 256
+    (A first: 15) or of 64 (B first: 63) inside 4096 rows; II-N cuts at
+    every multiple of 128 (A first: 7) or of 64 (B first: 15) inside 1024
+    columns -- 102 in all."""
     tab, gold = case_table(10.0, 3.0)
     M, N, K = gold["shape"]
     c = cm.distinct_candidates(tab, M, N, K)
@@ -144,8 +147,91 @@ def test_distinct_candidates_brute_force():
     assert costs == sorted(costs)
     assert costs[0] == pytest.approx(cm.exhaustive_best(tab, M, N, K)[0])
     assert sum(1 for x in c if x[1] == "I") == 2
+    assert sum(1 for x in c if x[1] == "II-M") == 15 + 63
+    assert sum(1 for x in c if x[1] == "II-N") == 7 + 15
+    assert len(c) == 102
     # with one split factor every enumerated plan is already distinct
     assert len(c) == sum(1 for _ in cm.enumerate_plans(tab, M, N, K))
+
+
+@pytest.mark.parametrize("Ta,Tb", [(10.0, 3.0), (10.0, 6.0)])
+def test_case_study_plan_is_a_candidate(Ta, Tb):
+    """The page's own strategy -- kernel A on rows [0, 3072), kernel B on
+    rows [3072, 4096) -- is in the enumerated space at cost Ta + 2 Tb (its
+    first region is 96 tasks of a 108-slot wave, not a whole wave).  Under
+    the page's ceil(f_parallel / |P|) the search may still find a cheaper
+    cut (3328 rows of A: 104 tasks, one wave; the rest on B in one wave)."""
+    tab, gold = case_table(Ta, Tb)
+    M, N, K = gold["shape"]
+    cut = gold["pattern_II"]["cut_m"]
+    found = [regs for pat, regs in cm.enumerate_plans(tab, M, N, K)
+             if pat == "II-M" and regs[0].kernel == "A" and regs[0].m == cut and regs[1].kernel == "B"]
+    assert len(found) == 1
+    assert cm.plan_cost(tab, found[0], K, 1) == pytest.approx(Ta + 2 * Tb, rel=1e-12)
+    cheaper = [regs for pat, regs in cm.enumerate_plans(tab, M, N, K)
+               if pat == "II-M" and regs[0].kernel == "A" and regs[0].m == 3328]
+    assert cm.plan_cost(tab, cheaper[0], K, 1) == pytest.approx(Ta + Tb, rel=1e-12)
+    assert cm.exhaustive_best(tab, M, N, K)[0] <= Ta + Tb + 1e-12
+
+
+def test_best_call_hand_worked():
+    """best_call against costs worked by hand: one slot, no launch cost,
+    g proportional to t.  A 16 x 16 x 16 call is one task of one K step: on
+    the K x N kernel 10 us; on the N x K kernel 2 us after a transpose of
+    1 us + 4 * 16 * 16 bytes at 1000 GB/s = 1.001024 us.  The copy wins at
+    3.001024 us, and loses once its fixed part reaches 20 us.  With batch 3
+    every term triples except the copy's fixed part."""
+    base = """device 1
+launch_us 0
+splitk 1
+kernel kn 16 16 16 1
+kernel nk 16 16 16 1 nk
+g kn 1:10
+g nk 1:2
+"""
+    tab = cm.parse_table(base + "transpose 1.0 1000\n")
+    cost, tr = cm.best_call(tab, 16, 16, 16)
+    assert tr is True and cost == pytest.approx(3.001024, rel=1e-12)
+    # B already N x K: no copy, the N x K kernel alone
+    assert cm.best_call(tab, 16, 16, 16, bt=True) == (pytest.approx(2.0), False)
+    # batch 3: three tasks on one slot -> 30 us direct, 6 + 1 + 3 * 0.001024 via the copy
+    cost3, tr3 = cm.best_call(tab, 16, 16, 16, batch=3)
+    assert tr3 is True and cost3 == pytest.approx(7.003072, rel=1e-12)
+    slow = cm.parse_table(base + "transpose 20.0 1000\n")
+    assert cm.best_call(slow, 16, 16, 16) == (pytest.approx(10.0), False)
+    # two K steps: 20 us direct against 4 + 1.002048 (the copy of a 32 x 16 B)
+    assert cm.best_call(tab, 16, 16, 32)[0] == pytest.approx(5.002048, rel=1e-12)
+
+
+def test_fused_cost_hand_worked():
+    """One launch for both regions, against a schedule worked by hand: 2
+    slots, launch 0.5 us, K = 32 (two K steps of 16), g_a(t) = 3t, g_b(t) =
+    t.  Region 1: 48 x 16 on kernel a, 3 tasks of 6 us; region 2: 32 x 16 on
+    kernel b with 2 splits, 4 tasks of 1 us.  Slots: a1, a2 at 0-6; a3 at
+    6-12 on one slot, b1..b4 at 6-7, 7-8, 8-9, 9-10 on the other: makespan
+    12.  Region 2's reduction: 0.25 + (2*2 + 1) * 4 * 32 * 16 bytes at 1000
+    GB/s = 0.26024.  Total 12.76024 us; regions launched one after the
+    other would cost 0.5 + 2 * 6 and 0.5 + 2 * 1 + 0.26024 = 15.26024."""
+    tab = cm.parse_table("""device 2
+launch_us 0.5
+splitk 1 2
+reduce 0.25 1000
+kernel a 16 16 16 1
+kernel b 16 16 16 1
+g a 1:3
+g b 1:1
+pair a b
+""")
+    r1 = cm.Region(0, 0, 48, 16, "a", 1)
+    r2 = cm.Region(48, 0, 32, 16, "b", 2)
+    assert cm.fused_cost(tab, (r1, r2), 32, 1) == pytest.approx(12.76024, rel=1e-12)
+    assert cm.plan_cost(tab, (r1, r2), 32, 1) == pytest.approx(15.26024, rel=1e-12)
+    # without splits: a1, a2 at 0-6, a3 at 6-12, b1 at 6-8, b2 at 8-10 -> 12.5
+    r2s = cm.Region(48, 0, 32, 16, "b", 1)
+    assert cm.fused_cost(tab, (r1, r2s), 32, 1) == pytest.approx(12.5, rel=1e-12)
+    # batch 2 doubles the tasks: a: 6 tasks (3 waves of 6 us, 0-18); b: 4 tasks
+    # of 2 us after them, 18-22 -> 22.5 us
+    assert cm.fused_cost(tab, (r1, r2s), 32, 2) == pytest.approx(22.5, rel=1e-12)
 
 
 def test_partial_wave_term_closed_form():

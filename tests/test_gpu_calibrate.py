@@ -1,0 +1,54 @@
+"""The offline stage on the GPU: mkp_calibrate measures a short performance
+table (every library kernel at full occupancy for t = 1, 2, 4 K steps; the
+MikPoly page's offline micro-kernel performance model, section 3) and the
+table it writes is usable by both parsers."""
+import os
+
+import pytest
+
+from oracle import cost_model as cm
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SHIPPED = os.path.join(ROOT, "dynamic_shape_gemm_amd", "calib", "gfx950.tbl")
+
+
+def test_calibrate_writes_a_usable_table(gpu, tmp_path):
+    import dynamic_shape_gemm_amd as mkp
+
+    path = str(tmp_path / "short.tbl")
+    print("[case] mkp_calibrate, 3 points per kernel", flush=True)
+    try:
+        assert mkp.mkp_calibrate(path, 3) == 0
+        text = open(path).read()
+        # the library's own parser takes it back
+        assert mkp.mkp_load_calibration(path) == 0
+        assert mkp.mkp_stats()["table"] == path
+    finally:
+        mkp.mkp_load_calibration(None)
+    # and the oracle's independent parser reads the same figures
+    tab = cm.parse_table(text)
+    names = mkp.mkp_kernel_names()
+    assert sorted(tab.kernels) == sorted(names)
+    shipped = cm.parse_table(open(SHIPPED).read())
+    for name in names:
+        k = tab.kernels[name]
+        # resident workgroups per CU from the occupancy query
+        assert 1 <= k.wg_per_cu <= 8, (name, k.wg_per_cu)
+        if name in shipped.kernels:
+            s = shipped.kernels[name]
+            assert (k.uM, k.uN, k.uK, k.bt) == (s.uM, s.uN, s.uK, s.bt), name
+        ts = [t for t, _ in k.pts]
+        assert ts == [1.0, 2.0, 4.0], (name, k.pts)
+        g = [v for _, v in k.pts]
+        assert all(v > 0 for v in g), (name, g)
+        # four K steps per task take longer than one
+        assert g[2] >= g[0], (name, g)
+    assert tab.cus >= 1 and tab.launch_us > 0
+    assert tab.red_gbps > 0 and tab.tr_gbps > 0
+    measured = [l.split() for l in text.splitlines() if l.startswith("measured")]
+    assert len(measured) == 1
+    mfma, hbm = float(measured[0][1]), float(measured[0][2])
+    # sustained rates measured on this GPU, below its spec sheet
+    assert 100.0 < mfma < 2600.0 and 500.0 < hbm < 8100.0, (mfma, hbm)

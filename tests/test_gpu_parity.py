@@ -500,3 +500,73 @@ def test_concurrent_callers_on_separate_streams(mkp):
         for i, (a, b) in enumerate(jobs[t]):
             ref, refabs = oracle.gemm(a, b, with_abs=True)
             assert_close(results[t][i], ref, refabs, a.shape[1], f"thread {t} case {i}")
+
+
+def test_concurrent_callers_on_one_stream(mkp):
+    """Two host threads call the library at once on the SAME stream, every
+    call using the stream's workspace (split-K partials forced, B copied to
+    N x K first), with shapes that grow so the workspace is regrown between
+    calls: each call holds the workspace until its launches are enqueued,
+    so no call's partials or transposed B are overwritten or freed by the
+    other's; every result matches the oracle."""
+    import threading
+
+    import torch
+
+    rng = np.random.default_rng(101)
+    jobs = []
+    for t in range(2):
+        cases = []
+        for i in range(8):
+            # sizes rise call by call (workspace regrowth), ragged and deep enough for 4 splits
+            M = int(rng.integers(40, 120)) * (i + 1)
+            N = int(rng.integers(40, 150)) * (i + 1)
+            K = int(rng.integers(256, 1500))
+            cases.append((rand_bits(rng, (M, K)), rand_bits(rng, (K, N))))
+        jobs.append(cases)
+    results = [[None] * 8 for _ in range(2)]
+    errors = []
+    stream = torch.cuda.Stream()
+    barrier = threading.Barrier(2)
+    print("[case] two threads, one shared stream, split 4, transposed B", flush=True)
+
+    def worker(t):
+        try:
+            with torch.cuda.stream(stream):
+                ins = []
+                for a, b in jobs[t]:
+                    M, K = a.shape
+                    N = b.shape[1]
+                    ta, pa = dev_bf16(a)
+                    tb, pb = dev_bf16(b)
+                    tc = torch.empty((M, N), dtype=torch.float32, device="cuda")
+                    ins.append((ta, tb, tc, pa, pb, M, N, K))
+                torch.cuda.current_stream().synchronize()
+                barrier.wait()
+                for _ in range(3):
+                    for ta, tb, tc, pa, pb, M, N, K in ins:
+                        rc = mkp.mkp_gemm(M, N, K, pa, K, pb, N, tc, N, stream.cuda_stream)
+                        assert rc == 0
+                stream.synchronize()
+                for i, (_, _, tc, *_rest) in enumerate(ins):
+                    results[t][i] = tc.cpu().numpy().astype(np.float64)
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    try:
+        mkp.mkp_set_option("force_splitk", 4)
+        mkp.mkp_set_option("transpose_b", 2)
+        mkp.mkp_cache_clear()   # start from an empty workspace, so it grows under both threads
+        threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+    finally:
+        mkp.mkp_set_option("force_splitk", 0)
+        mkp.mkp_set_option("transpose_b", 1)
+    assert not errors, errors
+    for t in range(2):
+        for i, (a, b) in enumerate(jobs[t]):
+            ref, refabs = oracle.gemm(a, b, with_abs=True)
+            assert_close(results[t][i], ref, refabs, a.shape[1], f"shared stream: thread {t} case {i}")

@@ -6,8 +6,9 @@ mathematics, never against the oracle itself:
 * closed forms: identity, permutation, all-ones, outer product (K = 1), K = 0;
 * linearity in each operand (Korch page, section 3, linear-transformation
   primitive: additivity and homogeneity in every input);
-* the page's loop-tiled form (same item, tiled loop) equals the untiled one
-  bit for bit, since both add each element's terms in ascending k;
+* the product as K ascending rank-1 updates equals the row-by-row loop bit
+  for bit, since both add each element's terms in ascending k (the order in
+  which elements are visited does not change any element's rounding);
 * numpy's float64 matmul (an independent library) within rounding.
 
 Shapes use M != N != K so a transposed operand or swapped index fails.
@@ -132,13 +133,27 @@ def test_linearity_additive_and_homogeneous():
         assert np.array_equal(oracle.gemm(bits(a1 * 2.0 ** p), bits(b)), 2.0 ** p * oracle.gemm(bits(a1), bits(b)))
 
 
-def test_tiled_equals_untiled_bitwise():
+def test_outer_product_form_equals_row_form_bitwise():
+    """The product as K ascending rank-1 updates equals the row-by-row loop
+    bit for bit; summing one element's terms in descending k instead (a
+    plausible slip, planted here on the CPU) changes the rounding, so the
+    pin would see a wrong summation order."""
     rng = np.random.default_rng(12)
     for M, N, K in [(70, 45, 99), (33, 65, 31), (1, 1, 257)]:
         a = bits(rng.uniform(-1, 1, size=(M, K)))
         b = bits(rng.uniform(-1, 1, size=(K, N)))
-        assert np.array_equal(oracle.gemm_tiled(a, b, 32), oracle.gemm(a, b))
-        assert np.array_equal(oracle.gemm_tiled(a, b, 7), oracle.gemm(a, b))
+        assert np.array_equal(oracle.gemm_outer(a, b), oracle.gemm(a, b))
+    # terms 1, 2^-53, 2^-53: in ascending k each small term is a tie that
+    # rounds back to 1 (the sum is 1); in descending k the two small terms
+    # first add exactly to 2^-52, which then survives (1 + 2^-52)
+    a = bits(np.array([[1.0, 2.0 ** -53, 2.0 ** -53]]))
+    b = bits(np.ones((3, 1)))
+    assert oracle.gemm(a, b)[0, 0] == 1.0 and oracle.gemm_outer(a, b)[0, 0] == 1.0
+    A = bf16_bits_to_f32(a).astype(np.float64)
+    desc = 0.0
+    for k in (2, 1, 0):
+        desc += A[0, k]
+    assert desc == 1.0 + 2.0 ** -52
 
 
 def test_numpy_crosscheck():
@@ -180,8 +195,45 @@ def test_planted_mistake_is_caught():
     assert not np.array_equal(wrong, good)
 
 
-def test_error_bound_helper():
+def _f32_recursive_sum(terms):
+    """Left-to-right binary32 summation, every partial sum rounded to
+    binary32 by numpy (an independent model of the GPU's fp32 accumulator)."""
+    acc = np.float32(0.0)
+    for t in terms:
+        acc = np.float32(acc + np.float32(t))
+    return float(acc)
+
+
+def test_error_bound_is_attained_by_rounding_every_add_down():
+    """Tightness: 1 followed by K-1 copies of d = 2^-24 (1 - 2^-8) (a bf16
+    product: 2^-24 times the bf16 value 1 - 2^-8).  Each d is below half a
+    binary32 ulp of 1, so every add rounds back to 1: the binary32 sum is 1
+    and its error is (K-1) d, within a few per cent of gamma_K * sum|x|.
+    A bound that used u = 2^-23, dropped the factor K or its 1/(1 - Ku)
+    would be off by far more than that."""
+    d = 2.0 ** -24 * (1.0 - 2.0 ** -8)
+    for K in (512, 2048, 4096):
+        terms = [1.0] + [d] * (K - 1)
+        exact = 1.0 + (K - 1) * d               # exact in binary64 (few significant bits)
+        err = abs(_f32_recursive_sum(terms) - exact)
+        assert err == pytest.approx((K - 1) * d, rel=1e-12)
+        bound = oracle.error_bound(K, np.array([exact]), slack=1.0)[0]
+        assert err <= bound
+        assert err >= 0.98 * bound, (K, err, bound)
+
+
+def test_error_bound_holds_for_random_bf16_products():
+    """Validity: binary32 recursive sums of random bf16 x bf16 products stay
+    within gamma_K * sum|a b| of the correctly rounded exact sum (math.fsum)."""
+    import math
+    rng = np.random.default_rng(21)
+    for K in (1, 7, 100, 1000, 3000):
+        for _ in range(5):
+            a = bf16_bits_to_f32(bits(rng.uniform(-1, 1, size=K))).astype(np.float64)
+            b = bf16_bits_to_f32(bits(rng.normal(0, 1, size=K))).astype(np.float64)
+            prods = a * b                       # exact: at most 16 significant bits
+            exact = math.fsum(prods)
+            err = abs(_f32_recursive_sum(prods) - exact)
+            bound = oracle.error_bound(K, np.array([float(np.sum(np.abs(prods)))]), slack=1.0)[0]
+            assert err <= bound, (K, err, bound)
     assert oracle.error_bound(0, np.array([1.0]))[0] == 0.0
-    e = oracle.error_bound(1000, np.array([2.0]), slack=1.0)[0]
-    u = 2.0 ** -24
-    assert e == pytest.approx(2.0 * 1000 * u / (1 - 1000 * u))
