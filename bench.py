@@ -1,19 +1,26 @@
 """Throughput of the polymerized dynamic-shape GEMM on one MI355X.
 
-One step = one pass over a workload's whole GEMM sweep through the C-ABI
-(plan-cache lookup, polymerization on a miss, every region's micro-kernel).
-Default workload: the dynamic-sequence-length encoder linears, 64 GEMMs with
-M = 16*L, L ~ U{1..512}, (N,K) cycling over (2304,768), (768,768),
-(3072,768), (768,3072), bf16 U[-1,1] inputs, fp32 output.
+One step = one pass over the whole workload through the C-ABI (plan-cache
+lookup, polymerization on a miss, every region's micro-kernel).  Default
+workload: all five synthetic sweeps back to back in one process --
+the single (105,256,512) GEMM; the encoder linears (64 GEMMs, M = 16 L,
+L ~ U{1..512}); the irregular/square pair (105,1024,12544) and 4096^3; the
+skinny-M decoder projections (128 GEMMs, M ~ U{1..256}); the batched
+per-head scores (32 calls of 48 x (S,S,64)).  `--config C` times one sweep.
 
 Prints ONE JSON line (rank 0, N=1):
   value = total algorithmic FLOPs of the step / step time, in TFLOP/s;
   roofline = the dominant kernel's achieved rate over its launches (HIP
     events on the launch stream, via the library's launch trace) against the
     MI355X peak of its bound;
+  config.per_config = each sweep timed on its own (TFLOP/s, per-shape
+    fractions of their rooflines, its own dominant kernel);
+  config.gates = the 4096^3 GEMM's fraction of the bf16 MFMA peak and the
+    skinny-M sweep's fraction of the HBM peak;
   cpu_baseline = the CPU oracle on a bounded sample of the same workload.
-Inputs are resident in HBM before timing; every GEMM of the sweep has its
-own buffers, so the working set (GBs) is far beyond the 256 MB MALL.
+Inputs are resident in HBM before timing; every GEMM of a sweep has its own
+buffers (the decoder weights rotate over four copies), so the working set
+(GBs) is far beyond the 256 MB MALL.
 """
 from __future__ import annotations
 
@@ -155,6 +162,37 @@ class Workload:
                                      case.K * case.N, tc, case.N, case.M * case.N, stream)
 
 
+class MultiWorkload:
+    """Several sweeps run back to back as one step (the default benchmark:
+    all five configs in order)."""
+
+    def __init__(self, parts):
+        self.parts = parts
+        self.cfg = "all"
+        self.bt = parts[0].bt
+        self.qkv = parts[0].qkv if any(p.cfg == 2 for p in parts) else "merged"
+        self.epilogue = next((p.epilogue for p in parts if p.cfg == 2), "none")
+        self.cases = [c for p in parts for c in p.cases]
+        self.host = [h for p in parts for h in p.host]
+        self.flops = sum(p.flops for p in parts)
+        self.bytes = sum(p.bytes for p in parts)
+        self._owner = {c.tag: p for p in parts for c in p.cases}
+
+    def is_qkv(self, case) -> bool:
+        return self._owner[case.tag].is_qkv(case)
+
+    def calls_per_case(self):
+        return [n for p in self.parts for n in p.calls_per_case()]
+
+    def config_of_case(self):
+        """Config number of every case, in step order."""
+        return [p.cfg for p in self.parts for _ in p.cases]
+
+    def step(self, mkp, stream):
+        for p in self.parts:
+            p.step(mkp, stream)
+
+
 class ConvWorkload:
     """Device-resident operands for the convolution sweep (NHWC inputs, KRSC
     filters, NPQK fp32 outputs), each call through mkp_conv2d."""
@@ -252,7 +290,7 @@ def conv_cpu_baseline(wl, budget_s: float):
     dt = time.perf_counter() - t0
     import os as _os
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": len(_os.sched_getaffinity(0)),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"binary64 convolution oracle (numpy), one image at a time over the calls in order, {n} images, "
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
@@ -336,9 +374,20 @@ def cpu_baseline(wl, budget_s: float):
             break
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"fp64 oracle on the first rows of the sweep's first {len(wl.host)} GEMMs, 64-row blocks, "
-                      f"{sum(r for _, r in rows_done)} rows, {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"fp64 oracle on the first rows of the workload's {len(wl.host)} GEMMs in order (batch entry 0), "
+                      f"64-row blocks, {sum(r for _, r in rows_done)} rows, {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def kernel_source_hash() -> str:
@@ -353,13 +402,16 @@ def measured_ceilings(table_path: str):
         for line in open(table_path):
             tok = line.split("#", 1)[0].split()
             if tok and tok[0] == "measured":
-                return {"mfma_tflops": round(float(tok[1]), 1), "hbm_gbps": round(float(tok[2]), 1)}
+                out = {"mfma_tflops": round(float(tok[1]), 1), "hbm_gbps": round(float(tok[2]), 1)}
+                if len(tok) > 3:
+                    out["hbm_read_gbps"] = round(float(tok[3]), 1)
+                return out
     except OSError:
         pass
     return None
 
 
-def recorded_traffic(kernel: str, config: int):
+def recorded_traffic(kernel: str, config):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     record (profiles/traffic.json), valid only for the kernel source it was
     taken from; None otherwise."""
@@ -391,7 +443,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", default="all", choices=["all", "1", "2", "3", "4", "5"],
+                    help="all five sweeps back to back (default) or one of them")
     ap.add_argument("--workload", choices=["gemm", "conv"], default="gemm",
                     help="the GEMM sweep of --config (default) or the ResNet-50 convolution sweep")
     ap.add_argument("--vs-gemm", action="store_true",
@@ -409,8 +462,8 @@ def main():
                     help="encoder linears with a bias on every GEMM (and GELU on the FFN-up GEMMs), fused into the "
                          "GEMM epilogue or, for comparison, as separate passes")
     ap.add_argument("--fused-reduce", type=int, choices=[0, 1], default=None,
-                    help="split-K partials summed by the last split of each tile (1) or by a second pass (0); "
-                         "default: the library's setting")
+                    help="split-K partials summed by a second pass (0) or by the last split of each tile after "
+                         "agent-scope fences (1); default: the library's setting")
     ap.add_argument("--fuse-regions", type=int, choices=[0, 1], default=0,
                     help="one-launch Pattern II plans over kernel pairs when the model prefers them (1) or never (0)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MiB",
@@ -430,13 +483,18 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    every = args.workload == "gemm" and args.config == "all"
     log(f"[bench] generating {'convolution sweep' if args.workload == 'conv' else f'config {args.config}'} inputs")
     if args.epilogue != "none" and args.qkv != "merged":
         raise SystemExit("--epilogue and --qkv are separate experiments")
     if args.workload == "conv":
         wl = ConvWorkload()
+    elif every:
+        wl = MultiWorkload([Workload(c, copies=4, b_layout=args.b_layout, qkv=args.qkv,
+                                     epilogue=args.epilogue if c == 2 else "none")
+                            for c in (1, 2, 3, 4, 5)])
     else:
-        wl = Workload(args.config, copies=4, b_layout=args.b_layout, qkv=args.qkv, epilogue=args.epilogue)
+        wl = Workload(int(args.config), copies=4, b_layout=args.b_layout, qkv=args.qkv, epilogue=args.epilogue)
     stream = torch.cuda.current_stream().cuda_stream
     mkp.mkp_set_option("fuse_regions", args.fuse_regions)
     if args.fused_reduce is not None:
@@ -459,6 +517,13 @@ def main():
     ms_per_step = ms / args.steps
     value = wl.flops / (ms_per_step * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+    # each sweep of the pass timed on its own (same step count)
+    part_ms = {}
+    if every:
+        for part in wl.parts:
+            part_ms[part.cfg] = timed_steps(part, mkp, args.steps, stream) / args.steps
+            log(f"[bench]   config {part.cfg}: {part_ms[part.cfg]:.3f} ms/step, "
+                f"{part.flops / (part_ms[part.cfg] * 1e-3) / 1e12:.1f} TFLOP/s")
 
     # traced steps: per-launch HIP events on the launch stream
     ntr = 3
@@ -470,19 +535,24 @@ def main():
         recs_all.append(mkp.mkp_trace_dump())
     mkp.mkp_set_option("trace", 0)
     roof, per_kernel = roofline_from_trace([r for recs in recs_all for r in recs])
-    roof["traffic"] = recorded_traffic(roof["kernel"], args.config) if args.workload == "gemm" else None
-    # per-call durations (a call may hold several launches), median of the traced steps
+    traffic_key = "all" if every else (int(args.config) if args.workload == "gemm" else None)
+    roof["traffic"] = recorded_traffic(roof["kernel"], traffic_key) if traffic_key is not None else None
+    # per-call durations (a call may hold several launches), median of the
+    # traced steps; each record also learns which case it belongs to
+    counts = wl.calls_per_case()
     per_step = []
+    case_recs = [[] for _ in wl.cases]
     for recs in recs_all:
         by_call = {}
         for r in recs:
-            by_call[r["call"]] = by_call.get(r["call"], 0.0) + r["us"]
-        calls = [by_call[k] for k in sorted(by_call)]
-        counts = wl.calls_per_case()
+            by_call.setdefault(r["call"], []).append(r)
+        calls = sorted(by_call)
         assert len(calls) == sum(counts), (len(calls), sum(counts))
         per_case, i = [], 0
-        for c in counts:   # a case made of several library calls sums them
-            per_case.append(sum(calls[i:i + c]))
+        for ci, c in enumerate(counts):   # a case made of several library calls sums them
+            rs = [r for k in calls[i:i + c] for r in by_call[k]]
+            per_case.append(sum(r["us"] for r in rs))
+            case_recs[ci] += rs
             i += c
         per_step.append(per_case)
     per_call = [float(np.median(v)) for v in zip(*per_step)]
@@ -502,6 +572,44 @@ def main():
             log(f"  {case.tag:>14} {gm:5d}x{gn:5d}x{gk:5d} b{case.batch:<3d} {us:9.2f} us "
                 f"{case.flops / us / 1e6:8.1f} TF/s  {100 * f:5.1f}% of R  {plan['pattern']:4s} {ks}")
 
+    per_config, gates = None, None
+    if every:
+        cfg_of = wl.config_of_case()
+        per_config = {}
+        for part in wl.parts:
+            idx = [i for i, c in enumerate(cfg_of) if c == part.cfg]
+            sub_recs = [r for i in idx for r in case_recs[i]]
+            sub_roof, _ = roofline_from_trace(sub_recs)
+            sub_roof["traffic"] = recorded_traffic(sub_roof["kernel"], part.cfg)
+            kern_us = sum(per_call[i] for i in idx)
+            per_config[str(part.cfg)] = {
+                "workload": workloads.CONFIG_NAMES[part.cfg],
+                "gemm_calls": len(part.cases),
+                "ms_per_step": round(part_ms[part.cfg], 4),
+                "tflops": round(part.flops / (part_ms[part.cfg] * 1e-3) / 1e12, 2),
+                "flops_per_step": part.flops,
+                "bytes_per_step": part.bytes,
+                # algorithmic bytes over the sweep's kernel time (traced)
+                "hbm_gbps_kernel_time": round(part.bytes / (kern_us * 1e-6) / 1e9, 1),
+                "roofline_frac_median": round(float(np.median([fr[i] for i in idx])), 4),
+                "roofline_frac_min": round(float(np.min([fr[i] for i in idx])), 4),
+                "dominant": sub_roof,
+            }
+        sq = next(i for i, c in enumerate(wl.cases) if c.tag == "c3[square]")
+        dec = [i for i, c in enumerate(cfg_of) if c == 4]
+        gates = {
+            "square_4096_tflops": round(wl.cases[sq].flops / (per_call[sq] * 1e-6) / 1e12, 1),
+            "square_4096_frac_of_bf16_peak": round(wl.cases[sq].flops / (per_call[sq] * 1e-6) / 1e12 /
+                                                   PEAK_BF16_TFLOPS, 4),
+            "decoder_sweep_frac_of_hbm_peak": round(sum(wl.cases[i].bytes for i in dec) /
+                                                    (sum(per_call[i] for i in dec) * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "decoder_dominant_kernel_frac": per_config["4"]["dominant"]["frac"],
+            "decoder_dominant_kernel_bound": per_config["4"]["dominant"]["bound"],
+        }
+
+    workload_name = (workloads.CONV_NAME if args.workload == "conv" else
+                     "all five sweeps: " + "; ".join(workloads.CONFIG_NAMES[c] for c in (1, 2, 3, 4, 5)) if every
+                     else workloads.CONFIG_NAMES[int(args.config)])
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -516,8 +624,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": workloads.CONV_NAME if args.workload == "conv" else workloads.CONFIG_NAMES[args.config],
-            "config_index": None if args.workload == "conv" else args.config,
+            "workload": workload_name,
+            "config_index": None if args.workload == "conv" else ("all" if every else int(args.config)),
             "b_layout": "nk" if args.workload == "conv" else args.b_layout,
             "qkv": wl.qkv,
             "epilogue": wl.epilogue,
@@ -539,6 +647,9 @@ def main():
         },
         "roofline": roof,
     }
+    if per_config is not None:
+        out["config"]["per_config"] = per_config
+        out["config"]["gates"] = gates
     if args.vs_gemm and args.workload == "conv":
         log("[bench] each convolution against the GEMM of its shape")
         out["config"]["conv_vs_gemm"] = conv_vs_gemm(wl, mkp, stream)
@@ -547,7 +658,6 @@ def main():
         out["cpu_baseline"] = (conv_cpu_baseline(wl, args.cpu_seconds) if args.workload == "conv"
                                else cpu_baseline(wl, args.cpu_seconds))
     print(json.dumps(out), flush=True)
-
 
 if __name__ == "__main__":
     main()

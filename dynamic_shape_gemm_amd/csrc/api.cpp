@@ -122,7 +122,9 @@ struct Library {
     std::atomic<int64_t> hits{0}, misses{0}, launches{0};
     std::atomic<int64_t> plan_ns{0};
 
-    std::atomic<bool> fused_reduce{false};        // split-K: fused last-arrival sum (else 2 passes)
+    // split-K: 0 = a second pass sums the partials; 1 = the last split of a
+    // tile sums them after agent-scope fences
+    std::atomic<int> fused_reduce{0};
     std::atomic<bool> pack_unaligned{true};       // stage unaligned re-read operands aligned
     std::atomic<int> transpose_b{1};              // K x N calls as transpose + N x K: 0 no, 1 by cost, 2 always
     std::atomic<bool> trace{false};               // time every launch with events
@@ -184,6 +186,8 @@ int dual_find(int a, int b) {
     return -1;
 }
 
+int conv_for(int lib);
+
 bool bind_table(PerfTable& t, std::string& err) {
     for (auto& k : t.kernels) {
         k.lib_index = kernel_find(k.name.c_str());
@@ -196,13 +200,17 @@ bool bind_table(PerfTable& t, std::string& err) {
             err = "table tile or layout of kernel '" + k.name + "' differs from the library's";
             return false;
         }
+        k.conv_ok = conv_for(k.lib_index) >= 0;
     }
     // library kernels the table does not price (it was written before the
     // library had them) get the analytic estimates
     for (auto& k : analytic_table().kernels) {
         bool listed = false;
         for (auto& e : t.kernels) listed |= e.name == k.name;
-        if (!listed) t.kernels.push_back(k);
+        if (!listed) {
+            t.kernels.push_back(k);
+            t.kernels.back().conv_ok = conv_for(k.lib_index) >= 0;
+        }
     }
     // kernel pairs: each listed pair must have a two-tile kernel; a table
     // without pair lines gets every pair the library has whose kernels it
@@ -345,6 +353,7 @@ std::shared_ptr<const Plan> get_plan(const Key& key) {
         in.generation = L.generation;
     }
     in.opts.bt = key.bt;
+    in.opts.conv = key.conv;
     if (key.conv) in.opts.fuse = false;   // no two-tile form of the convolution kernels
     in.transpose_mode = key.conv ? 0 : key.batch <= 65535 ? L.transpose_b.load(std::memory_order_relaxed) : 0;
     auto plan = std::make_shared<const Plan>(
@@ -698,7 +707,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         }
         // fused reduction when the per-tile counters fit, else a second pass
         const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n * batch;
-        R.fused_red = r.s > 1 && ki.fused_ok && L.fused_reduce.load(std::memory_order_relaxed) &&
+        R.fused_red = r.s > 1 && ki.fused_ok && L.fused_reduce.load(std::memory_order_relaxed) == 1 &&
                       counter0 + ntiles <= counter_cap;
         a.counters = R.fused_red ? (int*)ws + counter0 : nullptr;
         a.Cout = R.Creg;
@@ -1226,7 +1235,9 @@ int mkp_set_option(const char* key, const char* value) {
         L.pack_unaligned.store(std::atoi(v.c_str()) != 0);
         return MKP_OK;
     } else if (k == "fused_reduce") {
-        L.fused_reduce.store(std::atoi(v.c_str()) != 0);
+        const int x = std::atoi(v.c_str());
+        if (x < 0 || x > 1) return fail(MKP_ERR_INVALID_ARG, "fused_reduce must be 0 or 1");
+        L.fused_reduce.store(x);
         return MKP_OK;
     } else if (k == "trace") {
         L.trace.store(std::atoi(v.c_str()) != 0);
@@ -1558,6 +1569,19 @@ int mkp_calibrate(const char* path, int max_points) {
         const double us = time_launches(
             [&] { return launch_copy_probe(base, base + (half & ~int64_t(255)), bytes, cus * 8, nullptr); }, 3, 10, &err);
         t.hbm_gbps = 2.0 * (double)bytes / us / 1e3;
+    }
+    if (err == hipSuccess) {
+        // read-only streaming of up to 1 GB, alternating between the two
+        // halves of the pool (each launch reads data the last one did not)
+        const int64_t half = (int64_t)(pool_ab / 2) & ~int64_t(255);
+        const int64_t bytes = std::min<int64_t>(half, int64_t(1) << 30) & ~int64_t(15);
+        const int blocks = cus * 8;
+        char* base = (char*)dB;
+        int flip = 0;
+        const double us = time_launches(
+            [&] { return launch_read_probe(base + (flip++ & 1) * half, bytes, (uint32_t*)dC, blocks, nullptr); }, 3, 10,
+            &err);
+        t.hbm_read_gbps = (double)bytes / us / 1e3;
     }
     (void)hipDeviceSynchronize();
     (void)hipFree(pAB);

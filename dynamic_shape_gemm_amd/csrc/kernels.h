@@ -161,6 +161,8 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t ld_src, int64_t s_
 // 64*iters 32x32x16 MFMAs) and a streaming copy of `bytes` (multiple of 16).
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t st);
+// Read-only streaming of `bytes` (multiple of 16); `out` holds blocks * 256 words.
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t st);
 
 // Calibration helpers: fill a buffer with pseudo-random bf16 in [-1, 1).
 hipError_t launch_fill_random_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t st);

@@ -282,17 +282,47 @@ __device__ __forceinline__ void wait_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait for the step about to be used while `ahead` later steps (each IPS
+// direct-load instructions per wave, issued in order) stay in flight; the
+// vmcnt immediate is chosen from the compile-time range 0 .. S-2.
+template <class T, int A>
+__device__ __forceinline__ void wait_upto(int ahead) {
+    if constexpr (A <= 0) {
+        wait_and_barrier<0>();
+    } else {
+        if (ahead >= A) {
+            wait_and_barrier<A * T::IPS>();
+            return;
+        }
+        wait_upto<T, A - 1>(ahead);
+    }
+}
+
 template <class T>
 __device__ __forceinline__ void wait_step(int ahead) {
-    // `ahead` later steps may stay in flight (each IPS instructions per wave)
-    if constexpr (T::S >= 4) {
-        if (ahead >= 2) { wait_and_barrier<2 * T::IPS>(); return; }
-    }
-    if constexpr (T::S >= 3) {
-        if (ahead >= 1) { wait_and_barrier<T::IPS>(); return; }
-    }
-    wait_and_barrier<0>();
+    wait_upto<T, T::S - 2>(ahead);
 }
+
+// One direct global->LDS load: 16 bytes per lane, the wave's 64 chunks
+// landing in lane order at `lds` (wave-uniform).  Written out here rather
+// than through the compiler's builtin because the compiler's wait insertion
+// cannot tell the stages of the one LDS array apart: before any fragment
+// read it would wait for every direct load in flight -- including the ones
+// just issued for later steps -- and the loads would never overlap the
+// MFMAs.  The K loop's explicit waits (wait_step: a vmcnt count per step,
+// then a barrier) order these loads with the reads instead.  Loads complete
+// in issue order, so for the compiler's own loads an unseen direct load can
+// only make its waits stricter.  M0 carries the LDS address (one wait state
+// between writing it and the load that reads it).
+// (M0 is reserved to the compiler, which sets it right before each of its
+// own uses; the clobber still tells it this statement changes M0.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, lds_t* lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 struct TileCtx {
     const uint16_t* A;   // tile origin row m0 (row 0 of the tile), column 0; convolution: the input
@@ -392,7 +422,7 @@ struct DmaOffsets {
                 const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
                 const bool in = (unsigned)(ch0[i] + dr) < (unsigned)v.H && (unsigned)(cw0[i] + ds) < (unsigned)v.W;
                 const uint16_t* src = in ? c.A + (int64_t)(cbase[i] + tap) : v.zero;
-                __builtin_amdgcn_global_load_lds((const void*)src, (void*)(real ? stage + g * 1024 : junk), 16, 0, 0);
+                dma16((const void*)src, real ? stage + g * 1024 : junk);
             }
             tc0 += T::BK;   // C is a multiple of uK on this path
             if (tc0 == v.C) {
@@ -407,16 +437,14 @@ struct DmaOffsets {
             for (int i = 0; i < T::A_IPW; ++i) {
                 const int g = i * T::NW + wave;
                 const bool real = (T::A_GROUPS % T::NW == 0) || g < T::A_GROUPS;
-                __builtin_amdgcn_global_load_lds((const void*)(ab + a[i]), (void*)(real ? stage + g * 1024 : junk),
-                                                 16, 0, 0);
+                dma16((const void*)(ab + a[i]), real ? stage + g * 1024 : junk);
             }
         }
 #pragma unroll
         for (int i = 0; i < T::B_IPW; ++i) {
             const int g = i * T::NW + wave;
             const bool real = (T::B_GROUPS % T::NW == 0) || g < T::B_GROUPS;
-            __builtin_amdgcn_global_load_lds((const void*)(bb + b[i]),
-                                             (void*)(real ? stage + T::A_BYTES + g * 1024 : junk), 16, 0, 0);
+            dma16((const void*)(bb + b[i]), real ? stage + T::A_BYTES + g * 1024 : junk);
         }
     }
 };
@@ -500,6 +528,11 @@ __device__ __forceinline__ void reg_step(const TileCtx& c, int k0, lds_t* stage,
             if (p < TOT) *(u32x4 __attribute__((address_space(3)))*)(stage + p * 16) = v[u];
         }
     }
+    // every load of this step has landed on every path (also where no lane
+    // had an LDS write to make), so the compiler carries no pending load into
+    // the K loop's fragment reads (vmcnt 0; the other counters left alone);
+    // the convolution forms skip it (the largest one would spill)
+    if constexpr (!T::CONV) __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // One LDS stage through 32x32x16 MFMAs.  Fragments are double-buffered in
@@ -774,66 +807,6 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
         if (epi) v = epi4(args.epi, base + (int64_t)m * ld + n, vec, c.Nr - n, load_bias4(args.epi, n0 + n, c.Nr - n), v);
         store4(base, ld, vec, m, n, v);
     };
-    // visit every (row, first column, 4 values) the lane holds
-    auto for_each4 = [&](auto&& fn) {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
-                if constexpr (T::MF == 32) {
-                    // 32x32 block: lane holds row (lane&31), columns 8q + 4h + (0..3)
-                    const int m = wm * T::WTM + i * 32 + (lane & 31);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int n = wn * T::WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-                        fn(m, n, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                       acc[i][j][4 * q + 3]});
-                    }
-                } else {
-                    fn(wm * T::WTM + i * 16 + s16, wn * T::WTN + j * 16 + g4 * 4, acc[i][j]);
-                }
-            }
-        }
-    };
-    if (T::FUSED && args.splits > 1 && args.counters != nullptr) {
-        // Fused split-K reduction.  Every split stores its partial tile; once
-        // all waves' stores have completed, wave 0 alone publishes them at
-        // agent scope (one L2 write-back per workgroup) and counts the
-        // arrival.  The last split to arrive makes the other splits' partials
-        // visible (one L2/L1 invalidate) and sums them in split order -- the
-        // same order whichever split arrives last.
-        // the arrival flag lives in the stage memory, idle after the K loop
-        // (every wave is past its last stage read once the barrier below is passed)
-        int __attribute__((address_space(3)))* s_last_p = (int __attribute__((address_space(3)))*)smem;
-        float* Wt = args.C + (int64_t)b * args.sC + (int64_t)m0 * args.ldc + n0;   // split 0's tile
-        for_each4([&](int m, int n, f32x4 v) { store4(C, args.ldc, vecC, m, n, v); });
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
-        __syncthreads();
-        int* cnt = args.counters + (int64_t)b * args.tiles_m * args.tiles_n + tm * args.tiles_n + tn;
-        if (wave == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            int last = 0;
-            if (lane == 0)
-                last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.splits - 1;
-            last = __builtin_amdgcn_readfirstlane(last);
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (lane == 0) *s_last_p = last;
-        }
-        __syncthreads();
-        if (!*s_last_p) return;
-        float* Co = args.Cout + (int64_t)b * args.sCout + (int64_t)m0 * args.ldcout + n0;
-        const bool vecCo = args.flags & KF_VEC_COUT;
-        for_each4([&](int m, int n, f32x4 own) {
-            if (m >= c.Mr || n >= c.Nr) return;
-            const float* w = Wt + (int64_t)m * args.ldc + n;   // workspace rows: 16-byte aligned
-            f32x4 sum = split == 0 ? own : *(const f32x4*)w;
-            for (int z = 1; z < args.splits; ++z)
-                sum += z == split ? own : *(const f32x4*)(w + (int64_t)z * args.sCsplit);
-            emit4(Co, args.ldcout, vecCo, m, n, sum);
-        });
-        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
     // Plain epilogue: the tile goes through LDS one fragment row at a time
     // so that every store instruction writes contiguous row segments.
     const bool epi_here = epi && args.splits == 1;
@@ -992,6 +965,61 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next row overwrites
+    }
+    if (T::FUSED && args.splits > 1 && args.counters != nullptr) {
+        // Fused split-K reduction.  Every split has stored its partial tile
+        // (the rows above, into the workspace); once all waves' stores have
+        // completed, wave 0 publishes them at agent scope (the splits may
+        // sit on different XCDs, whose L2s are not coherent: one L2
+        // write-back) and counts the arrival.  The last split to arrive
+        // makes the others' partials visible (an L2/L1 invalidate) and sums
+        // all of them in split order -- the same order whichever split
+        // arrives last -- reading whole rows (16 bytes per lane, consecutive
+        // lanes along a row), then writes C through the epilogue.
+        // the arrival flag lives in the stage memory, idle after the
+        // epilogue (every wave is past its staging once the barrier is passed)
+        int __attribute__((address_space(3)))* s_last_p = (int __attribute__((address_space(3)))*)smem;
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
+        __syncthreads();
+        int* cnt = args.counters + (int64_t)b * args.tiles_m * args.tiles_n + tm * args.tiles_n + tn;
+        if (wave == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            int last = 0;
+            if (lane == 0)
+                last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.splits - 1;
+            last = __builtin_amdgcn_readfirstlane(last);
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (lane == 0) *s_last_p = last;
+        }
+        __syncthreads();
+        if (!*s_last_p) return;
+        const float* Wt = args.C + (int64_t)b * args.sC + (int64_t)m0 * args.ldc + n0;   // split 0's tile
+        float* Co = args.Cout + (int64_t)b * args.sCout + (int64_t)m0 * args.ldcout + n0;
+        const bool vecCo = args.flags & KF_VEC_COUT;
+        const int rows = min(c.Mr, T::BM);
+        constexpr int CH = T::BN / 4;   // 16-byte chunks per tile row
+#pragma unroll 1
+        for (int id = tid; id < rows * CH; id += T::NT) {
+            const int m = id / CH, n = (id % CH) * 4;
+            if (n >= c.Nr) continue;
+            const int64_t e = (int64_t)m * args.ldc + n;   // workspace rows: 16-byte aligned
+            // partials in split order, eight loads issued before their adds
+            // (one load per add would wait out a round trip per split)
+            f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int z0 = 0; z0 < args.splits; z0 += 8) {
+                f32x4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (z0 + u < args.splits) {
+                        v[u] = *(const f32x4*)(Wt + (int64_t)(z0 + u) * args.sCsplit + e);
+                    }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (z0 + u < args.splits) sum = (z0 + u == 0) ? v[u] : sum + v[u];
+            }
+            emit4(Co, args.ldcout, vecCo, m, n, sum);
+        }
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1245,6 +1273,26 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* __restrict
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = src[i];
 }
 
+// Read-only streaming probe: every lane reads 16-byte chunks, eight in
+// flight, grid-stride over n chunks; one word per lane keeps the loads.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ src, int64_t n, uint32_t* out) {
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 7 * stride < n; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < n; i += stride) {
+        const u32x4 v = src[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 __global__ __launch_bounds__(256) void fill_random_bf16_kernel(uint16_t* p, int64_t n, uint32_t seed) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         uint32_t x = (uint32_t)i * 0x9E3779B1u ^ seed;
@@ -1282,6 +1330,10 @@ using T_32x64 = Tile<32, 64, 64, 2, 2, 4>;
 // loads in flight instead of two workgroups with one each -- faster where K
 // is deep or the tiles are few, slower on many shallow tiles
 using T_128x128x4 = Tile<128, 128, 64, 2, 2, 4>;
+// 256 x 256 on four waves of 128 x 128 accumulators (all 256 AGPRs), one
+// wave per SIMD: each fragment read from LDS feeds four MFMAs instead of
+// two, halving the LDS bytes per MFMA of the eight-wave form.
+using T_256x256w4 = Tile<256, 256, 64, 2, 2, 2>;
 // the same tiles for B given as N x K
 using U_256x256 = Tile<256, 256, 64, 4, 2, 2, false, true>;
 using U_256x128 = Tile<256, 128, 64, 4, 2, 2, true, true>;
@@ -1295,6 +1347,7 @@ using U_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true>;
 using U_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true>;
 using U_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true>;
 using U_128x128x4 = Tile<128, 128, 64, 2, 2, 4, false, true>;
+using U_256x256w4 = Tile<256, 256, 64, 2, 2, 2, false, true>;
 
 #if MKP_PART == 0 || MKP_PART == 1
 #define MKP_KERNEL(NAME, T)                                                                               \
@@ -1316,6 +1369,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m16n256k64", T_16x256),
     MKP_KERNEL("m32n64k64", T_32x64),
     MKP_KERNEL("m128n128k64x4", T_128x128x4),
+    MKP_KERNEL("m256n256k64w4", T_256x256w4),
     MKP_KERNEL("m256n256k64_nk", U_256x256),
     MKP_KERNEL("m256n128k64_nk", U_256x128),
     MKP_KERNEL("m128n256k64_nk", U_128x256),
@@ -1328,6 +1382,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m16n256k64_nk", U_16x256),
     MKP_KERNEL("m32n64k64_nk", U_32x64),
     MKP_KERNEL("m128n128k64x4_nk", U_128x128x4),
+    MKP_KERNEL("m256n256k64w4_nk", U_256x256w4),
 };
 
 #endif  // single-tile registry
@@ -1345,6 +1400,7 @@ using V_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true, true>;
 using V_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true, true>;
 using V_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true, true>;
 using V_128x128x4 = Tile<128, 128, 64, 2, 2, 4, false, true, true>;
+using V_256x256w4 = Tile<256, 256, 64, 2, 2, 2, false, true, true>;
 
 #if MKP_PART == 0 || MKP_PART == 4
 #define MKP_CONV(TWIN, T) \
@@ -1356,6 +1412,7 @@ const ConvInfo g_conv[] = {
     MKP_CONV("m64n64k64_nk", V_64x64),     MKP_CONV("m32n128k64_nk", V_32x128),
     MKP_CONV("m16n128k64_nk", V_16x128),   MKP_CONV("m16n256k64_nk", V_16x256),
     MKP_CONV("m32n64k64_nk", V_32x64),     MKP_CONV("m128n128k64x4_nk", V_128x128x4),
+    MKP_CONV("m256n256k64w4_nk", V_256x256w4),
 };
 #endif
 
@@ -1488,6 +1545,11 @@ hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st) 
 
 hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t st) {
     hipLaunchKernelGGL(copy_probe_kernel, dim3(blocks), dim3(256), 0, st, (const u32x4*)src, (u32x4*)dst, bytes / 16);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t st) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, st, (const u32x4*)src, bytes / 16, out);
     return hipGetLastError();
 }
 

@@ -51,8 +51,11 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
             }
             if (t.splits.empty()) return fail("empty splitk");
         } else if (key == "measured") {
-            // measured <mfma_tflops> <hbm_gbps>: sustained ceilings, reported only
+            // measured <mfma_tflops> <copy_gbps> [<read_gbps>]: sustained
+            // ceilings, reported only
             if (!(ls >> t.mfma_tflops >> t.hbm_gbps)) return fail("bad measured line");
+            double rd = 0.0;
+            if (ls >> rd) t.hbm_read_gbps = rd;
         } else if (key == "patterns") {
             t.pat_I = t.pat_IIM = t.pat_IIN = false;
             std::string p;
@@ -180,7 +183,11 @@ std::string table_to_text(const PerfTable& t) {
     for (int s : t.splits) o << " " << s;
     o << "\npatterns" << (t.pat_I ? " I" : "") << (t.pat_IIM ? " II-M" : "") << (t.pat_IIN ? " II-N" : "")
       << "\n";
-    if (t.mfma_tflops > 0 || t.hbm_gbps > 0) o << "measured " << t.mfma_tflops << " " << t.hbm_gbps << "\n";
+    if (t.mfma_tflops > 0 || t.hbm_gbps > 0) {
+        o << "measured " << t.mfma_tflops << " " << t.hbm_gbps;
+        if (t.hbm_read_gbps > 0) o << " " << t.hbm_read_gbps;
+        o << "\n";
+    }
     for (auto& k : t.kernels)
         o << "kernel " << k.name << " " << k.uM << " " << k.uN << " " << k.uK << " " << k.wg_per_cu
           << (k.bt ? " nk" : "") << "\n";
@@ -394,7 +401,8 @@ struct Searcher {
     }
 
     bool kernel_allowed(int k) const {
-        return tab.kernels[k].bt == opt.bt && (opt.force_kernel < 0 || opt.force_kernel == k);
+        return tab.kernels[k].bt == opt.bt && (!opt.conv || tab.kernels[k].conv_ok) &&
+               (opt.force_kernel < 0 || opt.force_kernel == k);
     }
 
     double red_cost(int s_eff, int64_t m, int64_t n) const {

@@ -34,6 +34,7 @@ struct TableKernel {
     // it overlaps.
     std::vector<std::pair<double, double>> tail, tailx;
     int lib_index = -1;                              // index in the kernel library, -1 if none
+    bool conv_ok = false;                            // the library has a convolution form of it
 };
 
 struct PerfTable {
@@ -48,7 +49,8 @@ struct PerfTable {
     std::vector<int> splits{1};
     bool pat_I = true, pat_IIM = true, pat_IIN = true;
     double mfma_tflops = 0.0;     // measured sustained bf16 MFMA rate (0: unknown)
-    double hbm_gbps = 0.0;        // measured streaming-copy bandwidth (0: unknown)
+    double hbm_gbps = 0.0;        // measured streaming-copy bandwidth, read + write (0: unknown)
+    double hbm_read_gbps = 0.0;   // measured read-only streaming bandwidth (0: unknown)
     std::vector<TableKernel> kernels;
     // Kernel pairs (indices into kernels) compiled into one launch: a Pattern
     // II plan over such a pair may run both regions in one launch.  Both
@@ -99,6 +101,7 @@ struct SearchOptions {
     int plan_rank = 0;       // >0: return the rank-th cheapest candidate of the whole space
     bool bt = false;         // B is N x K: only kernels of that layout take part
     bool fuse = false;       // consider one-launch Pattern II plans over kernel pairs
+    bool conv = false;       // implicit-GEMM convolution: only kernels with a convolution form
 };
 
 // Parse the text form of a table.  Returns false and sets err on bad input.

@@ -31,7 +31,7 @@ def test_kernel_library_listing(mkp):
     names = mkp.mkp_kernel_names()
     assert len(names) == len(set(names)) >= 8
     for n in names:
-        m = re.fullmatch(r"m(\d+)n(\d+)k(\d+)(x\d+)?(_nk)?", n)
+        m = re.fullmatch(r"m(\d+)n(\d+)k(\d+)(x\d+|w\d+)?(_nk)?", n)
         assert m, n
     # every tile exists for both B layouts
     kn = sorted(n for n in names if not n.endswith("_nk"))

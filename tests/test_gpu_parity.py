@@ -111,14 +111,15 @@ def test_splitk(mkp, s, fused):
         mkp.mkp_set_option("fused_reduce", 0)
 
 
-def test_splitk_repeated_calls_reuse_counters(mkp):
+@pytest.mark.parametrize("fused", [1])
+def test_splitk_repeated_calls_reuse_counters(mkp, fused):
     """Back-to-back fused split-K calls on one stream (counters must return
     to zero after every launch) and batched split-K."""
     import torch
     rng = np.random.default_rng(321)
     try:
         mkp.mkp_set_option("force_splitk", 8)
-        mkp.mkp_set_option("fused_reduce", 1)
+        mkp.mkp_set_option("fused_reduce", fused)
         for it in range(3):
             run_case(mkp, rand_bits(rng, (70, 3000)), rand_bits(rng, (3000, 500)),
                      what=f"repeat {it}")

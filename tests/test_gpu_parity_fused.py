@@ -4,6 +4,8 @@ the slots the first region's last wave leaves free (the merged-wave view of
 the MikPoly page's case study).  Results are compared element by element with
 the CPU oracle, NaN guard bands around C.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -93,37 +95,66 @@ def _walk_fused(mkp, shapes, bt, limit, want):
     return found
 
 
+SHIPPED = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "dynamic_shape_gemm_amd", "calib",
+                       "gfx950.tbl")
+
+
+def _pair_table(a, b, path):
+    """The shipped table with kernels a and b made 100x cheaper and the pair
+    (a, b) its only one-launch pair: the ranked candidate lists then start
+    with plans on a and b, so one-launch plans over the pair come early."""
+    out = []
+    for line in open(SHIPPED).read().splitlines():
+        tok = line.split("#", 1)[0].split()
+        if tok and tok[0] == "pair":
+            continue
+        if tok and tok[0] == "g" and tok[1] in (a, b):
+            pts = " ".join(f"{x.split(':')[0]}:{float(x.split(':')[1]) * 0.01:.6f}" for x in tok[2:])
+            line = f"g {tok[1]} {pts}"
+        out.append(line)
+    out.append(f"pair {a} {b}")
+    open(path, "w").write("\n".join(out) + "\n")
+
+
 @pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
-def test_ranked_one_launch_plans(mkp, bt):
-    """Walk ranked candidate lists and run the first one-launch candidate of
-    every kernel pair, with split-K off and on in either region, under both
-    split-K reductions (the last-arriving split, with each region's own
-    counters, and the second pass)."""
+def test_ranked_one_launch_plans(mkp, bt, tmp_path):
+    """Run one-launch plans of every kernel pair of the layout, with split-K
+    off and on in either region, under both split-K reductions (the
+    last-arriving split, with each region's own counters, and the second
+    pass): for each pair, a table that makes the pair's kernels the cheap
+    ones, and the first one-launch candidates of its ranked lists."""
+    from oracle import cost_model as cm
+
     rng = np.random.default_rng(10 + bt)
+    pairs = [(x, y) for x, y in cm.parse_table(open(SHIPPED).read()).pairs if x.endswith("_nk") == bt]
+    assert len(pairs) == 8, pairs   # every pair of the layout
+    key = lambda p: (p["regions"][0]["s"] > 1, p["regions"][1]["s"] > 1)
+    both = 0
     try:
         mkp.mkp_set_option("transpose_b", 0)
-        key = lambda p: (p["regions"][0]["kernel"], p["regions"][1]["kernel"], p["regions"][0]["s"] > 1,
-                         p["regions"][1]["s"] > 1)
-        found = _walk_fused(mkp, [(1500, 1600, 256)], bt, 1300, key)
-        big = lambda p: key(p) if p["regions"][0]["kernel"].startswith("m256n256") else None
-        found.update(_walk_fused(mkp, [(4500, 4200, 128)], bt, 140, big))
-        pairs = {k[:2] for k in found}
-        print(f"[case] one-launch keys {len(found)} pairs {sorted(pairs)}", flush=True)
-        assert len(pairs) == 8, pairs   # every pair of the layout
-        assert any(k[2] and k[3] for k in found)
-        operands = {}
-        for k, ((M, N, K), r) in sorted(found.items(), key=lambda x: x[1]):
-            if (M, N, K) not in operands:
-                operands[(M, N, K)] = (rand_bits(rng, (M, K)), rand_bits(rng, (N, K) if bt else (K, N)))
-            a, b = operands[(M, N, K)]
-            mkp.mkp_set_option("plan_rank", r)
-            for fused_reduce in (1, 0):
-                mkp.mkp_set_option("fused_reduce", fused_reduce)
-                run(mkp, a, b, bt, f"rank {r} {k} fused_reduce={fused_reduce}")
+        for a, b in pairs:
+            path = str(tmp_path / f"{a}_{b}.tbl")
+            _pair_table(a, b, path)
+            mkp.mkp_load_calibration(path)
+            want = lambda p: key(p) if (p["regions"][0]["kernel"], p["regions"][1]["kernel"]) == (a, b) else None
+            found = _walk_fused(mkp, [(1500, 1600, 256), (700, 900, 6144)], bt, 150, want)
+            print(f"[case] pair {a} + {b}: one-launch candidates {sorted(found.items())}", flush=True)
+            assert found, (a, b)
+            both += sum(1 for k in found if k[0] and k[1])
+            for k, ((M, N, K), r) in sorted(found.items(), key=lambda x: x[1]):
+                a_bits = rand_bits(rng, (M, K))
+                b_bits = rand_bits(rng, (N, K) if bt else (K, N))
+                mkp.mkp_set_option("plan_rank", r)
+                for fused_reduce in (1, 0):
+                    mkp.mkp_set_option("fused_reduce", fused_reduce)
+                    run(mkp, a_bits, b_bits, bt, f"pair {a}+{b} rank {r} splits {k} fused_reduce={fused_reduce}")
+                mkp.mkp_set_option("plan_rank", 0)
+        assert both > 0
     finally:
         mkp.mkp_set_option("plan_rank", 0)
         mkp.mkp_set_option("fused_reduce", 1)
         mkp.mkp_set_option("transpose_b", 1)
+        mkp.mkp_load_calibration(None)
 
 
 def test_one_launch_off_matches_oracle(mkp):
