@@ -61,6 +61,10 @@ _lib.mkp_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.mkp_gemm.restype = _int
 _lib.mkp_gemm_batched.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
 _lib.mkp_gemm_batched.restype = _int
+_lib.mkp_gemm_batched_noalloc.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
+_lib.mkp_gemm_batched_noalloc.restype = _int
+_lib.mkp_noalloc_scratch_bytes.argtypes = []
+_lib.mkp_noalloc_scratch_bytes.restype = ctypes.c_size_t
 _lib.mkp_gemm_bt.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.mkp_gemm_bt.restype = _int
 _lib.mkp_gemm_batched_bt.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p]
@@ -112,7 +116,7 @@ _f_gemm_bt = _fast.gemm_bt if _fast else _lib.mkp_gemm_bt
 _f_gemm_batched = _fast.gemm_batched if _fast else _lib.mkp_gemm_batched
 _f_gemm_batched_bt = _fast.gemm_batched_bt if _fast else _lib.mkp_gemm_batched_bt
 
-EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_ex", "mkp_conv2d", "mkp_gemm_grouped",
+EXPORTED = ["mkp_gemm", "mkp_gemm_batched", "mkp_gemm_batched_noalloc", "mkp_noalloc_scratch_bytes", "mkp_gemm_bt", "mkp_gemm_batched_bt", "mkp_gemm_ex", "mkp_conv2d", "mkp_gemm_grouped",
             "mkp_gemm_grouped_bt", "mkp_plan_describe", "mkp_plan_describe_grouped", "mkp_plan_with_table",
             "mkp_load_calibration",
             "mkp_calibrate", "mkp_set_option", "mkp_kernel_count", "mkp_kernel_name", "mkp_cache_clear",
@@ -156,6 +160,17 @@ def mkp_gemm(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 def mkp_gemm_batched(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream=None) -> int:
     return _check(_f_gemm_batched(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB, _addr(C),
                                   ldc, strideC, _stream(stream)))
+
+
+def mkp_gemm_batched_noalloc(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream=None) -> int:
+    """mkp_gemm_batched without any device allocation: its scratch is the
+    library's fixed per-GPU array (calls that overlap on one GPU race)."""
+    return _check(_lib.mkp_gemm_batched_noalloc(batch, M, N, K, _addr(A), lda, strideA, _addr(B), ldb, strideB,
+                                                _addr(C), ldc, strideC, _stream(stream)))
+
+
+def mkp_noalloc_scratch_bytes() -> int:
+    return int(_lib.mkp_noalloc_scratch_bytes())
 
 
 def mkp_gemm_raw(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:

@@ -50,9 +50,12 @@ struct Key {
     int align, device;
     bool bt;   // B given as N x K
     bool conv = false;   // implicit-GEMM convolution: single-tile plans, B as N x K, no transpose
+    // > 0: at most this many K splits and no staging copies (a plan made to
+    // fit the allocation-free entry point's fixed scratch)
+    int cap = 0;
     bool operator==(const Key& o) const {
         return batch == o.batch && M == o.M && N == o.N && K == o.K && align == o.align && device == o.device &&
-               bt == o.bt && conv == o.conv;
+               bt == o.bt && conv == o.conv && cap == o.cap;
     }
 };
 struct KeyHash {
@@ -70,6 +73,7 @@ struct KeyHash {
         mix((uint64_t)k.device);
         mix((uint64_t)k.bt);
         mix((uint64_t)k.conv);
+        mix((uint64_t)k.cap);
         return (size_t)h;
     }
 };
@@ -356,6 +360,11 @@ std::shared_ptr<const Plan> get_plan(const Key& key) {
     in.opts.conv = key.conv;
     if (key.conv) in.opts.fuse = false;   // no two-tile form of the convolution kernels
     in.transpose_mode = key.conv ? 0 : key.batch <= 65535 ? L.transpose_b.load(std::memory_order_relaxed) : 0;
+    if (key.cap > 0) {
+        in.opts.splitk_max = std::min(in.opts.splitk_max, key.cap);
+        in.opts.force_splitk = 0;
+        in.transpose_mode = 0;
+    }
     auto plan = std::make_shared<const Plan>(
         plan_call(*in.table, key.batch, key.M, key.N, key.K, in.opts, in.transpose_mode));
     L.misses.fetch_add(1, std::memory_order_relaxed);
@@ -495,9 +504,12 @@ int conv_for(int lib) {
 // With `epi` (non-null) every final value goes through the fused epilogue.
 // With `conv` (non-null) A is the NHWC input of an implicit-GEMM
 // convolution (bt must be set: B is the KRSC filter bank).
+// With `noalloc` the call's scratch is the library's fixed device array
+// (kStaticScratchBytes): no allocation, and a plan whose scratch would not
+// fit is replaced by one with fewer K splits and no staging copies.
 int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int64_t lda, int64_t sA,
              const void* Bv, int64_t ldb, int64_t sB, float* C, int64_t ldc, int64_t sC, void* stream_v,
-             bool bt = false, const KEpi* epi = nullptr, const KConv* conv = nullptr) {
+             bool bt = false, const KEpi* epi = nullptr, const KConv* conv = nullptr, bool noalloc = false) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return fail(MKP_ERR_INVALID_ARG, "negative dimension");
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return fail(MKP_ERR_INVALID_ARG, "dimension exceeds 2^31-1");
     if (batch == 0 || M == 0 || N == 0) return MKP_OK;
@@ -567,26 +579,8 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     // stream sharing it: [split-K counters][split-K partials][A copy][B copy].
     // The two regions of a one-launch plan run together: each gets its own
     // partial area and its own range of counters.
-    const bool one_launch = !conv && plan->fused && plan->regions.size() == 2;
-    auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
-    size_t part_bytes = 0;
-    size_t part_off[2] = {0, 0};
-    for (size_t i = 0; i < plan->regions.size() && i < 2; ++i) {
-        const Region& r = plan->regions[i];
-        if (r.s <= 1) continue;
-        const int64_t ldw = (r.n + 3) & ~int64_t(3);
-        const size_t bytes = (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float);
-        if (one_launch && !conv) {
-            part_off[i] = i == 0 ? 0 : round256(part_bytes);
-            part_bytes = part_off[i] + bytes;
-        } else {
-            part_bytes = std::max(part_bytes, bytes);
-        }
-    }
-    const bool pack_on = L.pack_unaligned.load(std::memory_order_relaxed);
     // A K x N B the plan runs on N x K kernels is first transposed into the
     // workspace (rows of K padded to 8 elements, aligned)
-    const bool tr = plan->transpose_b && !bt;
     const int64_t ldt = (K + 7) & ~int64_t(7);
     // B rows: N long for a K x N B, K long for an N x K one
     const int64_t b_rows = bt ? N : K, b_cols = bt ? K : N;
@@ -596,16 +590,68 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
     // launch: measured, batched 505 x 505 x 64 calls run 7 % faster without
     // the copy and 8 x (777 x 777 x 777) 26 % faster with it)
     constexpr int64_t kPackMinK = 512;
-    const bool packA = !conv && pack_on && !vA && N > 192 && K >= kPackMinK && ldap < (int64_t(1) << 23);
-    const bool packB = !tr && pack_on && !vB && M > 192 && K >= kPackMinK && ldbp < (int64_t(1) << (bt ? 23 : 25));
-    const size_t offA = kCounterBytes + round256(part_bytes);
-    const size_t bytesA = packA ? (size_t)batch * M * ldap * 2 : 0;
-    const size_t offB = offA + round256(bytesA);
-    const size_t bytesB = tr ? (size_t)batch * N * ldt * 2 : packB ? (size_t)batch * b_rows * ldbp * 2 : 0;
-    const size_t ws_bytes = (part_bytes || packA || packB || tr) ? offB + bytesB : 0;
+    auto round256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+    struct Layout {
+        bool one_launch = false, tr = false, packA = false, packB = false;
+        size_t part_bytes = 0, part_off[2] = {0, 0};
+        size_t offA = 0, offB = 0, ws_bytes = 0;
+    };
+    auto layout_of = [&](const Plan& p, bool copies_ok) {
+        Layout w;
+        w.one_launch = !conv && p.fused && p.regions.size() == 2;
+        for (size_t i = 0; i < p.regions.size() && i < 2; ++i) {
+            const Region& r = p.regions[i];
+            if (r.s <= 1) continue;
+            const int64_t ldw = (r.n + 3) & ~int64_t(3);
+            const size_t bytes = (size_t)r.s * (size_t)batch * (size_t)r.m * (size_t)ldw * sizeof(float);
+            if (w.one_launch) {
+                w.part_off[i] = i == 0 ? 0 : round256(w.part_bytes);
+                w.part_bytes = w.part_off[i] + bytes;
+            } else {
+                w.part_bytes = std::max(w.part_bytes, bytes);
+            }
+        }
+        const bool pack_on = copies_ok && L.pack_unaligned.load(std::memory_order_relaxed);
+        w.tr = p.transpose_b && !bt;
+        w.packA = !conv && pack_on && !vA && N > 192 && K >= kPackMinK && ldap < (int64_t(1) << 23);
+        w.packB = !w.tr && pack_on && !vB && M > 192 && K >= kPackMinK && ldbp < (int64_t(1) << (bt ? 23 : 25));
+        w.offA = kCounterBytes + round256(w.part_bytes);
+        const size_t bytesA = w.packA ? (size_t)batch * M * ldap * 2 : 0;
+        w.offB = w.offA + round256(bytesA);
+        const size_t bytesB = w.tr ? (size_t)batch * N * ldt * 2 : w.packB ? (size_t)batch * b_rows * ldbp * 2 : 0;
+        w.ws_bytes = (w.part_bytes || w.packA || w.packB || w.tr) ? w.offB + bytesB : 0;
+        return w;
+    };
+    Layout lay = layout_of(*plan, true);
+    if (noalloc && lay.ws_bytes > kStaticScratchBytes) {
+        // fewer K splits and no copies, until the scratch fits
+        int most = 1;
+        for (const Region& r : plan->regions) most = std::max(most, r.s);
+        for (int cap = std::max(1, most / 2);; cap = std::max(1, cap / 2)) {
+            Key k2 = key;
+            k2.cap = cap;
+            plan = get_plan(k2);
+            if (plan->regions.empty()) return fail(MKP_ERR_UNSUPPORTED, "no plan for this shape");
+            lay = layout_of(*plan, false);
+            if (lay.ws_bytes <= kStaticScratchBytes || cap == 1) break;
+        }
+        if (lay.ws_bytes > kStaticScratchBytes)
+            return fail(MKP_ERR_UNSUPPORTED, "the call needs " + std::to_string(lay.ws_bytes) +
+                                                 " bytes of scratch, more than the " +
+                                                 std::to_string(kStaticScratchBytes) +
+                                                 " bytes of the allocation-free entry point");
+    }
+    const bool one_launch = lay.one_launch, tr = lay.tr, packA = lay.packA, packB = lay.packB;
+    const size_t part_off[2] = {lay.part_off[0], lay.part_off[1]};
+    const size_t offA = lay.offA, offB = lay.offB, ws_bytes = lay.ws_bytes;
     void* ws = nullptr;
     WsLease lease;   // held until this call's last launch is enqueued
-    if (ws_bytes) {
+    if (ws_bytes && noalloc) {
+        // the fixed array of this device (calls that overlap on one GPU share it)
+        he = static_scratch(dev, &ws);
+        if (he != hipSuccess)
+            return fail(MKP_ERR_HIP, std::string("scratch address: ") + hipGetErrorString(he));
+    } else if (ws_bytes) {
         int rc = lease.acquire(dev, st, ws_bytes, &ws);
         if (rc != MKP_OK) return rc;
     }
@@ -707,7 +753,9 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         }
         // fused reduction when the per-tile counters fit, else a second pass
         const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n * batch;
-        R.fused_red = r.s > 1 && ki.fused_ok && L.fused_reduce.load(std::memory_order_relaxed) == 1 &&
+        // (the allocation-free call sums splits in a second pass: its
+        // scratch then holds nothing that must start at zero)
+        R.fused_red = r.s > 1 && ki.fused_ok && !noalloc && L.fused_reduce.load(std::memory_order_relaxed) == 1 &&
                       counter0 + ntiles <= counter_cap;
         a.counters = R.fused_red ? (int*)ws + counter0 : nullptr;
         a.Cout = R.Creg;
@@ -989,6 +1037,15 @@ int mkp_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const void*
                      void* stream) {
     return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream);
 }
+
+int mkp_gemm_batched_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             int64_t strideA, const void* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc,
+                             int64_t strideC, void* stream) {
+    return run_gemm(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, stream, false, nullptr, nullptr,
+                    true);
+}
+
+size_t mkp_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
 
 int mkp_gemm_bt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                 int64_t ldc, void* stream) {

@@ -109,6 +109,12 @@ struct LaunchEvents {
 };
 LaunchEvents& launch_events();
 
+// The allocation-free entry point's device memory: kStaticScratchBytes at a
+// 256-byte aligned address of device `dev` (which must be current), looked up
+// on the first call for that device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(int dev, void** out);
+
 int kernel_count();
 const KernelInfo& kernel_info(int i);
 int kernel_find(const char* name);

@@ -40,6 +40,8 @@
 #define MKP_PART 0
 #endif
 
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 namespace mkp {
@@ -1485,6 +1487,32 @@ const DualInfo& dual_info(int i) {
 #endif
 
 #if MKP_PART == 0 || MKP_PART == 1
+// Device memory of the allocation-free entry point: a fixed array in the
+// code object (zero at load, held by every GPU the library runs on until the
+// process ends), serving as that call's split-K partials and staging copies.
+// Host code never passes the name itself (on the host it only stands for
+// the symbol): static_scratch() gives each device's own address, looked up
+// once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(int dev, void** out) {
+    static std::mutex mu;
+    static std::map<int, void*> ptrs;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = ptrs.find(dev);
+    if (it != ptrs.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+    ptrs.emplace(dev, p);
+    *out = p;
+    return hipSuccess;
+}
+
 LaunchEvents& launch_events() {
     thread_local LaunchEvents slot;
     return slot;

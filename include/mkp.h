@@ -103,6 +103,30 @@ int mkp_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                      void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as mkp_gemm_batched -- same arguments, layout, result and errors --
+ * that never allocates.  Its split-K partials and staging copies live in a
+ * fixed device array inside the library, mkp_noalloc_scratch_bytes() bytes
+ * (64 MiB) on every GPU the library runs on, held until the process ends.
+ * A plan whose scratch would not fit is replaced by one with fewer K splits
+ * and no staging copies (at the last resort no split at all, which needs
+ * none), so every shape runs; split-K partials are always summed by a
+ * second pass.  The array keeps the last call's contents between calls.
+ * All calls on one GPU share that one array: calls that overlap on one GPU
+ * (concurrent streams, or several host threads) race and may corrupt each
+ * other's results -- issue them on one stream, one after the other.
+ */
+int mkp_gemm_batched_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda, int64_t strideA,
+                             const void *B, int64_t ldb, int64_t strideB,
+                             float *C, int64_t ldc, int64_t strideC,
+                             void *stream);
+
+/* Size in bytes of mkp_gemm_batched_noalloc's per-GPU scratch array. */
+size_t mkp_noalloc_scratch_bytes(void);
+
+/*
  * C[M x N] := A[M x K] . B^T with B given as N x K (row n holds the K values
  * of output column n; ldb >= K), the layout in which a linear layer keeps
  * its weights and attention keeps K.  Otherwise as mkp_gemm: same C, errors
