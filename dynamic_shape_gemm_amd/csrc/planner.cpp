@@ -660,7 +660,7 @@ struct Searcher {
     Plan run() {
         if (opt.plan_rank > 0) return ranked(opt.plan_rank);
         Plan best;
-        best.cost_us = std::numeric_limits<double>::infinity();
+        best.cost_us = prune() && opt.bound < 1e300 ? opt.bound : std::numeric_limits<double>::infinity();
         const int nk = (int)tab.kernels.size();
         if (tab.pat_I) {
             for (int a = 0; a < nk; ++a) {
@@ -675,8 +675,15 @@ struct Searcher {
                 }
             }
         }
-        if (opt.force_kernel >= 0 || !opt.allow_II) return best;
-        for (int dir = 0; dir < 2; ++dir) {
+        if (opt.force_kernel >= 0 || !opt.allow_II) {
+            if (best.regions.empty()) best.cost_us = std::numeric_limits<double>::infinity();
+            return best;
+        }
+        // any Pattern II plan costs at least two launches plus the whole
+        // output at the cheapest rate per element of any kernel
+        const bool II_hopeless =
+            prune() && 2.0 * tab.launch_us + (double)M * (double)N * (double)batch * min_rate >= best.cost_us;
+        for (int dir = 0; dir < 2 && !II_hopeless; ++dir) {
             if (dir == 0 && !tab.pat_IIM) continue;
             if (dir == 1 && !tab.pat_IIN) continue;
             const int64_t ext = dir == 0 ? M : N;
@@ -723,6 +730,7 @@ struct Searcher {
                 best.regions.assign({r1, r2});
                 return true;
             });
+        if (best.regions.empty()) best.cost_us = std::numeric_limits<double>::infinity();
         return best;
     }
 };
@@ -822,6 +830,8 @@ Plan plan_call(const PerfTable& tab, int64_t batch, int64_t M, int64_t N, int64_
     }
     SearchOptions o = opt;
     o.bt = true;
+    // only an N x K plan cheaper than the K x N one after paying for the copy matters
+    if (transpose_mode != 2 && !p.regions.empty()) o.bound = std::min(o.bound, p.cost_us - tc);
     Plan q = polymerize(tab, batch, M, N, K, o);
     if (q.regions.empty() || !(transpose_mode == 2 || q.cost_us + tc < p.cost_us || p.regions.empty())) {
         p.plan_us += q.plan_us;

@@ -102,6 +102,9 @@ struct SearchOptions {
     bool bt = false;         // B is N x K: only kernels of that layout take part
     bool fuse = false;       // consider one-launch Pattern II plans over kernel pairs
     bool conv = false;       // implicit-GEMM convolution: only kernels with a convolution form
+    // only plans strictly cheaper than this are of interest (infinity: any);
+    // when none is, the result has no regions
+    double bound = 1e300;
 };
 
 // Parse the text form of a table.  Returns false and sets err on bad input.
