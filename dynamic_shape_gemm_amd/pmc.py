@@ -2,7 +2,7 @@
 
 HBM traffic per launch (the default mode):
 
-    python -m dynamic_shape_gemm_amd.pmc --config 2 \
+    python -m dynamic_shape_gemm_amd.pmc --config all \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes BYTES --out profiles/traffic.json
 
@@ -35,9 +35,11 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Tile<uM, uN, uK, waves_m, waves_n, stages, preread, N x K B[, convolution]>
-TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), \d+, \d+, (\d+), (?:true|false), (true|false)(?:, (true|false))?>")
+TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (?:true|false), (true|false)(?:, (true|false))?>")
 # tiles the library also has in a deeper-pipelined form, named with "x<stages>"
 DEEP = {(128, 128, 4)}
+# tiles the library also has on fewer, larger waves, named with "w<waves>"
+WIDE = {(256, 256, 4)}
 
 
 def read_counter(d: str, counter: str):
@@ -60,10 +62,12 @@ def lib_name(kernel_name: str):
         return None
     # the N x K flag marks the kernels that take B as N x K; the convolution
     # forms of those count apart
-    bm, bn, stages = int(m.group(1)), int(m.group(2)), int(m.group(4))
+    bm, bn, stages = int(m.group(1)), int(m.group(2)), int(m.group(6))
+    waves = int(m.group(4)) * int(m.group(5))
     name = f"m{bm}n{bn}k{m.group(3)}" + (f"x{stages}" if (bm, bn, stages) in DEEP else "")
-    name += "_nk" if m.group(5) == "true" else ""
-    return name + ("_conv" if m.group(6) == "true" else "")
+    name += f"w{waves}" if (bm, bn, waves) in WIDE else ""
+    name += "_nk" if m.group(7) == "true" else ""
+    return name + ("_conv" if m.group(8) == "true" else "")
 
 
 def copy_scale(d: str, counter: str, nbytes: float) -> float:
@@ -137,7 +141,7 @@ def main():
         print(text)
         return
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", type=int, required=True)
+    ap.add_argument("--config", required=True, help="all (the default benchmark) or a sweep number")
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-fetch", required=True)
@@ -164,7 +168,7 @@ def main():
         }
     src = os.path.join(HERE, "csrc", "kernels.hip")
     rec = {
-        "config": a.config,
+        "config": a.config if a.config == "all" else int(a.config),
         "kernel_source_sha256_16": hashlib.sha256(open(src, "rb").read()).hexdigest()[:16],
         "copy_reference": {"kernel": cname[:80], "bytes": a.copy_bytes, "fetch_kib": round(cf, 1),
                            "write_kib": round(cw, 1), "fetch_scale": round(sf, 4), "write_scale": round(sw, 4)},
