@@ -7,11 +7,47 @@
 #include <cstdio>
 #include <limits>
 #include <sstream>
+#include <numeric>
 #include <unordered_map>
 
 namespace mkp {
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Exact division by a fixed positive divisor through its reciprocal: a 64-bit
+// integer division costs tens of cycles and the search divides a few times
+// per candidate.  For 0 <= x < 2^50 the product x * (1/d) is within 0.25 of
+// x / d, so one correction step makes the quotient exact; larger x divide.
+struct FastDiv {
+    int64_t d = 1;
+    double inv = 1.0;
+    void set(int64_t v) {
+        d = v;
+        inv = 1.0 / (double)v;
+    }
+    int64_t quot(int64_t x, int64_t& rem) const {
+        if (x >= (int64_t(1) << 50)) {
+            rem = x % d;
+            return x / d;
+        }
+        int64_t q = (int64_t)((double)x * inv);
+        int64_t r = x - q * d;
+        if (r < 0) {
+            --q;
+            r += d;
+        } else if (r >= d) {
+            ++q;
+            r -= d;
+        }
+        rem = r;
+        return q;
+    }
+    int64_t ceil(int64_t x) const {
+        int64_t r;
+        const int64_t q = quot(x, r);
+        return q + (r != 0);
+    }
+};
 
 bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
     PerfTable t;
@@ -343,6 +379,9 @@ struct Searcher {
     std::vector<double> min_g;                   // per kernel: cheapest single (possibly partial) wave
     std::vector<double> rate;                    // per kernel: lowest cost per output element
     std::vector<double> tmin_alone, tmin_after;  // per kernel: smallest partial-wave ratio (tail, tailx)
+    std::vector<double> rho;                     // per kernel: smallest partial-wave ratio per filled slot
+    std::vector<double> gmin, sgmin;             // per kernel: smallest g and s * g over its splits
+    std::vector<FastDiv> dm, dn, dslots;         // per kernel: uM, uN and its slots as dividers
     double lb_region = 0.0;                      // lower bound of any region's cost
     double min_rate = 0.0;                       // lowest rate over allowed kernels
 
@@ -362,22 +401,33 @@ struct Searcher {
         rate.assign(nk, std::numeric_limits<double>::infinity());
         tmin_alone.assign(nk, 1.0);
         tmin_after.assign(nk, 1.0);
+        rho.assign(nk, 1.0);
+        gmin.assign(nk, std::numeric_limits<double>::infinity());
+        sgmin.assign(nk, std::numeric_limits<double>::infinity());
+        dm.resize(nk);
+        dn.resize(nk);
+        dslots.resize(nk);
         lb_region = std::numeric_limits<double>::infinity();
         min_rate = std::numeric_limits<double>::infinity();
         for (size_t ki = 0; ki < nk; ++ki) {
+            if (!kernel_allowed((int)ki)) continue;   // never scored
             const TableKernel& kk = tab.kernels[ki];
             const int64_t t3 = ceil_div(K, kk.uK);
+            sc[ki].reserve(req.size());
+            dm[ki].set(kk.uM);
+            dn[ki].set(kk.uN);
+            dslots[ki].set((int64_t)tab.cus * kk.wg_per_cu);
             // a region's wave factor is at least tmin (one possibly partial
             // wave) and at least rho * tasks/slots (piecewise-linear ratios:
             // r(f)/f is smallest at a point or at f = 1)
-            double rho = 1.0;
+            double& rh = rho[ki];
             for (auto& p : kk.tail) {
                 tmin_alone[ki] = std::min(tmin_alone[ki], p.second);
-                rho = std::min(rho, p.second / p.first);
+                rh = std::min(rh, p.second / p.first);
             }
             for (auto& p : kk.tailx) {
                 tmin_after[ki] = std::min(tmin_after[ki], p.second);
-                rho = std::min(rho, p.second / p.first);
+                rh = std::min(rh, p.second / p.first);
             }
             for (int s_req : req) {
                 // a factor above the K-step count is only kept when forced
@@ -389,14 +439,15 @@ struct Searcher {
                 for (auto& c : sc[ki]) dup |= c.s_eff == s_eff;
                 if (dup) continue;
                 sc[ki].push_back({s_eff, (int)per, g_predict(kk, (double)per)});
-                min_g[ki] = std::min(min_g[ki], tmin_alone[ki] * sc[ki].back().g);
+                const double g = sc[ki].back().g;
+                min_g[ki] = std::min(min_g[ki], tmin_alone[ki] * g);
+                gmin[ki] = std::min(gmin[ki], g);
+                sgmin[ki] = std::min(sgmin[ki], (double)s_eff * g);
                 const double slots = (double)tab.cus * kk.wg_per_cu;
-                rate[ki] = std::min(rate[ki], rho * (double)s_eff * sc[ki].back().g / (slots * kk.uM * kk.uN));
+                rate[ki] = std::min(rate[ki], rh * (double)s_eff * g / (slots * kk.uM * kk.uN));
             }
-            if (kernel_allowed((int)ki)) {
-                lb_region = std::min(lb_region, tab.launch_us + min_g[ki]);
-                min_rate = std::min(min_rate, rate[ki]);
-            }
+            lb_region = std::min(lb_region, tab.launch_us + min_g[ki]);
+            min_rate = std::min(min_rate, rate[ki]);
         }
     }
 
@@ -411,13 +462,19 @@ struct Searcher {
                          : 0.0;
     }
 
+    int64_t tiles_of(int k, int64_t m, int64_t n) const { return dm[k].ceil(m) * dn[k].ceil(n); }
+
     double cost(int ki, const SplitChoice& c, int64_t m, int64_t n, Region* r) {
         ++evaluated;
         const TableKernel& k = tab.kernels[ki];
-        const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * c.s_eff * batch;
-        const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
-        const int64_t waves = ceil_div(tasks, slots);
-        const double wf = wave_factor(k, tasks, slots);
+        const int64_t tasks = tiles_of(ki, m, n) * c.s_eff * batch;
+        const int64_t slots = dslots[ki].d;
+        int64_t rem;
+        const int64_t full = dslots[ki].quot(tasks, rem);
+        const int64_t waves = full + (rem != 0);
+        // full waves plus the partial last one (as wave_factor)
+        const double wf = rem ? (double)full + tail_ratio(full ? k.tailx : k.tail, (double)rem / (double)slots)
+                              : (double)full;
         double v = tab.launch_us;
         if (opt.cost_mode == COST_WAVE) v += (double)waves;   // the page's f_wave alone
         else if (opt.cost_mode == COST_PIPE) v += c.g;
@@ -442,18 +499,35 @@ struct Searcher {
     // cut of at least m x n (a larger cut has at least as many full waves,
     // a partial wave costs at least the kernel's smallest tail ratio, and
     // the reduction grows with the area).
-    double lb_from(int a, const SplitChoice& c, int64_t m, int64_t n) const {
-        const TableKernel& k = tab.kernels[a];
-        const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * c.s_eff * batch;
-        const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
-        const int64_t full = tasks / slots;
-        const double part = tasks % slots ? (full ? tmin_after[a] : tmin_alone[a]) : 0.0;
-        return tab.launch_us + ((double)full + part) * c.g + red_cost(c.s_eff, m, n);
+    // With lin, also the bound from the wave factor's linear floor, rho *
+    // tasks/slots, which grows with the cut at least at the kernel's
+    // lowest cost per output element.
+    double lb_from(int a, const SplitChoice& c, int64_t m, int64_t n, double* lin = nullptr) const {
+        const int64_t tasks = tiles_of(a, m, n) * c.s_eff * batch;
+        int64_t rem;
+        const int64_t full = dslots[a].quot(tasks, rem);
+        const double part = rem ? (full ? tmin_after[a] : tmin_alone[a]) : 0.0;
+        const double red = red_cost(c.s_eff, m, n);
+        if (lin) *lin = tab.launch_us + rho[a] * (double)tasks * dslots[a].inv * c.g + red;
+        return tab.launch_us + ((double)full + part) * c.g + red;
     }
 
     // Lower bound of any region 2 of m x n.
     double lb2(int64_t m, int64_t n) const {
         return tab.launch_us + std::max((double)m * (double)n * (double)batch * min_rate, lb_region - tab.launch_us);
+    }
+
+    // Lower bound of an m x n region on kernel k with split c: its wave
+    // factor is at least the smallest partial-wave ratio and at least rho
+    // times tasks/slots.
+    double lb_split(int k, const SplitChoice& c, int64_t tiles, int64_t m, int64_t n) const {
+        const double w = std::max(tmin_alone[k], rho[k] * (double)(tiles * c.s_eff * batch) * dslots[k].inv);
+        return tab.launch_us + w * c.g + red_cost(c.s_eff, m, n);
+    }
+    // ... and over all of k's splits (s >= 1, no reduction term).
+    double lb_kernel(int k, int64_t m, int64_t n) const {
+        const double tiles = (double)(tiles_of(k, m, n) * batch);
+        return tab.launch_us + std::max(tmin_alone[k] * gmin[k], rho[k] * tiles * sgmin[k] * dslots[k].inv);
     }
 
     // Both regions of a Pattern II cut in one launch over a kernel pair:
@@ -534,21 +608,43 @@ struct Searcher {
         return best;
     }
 
+    // The cheapest split of kernel k for an m x n region among those whose
+    // cost is below thr (infinity and r untouched when none is).
+    double best_region_below(int k, int64_t m, int64_t n, double thr, Region* r) {
+        const int64_t tiles = tiles_of(k, m, n);
+        double best = std::numeric_limits<double>::infinity();
+        for (auto& c : sc[k]) {
+            if (lb_split(k, c, tiles, m, n) >= std::min(thr, best)) continue;
+            Region tmp;
+            const double v = cost(k, c, m, n, &tmp);
+            if (v < best && v < thr) {
+                best = v;
+                *r = tmp;
+            }
+        }
+        return best;
+    }
+
     // Best region 2 for one remaining extent: the cheapest kernel and split,
     // and the cheapest on a different kernel (region 2 may not reuse region
-    // 1's kernel).  Kernels are visited in table order, so ties keep the
-    // earliest, as in a plain scan.
+    // 1's kernel), both only among regions cheaper than thr -- a kernel or
+    // split whose lower bound reaches thr is not scored.  Kernels are
+    // visited in table order, so ties keep the earliest, as in a plain scan.
     struct Second {
         double c1 = std::numeric_limits<double>::infinity(), c2 = std::numeric_limits<double>::infinity();
         Region r1, r2;
+        double thr = -1.0;   // exact for every cost below thr
     };
-    Second second_for(int64_t m, int64_t n) {
+    Second second_for(int64_t m, int64_t n, double thr = std::numeric_limits<double>::infinity()) {
         Second out;
+        out.thr = thr;
         const int nk = (int)tab.kernels.size();
         for (int b = 0; b < nk; ++b) {
             if (!kernel_allowed(b)) continue;
+            if (lb_kernel(b, m, n) >= thr) continue;
             Region r;
-            const double v = best_region(b, m, n, &r);
+            const double v = best_region_below(b, m, n, thr, &r);
+            if (!(v < thr)) continue;
             if (v < out.c1) {
                 if (out.r1.kernel >= 0 && out.r1.kernel != b) {
                     out.c2 = out.c1;
@@ -687,35 +783,78 @@ struct Searcher {
             if (dir == 0 && !tab.pat_IIM) continue;
             if (dir == 1 && !tab.pat_IIN) continue;
             const int64_t ext = dir == 0 ? M : N;
-            std::unordered_map<int64_t, Second> seconds;   // remaining extent -> best region 2
+            // remaining extent -> best region 2; every cut is a multiple of
+            // the gcd of the allowed kernels' steps, so cut / gcd indexes it
+            int64_t gstep = 0;
+            for (int a = 0; a < nk; ++a)
+                if (kernel_allowed(a)) gstep = std::gcd(gstep, (int64_t)(dir == 0 ? tab.kernels[a].uM : tab.kernels[a].uN));
+            if (gstep <= 0 || gstep >= ext) continue;
+            std::vector<int32_t> slot((size_t)(ext / gstep) + 1, -1);
+            std::vector<Second> seconds;
+            std::vector<char> dead;
             for (int a = 0; a < nk; ++a) {
                 if (!kernel_allowed(a)) continue;
                 const TableKernel& ka = tab.kernels[a];
                 const int64_t step = dir == 0 ? ka.uM : ka.uN;
-                for (auto& c1s : sc[a]) {
-                    for (int64_t cut = step; cut < ext; cut += step) {
-                        const int64_t e = ext - cut;
-                        const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
-                        const int64_t m2 = dir == 0 ? e : M, n2 = dir == 0 ? N : e;
-                        // no cut from here on can lead to a better plan
-                        if (prune() && lb_from(a, c1s, m1, n1) + lb_region >= best.cost_us) break;
-                        Region r1;
-                        const double c1 = cost(a, c1s, m1, n1, &r1);
-                        if (prune() && c1 + lb2(m2, n2) >= best.cost_us) continue;
-                        auto it = seconds.find(e);
-                        if (it == seconds.end()) it = seconds.emplace(e, second_for(m2, n2)).first;
-                        const Second& sd = it->second;
-                        const bool own = sd.r1.kernel == a;
-                        const double c2 = own ? sd.c2 : sd.c1;
-                        if (!(c1 + c2 < best.cost_us)) continue;
-                        Region r2 = own ? sd.r2 : sd.r1;
-                        best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
-                        best.cost_us = c1 + c2;
-                        r1.m0 = r1.n0 = 0;
-                        r2.m0 = dir == 0 ? cut : 0;
-                        r2.n0 = dir == 0 ? 0 : cut;
-                        best.regions.assign({r1, r2});
+                const std::vector<SplitChoice>& splits = sc[a];
+                dead.assign(splits.size(), 0);
+                size_t live = splits.size();
+                for (int64_t cut = step; cut < ext && live > 0; cut += step) {
+                    const int64_t e = ext - cut;
+                    const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
+                    const int64_t m2 = dir == 0 ? e : M, n2 = dir == 0 ? N : e;
+                    // region 1: the cheapest split at this cut; a split whose
+                    // bound for this and every larger cut reaches the best
+                    // plan is dropped for good
+                    double c1 = std::numeric_limits<double>::infinity();
+                    Region r1;
+                    const double l2 = prune() ? lb2(m2, n2) : 0.0;
+                    for (size_t i = 0; i < splits.size(); ++i) {
+                        if (dead[i]) continue;
+                        if (prune()) {
+                            double lin;
+                            const double lb = lb_from(a, splits[i], m1, n1, &lin);
+                            // lin + lb2 never falls as the cut grows: region
+                            // 1 gains at least min_rate per element it takes
+                            // from region 2
+                            if (lb + lb_region >= best.cost_us || lin + l2 >= best.cost_us) {
+                                dead[i] = 1;
+                                --live;
+                                continue;
+                            }
+                            if (lb + l2 >= best.cost_us) continue;
+                        }
+                        Region r;
+                        const double v = cost(a, splits[i], m1, n1, &r);
+                        if (v < c1) {
+                            c1 = v;
+                            r1 = r;
+                        }
                     }
+                    if (!(c1 < best.cost_us)) continue;
+                    if (prune() && c1 + lb2(m2, n2) >= best.cost_us) continue;
+                    // region 2 only matters below best - c1: score it to that
+                    // bound, once per extent (again if a later cut asks for a
+                    // higher bound)
+                    const double thr = prune() ? best.cost_us - c1 : std::numeric_limits<double>::infinity();
+                    int32_t& si = slot[(size_t)(cut / gstep)];
+                    if (si < 0) {
+                        si = (int32_t)seconds.size();
+                        seconds.push_back(second_for(m2, n2, thr));
+                    } else if (seconds[si].thr < thr) {
+                        seconds[si] = second_for(m2, n2, thr);
+                    }
+                    const Second& sd = seconds[si];
+                    const bool own = sd.r1.kernel == a;
+                    const double c2 = own ? sd.c2 : sd.c1;
+                    if (!(c1 + c2 < best.cost_us)) continue;
+                    Region r2 = own ? sd.r2 : sd.r1;
+                    best.pattern = dir == 0 ? PAT_IIM : PAT_IIN;
+                    best.cost_us = c1 + c2;
+                    r1.m0 = r1.n0 = 0;
+                    r2.m0 = dir == 0 ? cut : 0;
+                    r2.n0 = dir == 0 ? 0 : cut;
+                    best.regions.assign({r1, r2});
                 }
             }
         }

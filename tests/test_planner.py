@@ -127,6 +127,24 @@ def test_library_table_plans_cover_output(mkp):
             assert (r["s"] - 1) * r["steps"] * r["uK"] < K   # no empty split
 
 
+def test_pruned_search_is_exact_on_shipped_table(mkp):
+    """The bounds that cut the search (per-kernel tile-count bounds for the
+    second region, the linear wave floor for the first) never drop the
+    optimum: on the calibrated table, over shapes with many tile-aligned
+    cuts, the pruned search costs the same as the exhaustive one."""
+    path = os.path.join(os.path.dirname(mkp.__file__), "calib", "gfx950.tbl")
+    text = open(path).read()
+    rng = np.random.default_rng(17)
+    for trial in range(40):
+        M, N, K = int(rng.integers(1, 3000)), int(rng.integers(1, 3000)), int(rng.integers(1, 8000))
+        batch = int(rng.choice([1, 1, 1, 2, 5]))
+        bt = bool(trial & 1)
+        plan = mkp.mkp_plan_with_table(text, batch, M, N, K, bt=bt)
+        ex = mkp.mkp_plan_with_table(text, batch, M, N, K, exhaustive=True, bt=bt)
+        assert plan["cost_us"] == pytest.approx(ex["cost_us"], rel=1e-12), (M, N, K, batch, bt)
+        assert plan["evaluated"] <= ex["evaluated"]
+
+
 def test_plan_time_is_microseconds(mkp):
     import statistics
     ts = []
