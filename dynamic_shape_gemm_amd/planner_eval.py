@@ -13,9 +13,19 @@ For every distinct GEMM shape of a sweep it times, through the C ABI:
   split-K";
 * the R cheapest candidates of the whole modelled space (plan_rank 1..R).
 
-ORACLE (the page's exhaustive measured search) is read as the fastest
-measured plan of all of the above: every Pattern I plan and the R best
-modelled plans of Patterns I and II, MikPoly's own plan included.  Each
+ORACLE (the page's exhaustive measured search) is, with `--space full`
+(the default), the fastest plan of the whole candidate space: every Pattern
+I plan measured, and every Pattern II plan -- each tile-aligned cut of either
+dimension, each pair of distinct kernels, each split of each region --
+priced as the sum of its two regions' measured times.  A region is timed on
+its own as the forced kernel and split over a sub-matrix of the region's
+extent; its time does not depend on where the sub-matrix starts (the cuts
+keep every alignment), so each (kernel, split, extent) is timed once and
+serves as a first region at one cut and as a second region at others.  The
+two launches of a Pattern II plan run back to back on one stream, so their
+sum is the plan's time; the report checks this on the Pattern II plans the
+cost model picks, measured whole.  With `--space ranked` ORACLE is the
+fastest of the Pattern I plans and the R best modelled plans.  Each
 variant is timed as `reps` back-to-back calls after `warmup` calls.  The
 calls rotate over enough copies of the operands (at least 768 MB in all,
 beyond the 256 MB last-level cache) that each one streams them from HBM, as
@@ -81,41 +91,103 @@ class Shape:
     def flops(self):
         return 2.0 * self.b * self.M * self.N * self.K
 
-    def call(self):
+    def call(self, m_ext=None, n_ext=None):
+        """One call over the whole output, or over its first m_ext rows (or
+        n_ext columns) with the operands' strides unchanged."""
         m = self.mkp
         A, B, C = self.copies[self.i % len(self.copies)]
         self.i += 1
+        M = self.M if m_ext is None else m_ext
+        N = self.N if n_ext is None else n_ext
         if self.b == 1:
-            return m.mkp_gemm_raw(self.M, self.N, self.K, A, self.K, B, self.N, C, self.N, self.stream)
-        return m.mkp_gemm_batched_raw(self.b, self.M, self.N, self.K, A, self.K, self.M * self.K, B,
+            return m.mkp_gemm_raw(M, N, self.K, A, self.K, B, self.N, C, self.N, self.stream)
+        return m.mkp_gemm_batched_raw(self.b, M, N, self.K, A, self.K, self.M * self.K, B,
                                       self.N, self.K * self.N, C, self.N, self.M * self.N, self.stream)
 
     def free(self):
         del self.copies
 
 
-def time_variant(torch, shp, warmup, reps):
+def time_variant(torch, shp, warmup, reps, m_ext=None, n_ext=None):
     """Microseconds per call, or None if the library has no such plan."""
-    rc = shp.call()
+    rc = shp.call(m_ext, n_ext)
     if rc != 0:
         msg = shp.mkp.last_error()
         if "plan_rank" not in msg:   # a rank beyond the candidate list is expected
             log(f"[eval] {shp.b}x{shp.M}x{shp.N}x{shp.K}: error {rc}: {msg}")
         return None
     for _ in range(warmup):
-        shp.call()
+        shp.call(m_ext, n_ext)
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     cur = torch.cuda.current_stream()
     s.record(cur)
     for _ in range(reps):
-        shp.call()
+        shp.call(m_ext, n_ext)
     e.record(cur)
     torch.cuda.synchronize()
     return s.elapsed_time(e) * 1e3 / reps
 
 
-def evaluate_shape(torch, mkp, shp, kernels, splits, ranks, warmup, reps):
+def tile_dims(name):
+    """(uM, uN) from a kernel name m<uM>n<uN>k<uK>..."""
+    i, j = name.index("n"), name.index("k")
+    return int(name[1:i]), int(name[i + 1:j])
+
+
+def full_space_pattern_II(torch, mkp, shp, kernels, splits, warmup, reps):
+    """The cheapest measured Pattern II plan over every tile-aligned cut of
+    M and of N, every ordered pair of distinct kernels and every split of
+    each region: (us, label, regions timed).  Each (kernel, split, extent)
+    region is timed once, over the first rows (columns) of the output."""
+    t3 = max(-(-shp.K // 64), 1)
+    usable = [s for s in splits if s <= t3]
+    timed = {}
+    t0 = time.perf_counter()
+
+    def region(k, s, dim, ext):
+        key = (k, s, dim, ext)
+        if key not in timed:
+            mkp.mkp_set_option("force_kernel", k)
+            mkp.mkp_set_option("force_splitk", s)
+            timed[key] = time_variant(torch, shp, warmup, reps, *((ext, None) if dim == 0 else (None, ext)))
+            if len(timed) % 2000 == 0:
+                log(f"[eval]   {len(timed)} regions timed ({time.perf_counter() - t0:.0f} s)")
+        return timed[key]
+
+    best = (math.inf, None)
+    try:
+        for dim, ext in ((0, shp.M), (1, shp.N)):
+            dims = {k: tile_dims(k)[dim] for k in kernels}
+            # the best split of each kernel over each extent it serves
+            best_of = {}
+            for k in kernels:
+                exts = {c for c in range(dims[k], ext, dims[k])}
+                exts |= {ext - c for a in kernels for c in range(dims[a], ext, dims[a])}
+                for e in sorted(exts):
+                    vals = [(region(k, s, dim, e), s) for s in usable]
+                    vals = [v for v in vals if v[0] is not None]
+                    if vals:
+                        best_of[(k, e)] = min(vals)
+            for a in kernels:
+                for cut in range(dims[a], ext, dims[a]):
+                    r1 = best_of.get((a, cut))
+                    if r1 is None:
+                        continue
+                    for b in kernels:
+                        r2 = best_of.get((b, ext - cut))
+                        if b == a or r2 is None:
+                            continue
+                        if r1[0] + r2[0] < best[0]:
+                            tag = "M" if dim == 0 else "N"
+                            best = (r1[0] + r2[0], f"II-{tag} {a}/s{r1[1]}[{cut}] + {b}/s{r2[1]}[{ext - cut}]")
+    finally:
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("force_splitk", 0)
+    return best[0], best[1], len(timed), timed
+
+
+def evaluate_shape(torch, mkp, shp, kernels, splits, ranks, warmup, reps, space="full", region_reps=3):
     t0 = time.perf_counter()
     rec = {"shape": [shp.b, shp.M, shp.N, shp.K], "flops": shp.flops}
     measured = []   # (us, label)
@@ -164,6 +236,21 @@ def evaluate_shape(torch, mkp, shp, kernels, splits, ranks, warmup, reps):
     again = run("mikpoly", [])
     if again is not None and (rec["mikpoly_us"] is None or again < rec["mikpoly_us"]):
         rec["mikpoly_us"] = again
+    if space == "full":
+        us, label, n, timed = full_space_pattern_II(torch, mkp, shp, kernels, splits, 1, region_reps)
+        rec["regions_timed"] = n
+        if label is not None:
+            measured.append((us, label))
+            rec["best_II_us"], rec["best_II"] = us, label
+        # the composition checked on the cost model's own Pattern II plan
+        if plan["pattern"] in ("II-M", "II-N") and not plan.get("fused") and not plan.get("transpose_b"):
+            dim = 0 if plan["pattern"] == "II-M" else 1
+            parts = []
+            for r in plan["regions"]:
+                ext = r["m"] if dim == 0 else r["n"]
+                parts.append(timed.get((r["kernel"], r["s"], dim, ext)))
+            if all(p is not None for p in parts) and rec["mikpoly_us"]:
+                rec["II_sum_vs_whole"] = round(sum(parts) / rec["mikpoly_us"], 4)
     if not measured:
         raise RuntimeError(f"no variant of {rec['shape']} ran")
     best = min(measured)
@@ -198,15 +285,35 @@ def summarize(recs):
     out["plan_us_median"] = round(statistics.median(r["plan"]["plan_us"] for r in recs), 2)
     out["oracle_search_s_median"] = round(statistics.median(r["search_s"] for r in recs), 3)
     out["variants_per_shape_median"] = statistics.median(r["variants_measured"] for r in recs)
+    if any("regions_timed" in r for r in recs):
+        out["regions_timed_median"] = statistics.median(r.get("regions_timed", 0) for r in recs)
+        chk = [r["II_sum_vs_whole"] for r in recs if "II_sum_vs_whole" in r]
+        out["II_sum_vs_whole"] = {"plans": len(chk), "geomean": round(geomean(chk), 4) if chk else None,
+                                  "min": min(chk) if chk else None, "max": max(chk) if chk else None}
     return out
 
 
-def markdown(cfg, name, summary, recs, cmd):
+def markdown(cfg, name, summary, recs, cmd, space="full", sample=""):
+    if space == "full":
+        what = (f"{summary['shapes']} distinct shapes{sample}. ORACLE = the fastest plan of the whole candidate "
+                "space: every micro-kernel forced alone over the output with every split-K factor (Pattern I, "
+                "measured), and every Pattern II plan -- each tile-aligned cut of M and of N, each pair of "
+                "distinct kernels, each split of each region -- priced as the sum of its two regions, each "
+                f"region timed on its own (median {summary['regions_timed_median']:.0f} regions timed per "
+                "shape). The ablated cost models and the best modelled candidates by rank are measured as "
+                "well.")
+        chk = summary["II_sum_vs_whole"]
+        if chk["plans"]:
+            what += (f" Check of the sum: on the {chk['plans']} Pattern II plans the cost model picked, the "
+                     f"sum of the two regions' times over the plan measured whole is {chk['geomean']} "
+                     f"(geomean; {chk['min']} to {chk['max']}).")
+    else:
+        what = (f"{summary['shapes']} distinct shapes{sample}; per shape about "
+                f"{summary['variants_per_shape_median']:.0f} measured plans (every micro-kernel forced alone "
+                "with every split-K factor, the ablated cost models, the best modelled candidates by rank). "
+                "ORACLE = the fastest of them.")
     lines = [f"# Polymerizer, measured: config {cfg} ({name})", "",
-             "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
-             f"{summary['shapes']} distinct shapes; per shape about {summary['variants_per_shape_median']:.0f} "
-             "measured plans (every micro-kernel forced alone with every split-K factor, the ablated cost "
-             "models, the best modelled candidates by rank). ORACLE = the fastest of them.", "",
+             "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "", what, "",
              "| variant | TFLOP/s over the sweep | geomean vs ORACLE | worst shape vs ORACLE |",
              "|---|---:|---:|---:|"]
     label = {"oracle": "ORACLE (measured search)", "mikpoly": "MikPoly (cost model)",
@@ -238,6 +345,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--max-shapes", type=int, default=0, help="0 = every distinct shape")
+    ap.add_argument("--sample", type=int, default=0,
+                    help="time this many distinct shapes drawn at random (seeded), 0 = all")
+    ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--space", choices=["full", "ranked"], default="full")
+    ap.add_argument("--region-reps", type=int, default=3)
     ap.add_argument("--json", default="")
     ap.add_argument("--md", default="")
     a = ap.parse_args()
@@ -259,13 +371,18 @@ def main():
         if key not in seen:
             seen.add(key)
             cases.append(c)
+    sample = ""
+    if a.sample and a.sample < len(cases):
+        pick = sorted(np.random.default_rng(a.seed).choice(len(cases), size=a.sample, replace=False))
+        sample = f" (a seeded sample, seed {a.seed}, of the sweep's {len(cases)})"
+        cases = [cases[i] for i in pick]
     if a.max_shapes:
         cases = cases[:a.max_shapes]
     log(f"[eval] config {a.config}: {len(cases)} shapes, {len(kernels)} kernels, splits {splits}")
     recs = []
     for i, c in enumerate(cases):
         shp = Shape(c, torch, mkp)
-        rec = evaluate_shape(torch, mkp, shp, kernels, splits, a.ranks, a.warmup, a.reps)
+        rec = evaluate_shape(torch, mkp, shp, kernels, splits, a.ranks, a.warmup, a.reps, a.space, a.region_reps)
         shp.free()
         recs.append(rec)
         log(f"[eval] {i + 1}/{len(cases)} {rec['shape']} mikpoly {rec['mikpoly_us']:.2f} us, oracle "
@@ -277,11 +394,13 @@ def main():
     if a.json:
         json.dump({"summary": summary, "shapes": recs}, open(a.json, "w"), indent=1)
     if a.md:
-        cmd = ("python3 -m dynamic_shape_gemm_amd.planner_eval " + " ".join(
-            f"--{k.replace('_', '-')} {v}" for k, v in (("config", a.config), ("ranks", a.ranks),
-                                                        ("warmup", a.warmup), ("reps", a.reps)))
+        opts = [("config", a.config), ("ranks", a.ranks), ("warmup", a.warmup), ("reps", a.reps),
+                ("space", a.space), ("region-reps", a.region_reps)]
+        if a.sample:
+            opts += [("sample", a.sample), ("seed", a.seed)]
+        cmd = ("python3 -m dynamic_shape_gemm_amd.planner_eval " + " ".join(f"--{k} {v}" for k, v in opts)
                + f" --md {os.path.relpath(a.md, ROOT) if os.path.isabs(a.md) else a.md}")
-        open(a.md, "w").write(markdown(a.config, summary["workload"], summary, recs, cmd))
+        open(a.md, "w").write(markdown(a.config, summary["workload"], summary, recs, cmd, a.space, sample))
 
 
 if __name__ == "__main__":

@@ -36,8 +36,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Tile<uM, uN, uK, waves_m, waves_n, stages, preread, N x K B[, convolution]>
 TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (?:true|false), (true|false)(?:, (true|false))?>")
-# tiles the library also has in a deeper-pipelined form, named with "x<stages>"
-DEEP = {(128, 128, 4)}
+# tiles the library also has with another stage count, named with "x<stages>"
+DEEP = {(128, 128, 4), (64, 64, 2), (64, 128, 2), (128, 64, 2)}
 # tiles the library also has on fewer, larger waves, named with "w<waves>"
 WIDE = {(256, 256, 4)}
 
