@@ -755,8 +755,10 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n * batch;
         // (the allocation-free call sums splits in a second pass: its
         // scratch then holds nothing that must start at zero)
+        // (its partial stores and loads take 32-bit byte offsets within a
+        // tile: 256 rows of ldw floats)
         R.fused_red = r.s > 1 && ki.fused_ok && !noalloc && L.fused_reduce.load(std::memory_order_relaxed) == 1 &&
-                      counter0 + ntiles <= counter_cap;
+                      counter0 + ntiles <= counter_cap && R.ldw * 256 * 4 < (int64_t(1) << 31);
         a.counters = R.fused_red ? (int*)ws + counter0 : nullptr;
         a.Cout = R.Creg;
         a.ldcout = ldc;

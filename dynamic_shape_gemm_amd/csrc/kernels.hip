@@ -326,6 +326,24 @@ __device__ __forceinline__ void dma16(const void* g, lds_t* lds) {
 }
 #pragma clang diagnostic pop
 
+// Agent-coherent 16-byte accesses for the fused split-K exchange: sc1 makes
+// a store write through the XCD's L2 to the level every XCD sees, and a load
+// read from there rather than from a line its own L2 may hold (the memory
+// model's encoding of agent-scope atomic loads and stores).  Their completion
+// (vmcnt) is their visibility at agent scope, so the exchange needs no L2
+// write-back or invalidate.  `base` is wave-uniform; byte offsets stay below
+// 2^31.
+constexpr int kCoherentAgent = 16;   // the sc1 cache-policy bit
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCoherentAgent);
+}
+__device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherentAgent));
+}
+
 struct TileCtx {
     const uint16_t* A;   // tile origin row m0 (row 0 of the tile), column 0; convolution: the input
     const uint16_t* B;   // tile origin column n0, row 0
@@ -812,6 +830,9 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     // Plain epilogue: the tile goes through LDS one fragment row at a time
     // so that every store instruction writes contiguous row segments.
     const bool epi_here = epi && args.splits == 1;
+    // this split's partial goes to the fused reduction (workspace rows are
+    // 16-byte aligned, so the vector store loop writes it)
+    const bool fused_split = T::FUSED && args.splits > 1 && args.counters != nullptr;
     const int col0 = wn * T::WTN;   // first tile column of this wave
     constexpr int C4 = T::WTN / 4;  // 16-byte chunks per staged row
     static_assert(64 % C4 == 0, "a lane's chunk column must not change across the store loop");
@@ -904,6 +925,22 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
                     }
                 }
             }
+        } else if (vecC && fused_split) {
+            // a split's partial tile for the fused reduction: written
+            // through to where the last-arriving split, on any XCD, reads it
+            const __amdgpu_buffer_rsrc_t rc = coherent_rsrc(C);
+#pragma unroll 1
+            for (int it = 0; it < ITS; ++it) {
+                const int id = it * 64 + lane;
+                if ((T::MF * C4) % 64 == 0 || id < T::MF * C4) {
+                    const int r = id / C4, c4 = (id % C4) * 4;
+                    const f32x4 v = *(const f32x4 __attribute__((address_space(3)))*)(stg + r * T::EPI_LD + c4);
+                    // whole chunks up to the row's last column (workspace
+                    // rows are padded to a multiple of 4 floats)
+                    if (row0 + r < c.Mr && col0 + c4 < c.Nr)
+                        store4_coherent(rc, (uint32_t)(((row0 + r) * args.ldc + col0 + c4) * 4), v);
+                }
+            }
         } else if (vecC) {
 #pragma unroll 1
             for (int it = 0; it < ITS; ++it) {
@@ -968,29 +1005,28 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next row overwrites
     }
-    if (T::FUSED && args.splits > 1 && args.counters != nullptr) {
-        // Fused split-K reduction.  Every split has stored its partial tile
-        // (the rows above, into the workspace); once all waves' stores have
-        // completed, wave 0 publishes them at agent scope (the splits may
-        // sit on different XCDs, whose L2s are not coherent: one L2
-        // write-back) and counts the arrival.  The last split to arrive
-        // makes the others' partials visible (an L2/L1 invalidate) and sums
-        // all of them in split order -- the same order whichever split
-        // arrives last -- reading whole rows (16 bytes per lane, consecutive
-        // lanes along a row), then writes C through the epilogue.
-        // the arrival flag lives in the stage memory, idle after the
-        // epilogue (every wave is past its staging once the barrier is passed)
+    if (fused_split) {
+        // Fused split-K reduction.  Every split has written its partial tile
+        // through to the level all XCDs share (the rows above, into the
+        // workspace).  Once every wave's stores have completed -- and so
+        // are visible there -- wave 0 counts the arrival with an
+        // agent-scope atomic.  The last split to arrive reads all partials
+        // with agent-coherent loads (not from its own L2, which may hold
+        // stale lines of the workspace) and sums them in split order -- the
+        // same order whichever split arrives last -- whole rows at a time
+        // (16 bytes per lane, consecutive lanes along a row), then writes C
+        // through the epilogue.  No L2 write-back or invalidate is needed.
+        // The arrival flag lives in the stage memory, idle after the
+        // epilogue (every wave is past its staging once the barrier is passed).
         int __attribute__((address_space(3)))* s_last_p = (int __attribute__((address_space(3)))*)smem;
         __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
         __syncthreads();
         int* cnt = args.counters + (int64_t)b * args.tiles_m * args.tiles_n + tm * args.tiles_n + tn;
         if (wave == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             int last = 0;
             if (lane == 0)
                 last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.splits - 1;
             last = __builtin_amdgcn_readfirstlane(last);
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             if (lane == 0) *s_last_p = last;
         }
         __syncthreads();
@@ -1004,7 +1040,7 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
         for (int id = tid; id < rows * CH; id += T::NT) {
             const int m = id / CH, n = (id % CH) * 4;
             if (n >= c.Nr) continue;
-            const int64_t e = (int64_t)m * args.ldc + n;   // workspace rows: 16-byte aligned
+            const uint32_t e = (uint32_t)((m * args.ldc + n) * 4);   // workspace rows: 16-byte aligned
             // partials in split order, eight loads issued before their adds
             // (one load per add would wait out a round trip per split)
             f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1012,9 +1048,7 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
                 f32x4 v[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    if (z0 + u < args.splits) {
-                        v[u] = *(const f32x4*)(Wt + (int64_t)(z0 + u) * args.sCsplit + e);
-                    }
+                    if (z0 + u < args.splits) v[u] = load4_coherent(coherent_rsrc(Wt + (int64_t)(z0 + u) * args.sCsplit), e);
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
                     if (z0 + u < args.splits) sum = (z0 + u == 0) ? v[u] : sum + v[u];
