@@ -25,6 +25,7 @@ buffers (the decoder weights rotate over four copies), so the working set
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -245,11 +246,15 @@ def conv_vs_gemm(wl, mkp, stream):
             fn()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
-        s.record(cur)
-        for _ in range(50):
-            fn()
-        e.record(cur)
-        torch.cuda.synchronize()
+        gc.disable()   # as in timed_steps
+        try:
+            s.record(cur)
+            for _ in range(50):
+                fn()
+            e.record(cur)
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
         return s.elapsed_time(e) * 1e3 / 50
 
     rows = []
@@ -296,16 +301,27 @@ def conv_cpu_baseline(wl, budget_s: float):
 
 
 def timed_steps(wl, mkp, steps, stream):
+    """Milliseconds for `steps` steps between two events on the stream.  The
+    Python collector is run before and paused inside (as timeit does): a
+    full collection stalls the host for tens of ms and the GPU then idles,
+    which would be charged to whichever call it interrupted."""
     import torch
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    cur = torch.cuda.current_stream()
-    s.record(cur)
-    for _ in range(steps):
-        wl.step(mkp, stream)
-    e.record(cur)
-    torch.cuda.synchronize()
+    gc.collect()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream()
+        s.record(cur)
+        for _ in range(steps):
+            wl.step(mkp, stream)
+        e.record(cur)
+        torch.cuda.synchronize()
+    finally:
+        if was:
+            gc.enable()
     return s.elapsed_time(e)  # ms
 
 

@@ -36,6 +36,7 @@ a shape does not count against it.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -121,11 +122,17 @@ def time_variant(torch, shp, warmup, reps, m_ext=None, n_ext=None):
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     cur = torch.cuda.current_stream()
-    s.record(cur)
-    for _ in range(reps):
-        shp.call(m_ext, n_ext)
-    e.record(cur)
-    torch.cuda.synchronize()
+    # no collector pass inside the timed calls (it stalls the host, and the
+    # GPU idles, for tens of ms)
+    gc.disable()
+    try:
+        s.record(cur)
+        for _ in range(reps):
+            shp.call(m_ext, n_ext)
+        e.record(cur)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     return s.elapsed_time(e) * 1e3 / reps
 
 
