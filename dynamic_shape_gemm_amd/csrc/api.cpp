@@ -1412,10 +1412,13 @@ int mkp_calibrate(const char* path, int max_points) {
     int npts = (int)(sizeof(grid_t) / sizeof(grid_t[0]));
     if (max_points > 0) npts = std::min(npts, max_points);
     const int64_t kmax_cap = 16384;
+    // the skinny tiles' layout splits K (below): its K is the split depth
+    // times the splits, allowed up to 65536
+    const int64_t kmax_split = 65536;
 
     // buffers sized for the largest point of any kernel
     size_t a_elems = 0, b_elems = 0, c_elems = 0;
-    struct Shape { int tm, tn; };
+    struct Shape { int tm, tn, s; };
     std::vector<Shape> shapes;
     std::vector<int> occ;
     for (int i = 0; i < kernel_count(); ++i) {
@@ -1427,18 +1430,23 @@ int mkp_calibrate(const char* path, int max_points) {
         const int slots = cus * n;
         Shape s;
         if (ki.uM <= 32) {
-            s = {1, slots};
+            // skinny tiles serve outputs of a few rows, where the wave is
+            // filled by K splits: one tile row, at most 32 tile columns, the
+            // rest of the slots as splits (as such a call runs)
+            int tn = std::min(slots, 32);
+            while (slots % tn) --tn;
+            s = {1, tn, slots / tn};
         } else {
             int tm = (int)std::floor(std::sqrt((double)slots));
             while (slots % tm) --tm;
-            s = {tm, slots / tm};
+            s = {tm, slots / tm, 1};
         }
         shapes.push_back(s);
         const int64_t M = (int64_t)s.tm * ki.uM, N = (int64_t)s.tn * ki.uN;
-        const int64_t K = std::min<int64_t>((int64_t)grid_t[npts - 1] * ki.uK, kmax_cap);
+        const int64_t K = std::min<int64_t>((int64_t)grid_t[npts - 1] * ki.uK * s.s, s.s > 1 ? kmax_split : kmax_cap);
         a_elems = std::max(a_elems, (size_t)(M * K));
         b_elems = std::max(b_elems, (size_t)(K * N));
-        c_elems = std::max(c_elems, (size_t)(M * N));
+        c_elems = std::max(c_elems, (size_t)(M * N * s.s));
     }
     // Operands come from a pool of at least 2 GiB (C from one of 1 GiB) whose
     // slices rotate from launch to launch, so every timed launch streams its
@@ -1462,7 +1470,7 @@ int mkp_calibrate(const char* path, int max_points) {
     // point a, for an M x K by K x N product, at the next slices of the pools
     auto next_operands = [&](KArgs& a) {
         const size_t fa = round256((size_t)a.M * a.K * 2), fb = round256((size_t)a.K * a.N * 2);
-        const size_t fc = round256((size_t)a.M * a.N * 4);
+        const size_t fc = round256((size_t)a.M * a.N * 4 * std::max(a.splits, 1));
         const size_t nab = std::max<size_t>(1, pool_ab / (fa + fb)), nc = std::max<size_t>(1, pool_c / fc);
         const size_t i = (size_t)rotation++;
         char* base = pAB + (i % nab) * (fa + fb);
@@ -1537,8 +1545,8 @@ int mkp_calibrate(const char* path, int max_points) {
         const Shape s = shapes[i];
         for (int p = 0; p < npts; ++p) {
             const int tt = grid_t[p];
-            const int64_t K = (int64_t)tt * ki.uK;
-            if (K > kmax_cap) break;
+            const int64_t K = (int64_t)tt * ki.uK * s.s;
+            if (K > (s.s > 1 ? kmax_split : kmax_cap)) break;
             KArgs a{};
             a.M = s.tm * ki.uM;
             a.N = s.tn * ki.uN;
@@ -1549,10 +1557,11 @@ int mkp_calibrate(const char* path, int max_points) {
             a.tiles_m = s.tm;
             a.tiles_n = s.tn;
             a.steps_per_split = tt;
-            a.splits = 1;
+            a.splits = s.s;
+            a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;   // each split's partial tile
             a.batch = 1;
             a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
-            const dim3 grid((unsigned)(s.tm * s.tn));
+            const dim3 grid((unsigned)(s.tm * s.tn * s.s));
             // single-launch time, then enough repetitions for ~2 ms
             auto launch = [&] {
                 next_operands(a);
@@ -1574,7 +1583,7 @@ int mkp_calibrate(const char* path, int max_points) {
             if (pt.first == t_ref) g_ref = pt.second;
         if (err == hipSuccess && g_ref > 0) {
             static const double fills[] = {1.0 / 16, 1.0 / 8, 1.0 / 4, 1.0 / 2, 3.0 / 4};
-            const int slots = s.tm * s.tn;
+            const int slots = s.tm * s.tn * s.s;
             int prev_tn = 0;
             for (double f : fills) {
                 const int tn = std::max(1, (int)std::lround(f * s.tn));
@@ -1586,17 +1595,18 @@ int mkp_calibrate(const char* path, int max_points) {
                     KArgs a{};
                     a.M = s.tm * ki.uM;
                     a.N = cols * ki.uN;
-                    a.K = t_ref * ki.uK;
+                    a.K = t_ref * ki.uK * s.s;
                     a.lda = a.K;
                     a.ldb = ki.bt ? a.K : a.N;
                     a.ldc = a.N;
                     a.tiles_m = s.tm;
                     a.tiles_n = cols;
                     a.steps_per_split = t_ref;
-                    a.splits = 1;
+                    a.splits = s.s;
+                    a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;
                     a.batch = 1;
                     a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
-                    const dim3 grid((unsigned)(s.tm * cols));
+                    const dim3 grid((unsigned)(s.tm * cols * s.s));
                     us[after] = time_launches(
                         [&] {
                             next_operands(a);
@@ -1605,7 +1615,7 @@ int mkp_calibrate(const char* path, int max_points) {
                         20, 50, &err);
                 }
                 if (err != hipSuccess) break;
-                const double fill = (double)(s.tm * tn) / slots;
+                const double fill = (double)(s.tm * tn * s.s) / slots;
                 auto clamp = [](double r) { return std::min(1.0, std::max(0.02, r)); };
                 k.tail.emplace_back(fill, clamp(std::max(us[0] - t.launch_us, 0.05) / g_ref));
                 k.tailx.emplace_back(fill, clamp((us[1] - t.launch_us - g_ref) / g_ref));

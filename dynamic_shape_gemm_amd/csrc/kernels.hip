@@ -645,6 +645,57 @@ __device__ __forceinline__ void compute_stage32(const lds_t* sa, const lds_t* sb
     }
 }
 
+// One LDS stage through 16x16x32 MFMAs (16-row wave tiles): per K sub-step
+// of 32, each fragment is two 64-bit reads (N x K tiles and A), or two
+// transposed reads (K x N tiles).
+template <class T, class Acc>
+__device__ __forceinline__ void compute_stage16(const lds_t* sa, const lds_t* sb, Acc (&acc)[T::FM][T::FN], int lane,
+                                                int wm, int wn) {
+    const int g4 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < T::BK / 32; ++ks) {
+        const int kk = ks * 32;
+        bf16x8 xb[T::FN], ya[T::FM];
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+            if constexpr (T::BT) {
+                // N x K tile: the A fragments' K assignment
+                const int n = wn * T::WTN + j * 16 + s16;
+                const int c1 = (kk >> 3) + (g4 >> 1), hb = (g4 & 1) * 8;
+                const u32x2 lo = *(const u32x2 __attribute__((address_space(3)))*)(
+                    sb + n * T::B_ROWB + ((c1 ^ swzA<T::BK>(n)) << 4) + hb);
+                const u32x2 hi = *(const u32x2 __attribute__((address_space(3)))*)(
+                    sb + n * T::B_ROWB + (((c1 + 2) ^ swzA<T::BK>(n)) << 4) + hb);
+                xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+                continue;
+            }
+            const int seg = (wn * T::WTN + j * 16) >> 4;
+            const int k1 = kk + 4 * g4 + (s16 >> 2), k2 = k1 + 16;
+            const int o = (s16 & 3) * 8;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
+                sb + k1 * T::B_ROWB + ((seg ^ swzB<T::BN, 16>(k1)) << 5) + o));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
+                sb + k2 * T::B_ROWB + ((seg ^ swzB<T::BN, 16>(k2)) << 5) + o));
+            xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+            const int row = wm * T::WTM + i * 16 + s16;
+            const int c1 = (kk >> 3) + (g4 >> 1), hb = (g4 & 1) * 8;
+            const u32x2 lo = *(const u32x2 __attribute__((address_space(3)))*)(
+                sa + row * T::A_ROWB + ((c1 ^ swzA<T::BK>(row)) << 4) + hb);
+            const u32x2 hi = *(const u32x2 __attribute__((address_space(3)))*)(
+                sa + row * T::A_ROWB + (((c1 + 2) ^ swzA<T::BK>(row)) << 4) + hb);
+            ya[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], ya[i], acc[i][j], 0, 0, 0);
+    }
+}
+
 // Map the flat workgroup id to (tile_m, tile_n, split, batch).  Workgroups
 // are dealt round-robin to the 8 XCDs; ids are first regrouped so that each
 // XCD receives a contiguous run of logical ids, then the logical id walks
@@ -759,48 +810,7 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
         if constexpr (T::MF == 32) {
             compute_stage32<T>(sa, sb, acc, lane, wm, wn);
         } else {
-#pragma unroll
-            for (int ks = 0; ks < T::BK / 32; ++ks) {
-                const int kk = ks * 32;
-                bf16x8 xb[T::FN], ya[T::FM];
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j) {
-                    if constexpr (T::BT) {
-                        // N x K tile: the A fragments' K assignment
-                        const int n = wn * T::WTN + j * 16 + s16;
-                        const int c1 = (kk >> 3) + (g4 >> 1), hb = (g4 & 1) * 8;
-                        const u32x2 lo = *(const u32x2 __attribute__((address_space(3)))*)(
-                            sb + n * T::B_ROWB + ((c1 ^ swzA<T::BK>(n)) << 4) + hb);
-                        const u32x2 hi = *(const u32x2 __attribute__((address_space(3)))*)(
-                            sb + n * T::B_ROWB + (((c1 + 2) ^ swzA<T::BK>(n)) << 4) + hb);
-                        xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
-                        continue;
-                    }
-                    const int seg = (wn * T::WTN + j * 16) >> 4;
-                    const int k1 = kk + 4 * g4 + (s16 >> 2), k2 = k1 + 16;
-                    const int o = (s16 & 3) * 8;
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
-                        sb + k1 * T::B_ROWB + ((seg ^ swzB<T::BN, 16>(k1)) << 5) + o));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(
-                        sb + k2 * T::B_ROWB + ((seg ^ swzB<T::BN, 16>(k2)) << 5) + o));
-                    xb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                }
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i) {
-                    const int row = wm * T::WTM + i * 16 + s16;
-                    const int c1 = (kk >> 3) + (g4 >> 1), hb = (g4 & 1) * 8;
-                    const u32x2 lo = *(const u32x2 __attribute__((address_space(3)))*)(
-                        sa + row * T::A_ROWB + ((c1 ^ swzA<T::BK>(row)) << 4) + hb);
-                    const u32x2 hi = *(const u32x2 __attribute__((address_space(3)))*)(
-                        sa + row * T::A_ROWB + (((c1 + 2) ^ swzA<T::BK>(row)) << 4) + hb);
-                    ya[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
-                }
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < T::FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], ya[i], acc[i][j], 0, 0, 0);
-            }
+            compute_stage16<T>(sa, sb, acc, lane, wm, wn);
         }
     }
 
@@ -1084,6 +1094,182 @@ template <class T>
 hipError_t launch_tile(const KArgs& a, dim3 grid, hipStream_t st) {
     return launch_kernel(gemm_tile_kernel<T>, grid, dim3(T::NT), st, a);
 }
+
+// ---- skinny-M tiles: the K range split across the waves ---------------------
+//
+// For outputs with few rows the tile count of a plain tile is too small to
+// fill the CUs, and splitting K across workgroups costs a second pass over
+// fp32 partials.  Here the KW waves of one workgroup split K instead: wave w
+// takes the 64-wide K chunks w, w + KW, w + 2 KW, ... of the workgroup's K
+// range, each through its own S-stage LDS pipeline (direct loads, no
+// barrier: a wave waits only for its own loads), so one K step of the tile
+// is 64 KW deep.  Every wave accumulates the whole BM x BN tile; at the end
+// the waves' sums meet in LDS (added in wave order) and go out as C -- or
+// as one split's partial when the plan also splits K across workgroups.
+template <int BM_, int BN_, int KW_, int S_, bool BT_>
+struct WSplit {
+    static constexpr int BM = BM_, BN = BN_, KW = KW_, S = S_;
+    static constexpr bool BT = BT_;
+    static constexpr int NT = 64 * KW;
+    static constexpr int BK = 64 * KW;                       // K per step of the workgroup (the table's uK)
+    using T1 = Tile<BM, BN, 64, 1, 1, S, false, BT>;        // one wave's pipeline over 64-wide chunks
+    static constexpr int WAVE_LDS = S * T1::STAGE;
+    static constexpr int RED_LD = BN + 4;                    // staged row, padded by 4 floats
+    static constexpr int RED = KW * BM * RED_LD * 4;
+    static constexpr int LDS = (KW * WAVE_LDS > RED ? KW * WAVE_LDS : RED);
+    static_assert(!T1::JUNK, "a wave's chunk must fill whole 1 KB load groups");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// Wait until at most A chunks' direct loads of this wave are in flight and
+// its LDS reads are done (no barrier: the stages are the wave's own).
+template <class T1, int A>
+__device__ __forceinline__ void wave_wait_upto(int ahead) {
+    if constexpr (A <= 0) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    } else {
+        if (ahead >= A) {
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(A * T1::IPS) : "memory");
+            return;
+        }
+        wave_wait_upto<T1, A - 1>(ahead);
+    }
+}
+
+template <class W>
+__device__ __forceinline__ void wsplit_task(KArgs args, int bid, int nblk, lds_t* smem) {
+    using T1 = typename W::T1;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    int tm, tn, split, b;
+    map_tile<8>(bid, nblk, args.tiles_m, args.tiles_n, args.splits, tm, tn, split, b);
+    if (args.ngroups > 0) {
+        // grouped call: the tile column's group (as in tile_task)
+        KGroup G = args.group[0];
+#pragma unroll
+        for (int i = 1; i < kMaxGroups; ++i)
+            if (i < args.ngroups && tn >= args.group[i].tile0) G = args.group[i];
+        tn -= G.tile0;
+        args.B = G.B;
+        args.ldb = G.ldb;
+        args.N = G.N;
+        args.flags = (args.flags & ~KF_VEC_B) | (G.flags & KF_VEC_B);
+        if (args.splits == 1) {
+            args.C = G.C;
+            args.ldc = G.ldc;
+            args.flags = (args.flags & ~KF_VEC_C) | (G.flags & KF_VEC_C);
+        } else {
+            args.C += (int64_t)G.tile0 * W::BN;
+        }
+        args.counters = nullptr;
+    }
+    const int m0 = tm * W::BM, n0 = tn * W::BN;
+    TileCtx c;
+    c.A = args.A + (int64_t)b * args.sA + (int64_t)m0 * args.lda;
+    c.B = args.B + (int64_t)b * args.sB + (W::BT ? (int64_t)n0 * args.ldb : (int64_t)n0);
+    c.lda = args.lda;
+    c.ldb = args.ldb;
+    c.Mr = args.M - m0;
+    c.Nr = args.N - n0;
+    const int kbeg = split * args.steps_per_split * W::BK;
+    c.kend = min(args.K, kbeg + args.steps_per_split * W::BK);
+    c.vecA = args.flags & KF_VEC_A;
+    c.vecB = args.flags & KF_VEC_B;
+    const int nchunks = (c.kend - kbeg + 63) / 64;
+    const bool dma_tile = c.vecA && c.vecB && (c.Nr >= W::BN || (args.N & 7) == 0);
+    const int dma_chunks = dma_tile ? (c.kend - kbeg) / 64 : 0;   // full chunks
+    const int mine = nchunks > wave ? (nchunks - wave + W::KW - 1) / W::KW : 0;
+
+    lds_t* ws = smem + wave * W::WAVE_LDS;
+    DmaOffsets<T1> dma;
+    if (dma_tile) dma.init(c, 0, lane);
+    auto load = [&](int j) {   // this wave's j-th chunk
+        const int q = wave + j * W::KW;
+        lds_t* st = ws + (j % W::S) * T1::STAGE;
+        const int k0 = kbeg + q * 64;
+        if (q < dma_chunks) dma.issue(c, k0, st, st, 0);
+        else reg_step<T1>(c, k0, st, lane);
+    };
+
+    using acc_t = typename std::conditional<T1::MF == 32, f32x16, f32x4>::type;
+    acc_t acc[T1::FM][T1::FN];
+#pragma unroll
+    for (int i = 0; i < T1::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T1::FN; ++j) acc[i][j] = acc_t{};
+
+#pragma unroll
+    for (int j = 0; j < W::S - 1; ++j)
+        if (j < mine) load(j);
+    for (int j = 0; j < mine; ++j) {
+        wave_wait_upto<T1, W::S - 2>(min(W::S - 2, mine - 1 - j));
+        if (j + W::S - 1 < mine) load(j + W::S - 1);
+        const lds_t* sa = ws + (j % W::S) * T1::STAGE;
+        const lds_t* sb = sa + T1::A_BYTES;
+        if constexpr (T1::MF == 32) compute_stage32<T1>(sa, sb, acc, lane, 0, 0);
+        else compute_stage16<T1>(sa, sb, acc, lane, 0, 0);
+    }
+
+    // the waves' sums meet in LDS: wave w's tile at rows of RED_LD floats
+    __syncthreads();   // every wave is done with its stages
+    float __attribute__((address_space(3)))* red = (float __attribute__((address_space(3)))*)smem;
+    float __attribute__((address_space(3)))* mine_t = red + wave * W::BM * W::RED_LD;
+#pragma unroll
+    for (int i = 0; i < T1::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T1::FN; ++j) {
+            if constexpr (T1::MF == 32) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = i * 32 + (lane & 31), col = j * 32 + 8 * q + 4 * (lane >> 5);
+                    *(f32x4 __attribute__((address_space(3)))*)(mine_t + r * W::RED_LD + col) =
+                        f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                }
+            } else {
+                const int r = i * 16 + (lane & 15), col = j * 16 + (lane >> 4) * 4;
+                *(f32x4 __attribute__((address_space(3)))*)(mine_t + r * W::RED_LD + col) = acc[i][j];
+            }
+        }
+    __syncthreads();
+
+    // sum in wave order, 16 bytes per thread along the rows, and store
+    float* C = args.C + (int64_t)b * args.sC + (int64_t)split * args.sCsplit + (int64_t)m0 * args.ldc + n0;
+    const bool vecC = args.flags & KF_VEC_C;
+    const bool epi = (args.flags & KF_EPI) && args.splits == 1;
+    constexpr int CH = W::BN / 4;
+    const int rows = min(c.Mr, W::BM);
+#pragma unroll 1
+    for (int id = tid; id < rows * CH; id += W::NT) {
+        const int m = id / CH, n = (id % CH) * 4;
+        if (n >= c.Nr) continue;
+        f32x4 v = *(const f32x4 __attribute__((address_space(3)))*)(red + m * W::RED_LD + n);
+#pragma unroll
+        for (int w = 1; w < W::KW; ++w)
+            v += *(const f32x4 __attribute__((address_space(3)))*)(red + (w * W::BM + m) * W::RED_LD + n);
+        float* p = C + (int64_t)m * args.ldc + n;
+        if (epi) v = epi4(args.epi, p, vecC, c.Nr - n, load_bias4(args.epi, n0 + n, c.Nr - n), v);
+        if (vecC && n + 4 <= c.Nr) {
+            *(f32x4*)p = v;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < c.Nr) p[r] = v[r];
+        }
+    }
+}
+
+template <class W>
+__global__ __launch_bounds__(W::NT) void gemm_wsplit_kernel(KArgs args) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[W::LDS];
+    wsplit_task<W>(args, blockIdx.x, gridDim.x, (lds_t*)smem_raw);
+}
+
+template <class W>
+hipError_t launch_wsplit(const KArgs& a, dim3 grid, hipStream_t st) {
+    return launch_kernel(gemm_wsplit_kernel<W>, grid, dim3(W::NT), st, a);
+}
+
 
 // The two regions of a plan in one launch: workgroups [0, n1) run tile T1
 // over region a1, the others tile T2 over region a2.  The hardware hands out
@@ -1377,6 +1563,16 @@ using T_256x256w4 = Tile<256, 256, 64, 2, 2, 2>;
 using T_64x64x2 = Tile<64, 64, 64, 2, 2, 2>;
 using T_64x128x2 = Tile<64, 128, 64, 2, 2, 2>;
 using T_128x64x2 = Tile<128, 64, 64, 2, 2, 2>;
+// skinny-M tiles with the K range split across 4 waves (uK = 256 per
+// workgroup step; see WSplit)
+using W_16x64 = WSplit<16, 64, 4, 3, false>;
+using W_32x64 = WSplit<32, 64, 4, 3, false>;
+using W_64x64 = WSplit<64, 64, 4, 2, false>;
+using W_16x128 = WSplit<16, 128, 4, 2, false>;
+using X_16x64 = WSplit<16, 64, 4, 3, true>;
+using X_32x64 = WSplit<32, 64, 4, 3, true>;
+using X_64x64 = WSplit<64, 64, 4, 2, true>;
+using X_16x128 = WSplit<16, 128, 4, 2, true>;
 // the same tiles for B given as N x K
 using U_256x256 = Tile<256, 256, 64, 4, 2, 2, false, true>;
 using U_256x128 = Tile<256, 128, 64, 4, 2, 2, true, true>;
@@ -1401,6 +1597,8 @@ using U_128x64x2 = Tile<128, 64, 64, 2, 2, 2, false, true>;
         NAME, T::BM, T::BN, T::BK, T::NT, T::LDS, T::FUSED, T::BT, (const void*)&gemm_tile_kernel<T>, \
             &launch_tile<T>                                                                                \
     }
+#define MKP_WSPLIT(NAME, W) \
+    { NAME, W::BM, W::BN, W::BK, W::NT, W::LDS, false, W::BT, (const void*)&gemm_wsplit_kernel<W>, &launch_wsplit<W> }
 
 const KernelInfo g_kernels[] = {
     MKP_KERNEL("m256n256k64", T_256x256),
@@ -1419,6 +1617,10 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m64n64k64x2", T_64x64x2),
     MKP_KERNEL("m64n128k64x2", T_64x128x2),
     MKP_KERNEL("m128n64k64x2", T_128x64x2),
+    MKP_WSPLIT("m16n64k256", W_16x64),
+    MKP_WSPLIT("m32n64k256", W_32x64),
+    MKP_WSPLIT("m64n64k256", W_64x64),
+    MKP_WSPLIT("m16n128k256", W_16x128),
     MKP_KERNEL("m256n256k64_nk", U_256x256),
     MKP_KERNEL("m256n128k64_nk", U_256x128),
     MKP_KERNEL("m128n256k64_nk", U_128x256),
@@ -1435,6 +1637,10 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m64n64k64x2_nk", U_64x64x2),
     MKP_KERNEL("m64n128k64x2_nk", U_64x128x2),
     MKP_KERNEL("m128n64k64x2_nk", U_128x64x2),
+    MKP_WSPLIT("m16n64k256_nk", X_16x64),
+    MKP_WSPLIT("m32n64k256_nk", X_32x64),
+    MKP_WSPLIT("m64n64k256_nk", X_64x64),
+    MKP_WSPLIT("m16n128k256_nk", X_16x128),
 };
 
 #endif  // single-tile registry

@@ -36,6 +36,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Tile<uM, uN, uK, waves_m, waves_n, stages, preread, N x K B[, convolution]>
 TILE = re.compile(r"Tile<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (?:true|false), (true|false)(?:, (true|false))?>")
+# skinny-M tiles whose waves split K: WSplit<uM, uN, waves, stages, N x K B>,
+# named m<uM>n<uN>k<64 * waves>
+WSPLIT = re.compile(r"WSplit<(\d+), (\d+), (\d+), (\d+), (true|false)>")
 # tiles the library also has with another stage count, named with "x<stages>"
 DEEP = {(128, 128, 4), (64, 64, 2), (64, 128, 2), (128, 64, 2)}
 # tiles the library also has on fewer, larger waves, named with "w<waves>"
@@ -57,6 +60,10 @@ def read_counter(d: str, counter: str):
 
 
 def lib_name(kernel_name: str):
+    w = WSPLIT.search(kernel_name)
+    if w and "gemm_wsplit_kernel" in kernel_name:
+        name = f"m{w.group(1)}n{w.group(2)}k{64 * int(w.group(3))}"
+        return name + ("_nk" if w.group(5) == "true" else "")
     m = TILE.search(kernel_name)
     if not m or "gemm_tile_kernel" not in kernel_name:
         return None

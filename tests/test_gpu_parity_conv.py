@@ -85,13 +85,14 @@ def test_conv_geometries(mkp, case):
 
 @pytest.mark.parametrize("C", [64, 40, 3])
 def test_conv_each_kernel_forced(mkp, C):
-    """The convolution form of every N x K tile, on the direct-load (C = 64),
+    """The convolution form of every N x K tile that has one, on the direct-load (C = 64),
     8-channel (C = 40) and element (C = 3) paths."""
     rng = np.random.default_rng(C)
     x = bits(rng, (2, 9, 8, C))
     w = bits(rng, (70, 3, 3, C))
     try:
-        for name in [n for n in mkp.mkp_kernel_names() if n.endswith("_nk")]:
+        # (the skinny tiles whose waves split K, uK = 256, have no convolution form)
+        for name in [n for n in mkp.mkp_kernel_names() if n.endswith("_nk") and "k256" not in n]:
             mkp.mkp_set_option("force_kernel", name)
             run_conv(mkp, x, w, (1, 1), (1, 1), (1, 1), what=name)
     finally:

@@ -19,7 +19,10 @@ def _registry():
         tiles[m.group(1)] = ", ".join(args)
     kernels = re.findall(r'MKP_KERNEL\("([^"]+)", (\w+)\)', text)
     convs = re.findall(r'MKP_CONV\("([^"]+)", (\w+)\)', text)
-    return tiles, kernels, convs
+    wsplit = {m.group(1): ", ".join(a.strip() for a in m.group(2).split(","))
+              for m in re.finditer(r"using (\w+) = WSplit<([^>]*)>;", text)}
+    wkernels = re.findall(r'MKP_WSPLIT\("([^"]+)", (\w+)\)', text)
+    return tiles, kernels, convs, wsplit, wkernels
 
 
 def _demangled(tile_args):
@@ -28,9 +31,13 @@ def _demangled(tile_args):
 
 
 def test_counter_tool_names_every_kernel():
-    tiles, kernels, convs = _registry()
-    assert len(kernels) >= 20 and convs
+    tiles, kernels, convs, wsplit, wkernels = _registry()
+    assert len(kernels) >= 20 and convs and wkernels
     for name, t in kernels:
         assert pmc.lib_name(_demangled(tiles[t])) == name, (name, tiles[t])
     for twin, t in convs:
         assert pmc.lib_name(_demangled(tiles[t])) == twin + "_conv", (twin, tiles[t])
+    for name, w in wkernels:
+        demangled = (f"void mkp::(anonymous namespace)::gemm_wsplit_kernel<mkp::(anonymous namespace)::"
+                     f"WSplit<{wsplit[w]}> >(mkp::KArgs)")
+        assert pmc.lib_name(demangled) == name, (name, wsplit[w])
