@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <chrono>
 #include <climits>
@@ -1412,14 +1413,21 @@ int mkp_calibrate(const char* path, int max_points) {
     int npts = (int)(sizeof(grid_t) / sizeof(grid_t[0]));
     if (max_points > 0) npts = std::min(npts, max_points);
     const int64_t kmax_cap = 16384;
-    // the skinny tiles' layout splits K (below): its K is the split depth
+    // the few-row layouts split K (below): their K is the split depth
     // times the splits, allowed up to 65536
     const int64_t kmax_split = 65536;
 
-    // buffers sized for the largest point of any kernel
-    size_t a_elems = 0, b_elems = 0, c_elems = 0;
+    // Every kernel is measured on several wave layouts: square (tm x tn
+    // tiles, tm about sqrt(slots)), where each A and B tile is shared by
+    // many workgroups of the wave, and one for each row class r (r tile
+    // rows, at most 32 tile columns, the rest of the slots as K splits), as
+    // an output of a few rows runs, where each B tile is shared by r
+    // workgroups at most.
+    static const int row_classes[] = {1, 2, 4, 8};
+    constexpr int nclass = (int)(sizeof(row_classes) / sizeof(row_classes[0]));
+    size_t a_elems = 0, b_elems = 0, c_elems = 0;   // buffers for the largest point of any kernel
     struct Shape { int tm, tn, s; };
-    std::vector<Shape> shapes;
+    std::vector<std::array<Shape, nclass + 1>> shapes;   // [nclass]: square
     std::vector<int> occ;
     for (int i = 0; i < kernel_count(); ++i) {
         const KernelInfo& ki = kernel_info(i);
@@ -1428,25 +1436,26 @@ int mkp_calibrate(const char* path, int max_points) {
         if (he != hipSuccess || n < 1) n = 1;
         occ.push_back(n);
         const int slots = cus * n;
-        Shape s;
-        if (ki.uM <= 32) {
-            // skinny tiles serve outputs of a few rows, where the wave is
-            // filled by K splits: one tile row, at most 32 tile columns, the
-            // rest of the slots as splits (as such a call runs)
-            int tn = std::min(slots, 32);
-            while (slots % tn) --tn;
-            s = {1, tn, slots / tn};
-        } else {
-            int tm = (int)std::floor(std::sqrt((double)slots));
-            while (slots % tm) --tm;
-            s = {tm, slots / tm, 1};
+        std::array<Shape, nclass + 1> sh;
+        for (int c = 0; c < nclass; ++c) {
+            const int r = std::min(row_classes[c], slots);
+            const int cols = slots / r;
+            int tn = std::min(cols, 32);
+            while (cols % tn) --tn;
+            sh[c] = Shape{r, tn, cols / tn};
         }
-        shapes.push_back(s);
-        const int64_t M = (int64_t)s.tm * ki.uM, N = (int64_t)s.tn * ki.uN;
-        const int64_t K = std::min<int64_t>((int64_t)grid_t[npts - 1] * ki.uK * s.s, s.s > 1 ? kmax_split : kmax_cap);
-        a_elems = std::max(a_elems, (size_t)(M * K));
-        b_elems = std::max(b_elems, (size_t)(K * N));
-        c_elems = std::max(c_elems, (size_t)(M * N * s.s));
+        int tm = (int)std::floor(std::sqrt((double)slots));
+        while (slots % tm) --tm;
+        sh[nclass] = Shape{tm, slots / tm, 1};
+        shapes.push_back(sh);
+        for (const Shape& s : shapes.back()) {
+            const int64_t M = (int64_t)s.tm * ki.uM, N = (int64_t)s.tn * ki.uN;
+            const int64_t K =
+                std::min<int64_t>((int64_t)grid_t[npts - 1] * ki.uK * s.s, s.s > 1 ? kmax_split : kmax_cap);
+            a_elems = std::max(a_elems, (size_t)(M * K));
+            b_elems = std::max(b_elems, (size_t)(K * N));
+            c_elems = std::max(c_elems, (size_t)(M * N * s.s));
+        }
     }
     // Operands come from a pool of at least 2 GiB (C from one of 1 GiB) whose
     // slices rotate from launch to launch, so every timed launch streams its
@@ -1482,6 +1491,7 @@ int mkp_calibrate(const char* path, int max_points) {
     PerfTable t;
     t.cus = cus;
     t.splits = {1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32};
+    t.row_classes.assign(row_classes, row_classes + nclass);
     hipError_t err = hipSuccess;
     // launch overhead: a one-workgroup kernel back to back
     t.launch_us = time_launches([&] { return launch_zero_fill(dC, 1, 0, 1, 1, 1, nullptr); }, 20, 200, &err);
@@ -1542,86 +1552,101 @@ int mkp_calibrate(const char* path, int max_points) {
         k.wg_per_cu = occ[i];
         k.lib_index = i;
         k.bt = ki.bt;
-        const Shape s = shapes[i];
-        for (int p = 0; p < npts; ++p) {
-            const int tt = grid_t[p];
-            const int64_t K = (int64_t)tt * ki.uK * s.s;
-            if (K > (s.s > 1 ? kmax_split : kmax_cap)) break;
-            KArgs a{};
-            a.M = s.tm * ki.uM;
-            a.N = s.tn * ki.uN;
-            a.K = (int)K;
-            a.lda = K;
-            a.ldb = ki.bt ? a.K : a.N;
-            a.ldc = a.N;
-            a.tiles_m = s.tm;
-            a.tiles_n = s.tn;
-            a.steps_per_split = tt;
-            a.splits = s.s;
-            a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;   // each split's partial tile
-            a.batch = 1;
-            a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
-            const dim3 grid((unsigned)(s.tm * s.tn * s.s));
-            // single-launch time, then enough repetitions for ~2 ms
-            auto launch = [&] {
-                next_operands(a);
-                return ki.launch(a, grid, nullptr);
-            };
-            double us = time_launches(launch, 3, 3, &err);
-            if (err != hipSuccess) break;
-            int reps = (int)std::min(200.0, std::max(5.0, 2000.0 / std::max(us, 1.0)));
-            us = time_launches(launch, 20, reps, &err);
-            if (err != hipSuccess) break;
-            k.pts.emplace_back((double)tt, std::max(us - t.launch_us, 0.05));
-        }
-        // partial last wave, at 16 K steps, relative to a full wave of the
-        // same depth: a wave filling a fraction f of the slots on its own
-        // (tail), and the time f adds after one full wave (tailx)
-        const int t_ref = 16;
-        double g_ref = 0;
-        for (auto& pt : k.pts)
-            if (pt.first == t_ref) g_ref = pt.second;
-        if (err == hipSuccess && g_ref > 0) {
-            static const double fills[] = {1.0 / 16, 1.0 / 8, 1.0 / 4, 1.0 / 2, 3.0 / 4};
-            const int slots = s.tm * s.tn * s.s;
-            int prev_tn = 0;
-            for (double f : fills) {
-                const int tn = std::max(1, (int)std::lround(f * s.tn));
-                if (tn == prev_tn || tn >= s.tn) continue;
-                prev_tn = tn;
-                double us[2];
-                for (int after = 0; after < 2 && err == hipSuccess; ++after) {
-                    const int cols = tn + (after ? s.tn : 0);
-                    KArgs a{};
-                    a.M = s.tm * ki.uM;
-                    a.N = cols * ki.uN;
-                    a.K = t_ref * ki.uK * s.s;
-                    a.lda = a.K;
-                    a.ldb = ki.bt ? a.K : a.N;
-                    a.ldc = a.N;
-                    a.tiles_m = s.tm;
-                    a.tiles_n = cols;
-                    a.steps_per_split = t_ref;
-                    a.splits = s.s;
-                    a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;
-                    a.batch = 1;
-                    a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
-                    const dim3 grid((unsigned)(s.tm * cols * s.s));
-                    us[after] = time_launches(
-                        [&] {
-                            next_operands(a);
-                            return ki.launch(a, grid, nullptr);
-                        },
-                        20, 50, &err);
-                }
+        k.by_rows.assign(nclass, Curves{});
+        for (int layout = 0; layout <= nclass && err == hipSuccess; ++layout) {
+            const Shape s = shapes[i][layout];
+            Curves square;
+            Curves& cv = layout < nclass ? k.by_rows[layout] : square;
+            auto& pts = cv.pts;
+            auto& tail = cv.tail;
+            auto& tailx = cv.tailx;
+            for (int p = 0; p < npts; ++p) {
+                const int tt = grid_t[p];
+                const int64_t K = (int64_t)tt * ki.uK * s.s;
+                if (K > (s.s > 1 ? kmax_split : kmax_cap)) break;
+                KArgs a{};
+                a.M = s.tm * ki.uM;
+                a.N = s.tn * ki.uN;
+                a.K = (int)K;
+                a.lda = K;
+                a.ldb = ki.bt ? a.K : a.N;
+                a.ldc = a.N;
+                a.tiles_m = s.tm;
+                a.tiles_n = s.tn;
+                a.steps_per_split = tt;
+                a.splits = s.s;
+                a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;   // each split's partial tile
+                a.batch = 1;
+                a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+                const dim3 grid((unsigned)(s.tm * s.tn * s.s));
+                // single-launch time, then enough repetitions for ~2 ms
+                auto launch = [&] {
+                    next_operands(a);
+                    return ki.launch(a, grid, nullptr);
+                };
+                double us = time_launches(launch, 3, 3, &err);
                 if (err != hipSuccess) break;
-                const double fill = (double)(s.tm * tn * s.s) / slots;
-                auto clamp = [](double r) { return std::min(1.0, std::max(0.02, r)); };
-                k.tail.emplace_back(fill, clamp(std::max(us[0] - t.launch_us, 0.05) / g_ref));
-                k.tailx.emplace_back(fill, clamp((us[1] - t.launch_us - g_ref) / g_ref));
+                int reps = (int)std::min(200.0, std::max(5.0, 2000.0 / std::max(us, 1.0)));
+                us = time_launches(launch, 20, reps, &err);
+                if (err != hipSuccess) break;
+                pts.emplace_back((double)tt, std::max(us - t.launch_us, 0.05));
+            }
+            // partial last wave, at 16 K steps, relative to a full wave of the
+            // same depth: a wave filling a fraction f of the slots on its own
+            // (tail), and the time f adds after one full wave (tailx)
+            const int t_ref = 16;
+            double g_ref = 0;
+            for (auto& pt : pts)
+                if (pt.first == t_ref) g_ref = pt.second;
+            if (err == hipSuccess && g_ref > 0) {
+                static const double fills[] = {1.0 / 16, 1.0 / 8, 1.0 / 4, 1.0 / 2, 3.0 / 4};
+                const int slots = s.tm * s.tn * s.s;
+                int prev_tn = 0;
+                for (double f : fills) {
+                    const int tn = std::max(1, (int)std::lround(f * s.tn));
+                    if (tn == prev_tn || tn >= s.tn) continue;
+                    prev_tn = tn;
+                    double us[2];
+                    for (int after = 0; after < 2 && err == hipSuccess; ++after) {
+                        const int cols = tn + (after ? s.tn : 0);
+                        KArgs a{};
+                        a.M = s.tm * ki.uM;
+                        a.N = cols * ki.uN;
+                        a.K = t_ref * ki.uK * s.s;
+                        a.lda = a.K;
+                        a.ldb = ki.bt ? a.K : a.N;
+                        a.ldc = a.N;
+                        a.tiles_m = s.tm;
+                        a.tiles_n = cols;
+                        a.steps_per_split = t_ref;
+                        a.splits = s.s;
+                        a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;
+                        a.batch = 1;
+                        a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+                        const dim3 grid((unsigned)(s.tm * cols * s.s));
+                        us[after] = time_launches(
+                            [&] {
+                                next_operands(a);
+                                return ki.launch(a, grid, nullptr);
+                            },
+                            20, 50, &err);
+                    }
+                    if (err != hipSuccess) break;
+                    const double fill = (double)(s.tm * tn * s.s) / slots;
+                    auto clamp = [](double r) { return std::min(1.0, std::max(0.02, r)); };
+                    tail.emplace_back(fill, clamp(std::max(us[0] - t.launch_us, 0.05) / g_ref));
+                    tailx.emplace_back(fill, clamp((us[1] - t.launch_us - g_ref) / g_ref));
+                }
+            }
+            if (layout == nclass) {
+                k.pts = square.pts;
+                k.tail = square.tail;
+                k.tailx = square.tailx;
             }
         }
         t.kernels.push_back(k);
+        std::fprintf(stderr, "[calibrate] %d/%d %s\n", i + 1, kernel_count(), ki.name);
+        std::fflush(stderr);
     }
     // sustained ceilings: MFMA on random operands, streaming copy
     if (err == hipSuccess) {

@@ -2,6 +2,7 @@
 #include "planner.h"
 
 #include <algorithm>
+#include <array>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
@@ -55,7 +56,13 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
     std::istringstream in(text);
     std::string raw;
     int lineno = 0;
-    std::vector<std::pair<std::string, std::vector<std::pair<double, double>>>> gs, tails, tailxs;
+    struct CurveLine {
+        int kind;   // 0 g, 1 tail, 2 tailx
+        int rows;   // 0: square wave
+        std::string name;
+        std::vector<std::pair<double, double>> pts;
+    };
+    std::vector<CurveLine> curves;
     std::vector<std::pair<std::string, std::string>> pair_names;
     while (std::getline(in, raw)) {
         ++lineno;
@@ -64,7 +71,7 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
         std::istringstream ls(line);
         std::string key;
         if (!(ls >> key)) continue;
-        auto fail = [&](const char* what) {
+        auto fail = [&](const std::string& what) {
             err = "table line " + std::to_string(lineno) + ": " + what;
             return false;
         };
@@ -113,76 +120,79 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err) {
             for (auto& e : t.kernels)
                 if (e.name == k.name) return fail("duplicate kernel");
             t.kernels.push_back(k);
-        } else if (key == "tail" || key == "tailx") {
-            // tail[x] <kernel> <f>:<ratio> ...  (partial-wave time relative to a full wave)
-            std::string name, tok;
-            if (!(ls >> name)) return fail("bad tail line");
-            std::vector<std::pair<double, double>> pts;
+        } else if (key == "rows") {
+            // rows <r1> <r2> ...: tile-row classes with curves of their own
+            int r;
+            while (ls >> r) {
+                if (r <= 0 || r > 4096 || (!t.row_classes.empty() && r <= t.row_classes.back()) || t.row_classes.size() >= 7)
+                    return fail("rows must be at most 7 increasing counts in 1..4096");
+                t.row_classes.push_back(r);
+            }
+        } else if (key.rfind("g", 0) == 0 || key.rfind("tail", 0) == 0) {
+            // g[@r] <kernel> <t>:<us> ...           (full-wave time per K steps)
+            // tail[x][@r] <kernel> <f>:<ratio> ...  (partial-wave time relative to a full wave)
+            CurveLine cl;
+            const auto at = key.find('@');
+            const std::string base = key.substr(0, at);
+            cl.kind = base == "g" ? 0 : base == "tail" ? 1 : base == "tailx" ? 2 : -1;
+            if (cl.kind < 0) return fail("unknown key");
+            cl.rows = 0;
+            if (at != std::string::npos && ((cl.rows = std::atoi(key.c_str() + at + 1)) <= 0))
+                return fail("bad row class in " + key);
+            std::string tok;
+            if (!(ls >> cl.name)) return fail("bad curve line");
             while (ls >> tok) {
                 auto c = tok.find(':');
-                if (c == std::string::npos) return fail("bad tail point");
-                double f = std::atof(tok.substr(0, c).c_str());
-                double r = std::atof(tok.substr(c + 1).c_str());
-                if (!(f > 0 && f < 1) || !(r > 0 && r <= 1)) return fail("bad tail value");
-                pts.emplace_back(f, r);
+                if (c == std::string::npos) return fail("bad curve point");
+                double x = std::atof(tok.substr(0, c).c_str());
+                double y = std::atof(tok.substr(c + 1).c_str());
+                if (cl.kind == 0 ? !(x > 0) || !(y >= 0) : !(x > 0 && x < 1) || !(y > 0 && y <= 1))
+                    return fail(cl.kind == 0 ? "bad g value" : "bad tail value");
+                cl.pts.emplace_back(x, y);
             }
-            (key == "tail" ? tails : tailxs).emplace_back(name, pts);
+            curves.push_back(std::move(cl));
         } else if (key == "pair") {
             // pair <kernel a> <kernel b>: a and b can share one launch
             std::string a, b;
             if (!(ls >> a >> b) || a == b) return fail("bad pair line");
             pair_names.emplace_back(a, b);
-        } else if (key == "g") {
-            std::string name, tok;
-            if (!(ls >> name)) return fail("bad g line");
-            std::vector<std::pair<double, double>> pts;
-            while (ls >> tok) {
-                auto c = tok.find(':');
-                if (c == std::string::npos) return fail("bad g point");
-                double tt = std::atof(tok.substr(0, c).c_str());
-                double v = std::atof(tok.substr(c + 1).c_str());
-                if (!(tt > 0) || !(v >= 0)) return fail("bad g value");
-                pts.emplace_back(tt, v);
-            }
-            gs.emplace_back(name, pts);
         } else {
             return fail("unknown key");
         }
     }
-    for (auto& g : gs) {
-        bool found = false;
-        for (auto& k : t.kernels)
-            if (k.name == g.first) {
-                k.pts.insert(k.pts.end(), g.second.begin(), g.second.end());
-                found = true;
-            }
-        if (!found) {
-            err = "g line for unknown kernel " + g.first;
-            return false;
-        }
-    }
-    for (int which = 0; which < 2; ++which)
-        for (auto& tl : which ? tailxs : tails) {
-            bool found = false;
-            for (auto& k : t.kernels)
-                if (k.name == tl.first) {
-                    auto& dst = which ? k.tailx : k.tail;
-                    dst.insert(dst.end(), tl.second.begin(), tl.second.end());
-                    found = true;
-                }
-            if (!found) {
-                err = "tail line for unknown kernel " + tl.first;
+    for (auto& k : t.kernels) k.by_rows.assign(t.row_classes.size(), Curves{});
+    for (auto& cl : curves) {
+        int set = -1;   // -1: square
+        if (cl.rows > 0) {
+            for (size_t i = 0; i < t.row_classes.size(); ++i)
+                if (t.row_classes[i] == cl.rows) set = (int)i;
+            if (set < 0) {
+                err = "curve for row class " + std::to_string(cl.rows) + " not listed in rows";
                 return false;
             }
         }
+        bool found = false;
+        for (auto& k : t.kernels)
+            if (k.name == cl.name) {
+                auto& dst = set < 0 ? (cl.kind == 0 ? k.pts : cl.kind == 1 ? k.tail : k.tailx)
+                                    : (cl.kind == 0 ? k.by_rows[set].pts : cl.kind == 1 ? k.by_rows[set].tail
+                                                                                         : k.by_rows[set].tailx);
+                dst.insert(dst.end(), cl.pts.begin(), cl.pts.end());
+                found = true;
+            }
+        if (!found) {
+            err = "curve line for unknown kernel " + cl.name;
+            return false;
+        }
+    }
     for (auto& k : t.kernels) {
-        std::sort(k.tail.begin(), k.tail.end());
-        std::sort(k.tailx.begin(), k.tailx.end());
+        for (auto* v : {&k.tail, &k.tailx, &k.pts}) std::sort(v->begin(), v->end());
+        for (auto& c : k.by_rows)
+            for (auto* v : {&c.tail, &c.tailx, &c.pts}) std::sort(v->begin(), v->end());
         if (k.pts.empty()) {
             err = "kernel " + k.name + " has no g points";
             return false;
         }
-        std::sort(k.pts.begin(), k.pts.end());
     }
     if (t.kernels.empty()) {
         err = "table has no kernels";
@@ -227,19 +237,26 @@ std::string table_to_text(const PerfTable& t) {
     for (auto& k : t.kernels)
         o << "kernel " << k.name << " " << k.uM << " " << k.uN << " " << k.uK << " " << k.wg_per_cu
           << (k.bt ? " nk" : "") << "\n";
-    for (auto& k : t.kernels) {
-        o << "g " << k.name;
-        for (auto& p : k.pts) o << " " << p.first << ":" << p.second;
+    if (!t.row_classes.empty()) {
+        o << "rows";
+        for (int r : t.row_classes) o << " " << r;
         o << "\n";
     }
-    for (int which = 0; which < 2; ++which)
-        for (auto& k : t.kernels) {
-            const auto& pts = which ? k.tailx : k.tail;
-            if (pts.empty()) continue;
-            o << (which ? "tailx " : "tail ") << k.name;
-            for (auto& p : pts) o << " " << p.first << ":" << p.second;
-            o << "\n";
-        }
+    static const char* const kCurve[] = {"g", "tail", "tailx"};
+    for (int set = -1; set < (int)t.row_classes.size(); ++set)
+        for (int kind = 0; kind < 3; ++kind)
+            for (auto& k : t.kernels) {
+                const Curves* c = set >= 0 && set < (int)k.by_rows.size() ? &k.by_rows[set] : nullptr;
+                if (set >= 0 && !c) continue;
+                const auto& pts = kind == 0 ? (c ? c->pts : k.pts) : kind == 1 ? (c ? c->tail : k.tail)
+                                                                                : (c ? c->tailx : k.tailx);
+                if (pts.empty()) continue;
+                o << kCurve[kind];
+                if (set >= 0) o << "@" << t.row_classes[set];
+                o << " " << k.name;
+                for (auto& p : pts) o << " " << p.first << ":" << p.second;
+                o << "\n";
+            }
     for (auto& pr : t.pairs) o << "pair " << t.kernels[pr.first].name << " " << t.kernels[pr.second].name << "\n";
     return o.str();
 }
@@ -280,8 +297,7 @@ double merged_makespan(int64_t S, int64_t n1, double d1, int64_t n2, double d2) 
 
 // Piecewise-linear in t between measured points; the first point's value
 // below it; the last segment's slope beyond the last point.
-double g_predict(const TableKernel& k, double t) {
-    const auto& p = k.pts;
+double g_predict_pts(const std::vector<std::pair<double, double>>& p, double t) {
     if (p.size() == 1) return p[0].second * t / p[0].first;
     if (t <= p[0].first) return p[0].second;
     for (size_t i = 1; i < p.size(); ++i) {
@@ -294,6 +310,26 @@ double g_predict(const TableKernel& k, double t) {
     const double t0 = p[p.size() - 2].first, v0 = p[p.size() - 2].second;
     const double t1 = p.back().first, v1 = p.back().second;
     return v1 + (v1 - v0) * (t - t1) / (t1 - t0);
+}
+
+double g_predict(const TableKernel& k, double t) { return g_predict_pts(k.pts, t); }
+
+int curve_set(const PerfTable& tab, const TableKernel& k, int64_t m) {
+    const int classes = (int)tab.row_classes.size();
+    const int64_t rows = ceil_div(m, k.uM);
+    for (int i = 0; i < classes; ++i)
+        if (rows <= tab.row_classes[i])
+            return i < (int)k.by_rows.size() && !k.by_rows[i].pts.empty() ? i : classes;
+    return classes;
+}
+
+const std::vector<std::pair<double, double>>& set_pts(const TableKernel& k, int set) {
+    return set >= 0 && set < (int)k.by_rows.size() ? k.by_rows[set].pts : k.pts;
+}
+
+const std::vector<std::pair<double, double>>& set_tail(const TableKernel& k, int set, bool after_full) {
+    if (set >= 0 && set < (int)k.by_rows.size()) return after_full ? k.by_rows[set].tailx : k.by_rows[set].tail;
+    return after_full ? k.tailx : k.tail;
 }
 
 double tail_ratio(const std::vector<std::pair<double, double>>& p, double f) {
@@ -309,16 +345,17 @@ double tail_ratio(const std::vector<std::pair<double, double>>& p, double f) {
     return 1.0;
 }
 
-double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots) {
+double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots, int set) {
     const int64_t full = tasks / slots, rem = tasks % slots;
     if (!rem) return (double)full;
-    return (double)full + tail_ratio(full ? k.tailx : k.tail, (double)rem / (double)slots);
+    return (double)full + tail_ratio(set_tail(k, set, full > 0), (double)rem / (double)slots);
 }
 
 // Cost of one region served by one kernel with a requested split factor:
 //   launch + (full waves + partial last wave) * g(steps) [+ split-K reduction]
 // (with a kernel that has no tail points the wave term is ceil(tasks/slots),
-// the page's f_wave).
+// the page's f_wave).  A region of few tile rows takes g and the tail ratios
+// from the kernel's curves for that many rows (curve_set).
 double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K, int64_t batch,
                    int s_req, Region* out) {
     const TableKernel& k = tab.kernels[kernel];
@@ -328,8 +365,9 @@ double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64
     const int64_t tasks = ceil_div(m, k.uM) * ceil_div(n, k.uN) * s_eff * batch;
     const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
     const int64_t waves = ceil_div(tasks, slots);
-    const double wf = wave_factor(k, tasks, slots);
-    double c = tab.launch_us + wf * g_predict(k, (double)per);
+    const int set = curve_set(tab, k, m);
+    const double wf = wave_factor(k, tasks, slots, set);
+    double c = tab.launch_us + wf * g_predict_pts(set_pts(k, set), (double)per);
     if (s_eff > 1)
         c += tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch /
                                      (tab.red_gbps * 1e3);
@@ -370,17 +408,39 @@ struct Searcher {
     int64_t batch, M, N, K;
     int64_t evaluated = 0;
 
+    // Curve sets: one per tile-row class of the table, then the square one.
+    // Per kernel, a class whose curves it lacks maps to the square set.
+    static constexpr int kSets = 8;
+    int nclass = 0;   // row classes; set index nclass = square
+    // g per row class (the square g for a class the kernel lacks, and at
+    // index nclass), and the smallest g of the sets a region of that class
+    // or more rows can take
     struct SplitChoice {
         int s_eff;
         int per;
-        double g;
+        std::array<double, kSets> g, glb;
+    };
+    struct Floors {
+        double tmin_alone = 1.0, tmin_after = 1.0;   // smallest partial-wave ratio (tail, tailx)
+        double rho = 1.0;                            // smallest partial-wave ratio per filled slot
+        double gmin = std::numeric_limits<double>::infinity();    // smallest g over the splits
+        double sgmin = std::numeric_limits<double>::infinity();   // smallest s * g over the splits
+        void merge(const Floors& o) {
+            tmin_alone = std::min(tmin_alone, o.tmin_alone);
+            tmin_after = std::min(tmin_after, o.tmin_after);
+            rho = std::min(rho, o.rho);
+            gmin = std::min(gmin, o.gmin);
+            sgmin = std::min(sgmin, o.sgmin);
+        }
     };
     std::vector<std::vector<SplitChoice>> sc;   // per kernel: distinct usable splits
     std::vector<double> min_g;                   // per kernel: cheapest single (possibly partial) wave
     std::vector<double> rate;                    // per kernel: lowest cost per output element
-    std::vector<double> tmin_alone, tmin_after;  // per kernel: smallest partial-wave ratio (tail, tailx)
-    std::vector<double> rho;                     // per kernel: smallest partial-wave ratio per filled slot
-    std::vector<double> gmin, sgmin;             // per kernel: smallest g and s * g over its splits
+    // per kernel and row class: bounds of that class's curves (fl), and of
+    // every set a region of that class or more rows may take (fls)
+    std::vector<std::array<Floors, kSets>> fl, fls;
+    std::vector<std::array<int8_t, kSets>> set_map;   // per kernel: row class -> curve set
+    std::vector<int8_t> class_by_rows;                // tile rows (up to the largest class) -> row class
     std::vector<FastDiv> dm, dn, dslots;         // per kernel: uM, uN and its slots as dividers
     double lb_region = 0.0;                      // lower bound of any region's cost
     double min_rate = 0.0;                       // lowest rate over allowed kernels
@@ -399,11 +459,17 @@ struct Searcher {
         sc.resize(nk);
         min_g.assign(nk, std::numeric_limits<double>::infinity());
         rate.assign(nk, std::numeric_limits<double>::infinity());
-        tmin_alone.assign(nk, 1.0);
-        tmin_after.assign(nk, 1.0);
-        rho.assign(nk, 1.0);
-        gmin.assign(nk, std::numeric_limits<double>::infinity());
-        sgmin.assign(nk, std::numeric_limits<double>::infinity());
+        nclass = std::min<int>((int)tab.row_classes.size(), kSets - 1);
+        if (nclass > 0) {
+            class_by_rows.assign((size_t)tab.row_classes[nclass - 1] + 1, 0);
+            for (int r = 0, c = 0; r <= tab.row_classes[nclass - 1]; ++r) {
+                while (r > tab.row_classes[c]) ++c;
+                class_by_rows[(size_t)r] = (int8_t)c;
+            }
+        }
+        fl.assign(nk, {});
+        fls.assign(nk, {});
+        set_map.assign(nk, {});
         dm.resize(nk);
         dn.resize(nk);
         dslots.resize(nk);
@@ -417,17 +483,22 @@ struct Searcher {
             dm[ki].set(kk.uM);
             dn[ki].set(kk.uN);
             dslots[ki].set((int64_t)tab.cus * kk.wg_per_cu);
+            for (int c = 0; c <= nclass; ++c)
+                set_map[ki][c] = (int8_t)(c < nclass && c < (int)kk.by_rows.size() && !kk.by_rows[c].pts.empty()
+                                              ? c : nclass);
             // a region's wave factor is at least tmin (one possibly partial
             // wave) and at least rho * tasks/slots (piecewise-linear ratios:
             // r(f)/f is smallest at a point or at f = 1)
-            double& rh = rho[ki];
-            for (auto& p : kk.tail) {
-                tmin_alone[ki] = std::min(tmin_alone[ki], p.second);
-                rh = std::min(rh, p.second / p.first);
-            }
-            for (auto& p : kk.tailx) {
-                tmin_after[ki] = std::min(tmin_after[ki], p.second);
-                rh = std::min(rh, p.second / p.first);
+            for (int c = 0; c <= nclass; ++c) {
+                Floors& f = fl[ki][c];
+                for (auto& p : set_tail(kk, set_map[ki][c] < nclass ? set_map[ki][c] : -1, false)) {
+                    f.tmin_alone = std::min(f.tmin_alone, p.second);
+                    f.rho = std::min(f.rho, p.second / p.first);
+                }
+                for (auto& p : set_tail(kk, set_map[ki][c] < nclass ? set_map[ki][c] : -1, true)) {
+                    f.tmin_after = std::min(f.tmin_after, p.second);
+                    f.rho = std::min(f.rho, p.second / p.first);
+                }
             }
             for (int s_req : req) {
                 // a factor above the K-step count is only kept when forced
@@ -438,13 +509,31 @@ struct Searcher {
                 bool dup = false;
                 for (auto& c : sc[ki]) dup |= c.s_eff == s_eff;
                 if (dup) continue;
-                sc[ki].push_back({s_eff, (int)per, g_predict(kk, (double)per)});
-                const double g = sc[ki].back().g;
-                min_g[ki] = std::min(min_g[ki], tmin_alone[ki] * g);
-                gmin[ki] = std::min(gmin[ki], g);
-                sgmin[ki] = std::min(sgmin[ki], (double)s_eff * g);
-                const double slots = (double)tab.cus * kk.wg_per_cu;
-                rate[ki] = std::min(rate[ki], rh * (double)s_eff * g / (slots * kk.uM * kk.uN));
+                SplitChoice ch{s_eff, (int)per, {}, {}};
+                ch.g[nclass] = g_predict(kk, (double)per);
+                for (int c = 0; c < nclass; ++c)
+                    ch.g[c] = set_map[ki][c] < nclass ? g_predict_pts(kk.by_rows[c].pts, (double)per) : ch.g[nclass];
+                ch.glb[nclass] = ch.g[nclass];
+                for (int c = nclass - 1; c >= 0; --c) ch.glb[c] = std::min(ch.g[c], ch.glb[c + 1]);
+                sc[ki].push_back(ch);
+                for (int c = 0; c <= nclass; ++c) {
+                    Floors& f = fl[ki][c];
+                    f.gmin = std::min(f.gmin, ch.g[c]);
+                    f.sgmin = std::min(f.sgmin, (double)s_eff * ch.g[c]);
+                }
+            }
+            // a region of class c or more rows takes one of the sets of
+            // classes c, c+1, ... or the square one
+            fls[ki][nclass] = fl[ki][nclass];
+            for (int c = nclass - 1; c >= 0; --c) {
+                fls[ki][c] = fl[ki][c];
+                fls[ki][c].merge(fls[ki][c + 1]);
+            }
+            const Floors& f = fls[ki][0];   // every set
+            const double slots = (double)tab.cus * kk.wg_per_cu;
+            for (const SplitChoice& ch : sc[ki]) {
+                min_g[ki] = std::min(min_g[ki], f.tmin_alone * ch.glb[0]);
+                rate[ki] = std::min(rate[ki], f.rho * (double)ch.s_eff * ch.glb[0] / (slots * kk.uM * kk.uN));
             }
             lb_region = std::min(lb_region, tab.launch_us + min_g[ki]);
             min_rate = std::min(min_rate, rate[ki]);
@@ -464,6 +553,17 @@ struct Searcher {
 
     int64_t tiles_of(int k, int64_t m, int64_t n) const { return dm[k].ceil(m) * dn[k].ceil(n); }
 
+    // Row class of an m-row region on kernel k (nclass: above every class);
+    // it never falls as the region grows.
+    int class_of(int k, int64_t m) const {
+        if (nclass == 0) return 0;
+        const int64_t rows = dm[k].ceil(m);
+        return rows < (int64_t)class_by_rows.size() ? class_by_rows[(size_t)rows] : nclass;
+    }
+    // The curve set that prices it (as curve_set).
+    int set_of(int k, int64_t m) const { return set_map[k][class_of(k, m)]; }
+    double g_of(int k, const SplitChoice& c, int64_t m) const { return c.g[class_of(k, m)]; }
+
     double cost(int ki, const SplitChoice& c, int64_t m, int64_t n, Region* r) {
         ++evaluated;
         const TableKernel& k = tab.kernels[ki];
@@ -472,13 +572,16 @@ struct Searcher {
         int64_t rem;
         const int64_t full = dslots[ki].quot(tasks, rem);
         const int64_t waves = full + (rem != 0);
+        const int cls = class_of(ki, m), set = set_map[ki][cls];
+        const double g = c.g[cls];
         // full waves plus the partial last one (as wave_factor)
-        const double wf = rem ? (double)full + tail_ratio(full ? k.tailx : k.tail, (double)rem / (double)slots)
+        const double wf = rem ? (double)full + tail_ratio(set_tail(k, set < nclass ? set : -1, full > 0),
+                                                          (double)rem / (double)slots)
                               : (double)full;
         double v = tab.launch_us;
         if (opt.cost_mode == COST_WAVE) v += (double)waves;   // the page's f_wave alone
-        else if (opt.cost_mode == COST_PIPE) v += c.g;
-        else v += wf * c.g;
+        else if (opt.cost_mode == COST_PIPE) v += g;
+        else v += wf * g;
         v += red_cost(c.s_eff, m, n);
         if (r) {
             r->kernel = ki;
@@ -501,15 +604,19 @@ struct Searcher {
     // the reduction grows with the area).
     // With lin, also the bound from the wave factor's linear floor, rho *
     // tasks/slots, which grows with the cut at least at the kernel's
-    // lowest cost per output element.
+    // lowest cost per output element.  A larger region may be of a higher
+    // row class, so every set from this class on is bounded together.
     double lb_from(int a, const SplitChoice& c, int64_t m, int64_t n, double* lin = nullptr) const {
         const int64_t tasks = tiles_of(a, m, n) * c.s_eff * batch;
         int64_t rem;
         const int64_t full = dslots[a].quot(tasks, rem);
-        const double part = rem ? (full ? tmin_after[a] : tmin_alone[a]) : 0.0;
+        const int cls = class_of(a, m);
+        const Floors& f = fls[a][cls];
+        const double g = c.glb[cls];
+        const double part = rem ? (full ? f.tmin_after : f.tmin_alone) : 0.0;
         const double red = red_cost(c.s_eff, m, n);
-        if (lin) *lin = tab.launch_us + rho[a] * (double)tasks * dslots[a].inv * c.g + red;
-        return tab.launch_us + ((double)full + part) * c.g + red;
+        if (lin) *lin = tab.launch_us + f.rho * (double)tasks * dslots[a].inv * g + red;
+        return tab.launch_us + ((double)full + part) * g + red;
     }
 
     // Lower bound of any region 2 of m x n.
@@ -521,13 +628,16 @@ struct Searcher {
     // factor is at least the smallest partial-wave ratio and at least rho
     // times tasks/slots.
     double lb_split(int k, const SplitChoice& c, int64_t tiles, int64_t m, int64_t n) const {
-        const double w = std::max(tmin_alone[k], rho[k] * (double)(tiles * c.s_eff * batch) * dslots[k].inv);
-        return tab.launch_us + w * c.g + red_cost(c.s_eff, m, n);
+        const int cls = class_of(k, m);
+        const Floors& f = fl[k][cls];
+        const double w = std::max(f.tmin_alone, f.rho * (double)(tiles * c.s_eff * batch) * dslots[k].inv);
+        return tab.launch_us + w * c.g[cls] + red_cost(c.s_eff, m, n);
     }
     // ... and over all of k's splits (s >= 1, no reduction term).
     double lb_kernel(int k, int64_t m, int64_t n) const {
         const double tiles = (double)(tiles_of(k, m, n) * batch);
-        return tab.launch_us + std::max(tmin_alone[k] * gmin[k], rho[k] * tiles * sgmin[k] * dslots[k].inv);
+        const Floors& f = fl[k][class_of(k, m)];
+        return tab.launch_us + std::max(f.tmin_alone * f.gmin, f.rho * tiles * f.sgmin * dslots[k].inv);
     }
 
     // Both regions of a Pattern II cut in one launch over a kernel pair:
@@ -540,7 +650,8 @@ struct Searcher {
         (void)cost(b, c2, m2, n2, r2);
         const TableKernel& ka = tab.kernels[a];
         const int64_t S = (int64_t)tab.cus * ka.wg_per_cu;
-        return tab.launch_us + merged_makespan(S, r1->tasks, c1.g, r2->tasks, c2.g) + red_cost(r1->s, r1->m, r1->n) +
+        return tab.launch_us + merged_makespan(S, r1->tasks, g_of(a, c1, m1), r2->tasks, g_of(b, c2, m2)) +
+               red_cost(r1->s, r1->m, r1->n) +
                red_cost(r2->s, r2->m, r2->n);
     }
 
@@ -574,13 +685,16 @@ struct Searcher {
                         const int64_t m1 = dir == 0 ? cut : M, n1 = dir == 0 ? N : cut;
                         const int64_t m2 = dir == 0 ? M - cut : M, n2 = dir == 0 ? N : N - cut;
                         const int64_t t1 = ceil_div(m1, ka.uM) * ceil_div(n1, ka.uN) * c1s.s_eff * batch;
-                        const double own1 = (double)ceil_div(t1, S) * c1s.g;
+                        const double g1 = g_of(a, c1s, m1);
+                        const double own1 = (double)ceil_div(t1, S) * g1;
                         const double red1 = red_cost(c1s.s_eff, m1, n1);
-                        if (use_bound && tab.launch_us + own1 + red1 >= bound) break;
+                        // every larger cut: the smallest g of the sets it may take
+                        const double own1_lb = (double)ceil_div(t1, S) * c1s.glb[class_of(a, m1)];
+                        if (use_bound && tab.launch_us + own1_lb + red1 >= bound) break;
                         for (auto& c2s : sc[b]) {
                             const int64_t t2 = ceil_div(m2, kb.uM) * ceil_div(n2, kb.uN) * c2s.s_eff * batch;
                             const double lbv = tab.launch_us + red1 + red_cost(c2s.s_eff, m2, n2) +
-                                               std::max(own1, ((double)t1 * c1s.g + (double)t2 * c2s.g) / (double)S);
+                                               std::max(own1, ((double)t1 * g1 + (double)t2 * g_of(b, c2s, m2)) / (double)S);
                             if (use_bound && lbv >= bound) continue;
                             Region r1, r2;
                             const double v = fused_cost(a, c1s, m1, n1, b, c2s, m2, n2, &r1, &r2);
@@ -923,8 +1037,9 @@ Plan polymerize_grouped(const PerfTable& tab, int64_t M, int64_t K, const std::v
             const int64_t per = ceil_div(t3, sr);
             const int64_t s_eff = ceil_div(t3, per);
             const int64_t tasks = ceil_div(M, k.uM) * cols * s_eff;
-            const double wf = wave_factor(k, tasks, slots);
-            double c = tab.launch_us + wf * g_predict(k, (double)per);
+            const int set = curve_set(tab, k, M);
+            const double wf = wave_factor(k, tasks, slots, set);
+            double c = tab.launch_us + wf * g_predict_pts(set_pts(k, set), (double)per);
             if (s_eff > 1)
                 for (int64_t n : Ns)
                     c += tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)M * (double)n / (tab.red_gbps * 1e3);

@@ -21,6 +21,12 @@
 
 namespace mkp {
 
+// One kernel's curves measured on one wave layout.
+struct Curves {
+    std::vector<std::pair<double, double>> pts;           // (t, us), sorted by t; empty: not measured
+    std::vector<std::pair<double, double>> tail, tailx;   // as TableKernel::tail, tailx
+};
+
 struct TableKernel {
     std::string name;
     int uM = 0, uN = 0, uK = 0;
@@ -33,6 +39,11 @@ struct TableKernel {
     // the extra time a partial wave adds after full waves, whose stragglers
     // it overlaps.
     std::vector<std::pair<double, double>> tail, tailx;
+    // The same three curves measured on waves of few tile rows (the rest of
+    // the slots filled by tile columns, at most 32, then by K splits):
+    // by_rows[i] on a wave of PerfTable::row_classes[i] rows.  The curves
+    // above are measured on a square wave.
+    std::vector<Curves> by_rows;
     int lib_index = -1;                              // index in the kernel library, -1 if none
     bool conv_ok = false;                            // the library has a convolution form of it
 };
@@ -47,6 +58,10 @@ struct PerfTable {
     double tr_launch_us = 0.0;
     double tr_gbps = 0.0;
     std::vector<int> splits{1};
+    // Tile-row counts, ascending, with curves of their own: a region of r
+    // tile rows takes the curves of the smallest class >= r when its kernel
+    // has them, else the square ones.
+    std::vector<int> row_classes;
     bool pat_I = true, pat_IIM = true, pat_IIN = true;
     double mfma_tflops = 0.0;     // measured sustained bf16 MFMA rate (0: unknown)
     double hbm_gbps = 0.0;        // measured streaming-copy bandwidth, read + write (0: unknown)
@@ -112,12 +127,19 @@ bool parse_table(const std::string& text, PerfTable& out, std::string& err);
 std::string table_to_text(const PerfTable& t);
 
 double g_predict(const TableKernel& k, double t);
+// g from an explicit list of (t, us) points (same interpolation).
+double g_predict_pts(const std::vector<std::pair<double, double>>& pts, double t);
+// Which curves price an m-row region on kernel k: an index into k.by_rows,
+// or row_classes.size() for the square curves.
+int curve_set(const PerfTable& tab, const TableKernel& k, int64_t m);
+const std::vector<std::pair<double, double>>& set_pts(const TableKernel& k, int set);
+const std::vector<std::pair<double, double>>& set_tail(const TableKernel& k, int set, bool after_full);
 // Time of a wave whose tasks fill a fraction f (0 < f <= 1) of the slots,
 // relative to a full wave: 1 without tail points; linear between points and
 // up to (1, 1); the first point's value below it.
 double tail_ratio(const std::vector<std::pair<double, double>>& pts, double f);
 // Waves a region of `tasks` tasks costs: full waves plus the partial last one.
-double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots);
+double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots, int set = -1);
 double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K,
                    int64_t batch, int s_req, Region* out);
 

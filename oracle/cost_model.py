@@ -33,6 +33,13 @@ Readings where the page is silent (each is listed in the design doc):
     alone), the `tailx` points when w > 0 (it follows full waves).  Without
     points it is ceil(tasks/slots), the page's f_wave.  The WAVE ablation
     keeps the page's ceil.
+  * wave layouts by tile rows (not on the page, whose g_predict depends on
+    the micro-kernel and t only): the table may list row classes
+    (`rows r1 r2 ...`, ascending) and, per kernel, the three curves again
+    for each class (`g@r`, `tail@r`, `tailx@r`), measured on a wave of r
+    tile rows.  A region of ceil(m/uM) tile rows takes the curves of the
+    smallest class >= that count if its kernel has a `g@` line for that
+    class, else (and above every class) the plain `g`, `tail`, `tailx`.
   * the ablations of section 5 "cost-model effectiveness" (MikPoly-WAVE,
     MikPoly-PIPE) keep one factor of the product and take the other as 1
     (f_pipe = 1 us, resp. f_wave = 1); the launch and reduction terms stay.
@@ -72,6 +79,8 @@ class Kernel:
     bt: bool = False  # serves B given as N x K
     tail: List[Tuple[float, float]] = dataclasses.field(default_factory=list)   # (fill, ratio), alone
     tailx: List[Tuple[float, float]] = dataclasses.field(default_factory=list)  # after full waves
+    # row class r -> (g points, tail points, tailx points) on a wave of r tile rows
+    by_rows: Dict[int, Tuple[list, list, list]] = dataclasses.field(default_factory=dict)
 
 
 @dataclasses.dataclass
@@ -86,9 +95,21 @@ class Table:
     tr_launch_us: float = 0.0
     tr_gbps: float = 0.0
     pairs: List[Tuple[str, str]] = dataclasses.field(default_factory=list)  # one-launch kernel pairs
+    row_classes: List[int] = dataclasses.field(default_factory=list)  # tile-row classes, ascending
 
     def slots(self, k: Kernel) -> int:
         return self.cus * k.wg_per_cu
+
+    def curves(self, k: Kernel, m: int):
+        """(g points, tail points, tailx points) that price an m-row region
+        on kernel k."""
+        rows = ceil_div(m, k.uM)
+        for r in self.row_classes:
+            if rows <= r:
+                if r in k.by_rows and k.by_rows[r][0]:
+                    return k.by_rows[r]
+                break
+        return k.pts, k.tail, k.tailx
 
 
 def parse_table(text: str) -> Table:
@@ -100,10 +121,10 @@ def parse_table(text: str) -> Table:
     splits = [1]
     patterns = ["I", "II-M", "II-N"]
     kernels: Dict[str, Kernel] = {}
-    gpts: Dict[str, List[Tuple[float, float]]] = {}
     pairs: List[Tuple[str, str]] = []
-    tails: Dict[str, List[Tuple[float, float]]] = {}
-    tailxs: Dict[str, List[Tuple[float, float]]] = {}
+    row_classes: List[int] = []
+    # (curve kind, row class or 0) -> kernel name -> points
+    curves: Dict[Tuple[str, int], Dict[str, List[Tuple[float, float]]]] = {}
     for raw in text.splitlines():
         line = raw.split("#", 1)[0].strip()
         if not line:
@@ -129,26 +150,34 @@ def parse_table(text: str) -> Table:
             if layout not in ("kn", "nk"):
                 raise ValueError(f"bad kernel layout: {raw!r}")
             kernels[tok[1]] = Kernel(tok[1], int(tok[2]), int(tok[3]), int(tok[4]), int(tok[5]), [], layout == "nk")
-        elif key == "g":
-            pts = []
+        elif key.split("@")[0] in ("g", "tail", "tailx"):
+            kind, _, rows = key.partition("@")
+            pts = curves.setdefault((kind, int(rows) if rows else 0), {}).setdefault(tok[1], [])
             for p in tok[2:]:
-                t, v = p.split(":")
-                pts.append((float(t), float(v)))
-            gpts.setdefault(tok[1], []).extend(pts)
+                x, y = p.split(":")
+                pts.append((float(x), float(y)))
+        elif key == "rows":
+            row_classes = [int(x) for x in tok[1:]]
+            if any(b <= a for a, b in zip(row_classes, row_classes[1:])) or min(row_classes) < 1:
+                raise ValueError(f"bad rows line: {raw!r}")
         elif key == "pair":
             pairs.append((tok[1], tok[2]))
-        elif key in ("tail", "tailx"):
-            for p in tok[2:]:
-                f, r = p.split(":")
-                (tails if key == "tail" else tailxs).setdefault(tok[1], []).append((float(f), float(r)))
         else:
             raise ValueError(f"unknown table line: {raw!r}")
-    for name, pts in gpts.items():
-        kernels[name].pts = sorted(pts)
-    for name, pts in tails.items():
-        kernels[name].tail = sorted(pts)
-    for name, pts in tailxs.items():
-        kernels[name].tailx = sorted(pts)
+    for (kind, rows), per_kernel in curves.items():
+        if rows and rows not in row_classes:
+            raise ValueError(f"curves for row class {rows} not listed in rows")
+        for name, pts in per_kernel.items():
+            k = kernels[name]
+            if not rows:
+                setattr(k, {"g": "pts", "tail": "tail", "tailx": "tailx"}[kind], sorted(pts))
+            else:
+                sets = k.by_rows.setdefault(rows, ([], [], []))
+                sets[("g", "tail", "tailx").index(kind)].extend(pts)
+    for k in kernels.values():
+        for sets in k.by_rows.values():
+            for pts in sets:
+                pts.sort()
     for k in kernels.values():
         if not k.pts:
             raise ValueError(f"kernel {k.name} has no g points")
@@ -156,12 +185,12 @@ def parse_table(text: str) -> Table:
         ka, kb = kernels[a], kernels[b]
         if a == b or ka.bt != kb.bt or ka.wg_per_cu != kb.wg_per_cu:
             raise ValueError(f"bad pair {a} {b}")
-    return Table(cus, launch, red_l, red_bw, splits, patterns, kernels, tr_l, tr_bw, pairs)
+    return Table(cus, launch, red_l, red_bw, splits, patterns, kernels, tr_l, tr_bw, pairs, row_classes)
 
 
-def g_predict(k: Kernel, t: float) -> float:
-    """Time of one wave of tasks that each run t micro-kernel instances."""
-    pts = k.pts
+def g_predict(pts: List[Tuple[float, float]], t: float) -> float:
+    """Time of one wave of tasks that each run t micro-kernel instances,
+    from one kernel's measured (t, us) points."""
     if len(pts) == 1 or t <= pts[0][0]:
         if len(pts) == 1:
             return pts[0][1] * t / pts[0][0]
@@ -190,11 +219,11 @@ def tail_ratio(points: List[Tuple[float, float]], f: float) -> float:
     return 1.0
 
 
-def wave_term(k: Kernel, tasks: int, slots: int) -> float:
+def wave_term(tail: List[Tuple[float, float]], tailx: List[Tuple[float, float]], tasks: int, slots: int) -> float:
     full, rem = divmod(tasks, slots)
     if not rem:
         return full
-    return full + tail_ratio(k.tailx if full else k.tail, rem / slots)
+    return full + tail_ratio(tailx if full else tail, rem / slots)
 
 
 def split_steps(t3: int, s: int) -> Tuple[int, int]:
@@ -221,8 +250,9 @@ def region_cost(tab: Table, r: Region, K: int, batch: int, mode: str = "full") -
     t3 = ceil_div(K, k.uK)
     per, s_eff = split_steps(t3, r.s)
     f_parallel = ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch
-    f_wave = wave_term(k, f_parallel, tab.slots(k))
-    f_pipe = g_predict(k, per)
+    g, tail, tailx = tab.curves(k, r.m)
+    f_wave = wave_term(tail, tailx, f_parallel, tab.slots(k))
+    f_pipe = g_predict(g, per)
     if mode == "wave":
         f_wave = ceil_div(f_parallel, tab.slots(k))
         f_pipe = 1.0
@@ -272,7 +302,7 @@ def fused_cost(tab: Table, regions: Sequence[Region], K: int, batch: int) -> flo
     c = tab.launch_us
     for r, k in ((r1, k1), (r2, k2)):
         per, s_eff = split_steps(ceil_div(K, k.uK), r.s)
-        parts.append((ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch, g_predict(k, per)))
+        parts.append((ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch, g_predict(tab.curves(k, r.m)[0], per)))
         if s_eff > 1:
             c += tab.red_launch_us + (2 * s_eff + 1) * 4.0 * r.m * r.n * batch / (tab.red_gbps * 1e3)
     return c + makespan_sim(S, parts[0][0], parts[0][1], parts[1][0], parts[1][1])
@@ -373,7 +403,8 @@ def grouped_cost(tab: Table, kernel: str, s: int, M: int, K: int, Ns: Sequence[i
     per, s_eff = split_steps(t3, s)
     columns = sum(ceil_div(n, k.uN) for n in Ns)
     tasks = ceil_div(M, k.uM) * columns * s_eff
-    c = tab.launch_us + wave_term(k, tasks, tab.slots(k)) * g_predict(k, per)
+    g, tail, tailx = tab.curves(k, M)
+    c = tab.launch_us + wave_term(tail, tailx, tasks, tab.slots(k)) * g_predict(g, per)
     if s_eff > 1:
         for n in Ns:
             c += tab.red_launch_us + (2 * s_eff + 1) * 4.0 * M * n / (tab.red_gbps * 1e3)

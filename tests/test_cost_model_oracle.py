@@ -77,10 +77,10 @@ def test_case_study_costs(Ta, Tb):
 def test_g_interpolation():
     tab = cm.parse_table("device 4\nkernel X 16 16 16 1\ng X 1:2 4:5 8:13\n")
     k = tab.kernels["X"]
-    assert cm.g_predict(k, 1) == 2 and cm.g_predict(k, 4) == 5 and cm.g_predict(k, 8) == 13
-    assert cm.g_predict(k, 2) == pytest.approx(3.0)
-    assert cm.g_predict(k, 6) == pytest.approx(9.0)
-    assert cm.g_predict(k, 10) == pytest.approx(17.0)
+    assert cm.g_predict(k.pts, 1) == 2 and cm.g_predict(k.pts, 4) == 5 and cm.g_predict(k.pts, 8) == 13
+    assert cm.g_predict(k.pts, 2) == pytest.approx(3.0)
+    assert cm.g_predict(k.pts, 6) == pytest.approx(9.0)
+    assert cm.g_predict(k.pts, 10) == pytest.approx(17.0)
 
 
 def test_split_accounting():
@@ -270,6 +270,66 @@ tailx k 0.5:0.2
     # without tail lines the full model is the page's ceil
     tab0 = cm.parse_table(text.replace("tail k 0.25:0.4 0.5:0.7\n", "").replace("tailx k 0.5:0.2\n", ""))
     assert cm.region_cost(tab0, r, 160, 1) == pytest.approx(0.5 + 2 * 11)
+
+
+def test_row_class_curves_closed_form():
+    """Curves per tile-row class: a region of r tile rows takes g and both
+    tail curves of the smallest listed class >= r when its kernel has a g
+    line for that class; a kernel without one, a region above every class
+    and a table without a rows line take the square curves.  Grouped and
+    one-launch costs follow the same rule."""
+    text = """device 4
+launch_us 0.5
+splitk 1
+rows 2 4
+kernel k 16 16 16 1
+kernel j 16 16 16 1
+g k 1:2 10:11
+g@2 k 1:4 10:31
+tail@2 k 0.5:0.8
+tailx@2 k 0.5:0.3
+g@4 k 1:3 10:21
+tail k 0.5:0.5
+g j 1:2 10:11
+g@4 j 1:1 10:5
+pair k j
+"""
+    tab = cm.parse_table(text)
+    k, j = tab.kernels["k"], tab.kernels["j"]
+    assert tab.row_classes == [2, 4]
+    assert k.by_rows[2] == ([(1.0, 4.0), (10.0, 31.0)], [(0.5, 0.8)], [(0.5, 0.3)])
+    assert k.by_rows[4][0] == [(1.0, 3.0), (10.0, 21.0)] and 2 not in j.by_rows
+    # 32 rows = 2 tile rows (class 2), 2 columns, K = 160 (10 steps): 4
+    # tasks, one full wave of g@2(10) = 31
+    assert cm.region_cost(tab, cm.Region(0, 0, 32, 32, "k", 1), 160, 1) == pytest.approx(0.5 + 31)
+    # 1 row, 1 column: class 2; 1 task of 4 slots alone: tail@2(0.25) = 0.8
+    # (held below the first point) on g@2(1) = 4
+    assert cm.region_cost(tab, cm.Region(0, 0, 1, 16, "k", 1), 16, 1) == pytest.approx(0.5 + 0.8 * 4)
+    # 16 rows, 6 columns: 1 full wave + 2 of 4 slots after it: tailx@2(0.5) = 0.3
+    assert cm.region_cost(tab, cm.Region(0, 0, 16, 96, "k", 1), 16, 1) == pytest.approx(0.5 + 1.3 * 4)
+    # 33 rows = 3 tile rows: class 4, whose set has no tail points: 6 tasks =
+    # 1 full wave + a partial one counted whole, on g@4(10) = 21
+    assert cm.region_cost(tab, cm.Region(0, 0, 33, 32, "k", 1), 160, 1) == pytest.approx(0.5 + 2 * 21)
+    # 65 rows = 5 tile rows: above every class, the square set: 10 tasks =
+    # 2 full waves + 2 of 4 after them (no square tailx points: whole)
+    assert cm.region_cost(tab, cm.Region(0, 0, 65, 32, "k", 1), 160, 1) == pytest.approx(0.5 + 3 * 11)
+    # j has no class-2 curves: a 2-row region takes the square set (not
+    # class 4's), 4 tasks of g(10) = 11; a 3-row one takes g@4
+    assert cm.region_cost(tab, cm.Region(0, 0, 32, 32, "j", 1), 160, 1) == pytest.approx(0.5 + 11)
+    assert cm.region_cost(tab, cm.Region(0, 0, 48, 16, "j", 1), 160, 1) == pytest.approx(0.5 + 5)
+    # curves of a class that no rows line lists are refused
+    with pytest.raises(ValueError):
+        cm.parse_table(text.replace("rows 2 4", "rows 2"))
+    # without class curves every region takes the square set
+    tab0 = cm.parse_table("\n".join(l for l in text.splitlines() if not l.startswith("rows") and "@" not in l) + "\n")
+    assert cm.region_cost(tab0, cm.Region(0, 0, 32, 32, "k", 1), 160, 1) == pytest.approx(0.5 + 11)
+    # grouped: M = 20 (2 tile rows) over two widths of 16: 4 tasks, one wave of g@2(10)
+    assert cm.grouped_cost(tab, "k", 1, 20, 160, [16, 16]) == pytest.approx(0.5 + 31)
+    # one launch of a 2-tile-row region on k (4 tasks of 31) then one tile
+    # row on j (class 2, which j lacks: 2 square tasks of 11): the 4 slots
+    # are busy until 31, then j's tasks run to 42
+    regs = (cm.Region(0, 0, 32, 32, "k", 1), cm.Region(32, 0, 16, 32, "j", 1))
+    assert cm.fused_cost(tab, regs, 160, 1) == pytest.approx(0.5 + 42)
 
 
 def test_transpose_cost_closed_form():

@@ -1,6 +1,7 @@
 """The offline stage on the GPU: mkp_calibrate measures a short performance
-table (every library kernel at full occupancy for t = 1, 2, 4 K steps; the
-MikPoly page's offline micro-kernel performance model, section 3) and the
+table (every library kernel at full occupancy for t = 1, 2, 4 K steps, on
+a square wave and on waves of 1, 2, 4 and 8 tile rows; the MikPoly page's offline
+micro-kernel performance model, section 3) and the
 table it writes is usable by both parsers."""
 import os
 
@@ -39,13 +40,17 @@ def test_calibrate_writes_a_usable_table(gpu, tmp_path):
         if name in shipped.kernels:
             s = shipped.kernels[name]
             assert (k.uM, k.uN, k.uK, k.bt) == (s.uM, s.uN, s.uK, s.bt), name
-        ts = [t for t, _ in k.pts]
-        assert ts == [1.0, 2.0, 4.0], (name, k.pts)
-        g = [v for _, v in k.pts]
-        assert all(v > 0 for v in g), (name, g)
-        # four K steps per task do not take less than one; a small tile's
-        # wave is a few us, mostly fixed cost, so allow 10% timing noise
-        assert g[2] >= 0.9 * g[0], (name, g)
+        # every wave layout: square, and each class of few tile rows
+        assert sorted(k.by_rows) == tab.row_classes, (name, sorted(k.by_rows))
+        for pts in [k.pts] + [k.by_rows[r][0] for r in tab.row_classes]:
+            ts = [t for t, _ in pts]
+            assert ts == [1.0, 2.0, 4.0], (name, pts)
+            g = [v for _, v in pts]
+            assert all(v > 0 for v in g), (name, g)
+            # four K steps per task do not take less than one; a small tile's
+            # wave is a few us, mostly fixed cost, so allow 10% timing noise
+            assert g[2] >= 0.9 * g[0], (name, g)
+    assert tab.row_classes == [1, 2, 4, 8]
     assert tab.cus >= 1 and tab.launch_us > 0
     assert tab.red_gbps > 0 and tab.tr_gbps > 0
     measured = [l.split() for l in text.splitlines() if l.startswith("measured")]

@@ -110,9 +110,9 @@ def _pair_table(a, b, path):
         tok = line.split("#", 1)[0].split()
         if tok and tok[0] == "pair":
             continue
-        if tok and tok[0] == "g" and tok[1] in (a, b):
+        if tok and tok[0].split("@")[0] == "g" and tok[1] in (a, b):   # every wave layout's g
             pts = " ".join(f"{x.split(':')[0]}:{float(x.split(':')[1]) * 0.01:.6f}" for x in tok[2:])
-            line = f"g {tok[1]} {pts}"
+            line = f"{tok[0]} {tok[1]} {pts}"
         out.append(line)
     out.append(f"pair {a} {b}")
     open(path, "w").write("\n".join(out) + "\n")

@@ -59,7 +59,7 @@ def test_case_study_through_library(mkp, Ta, Tb):
         assert plan["cost_us"] == pytest.approx(2 * Ta)
 
 
-def random_table(rng, nk, tails=False):
+def random_table(rng, nk, tails=False, skinny=False):
     cus = int(rng.integers(2, 12))
     lines = [f"device {cus}", f"launch_us {rng.uniform(0, 3):.3f}", "splitk 1 2 3 4 8",
              f"reduce {rng.uniform(0, 2):.3f} {rng.uniform(100, 2000):.1f}"]
@@ -79,6 +79,24 @@ def random_table(rng, nk, tails=False):
             for key in ("tail", "tailx"):
                 fs = sorted(rng.uniform(0.05, 0.95, size=int(rng.integers(1, 4))))
                 lines.append(f"{key} {n} " + " ".join(f"{f:.3f}:{rng.uniform(0.05, 1.0):.3f}" for f in fs))
+    if skinny:
+        # curves per tile-row class for most kernels and classes, cheaper or
+        # dearer than the square ones
+        classes = sorted(int(x) for x in rng.choice([1, 2, 3, 4, 6], size=int(rng.integers(1, 4)), replace=False))
+        lines.append("rows " + " ".join(str(r) for r in classes))
+        for n in names:
+            for r in classes:
+                if rng.uniform() < 0.3:
+                    continue
+                base = rng.uniform(0.2, 2.0)
+                slope = rng.uniform(0.05, 1.0)
+                pts = " ".join(f"{t}:{base + slope * t * rng.uniform(0.9, 1.1):.4f}" for t in (1, 4, 16))
+                lines.append(f"g@{r} {n} {pts}")
+                if tails:
+                    for key in ("tail", "tailx"):
+                        fs = sorted(rng.uniform(0.05, 0.95, size=int(rng.integers(1, 4))))
+                        lines.append(f"{key}@{r} {n} " +
+                                     " ".join(f"{f:.3f}:{rng.uniform(0.05, 1.0):.3f}" for f in fs))
     return "\n".join(lines) + "\n"
 
 
@@ -224,6 +242,30 @@ def test_partial_wave_search_is_exact(mkp):
         assert cm.covers_exactly(M, N, regs, {n: (k.uM, k.uN) for n, k in tab.kernels.items()})
 
 
+def test_row_class_curves_search_is_exact(mkp):
+    """Tables whose kernels carry curves per tile-row class: the pruned
+    search (whose bounds for a growing region take the smallest of the sets
+    it may still reach) still reaches the oracle's exhaustive minimum, and
+    the chosen plan recomputes to the oracle's cost.  Shapes of a few tile
+    rows make several sets appear in one plan."""
+    rng = np.random.default_rng(4242)
+    for trial in range(60):
+        text = random_table(rng, int(rng.integers(2, 4)), tails=bool(trial % 2), skinny=True)
+        tab = cm.parse_table(text)
+        M = int(rng.integers(1, 260)) if trial % 3 else int(rng.integers(1, 100))
+        N, K = (int(x) for x in rng.integers(1, 220, size=2))
+        batch = int(rng.choice([1, 1, 2]))
+        plan = mkp.mkp_plan_with_table(text, batch, M, N, K)
+        ex = mkp.mkp_plan_with_table(text, batch, M, N, K, exhaustive=True)
+        best = cm.exhaustive_best(tab, M, N, K, batch)
+        assert plan["cost_us"] == pytest.approx(best[0], rel=1e-9), (trial, text, M, N, K, batch)
+        assert ex["cost_us"] == pytest.approx(best[0], rel=1e-9)
+        regs = to_regions(plan)
+        assert cm.plan_cost(tab, regs, K, batch) == pytest.approx(plan["cost_us"], rel=1e-9)
+        assert cm.covers_exactly(M, N, regs, {n: (k.uM, k.uN) for n, k in tab.kernels.items()})
+        assert plan["evaluated"] <= ex["evaluated"]
+
+
 def test_layout_restricts_the_search(mkp):
     """A table holding kernels for both B layouts: the search for B given as
     N x K uses only the nk kernels and reaches the oracle's exhaustive
@@ -333,13 +375,23 @@ def test_grouped_plan_matches_oracle_on_random_tables(mkp, tmp_path):
                     fs = sorted(rng.uniform(0.05, 0.95, size=2))
                     lines.append(f"tail {name} " + " ".join(f"{f:.3f}:{rng.uniform(0.1, 1):.3f}" for f in fs))
                     lines.append(f"tailx {name} " + " ".join(f"{f:.3f}:{rng.uniform(0.1, 1):.3f}" for f in fs))
+                if trial >= 8:
+                    # curves for regions of one and of two tile rows
+                    for r in (1, 2):
+                        lines.append(f"g@{r} {name} " + " ".join(
+                            f"{t}:{base * 2 + slope * t * rng.uniform(0.5, 2):.4f}" for t in (1, 4, 16, 64)))
+                        lines.append(f"tail@{r} {name} 0.5:{rng.uniform(0.1, 1):.3f}")
+            if trial >= 8:
+                lines.append("rows 1 2")
             text = "\n".join(lines) + "\n"
             path = tmp_path / f"t{trial}.tbl"
             path.write_text(text)
             mkp.mkp_load_calibration(str(path))
             tab = cm.parse_table(text)
-            for _ in range(6):
+            for i in range(6):
                 M, K = (int(x) for x in rng.integers(1, 3000, size=2))
+                if trial >= 8 and i % 2:
+                    M = int(rng.integers(1, 300))
                 Ns = [int(x) for x in rng.integers(1, 3000, size=int(rng.integers(1, 5)))]
                 _check_grouped(mkp, tab, M, K, Ns, bool(rng.integers(0, 2)))
     finally:
@@ -372,8 +424,8 @@ def test_one_launch_plans_match_oracle(mkp, fuse_on):
     oracle's exhaustive minimum, whose makespan is simulated task by task."""
     rng = np.random.default_rng(77)
     fused_seen = 0
-    for trial in range(60):
-        text = random_table(rng, int(rng.integers(2, 5)), tails=bool(trial % 2))
+    for trial in range(80):
+        text = random_table(rng, int(rng.integers(2, 5)), tails=bool(trial % 2), skinny=trial >= 60)
         # equal workgroups per CU for most kernels, so that pairs exist
         text = "\n".join(l if not l.startswith("kernel") else " ".join(l.split()[:5] + ["2"])
                          for l in text.splitlines()) + "\n"
