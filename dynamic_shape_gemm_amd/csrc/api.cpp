@@ -1587,8 +1587,13 @@ int mkp_calibrate(const char* path, int max_points) {
                 double us = time_launches(launch, 3, 3, &err);
                 if (err != hipSuccess) break;
                 int reps = (int)std::min(200.0, std::max(5.0, 2000.0 / std::max(us, 1.0)));
-                us = time_launches(launch, 20, reps, &err);
+                // the median of three timed runs (a clock or power-state
+                // change can upset one of them)
+                double run[3];
+                for (int r = 0; r < 3 && err == hipSuccess; ++r) run[r] = time_launches(launch, r ? 3 : 20, reps, &err);
                 if (err != hipSuccess) break;
+                std::sort(run, run + 3);
+                us = run[1];
                 pts.emplace_back((double)tt, std::max(us - t.launch_us, 0.05));
             }
             // partial last wave, at 16 K steps, relative to a full wave of the

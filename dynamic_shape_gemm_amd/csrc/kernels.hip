@@ -1118,6 +1118,7 @@ struct WSplit {
     static constexpr int RED = KW * BM * RED_LD * 4;
     static constexpr int LDS = (KW * WAVE_LDS > RED ? KW * WAVE_LDS : RED);
     static_assert(!T1::JUNK, "a wave's chunk must fill whole 1 KB load groups");
+    static_assert(T1::IPS * (S - 1) <= 63, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -1202,9 +1203,15 @@ __device__ __forceinline__ void wsplit_task(KArgs args, int bid, int nblk, lds_t
 #pragma unroll
     for (int j = 0; j < W::S - 1; ++j)
         if (j < mine) load(j);
+    // chunk j+S-1 goes into the stage of chunk j-1 (whose reads have
+    // completed) before the wait for chunk j, so S chunks are in flight
+    // across the wait
     for (int j = 0; j < mine; ++j) {
-        wave_wait_upto<T1, W::S - 2>(min(W::S - 2, mine - 1 - j));
-        if (j + W::S - 1 < mine) load(j + W::S - 1);
+        if (j + W::S - 1 < mine) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            load(j + W::S - 1);
+        }
+        wave_wait_upto<T1, W::S - 1>(min(W::S - 1, mine - 1 - j));
         const lds_t* sa = ws + (j % W::S) * T1::STAGE;
         const lds_t* sb = sa + T1::A_BYTES;
         if constexpr (T1::MF == 32) compute_stage32<T1>(sa, sb, acc, lane, 0, 0);
