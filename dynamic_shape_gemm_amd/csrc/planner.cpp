@@ -345,10 +345,32 @@ double tail_ratio(const std::vector<std::pair<double, double>>& p, double f) {
     return 1.0;
 }
 
-double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots, int set) {
+double wave_fill(int64_t r, int64_t slots, int64_t cus) {
+    if (r <= cus) return (double)r / (double)slots;
+    return std::min(1.0, (double)(ceil_div(r, cus) * cus) / (double)slots);
+}
+
+double tail_ratio_tasks(const std::vector<std::pair<double, double>>& p, int64_t r, int64_t slots, int64_t cus) {
+    const double f = wave_fill(r, slots, cus);
+    if (f >= 1.0) return 1.0;
+    double x0 = 0.0, y0 = 0.0;
+    bool any = false;
+    for (auto& q : p) {
+        const double x = wave_fill(std::llround(q.first * (double)slots), slots, cus);
+        if (x >= 1.0) break;   // this point and the later ones lie at a whole wave
+        if (f <= x) return any ? y0 + (q.second - y0) * (f - x0) / (x - x0) : q.second;
+        x0 = x;
+        y0 = q.second;
+        any = true;
+    }
+    return any ? y0 + (1.0 - y0) * (f - x0) / (1.0 - x0) : 1.0;
+}
+
+double wave_factor(const PerfTable& tab, const TableKernel& k, int64_t tasks, int set) {
+    const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
     const int64_t full = tasks / slots, rem = tasks % slots;
     if (!rem) return (double)full;
-    return (double)full + tail_ratio(set_tail(k, set, full > 0), (double)rem / (double)slots);
+    return (double)full + tail_ratio_tasks(set_tail(k, set, full > 0), rem, slots, tab.cus);
 }
 
 // Cost of one region served by one kernel with a requested split factor:
@@ -366,7 +388,7 @@ double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64
     const int64_t slots = (int64_t)tab.cus * k.wg_per_cu;
     const int64_t waves = ceil_div(tasks, slots);
     const int set = curve_set(tab, k, m);
-    const double wf = wave_factor(k, tasks, slots, set);
+    const double wf = wave_factor(tab, k, tasks, set);
     double c = tab.launch_us + wf * g_predict_pts(set_pts(k, set), (double)per);
     if (s_eff > 1)
         c += tab.red_launch_us + (double)(2 * s_eff + 1) * 4.0 * (double)m * (double)n * (double)batch /
@@ -440,6 +462,9 @@ struct Searcher {
     // every set a region of that class or more rows may take (fls)
     std::vector<std::array<Floors, kSets>> fl, fls;
     std::vector<std::array<int8_t, kSets>> set_map;   // per kernel: row class -> curve set
+    // per kernel and row class: the tail and tailx points with their fills
+    // taken through wave_fill (points at a whole wave dropped)
+    std::vector<std::array<std::array<std::vector<std::pair<double, double>>, 2>, kSets>> tails;
     std::vector<int8_t> class_by_rows;                // tile rows (up to the largest class) -> row class
     std::vector<FastDiv> dm, dn, dslots;         // per kernel: uM, uN and its slots as dividers
     double lb_region = 0.0;                      // lower bound of any region's cost
@@ -470,6 +495,7 @@ struct Searcher {
         fl.assign(nk, {});
         fls.assign(nk, {});
         set_map.assign(nk, {});
+        tails.assign(nk, {});
         dm.resize(nk);
         dn.resize(nk);
         dslots.resize(nk);
@@ -488,16 +514,20 @@ struct Searcher {
                                               ? c : nclass);
             // a region's wave factor is at least tmin (one possibly partial
             // wave) and at least rho * tasks/slots (piecewise-linear ratios:
-            // r(f)/f is smallest at a point or at f = 1)
+            // r(f)/f is smallest at a point or at f = 1; the wave's fill
+            // through wave_fill is never below tasks/slots)
+            const int64_t kslots = (int64_t)tab.cus * kk.wg_per_cu;
             for (int c = 0; c <= nclass; ++c) {
                 Floors& f = fl[ki][c];
-                for (auto& p : set_tail(kk, set_map[ki][c] < nclass ? set_map[ki][c] : -1, false)) {
-                    f.tmin_alone = std::min(f.tmin_alone, p.second);
-                    f.rho = std::min(f.rho, p.second / p.first);
-                }
-                for (auto& p : set_tail(kk, set_map[ki][c] < nclass ? set_map[ki][c] : -1, true)) {
-                    f.tmin_after = std::min(f.tmin_after, p.second);
-                    f.rho = std::min(f.rho, p.second / p.first);
+                for (int after = 0; after < 2; ++after) {
+                    auto& dst = tails[ki][c][after];
+                    for (auto& p : set_tail(kk, set_map[ki][c] < nclass ? set_map[ki][c] : -1, after)) {
+                        const double x = wave_fill(std::llround(p.first * (double)kslots), kslots, tab.cus);
+                        if (x >= 1.0) break;
+                        dst.emplace_back(x, p.second);
+                        (after ? f.tmin_after : f.tmin_alone) = std::min(after ? f.tmin_after : f.tmin_alone, p.second);
+                        f.rho = std::min(f.rho, p.second / x);
+                    }
                 }
             }
             for (int s_req : req) {
@@ -553,6 +583,17 @@ struct Searcher {
 
     int64_t tiles_of(int k, int64_t m, int64_t n) const { return dm[k].ceil(m) * dn[k].ceil(n); }
 
+    // tail_ratio_tasks over points already taken through wave_fill
+    static double prepared_ratio(const std::vector<std::pair<double, double>>& p, double f) {
+        if (f >= 1.0) return 1.0;
+        if (p.empty()) return 1.0;
+        if (f <= p[0].first) return p[0].second;
+        for (size_t i = 1; i < p.size(); ++i)
+            if (f <= p[i].first)
+                return p[i - 1].second + (p[i].second - p[i - 1].second) * (f - p[i - 1].first) / (p[i].first - p[i - 1].first);
+        return p.back().second + (1.0 - p.back().second) * (f - p.back().first) / (1.0 - p.back().first);
+    }
+
     // Row class of an m-row region on kernel k (nclass: above every class);
     // it never falls as the region grows.
     int class_of(int k, int64_t m) const {
@@ -572,11 +613,10 @@ struct Searcher {
         int64_t rem;
         const int64_t full = dslots[ki].quot(tasks, rem);
         const int64_t waves = full + (rem != 0);
-        const int cls = class_of(ki, m), set = set_map[ki][cls];
+        const int cls = class_of(ki, m);
         const double g = c.g[cls];
         // full waves plus the partial last one (as wave_factor)
-        const double wf = rem ? (double)full + tail_ratio(set_tail(k, set < nclass ? set : -1, full > 0),
-                                                          (double)rem / (double)slots)
+        const double wf = rem ? (double)full + prepared_ratio(tails[ki][cls][full > 0], wave_fill(rem, slots, tab.cus))
                               : (double)full;
         double v = tab.launch_us;
         if (opt.cost_mode == COST_WAVE) v += (double)waves;   // the page's f_wave alone
@@ -1038,7 +1078,7 @@ Plan polymerize_grouped(const PerfTable& tab, int64_t M, int64_t K, const std::v
             const int64_t s_eff = ceil_div(t3, per);
             const int64_t tasks = ceil_div(M, k.uM) * cols * s_eff;
             const int set = curve_set(tab, k, M);
-            const double wf = wave_factor(k, tasks, slots, set);
+            const double wf = wave_factor(tab, k, tasks, set);
             double c = tab.launch_us + wf * g_predict_pts(set_pts(k, set), (double)per);
             if (s_eff > 1)
                 for (int64_t n : Ns)

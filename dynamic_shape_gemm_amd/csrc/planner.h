@@ -138,8 +138,16 @@ const std::vector<std::pair<double, double>>& set_tail(const TableKernel& k, int
 // relative to a full wave: 1 without tail points; linear between points and
 // up to (1, 1); the first point's value below it.
 double tail_ratio(const std::vector<std::pair<double, double>>& pts, double f);
+// The fill of a wave of r tasks on `slots` slots over `cus` CUs as its
+// busiest CU sees it: workgroups are spread over the CUs before any CU takes
+// a second, so up to one task per CU the fill is r/slots, and beyond it
+// some CU holds ceil(r/cus) tasks, as in a wave of ceil(r/cus) * cus.
+double wave_fill(int64_t r, int64_t slots, int64_t cus);
+// tail_ratio of a wave of r tasks with the measured fills and r both taken
+// through wave_fill (measured points at or past a whole wave drop out).
+double tail_ratio_tasks(const std::vector<std::pair<double, double>>& pts, int64_t r, int64_t slots, int64_t cus);
 // Waves a region of `tasks` tasks costs: full waves plus the partial last one.
-double wave_factor(const TableKernel& k, int64_t tasks, int64_t slots, int set = -1);
+double wave_factor(const PerfTable& tab, const TableKernel& k, int64_t tasks, int set = -1);
 double region_cost(const PerfTable& tab, int kernel, int64_t m, int64_t n, int64_t K,
                    int64_t batch, int s_req, Region* out);
 

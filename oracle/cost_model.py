@@ -33,6 +33,13 @@ Readings where the page is silent (each is listed in the design doc):
     alone), the `tailx` points when w > 0 (it follows full waves).  Without
     points it is ceil(tasks/slots), the page's f_wave.  The WAVE ablation
     keeps the page's ceil.
+  * the fill of a partial wave (not on the page): the dispatcher gives
+    every CU one workgroup before any CU a second, so a wave of r tasks
+    keeps its busiest CU as busy as a wave of ceil(r/CUs) * CUs tasks once
+    r exceeds the CU count.  The fill f above is r/slots up to r = CUs and
+    min(1, ceil(r/CUs) * CUs / slots) beyond; the measured fills of the
+    tail points are taken through the same map, and points that land on a
+    whole wave drop out.
   * wave layouts by tile rows (not on the page, whose g_predict depends on
     the micro-kernel and t only): the table may list row classes
     (`rows r1 r2 ...`, ascending) and, per kernel, the three curves again
@@ -219,11 +226,26 @@ def tail_ratio(points: List[Tuple[float, float]], f: float) -> float:
     return 1.0
 
 
-def wave_term(tail: List[Tuple[float, float]], tailx: List[Tuple[float, float]], tasks: int, slots: int) -> float:
+def busiest_fill(r: int, slots: int, cus: int) -> float:
+    """Fill of a wave of r tasks as its busiest CU sees it."""
+    if r <= cus:
+        return r / slots
+    busiest = -(-r // cus)          # tasks on the busiest CU
+    return min(1.0, busiest * cus / slots)
+
+
+def wave_term(tail: List[Tuple[float, float]], tailx: List[Tuple[float, float]], tasks: int, slots: int,
+              cus: int) -> float:
     full, rem = divmod(tasks, slots)
     if not rem:
         return full
-    return full + tail_ratio(tailx if full else tail, rem / slots)
+    pts = []
+    for f, ratio in (tailx if full else tail):
+        x = busiest_fill(math.floor(f * slots + 0.5), slots, cus)   # the point's task count, halves up
+        if x >= 1.0:
+            break
+        pts.append((x, ratio))
+    return full + tail_ratio(pts, busiest_fill(rem, slots, cus))
 
 
 def split_steps(t3: int, s: int) -> Tuple[int, int]:
@@ -251,7 +273,7 @@ def region_cost(tab: Table, r: Region, K: int, batch: int, mode: str = "full") -
     per, s_eff = split_steps(t3, r.s)
     f_parallel = ceil_div(r.m, k.uM) * ceil_div(r.n, k.uN) * s_eff * batch
     g, tail, tailx = tab.curves(k, r.m)
-    f_wave = wave_term(tail, tailx, f_parallel, tab.slots(k))
+    f_wave = wave_term(tail, tailx, f_parallel, tab.slots(k), tab.cus)
     f_pipe = g_predict(g, per)
     if mode == "wave":
         f_wave = ceil_div(f_parallel, tab.slots(k))
@@ -404,7 +426,7 @@ def grouped_cost(tab: Table, kernel: str, s: int, M: int, K: int, Ns: Sequence[i
     columns = sum(ceil_div(n, k.uN) for n in Ns)
     tasks = ceil_div(M, k.uM) * columns * s_eff
     g, tail, tailx = tab.curves(k, M)
-    c = tab.launch_us + wave_term(tail, tailx, tasks, tab.slots(k)) * g_predict(g, per)
+    c = tab.launch_us + wave_term(tail, tailx, tasks, tab.slots(k), tab.cus) * g_predict(g, per)
     if s_eff > 1:
         for n in Ns:
             c += tab.red_launch_us + (2 * s_eff + 1) * 4.0 * M * n / (tab.red_gbps * 1e3)

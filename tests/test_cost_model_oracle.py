@@ -332,6 +332,32 @@ pair k j
     assert cm.fused_cost(tab, regs, 160, 1) == pytest.approx(0.5 + 42)
 
 
+def test_partial_wave_fill_follows_busiest_cu():
+    """A partial wave of r tasks on C CUs with two slots each: up to r = C
+    its fill is r/slots; beyond, some CU runs two tasks, so the wave takes as
+    long as a full one.  Measured fills go through the same map (the point
+    at 3/4, six tasks on four CUs, lands on a whole wave and drops out)."""
+    assert cm.busiest_fill(3, 8, 4) == pytest.approx(0.375)
+    assert cm.busiest_fill(4, 8, 4) == pytest.approx(0.5)
+    assert cm.busiest_fill(5, 8, 4) == 1.0
+    assert cm.busiest_fill(5, 12, 4) == pytest.approx(8 / 12)    # three slots per CU: two on the busiest
+    assert cm.busiest_fill(9, 12, 4) == 1.0
+    text = """device 4
+launch_us 0
+splitk 1
+kernel k 16 16 16 2
+g k 1:2
+tail k 0.25:0.4 0.5:0.6 0.75:0.9
+"""
+    tab = cm.parse_table(text)
+    region = lambda tiles_n: cm.region_cost(tab, cm.Region(0, 0, 16, 16 * tiles_n, "k", 1), 16, 1)
+    assert region(3) == pytest.approx(0.5 * 2)    # 3/8: halfway between 0.4 and 0.6
+    assert region(4) == pytest.approx(0.6 * 2)
+    assert region(5) == pytest.approx(1.0 * 2)    # a CU runs two tasks: a whole wave
+    assert region(6) == pytest.approx(1.0 * 2)    # not the measured 0.9 at 6/8
+    assert region(1) == pytest.approx(0.4 * 2)
+
+
 def test_transpose_cost_closed_form():
     """The copy of a K x N B to N x K costs launch + 4*K*N*batch bytes at the
     table's bandwidth; without a transpose line it is never taken."""
