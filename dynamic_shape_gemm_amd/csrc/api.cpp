@@ -130,6 +130,11 @@ struct Library {
     // split-K: 0 = a second pass sums the partials; 1 = the last split of a
     // tile sums them after agent-scope fences
     std::atomic<int> fused_reduce{0};
+    // streaming stores, bits: 1 final C whose rows are whole 128-byte lines,
+    // 2 final C wherever 16-byte aligned, 4 split-K partials, 8 only in
+    // regions of more than one wave, 16 only for a region's C of at most
+    // 32 MB (the L2s' capacity); 5 measured best
+    std::atomic<int> nt_stores{5};
     std::atomic<bool> pack_unaligned{true};       // stage unaligned re-read operands aligned
     std::atomic<int> transpose_b{1};              // K x N calls as transpose + N x K: 0 no, 1 by cost, 2 always
     std::atomic<bool> trace{false};               // time every launch with events
@@ -308,6 +313,7 @@ void read_env_options(Library& L) {
     if (const char* e = std::getenv("MKP_SPLITK_MAX")) L.opts.splitk_max = std::max(1, std::atoi(e));
     if (const char* e = std::getenv("MKP_FORCE_SPLITK")) L.opts.force_splitk = std::max(0, std::atoi(e));
     if (const char* e = std::getenv("MKP_CACHE_CAP")) L.cache_cap = (size_t)std::max(1, std::atoi(e));
+    if (const char* e = std::getenv("MKP_NT_STORES")) L.nt_stores.store(std::min(31, std::max(0, std::atoi(e))));
     if (const char* e = std::getenv("MKP_FORCE_KERNEL")) {
         for (size_t i = 0; i < L.table->kernels.size(); ++i)
             if (L.table->kernels[i].name == e) L.opts.force_kernel = (int)i;
@@ -697,6 +703,8 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         KEpi e{};
         const KernelInfo* ki = nullptr;
         bool fused_red = false;   // split-K reduced by the last-arriving split
+        bool ntC = false;         // final C through streaming stores
+        bool ntRed = false;       // ... also from the second pass
         float* Creg = nullptr;
         int64_t ldw = 0, G = 0;
         double flops = 0, bytes = 0, red_bytes = 0;
@@ -739,18 +747,31 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         }
         R.Creg = C + r.m0 * ldc + r.n0;
         R.ldw = (r.n + 3) & ~int64_t(3);
+        // streaming stores for the region's final C and for its split-K
+        // partials, as the option's bits select
+        // (the streaming stores take 32-bit byte offsets from a tile's
+        // origin, or from C's for the second pass)
+        const int nt_mode = L.nt_stores.load(std::memory_order_relaxed);
+        const bool nt_here = (!(nt_mode & 8) || r.waves > 1) &&
+                             (!(nt_mode & 16) || 4.0 * r.m * r.n * batch <= 32.0 * 1024 * 1024);
+        R.ntC = nt_here && vC && ldc * 256 * 4 < (int64_t(1) << 31) &&
+                ((nt_mode & 2) || ((nt_mode & 1) && ldc % 32 == 0 && (batch == 1 || sC % 32 == 0) &&
+                                   ((uintptr_t)R.Creg & 127) == 0));
+        R.ntRed = R.ntC && ((batch - 1) * sC + r.m * ldc) * 4 < (int64_t(1) << 31);
         if (r.s == 1) {
             a.C = R.Creg;
             a.ldc = ldc;
             a.sC = sC;
             a.sCsplit = 0;
             a.flags |= vC ? KF_VEC_C : 0;
+            a.flags |= R.ntC ? KF_NT_C : 0;
         } else {
             a.C = (float*)((char*)ws + kCounterBytes + part_off[i < 2 ? i : 0]);
             a.ldc = R.ldw;
             a.sC = r.m * R.ldw;
             a.sCsplit = batch * r.m * R.ldw;
             a.flags |= KF_VEC_C;
+            a.flags |= (nt_here && (nt_mode & 4) && R.ldw * 256 * 4 < (int64_t(1) << 31)) ? KF_NT_C : 0;
         }
         // fused reduction when the per-tile counters fit, else a second pass
         const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n * batch;
@@ -792,7 +813,8 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
         if (r.s <= 1 || R.fused_red) return MKP_OK;
         he = traced(L, st, -1, 0.0, R.red_bytes, [&] {
             return launch_splitk_reduce(R.a.C, r.s, batch * r.m * R.ldw, r.m * R.ldw, R.ldw, R.Creg, ldc, sC, (int)r.m,
-                                        (int)r.n, (int)batch, vC ? 1 : 0, st, epi ? &R.e : nullptr);
+                                        (int)r.n, (int)batch, (vC ? 1 : 0) | (R.ntRed ? 2 : 0), st,
+                                        epi ? &R.e : nullptr);
         });
         if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
         L.launches.fetch_add(1, std::memory_order_relaxed);
@@ -1293,6 +1315,11 @@ int mkp_set_option(const char* key, const char* value) {
         L.transpose_b.store(x);
     } else if (k == "pack_unaligned") {
         L.pack_unaligned.store(std::atoi(v.c_str()) != 0);
+        return MKP_OK;
+    } else if (k == "nt_stores") {
+        const int x = std::atoi(v.c_str());
+        if (x < 0 || x > 31) return fail(MKP_ERR_INVALID_ARG, "nt_stores must be 0 .. 31");
+        L.nt_stores.store(x);
         return MKP_OK;
     } else if (k == "fused_reduce") {
         const int x = std::atoi(v.c_str());

@@ -20,6 +20,7 @@ enum : int {
     KF_EPI = 16,      // apply the epilogue below to the final C values
     KF_CONV_DMA = 32, // convolution with C % uK == 0 (a K step stays in one filter tap) and every
                       // input offset, padding included, within 32 bits: direct loads
+    KF_NT_C = 64,     // C (or the split-K partials) written with streaming (nontemporal) 16-byte stores
 };
 
 // Implicit-GEMM convolution (the MikPoly page runs convolutions as GEMMs):
@@ -143,7 +144,9 @@ const ConvInfo& conv_info(int i);
 
 // Sum of `splits` partials W[z] (z ascending) into C; W is [splits][batch][M][ldw].
 // With an epilogue (epi non-null) the sum goes through it; splits == 0 is an
-// empty sum (W unused), which with the epilogue serves K == 0.
+// empty sum (W unused), which with the epilogue serves K == 0.  vec: bit 0,
+// C rows 16-byte aligned (128-bit stores); bit 1, with bit 0, C written with
+// streaming stores (as KF_NT_C).
 hipError_t launch_splitk_reduce(const float* W, int splits, int64_t sWsplit, int64_t sWbatch, int64_t ldw,
                                 float* C, int64_t ldc, int64_t sC, int M, int N, int batch, int vec,
                                 hipStream_t st, const KEpi* epi = nullptr);

@@ -344,6 +344,22 @@ __device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t r, uint32
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherentAgent));
 }
 
+// 16 bytes of C (or of a split-K partial) at element idx of base (wave-
+// uniform), with a streaming store when nt (KF_NT_C): the data need not wait
+// in the XCD's L2 for the write-back at the kernel's end.  The streaming
+// store is a buffer store with the nt cache-policy bit (byte offsets below
+// 2^31, which the host checks before it sets the flag); an ordinary store
+// otherwise.  (A nontemporal global store in one branch and an ordinary one
+// in the other would be merged into one ordinary store.)
+constexpr int kStreaming = 2;   // the nt cache-policy bit
+__device__ __forceinline__ void st4(float* base, int64_t idx, f32x4 v, bool nt) {
+    if (nt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), coherent_rsrc(base), (int)(idx * 4), 0,
+                                               kStreaming);
+    else
+        *(f32x4*)(base + idx) = v;
+}
+
 struct TileCtx {
     const uint16_t* A;   // tile origin row m0 (row 0 of the tile), column 0; convolution: the input
     const uint16_t* B;   // tile origin column n0, row 0
@@ -818,11 +834,12 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     float* __restrict__ C = args.C + (int64_t)b * args.sC + (int64_t)split * args.sCsplit +
                             (int64_t)m0 * args.ldc + n0;
     const bool vecC = args.flags & KF_VEC_C;
+    const bool ntC = args.flags & KF_NT_C;
     auto store4 = [&](float* base, int64_t ld, bool vec, int m, int n, f32x4 v) {
         if (m >= c.Mr) return;
         float* p = base + (int64_t)m * ld + n;
         if (vec && n + 4 <= c.Nr) {
-            *(f32x4*)p = v;
+            st4(base, (int64_t)m * ld + n, v, ntC);
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -980,7 +997,7 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
                         const int col = h + 4 * j;
                         if (m < c.Mr && col + 4 <= W) {
                             const float __attribute__((address_space(3)))* sr = stg + r * T::EPI_LD + col;
-                            *(f32x4*)(d + col) = f32x4{sr[0], sr[1], sr[2], sr[3]};
+                            st4(C, (int64_t)m * args.ldc + col0 + col, f32x4{sr[0], sr[1], sr[2], sr[3]}, ntC);
                         }
                     }
                 }
@@ -1257,7 +1274,7 @@ __device__ __forceinline__ void wsplit_task(KArgs args, int bid, int nblk, lds_t
         float* p = C + (int64_t)m * args.ldc + n;
         if (epi) v = epi4(args.epi, p, vecC, c.Nr - n, load_bias4(args.epi, n0 + n, c.Nr - n), v);
         if (vecC && n + 4 <= c.Nr) {
-            *(f32x4*)p = v;
+            st4(C, (int64_t)m * args.ldc + n, v, args.flags & KF_NT_C);
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -1336,9 +1353,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         }
     }
     float* p = C + (int64_t)b * sC + (int64_t)m * ldc + n;
-    if (EPI) s = epi4(epi, p, vec, N - n, load_bias4(epi, n, N - n), s);
-    if (vec && n + 4 <= N) {
-        *(f32x4*)p = s;
+    if (EPI) s = epi4(epi, p, vec & 1, N - n, load_bias4(epi, n, N - n), s);
+    if ((vec & 1) && n + 4 <= N) {
+        st4(C, (int64_t)b * sC + (int64_t)m * ldc + n, s, vec & 2);
     } else {
         for (int r = 0; r < 4; ++r)
             if (n + r < N) p[r] = s[r];

@@ -309,6 +309,14 @@ int mkp_calibrate(const char *path, int max_points);
  * default: a K x N call may copy B into N x K workspace rows and run on the
  * N x K kernels, when the table prices the copy and the model finds it
  * cheaper; 2 = always, whenever an N x K plan exists).
+ * "nt_stores" (how the GEMM kernels and the split-K second pass write C: a
+ * sum of bits, 0 = ordinary stores everywhere, kept in the L2 until the
+ * kernel's end writes them back; 1 = streaming stores for the final C where
+ * its rows are whole 128-byte lines (ldc and the batch stride multiples of
+ * 32 floats, the region's first element 128-byte aligned); 2 = for the final
+ * C wherever its rows are 16-byte aligned; 4 = for split-K partials; 8 = only
+ * in regions of more than one wave of workgroups; 16 = only where the
+ * region's C is at most 32 MB; the default is 5).
  * "fuse_regions" (0 = the default: every region of a plan is a launch of its
  * own; 1 = a Pattern II plan over a kernel pair may run both regions in one
  * launch, the second region's workgroups taking the slots the first
@@ -327,8 +335,8 @@ int mkp_calibrate(const char *path, int max_points);
  * caller can launch and time candidates one by one; a rank beyond the
  * candidate count makes the GEMM fail with MKP_ERR_UNSUPPORTED).  Both also
  * apply to mkp_plan_with_table, whose JSON then carries "rank" and
- * "candidates".  Every option except "trace", "fused_reduce" and
- * "pack_unaligned" clears the plan cache.  Returns MKP_OK or
+ * "candidates".  Every option except "trace", "fused_reduce", "nt_stores"
+ * and "pack_unaligned" clears the plan cache.  Returns MKP_OK or
  * MKP_ERR_INVALID_ARG / MKP_ERR_UNSUPPORTED. */
 int mkp_set_option(const char *key, const char *value);
 
