@@ -1453,6 +1453,10 @@ int mkp_calibrate(const char* path, int max_points) {
     static const int row_classes[] = {1, 2, 4, 8};
     constexpr int nclass = (int)(sizeof(row_classes) / sizeof(row_classes[0]));
     size_t a_elems = 0, b_elems = 0, c_elems = 0;   // buffers for the largest point of any kernel
+    // the kernels write C (whole 128-byte rows from 256-byte aligned slices)
+    // and split-K partials as GEMM calls do under the nt_stores option
+    const int nt_mode = lib().nt_stores.load(std::memory_order_relaxed);
+    auto nt_flag = [&](int splits) { return (splits > 1 ? (nt_mode & 4) : (nt_mode & 3)) ? KF_NT_C : 0; };
     struct Shape { int tm, tn, s; };
     std::vector<std::array<Shape, nclass + 1>> shapes;   // [nclass]: square
     std::vector<int> occ;
@@ -1604,7 +1608,7 @@ int mkp_calibrate(const char* path, int max_points) {
                 a.splits = s.s;
                 a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;   // each split's partial tile
                 a.batch = 1;
-                a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+                a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C | nt_flag(s.s);
                 const dim3 grid((unsigned)(s.tm * s.tn * s.s));
                 // single-launch time, then enough repetitions for ~2 ms
                 auto launch = [&] {
@@ -1654,7 +1658,7 @@ int mkp_calibrate(const char* path, int max_points) {
                         a.splits = s.s;
                         a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;
                         a.batch = 1;
-                        a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+                        a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C | nt_flag(s.s);
                         const dim3 grid((unsigned)(s.tm * cols * s.s));
                         us[after] = time_launches(
                             [&] {

@@ -66,7 +66,7 @@ def test_planner_chosen_one_launch_plans(mkp, bt):
     # which shapes get a one-launch plan depends on the calibrated table:
     # walk the encoder linears' FFN-up rows and decoder-sized projections,
     # and run the first three
-    shapes = ([(16 * L, 3072, 768) for L in range(128, 400)] + [(336, 6000, 4096)] +
+    shapes = ([(16 * L, N, 768) for L in range(128, 513) for N in (3072, 2304)] + [(336, 6000, 4096)] +
               [(16 * L, N, K) for L in range(8, 64) for (N, K) in ((4096, 11008), (11008, 4096))])
     for (M, N, K) in shapes:
         if seen == 3:
