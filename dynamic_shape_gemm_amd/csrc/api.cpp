@@ -1453,10 +1453,9 @@ int mkp_calibrate(const char* path, int max_points) {
     static const int row_classes[] = {1, 2, 4, 8};
     constexpr int nclass = (int)(sizeof(row_classes) / sizeof(row_classes[0]));
     size_t a_elems = 0, b_elems = 0, c_elems = 0;   // buffers for the largest point of any kernel
-    // the kernels write C (whole 128-byte rows from 256-byte aligned slices)
-    // and split-K partials as GEMM calls do under the nt_stores option
-    const int nt_mode = lib().nt_stores.load(std::memory_order_relaxed);
-    auto nt_flag = [&](int splits) { return (splits > 1 ? (nt_mode & 4) : (nt_mode & 3)) ? KF_NT_C : 0; };
+    // (C and split-K partials are written with ordinary stores here: a
+    // table measured with the calls' streaming stores priced split-K lower
+    // and planned 60 % more second passes, for a step no faster)
     struct Shape { int tm, tn, s; };
     std::vector<std::array<Shape, nclass + 1>> shapes;   // [nclass]: square
     std::vector<int> occ;
@@ -1608,7 +1607,7 @@ int mkp_calibrate(const char* path, int max_points) {
                 a.splits = s.s;
                 a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;   // each split's partial tile
                 a.batch = 1;
-                a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C | nt_flag(s.s);
+                a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
                 const dim3 grid((unsigned)(s.tm * s.tn * s.s));
                 // single-launch time, then enough repetitions for ~2 ms
                 auto launch = [&] {
@@ -1658,7 +1657,7 @@ int mkp_calibrate(const char* path, int max_points) {
                         a.splits = s.s;
                         a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;
                         a.batch = 1;
-                        a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C | nt_flag(s.s);
+                        a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
                         const dim3 grid((unsigned)(s.tm * cols * s.s));
                         us[after] = time_launches(
                             [&] {
