@@ -130,11 +130,12 @@ struct Library {
     // split-K: 0 = a second pass sums the partials; 1 = the last split of a
     // tile sums them after agent-scope fences
     std::atomic<int> fused_reduce{0};
-    // streaming stores, bits: 1 final C whose rows are whole 128-byte lines,
-    // 2 final C wherever 16-byte aligned, 4 split-K partials, 8 only in
-    // regions of more than one wave, 16 only for a region's C of at most
-    // 32 MB (the L2s' capacity); 5 measured best
-    std::atomic<int> nt_stores{5};
+    // store policy, bits: streaming stores for 1 final C whose rows are
+    // whole 128-byte lines, 2 final C wherever 16-byte aligned, 4 split-K
+    // partials; 8 only in regions of more than one wave, 16 only for a
+    // region's C of at most 32 MB (the L2s' capacity); 32 split-K partials
+    // written through to the level every XCD shares; 33 measured best
+    std::atomic<int> nt_stores{33};
     std::atomic<bool> pack_unaligned{true};       // stage unaligned re-read operands aligned
     std::atomic<int> transpose_b{1};              // K x N calls as transpose + N x K: 0 no, 1 by cost, 2 always
     std::atomic<bool> trace{false};               // time every launch with events
@@ -313,7 +314,7 @@ void read_env_options(Library& L) {
     if (const char* e = std::getenv("MKP_SPLITK_MAX")) L.opts.splitk_max = std::max(1, std::atoi(e));
     if (const char* e = std::getenv("MKP_FORCE_SPLITK")) L.opts.force_splitk = std::max(0, std::atoi(e));
     if (const char* e = std::getenv("MKP_CACHE_CAP")) L.cache_cap = (size_t)std::max(1, std::atoi(e));
-    if (const char* e = std::getenv("MKP_NT_STORES")) L.nt_stores.store(std::min(31, std::max(0, std::atoi(e))));
+    if (const char* e = std::getenv("MKP_NT_STORES")) L.nt_stores.store(std::min(63, std::max(0, std::atoi(e))));
     if (const char* e = std::getenv("MKP_FORCE_KERNEL")) {
         for (size_t i = 0; i < L.table->kernels.size(); ++i)
             if (L.table->kernels[i].name == e) L.opts.force_kernel = (int)i;
@@ -772,6 +773,7 @@ int run_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, const void* Av, int
             a.sCsplit = batch * r.m * R.ldw;
             a.flags |= KF_VEC_C;
             a.flags |= (nt_here && (nt_mode & 4) && R.ldw * 256 * 4 < (int64_t(1) << 31)) ? KF_NT_C : 0;
+            a.flags |= (nt_here && (nt_mode & 32) && R.ldw * 256 * 4 < (int64_t(1) << 31)) ? KF_SC1_C : 0;
         }
         // fused reduction when the per-tile counters fit, else a second pass
         const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n * batch;
@@ -1318,7 +1320,7 @@ int mkp_set_option(const char* key, const char* value) {
         return MKP_OK;
     } else if (k == "nt_stores") {
         const int x = std::atoi(v.c_str());
-        if (x < 0 || x > 31) return fail(MKP_ERR_INVALID_ARG, "nt_stores must be 0 .. 31");
+        if (x < 0 || x > 63) return fail(MKP_ERR_INVALID_ARG, "nt_stores must be 0 .. 63");
         L.nt_stores.store(x);
         return MKP_OK;
     } else if (k == "fused_reduce") {

@@ -21,6 +21,7 @@ enum : int {
     KF_CONV_DMA = 32, // convolution with C % uK == 0 (a K step stays in one filter tap) and every
                       // input offset, padding included, within 32 bits: direct loads
     KF_NT_C = 64,     // C (or the split-K partials) written with streaming (nontemporal) 16-byte stores
+    KF_SC1_C = 128,   // ... written through to the level every XCD shares (sc1)
 };
 
 // Implicit-GEMM convolution (the MikPoly page runs convolutions as GEMMs):

@@ -345,19 +345,24 @@ __device__ __forceinline__ f32x4 load4_coherent(__amdgpu_buffer_rsrc_t r, uint32
 }
 
 // 16 bytes of C (or of a split-K partial) at element idx of base (wave-
-// uniform), with a streaming store when nt (KF_NT_C): the data need not wait
-// in the XCD's L2 for the write-back at the kernel's end.  The streaming
-// store is a buffer store with the nt cache-policy bit (byte offsets below
-// 2^31, which the host checks before it sets the flag); an ordinary store
-// otherwise.  (A nontemporal global store in one branch and an ordinary one
-// in the other would be merged into one ordinary store.)
+// uniform), with the store policy of the launch: a streaming store (nt,
+// KF_NT_C) or one written through to the level every XCD shares (sc1,
+// KF_SC1_C) need not wait dirty in the XCD's L2 for the write-back at the
+// kernel's end.  Both are buffer stores with those cache-policy bits (byte
+// offsets below 2^31, which the host checks before it sets a flag); an
+// ordinary store otherwise.  (A nontemporal global store in one branch and an
+// ordinary one in the other would be merged into one ordinary store.)
 constexpr int kStreaming = 2;   // the nt cache-policy bit
-__device__ __forceinline__ void st4(float* base, int64_t idx, f32x4 v, bool nt) {
-    if (nt)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), coherent_rsrc(base), (int)(idx * 4), 0,
-                                               kStreaming);
-    else
-        *(f32x4*)(base + idx) = v;
+__device__ __forceinline__ int store_policy(int flags) {
+    return ((flags & KF_NT_C) ? 1 : 0) | ((flags & KF_SC1_C) ? 2 : 0);
+}
+__device__ __forceinline__ void st4(float* base, int64_t idx, f32x4 v, int pol) {
+    const u32x4 w = __builtin_bit_cast(u32x4, v);
+    if (pol == 1) __builtin_amdgcn_raw_buffer_store_b128(w, coherent_rsrc(base), (int)(idx * 4), 0, kStreaming);
+    else if (pol == 2) __builtin_amdgcn_raw_buffer_store_b128(w, coherent_rsrc(base), (int)(idx * 4), 0, kCoherentAgent);
+    else if (pol == 3)
+        __builtin_amdgcn_raw_buffer_store_b128(w, coherent_rsrc(base), (int)(idx * 4), 0, kStreaming | kCoherentAgent);
+    else *(f32x4*)(base + idx) = v;
 }
 
 struct TileCtx {
@@ -834,7 +839,7 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     float* __restrict__ C = args.C + (int64_t)b * args.sC + (int64_t)split * args.sCsplit +
                             (int64_t)m0 * args.ldc + n0;
     const bool vecC = args.flags & KF_VEC_C;
-    const bool ntC = args.flags & KF_NT_C;
+    const int ntC = store_policy(args.flags);
     auto store4 = [&](float* base, int64_t ld, bool vec, int m, int n, f32x4 v) {
         if (m >= c.Mr) return;
         float* p = base + (int64_t)m * ld + n;
@@ -1274,7 +1279,7 @@ __device__ __forceinline__ void wsplit_task(KArgs args, int bid, int nblk, lds_t
         float* p = C + (int64_t)m * args.ldc + n;
         if (epi) v = epi4(args.epi, p, vecC, c.Nr - n, load_bias4(args.epi, n0 + n, c.Nr - n), v);
         if (vecC && n + 4 <= c.Nr) {
-            st4(C, (int64_t)m * args.ldc + n, v, args.flags & KF_NT_C);
+            st4(C, (int64_t)m * args.ldc + n, v, store_policy(args.flags));
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -1355,7 +1360,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     float* p = C + (int64_t)b * sC + (int64_t)m * ldc + n;
     if (EPI) s = epi4(epi, p, vec & 1, N - n, load_bias4(epi, n, N - n), s);
     if ((vec & 1) && n + 4 <= N) {
-        st4(C, (int64_t)b * sC + (int64_t)m * ldc + n, s, vec & 2);
+        st4(C, (int64_t)b * sC + (int64_t)m * ldc + n, s, (vec & 2) ? 1 : 0);
     } else {
         for (int r = 0; r < 4; ++r)
             if (n + r < N) p[r] = s[r];

@@ -316,7 +316,9 @@ int mkp_calibrate(const char *path, int max_points);
  * 32 floats, the region's first element 128-byte aligned); 2 = for the final
  * C wherever its rows are 16-byte aligned; 4 = for split-K partials; 8 = only
  * in regions of more than one wave of workgroups; 16 = only where the
- * region's C is at most 32 MB; the default is 5).
+ * region's C is at most 32 MB; 32 = split-K partials written through to the
+ * level every XCD shares, where the second pass reads them; the default is
+ * 33).
  * "fuse_regions" (0 = the default: every region of a plan is a launch of its
  * own; 1 = a Pattern II plan over a kernel pair may run both regions in one
  * launch, the second region's workgroups taking the slots the first
