@@ -90,10 +90,13 @@ def test_options_and_errors(mkp):
     assert e.value.code == mkp.MKP_ERR_UNSUPPORTED
     with pytest.raises(mkp.MkpError):
         mkp.mkp_set_option("patterns", "III")
-    for key, bad in (("cost_model", "flops"), ("plan_rank", "-1")):
+    for key, bad in (("cost_model", "flops"), ("plan_rank", "-1"), ("nt_stores", "64"), ("nt_stores", "-1")):
         with pytest.raises(mkp.MkpError) as e:
             mkp.mkp_set_option(key, bad)
         assert e.value.code == mkp.MKP_ERR_INVALID_ARG
+    # every store-policy value the option documents is accepted; 33 is the default
+    for v in (0, 63, 33):
+        assert mkp.mkp_set_option("nt_stores", v) == 0
     with pytest.raises(mkp.MkpError):
         mkp.mkp_load_calibration("/nonexistent/table.tbl")
     mkp.mkp_load_calibration(None)
