@@ -1455,9 +1455,13 @@ int mkp_calibrate(const char* path, int max_points) {
     static const int row_classes[] = {1, 2, 4, 8};
     constexpr int nclass = (int)(sizeof(row_classes) / sizeof(row_classes[0]));
     size_t a_elems = 0, b_elems = 0, c_elems = 0;   // buffers for the largest point of any kernel
-    // (C and split-K partials are written with ordinary stores here: a
-    // table measured with the calls' streaming stores priced split-K lower
-    // and planned 60 % more second passes, for a step no faster)
+    // the kernels write C (whole 128-byte rows from 256-byte aligned slices)
+    // and split-K partials with the store policy of GEMM calls
+    const int nt_mode = lib().nt_stores.load(std::memory_order_relaxed);
+    auto store_flags = [&](int splits) {
+        if (splits <= 1) return (nt_mode & 3) ? (int)KF_NT_C : 0;
+        return ((nt_mode & 4) ? (int)KF_NT_C : 0) | ((nt_mode & 32) ? (int)KF_SC1_C : 0);
+    };
     struct Shape { int tm, tn, s; };
     std::vector<std::array<Shape, nclass + 1>> shapes;   // [nclass]: square
     std::vector<int> occ;
@@ -1609,7 +1613,7 @@ int mkp_calibrate(const char* path, int max_points) {
                 a.splits = s.s;
                 a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;   // each split's partial tile
                 a.batch = 1;
-                a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+                a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C | store_flags(s.s);
                 const dim3 grid((unsigned)(s.tm * s.tn * s.s));
                 // single-launch time, then enough repetitions for ~2 ms
                 auto launch = [&] {
@@ -1659,7 +1663,7 @@ int mkp_calibrate(const char* path, int max_points) {
                         a.splits = s.s;
                         a.sCsplit = s.s > 1 ? (int64_t)a.M * a.N : 0;
                         a.batch = 1;
-                        a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C;
+                        a.flags = KF_VEC_A | KF_VEC_B | KF_VEC_C | store_flags(s.s);
                         const dim3 grid((unsigned)(s.tm * cols * s.s));
                         us[after] = time_launches(
                             [&] {
