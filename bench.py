@@ -574,9 +574,16 @@ def main():
     per_call = [float(np.median(v)) for v in zip(*per_step)]
     fr = sweep_fraction(per_call, wl)
     if args.detail:
-        for case, us, f in zip(wl.cases, per_call, fr):
+        for ci, (case, us, f) in enumerate(zip(wl.cases, per_call, fr)):
             # the GEMM view of the call (a convolution: N P Q x K x R S C)
             gm, gn, gk = (case.M, case.K, case.Kg) if wl.cfg == "conv" else (case.M, case.N, case.K)
+            if wl.cfg == "conv":
+                # a convolution is planned on the kernels with a convolution
+                # form: name the ones its traced calls launched
+                names = list(dict.fromkeys(r["kernel"] for r in case_recs[ci]))
+                log(f"  {case.tag:>14} {gm:5d}x{gn:5d}x{gk:5d} b{case.batch:<3d} {us:9.2f} us "
+                    f"{case.flops / us / 1e6:8.1f} TF/s  {100 * f:5.1f}% of R  conv {'+'.join(names)}")
+                continue
             if wl.is_qkv(case):
                 plan = mkp.mkp_plan_describe_grouped(case.M, case.K, [768] * 3, bt=wl.bt)
                 if wl.qkv == "separate":

@@ -962,6 +962,13 @@ int run_grouped(int64_t G, int64_t M, int64_t K, const void* Av, int64_t lda, co
     a.batch = 1;
     a.flags = vA ? KF_VEC_A : 0;
     a.ngroups = (int)live.size();
+    // the store policy of a plain call, applied per group (its C) and to the
+    // shared split-K workspace
+    const int nt_mode = L.nt_stores.load(std::memory_order_relaxed);
+    int64_t cbytes = 0;
+    for (int64_t g : live) cbytes += 4 * M * Ns[g];
+    const bool nt_here = (!(nt_mode & 8) || r.waves > 1) && (!(nt_mode & 16) || cbytes <= 32 * 1024 * 1024);
+    std::vector<bool> ntRed(live.size(), false);
     int tile0 = 0;
     double flops = 0, bytes = 2.0 * M * K;
     for (size_t i = 0; i < live.size(); ++i) {
@@ -975,7 +982,12 @@ int run_grouped(int64_t G, int64_t M, int64_t K, const void* Av, int64_t lda, co
         G_.tile0 = tile0;
         const bool vB = aligned16(Bs[g]) && ldbs[g] % 8 == 0 && ldbs[g] < (int64_t(1) << (bt ? 23 : 25));
         const bool vC = aligned16(Cs[g]) && ldcs[g] % 4 == 0;
-        G_.flags = (vB ? KF_VEC_B : 0) | (vC ? KF_VEC_C : 0);
+        // (streaming stores take 32-bit byte offsets from a tile's origin,
+        // or from the group's C in the second pass)
+        const bool ntC = nt_here && vC && ldcs[g] * 256 * 4 < (int64_t(1) << 31) &&
+                         ((nt_mode & 2) || ((nt_mode & 1) && ldcs[g] % 32 == 0 && ((uintptr_t)Cs[g] & 127) == 0));
+        ntRed[i] = ntC && M * ldcs[g] * 4 < (int64_t(1) << 31);
+        G_.flags = (vB ? KF_VEC_B : 0) | (vC ? KF_VEC_C : 0) | (ntC ? KF_NT_C : 0);
         tile0 += (int)ceil_div(Ns[g], ki.uN);
         flops += 2.0 * M * Ns[g] * K;
         bytes += 2.0 * K * Ns[g] + 4.0 * M * Ns[g];
@@ -995,6 +1007,8 @@ int run_grouped(int64_t G, int64_t M, int64_t K, const void* Av, int64_t lda, co
         a.sC = M * ldw;
         a.sCsplit = M * ldw;
         a.flags |= KF_VEC_C;
+        a.flags |= (nt_here && (nt_mode & 4) && ldw * 256 * 4 < (int64_t(1) << 31)) ? KF_NT_C : 0;
+        a.flags |= (nt_here && (nt_mode & 32) && ldw * 256 * 4 < (int64_t(1) << 31)) ? KF_SC1_C : 0;
     }
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
     if (grid > INT_MAX) return fail(MKP_ERR_UNSUPPORTED, "grid too large");
@@ -1006,7 +1020,7 @@ int run_grouped(int64_t G, int64_t M, int64_t K, const void* Av, int64_t lda, co
             const KGroup& G_ = a.group[i];
             he = traced(L, st, -1, 0.0, (double)(r.s + 1) * 4.0 * M * G_.N, [&] {
                 return launch_splitk_reduce(W + (int64_t)G_.tile0 * ki.uN, r.s, M * ldw, 0, ldw, G_.C, G_.ldc, 0,
-                                            (int)M, G_.N, 1, (G_.flags & KF_VEC_C) ? 1 : 0, st);
+                                            (int)M, G_.N, 1, ((G_.flags & KF_VEC_C) ? 1 : 0) | (ntRed[i] ? 2 : 0), st);
             });
             if (he != hipSuccess) return fail(MKP_ERR_HIP, std::string("reduce launch: ") + hipGetErrorString(he));
             L.launches.fetch_add(1, std::memory_order_relaxed);

@@ -57,7 +57,7 @@ struct KGroup {
     int64_t ldb, ldc;
     int N;
     int tile0;
-    int flags;   // this group's KF_VEC_B / KF_VEC_C bits
+    int flags;   // this group's KF_VEC_B / KF_VEC_C / KF_NT_C bits
 };
 enum : int { kMaxGroups = 4 };
 

@@ -769,7 +769,7 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
         if (args.splits == 1) {
             args.C = G.C;
             args.ldc = G.ldc;
-            args.flags = (args.flags & ~KF_VEC_C) | (G.flags & KF_VEC_C);
+            args.flags = (args.flags & ~(KF_VEC_C | KF_NT_C | KF_SC1_C)) | (G.flags & (KF_VEC_C | KF_NT_C));
         } else {
             args.C += (int64_t)G.tile0 * T::BN;   // the group's workspace columns
         }
@@ -1181,7 +1181,7 @@ __device__ __forceinline__ void wsplit_task(KArgs args, int bid, int nblk, lds_t
         if (args.splits == 1) {
             args.C = G.C;
             args.ldc = G.ldc;
-            args.flags = (args.flags & ~KF_VEC_C) | (G.flags & KF_VEC_C);
+            args.flags = (args.flags & ~(KF_VEC_C | KF_NT_C | KF_SC1_C)) | (G.flags & (KF_VEC_C | KF_NT_C));
         } else {
             args.C += (int64_t)G.tile0 * W::BN;
         }

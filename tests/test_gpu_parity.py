@@ -97,6 +97,31 @@ def test_each_kernel_forced(mkp, split):
         mkp.mkp_set_option("force_splitk", 0)
 
 
+@pytest.mark.parametrize("nt", [0, 2, 38])
+def test_each_kernel_store_policies(mkp, nt):
+    """Every micro-kernel under the C-store policies other than the default:
+    plain stores (0), streaming stores of every vector-aligned C (2), and
+    streaming plus shared-level write-through of split-K partials with the
+    second pass streaming (38); one split, and three with either reduction.
+    C rows are dense (ldc = N: 256 is a multiple of 32 floats, 388 of 4 only)."""
+    rng = np.random.default_rng(700 + nt)
+    try:
+        mkp.mkp_set_option("nt_stores", nt)
+        for split, fused in ((1, 0), (3, 1), (3, 0)):
+            mkp.mkp_set_option("force_splitk", split)
+            mkp.mkp_set_option("fused_reduce", fused)
+            for name in [n for n in mkp.mkp_kernel_names() if not n.endswith("_nk")]:
+                mkp.mkp_set_option("force_kernel", name)
+                for (M, N, K) in ((129, 256, 200), (257, 388, 130)):
+                    run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), ldc=N,
+                             what=f"{name} s={split} fused={fused} nt={nt}")
+    finally:
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("force_splitk", 0)
+        mkp.mkp_set_option("fused_reduce", 0)
+        mkp.mkp_set_option("nt_stores", 33)
+
+
 @pytest.mark.parametrize("fused", [1, 0])
 @pytest.mark.parametrize("s", [2, 4, 8, 32])
 def test_splitk(mkp, s, fused):

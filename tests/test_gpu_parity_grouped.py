@@ -113,6 +113,33 @@ def test_grouped_each_kernel_forced(mkp, bt):
         mkp.mkp_set_option("force_splitk", 0)
 
 
+@pytest.mark.parametrize("nt", [33, 0, 38])
+@pytest.mark.parametrize("bt", [False, True], ids=["kn", "nk"])
+def test_grouped_store_policies(mkp, bt, nt):
+    """Every micro-kernel over vector-aligned groups under the default
+    C-store policy (33: streaming stores where C is 128-byte aligned with a
+    leading dimension of 32 floats), plain stores (0), and streaming stores
+    with shared-level write-through of split-K partials (38); one split and
+    three."""
+    rng = np.random.default_rng(800 + nt + bt)
+    names = [n for n in mkp.mkp_kernel_names() if n.endswith("_nk") == bt]
+    M, K = 200, 160
+    Ns = [64, 256, 96]
+    a = rand_bits(rng, (M, K))
+    ws = make_ws(rng, K, Ns, bt)
+    try:
+        mkp.mkp_set_option("nt_stores", nt)
+        for split in (1, 3):
+            mkp.mkp_set_option("force_splitk", split)
+            for name in names:
+                mkp.mkp_set_option("force_kernel", name)
+                run_grouped(mkp, a, ws, bt=bt, ldcs=list(Ns), what=f"{name} s={split} nt={nt}")
+    finally:
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("force_splitk", 0)
+        mkp.mkp_set_option("nt_stores", 33)
+
+
 @pytest.mark.parametrize("s", [2, 8])
 def test_grouped_splitk(mkp, s):
     rng = np.random.default_rng(300 + s)
