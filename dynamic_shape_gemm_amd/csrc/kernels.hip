@@ -438,9 +438,14 @@ struct DmaOffsets {
                 n = min(n, c.Nr - 1);
                 b[i] = real ? (uint32_t)(n * c.ldb + col) : 0u;
             } else {
+                // chunks past the tile's last column repeat the last one
+                // that holds a valid column; when N % 8 != 0 that chunk also
+                // holds up to 7 columns past N, inside the same 16-byte block
+                // as a valid one (so on a page the operand occupies), and they
+                // feed only output columns >= N, which are never stored
                 int k, col;
                 slotB<T>(g * 64 + lane, k, col);
-                col = min(col, c.Nr - 8);
+                col = min(col, (c.Nr - 1) & ~7);
                 b[i] = real ? (uint32_t)(k * c.ldb + col) : 0u;
             }
         }
@@ -795,11 +800,9 @@ __device__ __forceinline__ void tile_task(KArgs args, int bid, int nblk, lds_t* 
     c.vecA = args.flags & KF_VEC_A;
     c.vecB = args.flags & KF_VEC_B;
     const int nsteps = (c.kend - kbeg + T::BK - 1) / T::BK;
-    // direct loads need 16-byte aligned rows, 32-bit tile offsets (host
+    // direct loads need 16-byte aligned rows and 32-bit tile offsets (host
     // clears the vector flags for leading dimensions too large for them)
-    // and, on the last tile column, N a multiple of 8
-    const bool dma_tile = c.vecA && c.vecB && (c.Nr >= T::BN || (args.N & 7) == 0) &&
-                          (!T::CONV || (args.flags & KF_CONV_DMA));
+    const bool dma_tile = c.vecA && c.vecB && (!T::CONV || (args.flags & KF_CONV_DMA));
     const int dma_steps = dma_tile ? (c.kend - kbeg) / T::BK : 0;   // full steps
 
     DmaOffsets<T> dma;
@@ -1200,7 +1203,7 @@ __device__ __forceinline__ void wsplit_task(KArgs args, int bid, int nblk, lds_t
     c.vecA = args.flags & KF_VEC_A;
     c.vecB = args.flags & KF_VEC_B;
     const int nchunks = (c.kend - kbeg + 63) / 64;
-    const bool dma_tile = c.vecA && c.vecB && (c.Nr >= W::BN || (args.N & 7) == 0);
+    const bool dma_tile = c.vecA && c.vecB;
     const int dma_chunks = dma_tile ? (c.kend - kbeg) / 64 : 0;   // full chunks
     const int mine = nchunks > wave ? (nchunks - wave + W::KW - 1) / W::KW : 0;
 

@@ -97,6 +97,26 @@ def test_each_kernel_forced(mkp, split):
         mkp.mkp_set_option("force_splitk", 0)
 
 
+@pytest.mark.parametrize("split", [1, 3])
+def test_each_kernel_forced_padded_b(mkp, split):
+    """Every K x N micro-kernel where N is not a multiple of 8 but B's rows
+    are 16-byte aligned (ldb = N rounded up to 8, the padding NaN): the last
+    tile column takes the direct loads, whose last chunk of each B row
+    reaches past N, and none of that may reach C."""
+    rng = np.random.default_rng(40 + split)
+    try:
+        mkp.mkp_set_option("force_splitk", split)
+        for name in [n for n in mkp.mkp_kernel_names() if not n.endswith("_nk")]:
+            mkp.mkp_set_option("force_kernel", name)
+            for (M, N, K) in ((129, 250, 200), (257, 385, 130), (65, 1001, 256), (16, 7, 64)):
+                ldb = (N + 7) // 8 * 8
+                run_case(mkp, rand_bits(rng, (M, K)), rand_bits(rng, (K, N)), ldb=ldb,
+                         what=f"{name} s={split} padded B")
+    finally:
+        mkp.mkp_set_option("force_kernel", "")
+        mkp.mkp_set_option("force_splitk", 0)
+
+
 @pytest.mark.parametrize("nt", [0, 2, 38])
 def test_each_kernel_store_policies(mkp, nt):
     """Every micro-kernel under the C-store policies other than the default:
