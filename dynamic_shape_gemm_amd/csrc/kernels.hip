@@ -1692,7 +1692,10 @@ using V_32x128 = Tile<32, 128, 64, 1, 4, 4, false, true, true>;
 using V_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true, true>;
 using V_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true, true>;
 using V_32x64 = Tile<32, 64, 64, 2, 2, 4, false, true, true>;
-using V_128x128x4 = Tile<128, 128, 64, 4, 2, 4, false, true, true>;
+// (the convolution form keeps four waves of 64 x 64: with eight, every wave
+// repeats the filter-tap bookkeeping of the gather, and the 3 x 3 layers ran
+// 8-14 % slower)
+using V_128x128x4 = Tile<128, 128, 64, 2, 2, 4, false, true, true>;
 using V_256x256w4 = Tile<256, 256, 64, 2, 2, 2, false, true, true>;
 using V_64x64x2 = Tile<64, 64, 64, 2, 2, 2, false, true, true>;
 using V_64x128x2 = Tile<64, 128, 64, 2, 2, 2, false, true, true>;
