@@ -1616,6 +1616,13 @@ using U_128x128 = Tile<128, 128, 64, 2, 2, 2, false, true>;
 using U_128x64 = Tile<128, 64, 64, 2, 2, 3, false, true>;
 using U_64x128 = Tile<64, 128, 64, 2, 2, 3, false, true>;
 using U_64x64 = Tile<64, 64, 64, 2, 2, 4, false, true>;
+// the single-kernel 64 x 128 tile runs eight waves of 32 x 32 (2 x 4): 4-26 %
+// faster than four waves of 32 x 64 on the shapes it serves, most on few
+// tiles and on one-step (K = 64) batches; the two-tile kernels keep the
+// four-wave form, the workgroup size of their 128 x 128 partner (the 64 x 64
+// tile lost 20-28 % with eight waves and keeps four)
+using T_64x128w8 = Tile<64, 128, 64, 2, 4, 3>;
+using U_64x128w8 = Tile<64, 128, 64, 2, 4, 3, false, true>;
 using U_32x128 = Tile<32, 128, 64, 1, 4, 4, false, true>;
 using U_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true>;
 using U_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true>;
@@ -1641,7 +1648,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m128n256k64", T_128x256),
     MKP_KERNEL("m128n128k64", T_128x128),
     MKP_KERNEL("m128n64k64", T_128x64),
-    MKP_KERNEL("m64n128k64", T_64x128),
+    MKP_KERNEL("m64n128k64", T_64x128w8),
     MKP_KERNEL("m64n64k64", T_64x64),
     MKP_KERNEL("m32n128k64", T_32x128),
     MKP_KERNEL("m16n128k64", T_16x128),
@@ -1661,7 +1668,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m128n256k64_nk", U_128x256),
     MKP_KERNEL("m128n128k64_nk", U_128x128),
     MKP_KERNEL("m128n64k64_nk", U_128x64),
-    MKP_KERNEL("m64n128k64_nk", U_64x128),
+    MKP_KERNEL("m64n128k64_nk", U_64x128w8),
     MKP_KERNEL("m64n64k64_nk", U_64x64),
     MKP_KERNEL("m32n128k64_nk", U_32x128),
     MKP_KERNEL("m16n128k64_nk", U_16x128),
