@@ -1623,6 +1623,15 @@ using U_64x64 = Tile<64, 64, 64, 2, 2, 4, false, true>;
 // tile lost 20-28 % with eight waves and keeps four)
 using T_64x128w8 = Tile<64, 128, 64, 2, 4, 3>;
 using U_64x128w8 = Tile<64, 128, 64, 2, 4, 3, false, true>;
+// likewise the single-kernel 128 x 64 tile (eight waves of 32 x 32, 4 x 2:
+// 4-10 % faster), and the K x N two-stage 64 x 128 and 128 x 64 tiles (even
+// to 5 % faster on GEMMs, 14-17 % on one-step K = 64 batches; their N x K
+// forms gained nothing and keep four waves, as does the two-stage 64 x 64
+// tile, 6-43 % slower with eight)
+using T_128x64w8 = Tile<128, 64, 64, 4, 2, 3>;
+using U_128x64w8 = Tile<128, 64, 64, 4, 2, 3, false, true>;
+using T_64x128x2w8 = Tile<64, 128, 64, 2, 4, 2>;
+using T_128x64x2w8 = Tile<128, 64, 64, 4, 2, 2>;
 using U_32x128 = Tile<32, 128, 64, 1, 4, 4, false, true>;
 using U_16x128 = Tile<16, 128, 64, 1, 4, 4, false, true>;
 using U_16x256 = Tile<16, 256, 64, 1, 4, 4, false, true>;
@@ -1647,7 +1656,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m256n128k64", T_256x128),
     MKP_KERNEL("m128n256k64", T_128x256),
     MKP_KERNEL("m128n128k64", T_128x128),
-    MKP_KERNEL("m128n64k64", T_128x64),
+    MKP_KERNEL("m128n64k64", T_128x64w8),
     MKP_KERNEL("m64n128k64", T_64x128w8),
     MKP_KERNEL("m64n64k64", T_64x64),
     MKP_KERNEL("m32n128k64", T_32x128),
@@ -1657,8 +1666,8 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m128n128k64x4", T_128x128x4),
     MKP_KERNEL("m256n256k64w4", T_256x256w4),
     MKP_KERNEL("m64n64k64x2", T_64x64x2),
-    MKP_KERNEL("m64n128k64x2", T_64x128x2),
-    MKP_KERNEL("m128n64k64x2", T_128x64x2),
+    MKP_KERNEL("m64n128k64x2", T_64x128x2w8),
+    MKP_KERNEL("m128n64k64x2", T_128x64x2w8),
     MKP_WSPLIT("m16n64k256", W_16x64),
     MKP_WSPLIT("m32n64k256", W_32x64),
     MKP_WSPLIT("m64n64k256", W_64x64),
@@ -1667,7 +1676,7 @@ const KernelInfo g_kernels[] = {
     MKP_KERNEL("m256n128k64_nk", U_256x128),
     MKP_KERNEL("m128n256k64_nk", U_128x256),
     MKP_KERNEL("m128n128k64_nk", U_128x128),
-    MKP_KERNEL("m128n64k64_nk", U_128x64),
+    MKP_KERNEL("m128n64k64_nk", U_128x64w8),
     MKP_KERNEL("m64n128k64_nk", U_64x128w8),
     MKP_KERNEL("m64n64k64_nk", U_64x64),
     MKP_KERNEL("m32n128k64_nk", U_32x128),
