@@ -168,9 +168,10 @@ def test_plan_time_is_microseconds(mkp):
     ts = []
     rng = np.random.default_rng(6)
     for _ in range(50):
-        p = mkp.mkp_plan_describe(1, int(rng.integers(1, 8192)), int(rng.integers(1, 8192)),
-                                  int(rng.integers(1, 8192)))
-        ts.append(p["plan_us"])
+        shape = (int(rng.integers(1, 8192)), int(rng.integers(1, 8192)), int(rng.integers(1, 8192)))
+        # the fastest of three searches of the shape: other load on the host
+        # only ever adds to a search's time
+        ts.append(min(mkp.mkp_plan_describe(1, *shape)["plan_us"] for _ in range(3)))
     # the page reports 2 us per shape; this host is slower and unpinned: report, bound loosely
     print(f"median plan time {statistics.median(ts):.1f} us")
     assert statistics.median(ts) < 1000
